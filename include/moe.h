@@ -1,0 +1,175 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) MoE expert layer with Split-LoRA.
+ *
+ * Three calls make up one training step of the layer:
+ *
+ *   moe_route  top-k routing and expert grouping. The Unsloth x NVIDIA blog
+ *              (d9249.github.io, section "core idea / structure / how it
+ *              works", MoE routing paragraph) replaces a per-expert where()
+ *              scan with one flatten, stable sort by expert id, bincount and
+ *              offset slice; this call produces exactly those four things
+ *              (topk_idx flattened, sorted_slot, counts, offsets) on the GPU,
+ *              with at most one device->host copy (the counts, optional).
+ *   moe_fwd    the grouped expert MLP: one grouped GEMM over all experts
+ *              (Unsloth 2026 wiki chapter, "Optimisation 3: grouped_mm and
+ *              Split-LoRA in MoE training", grouped_mm subsection), SwiGLU
+ *              h = silu(x W_g^T) * (x W_u^T), y = h W_d^T, each projection
+ *              with Split-LoRA (same chapter, Split-LoRA subsection): the
+ *              frozen W is applied and s * (x A^T) B^T is added, W + s B A is
+ *              never formed; then the combine out[t] = sum_j w[t,j] y[t,j].
+ *   moe_bwd    the backward with base W frozen: dX, dA and dB of gate, up and
+ *              down, and optionally the gradient of the combine weights and
+ *              its chain through the top-k softmax into the logits.
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless marked (host). All tensors are
+ *    row-major and contiguous. Device pointers must be 16-byte aligned.
+ *  - Weights use the nn.Linear orientation [out, in], stacked over experts:
+ *      w_gate, w_up [E,F,d]   w_down [E,d,F]
+ *      a_gate, a_up [E,r,d]   b_gate, b_up [E,F,r]   a_down [E,r,F]   b_down [E,d,r]
+ *  - A "slot" is q = t*k + j (token t, its j-th choice); S = T*k slots. A
+ *    "row" p is a slot's position in expert-grouped order; expert e owns rows
+ *    offsets[e] .. offsets[e+1]-1, in increasing token order.
+ *  - dtype (moe_problem_t.dtype) applies to x, the weights, out, dout, dx and
+ *    the activations kept in `saved`. logits, topk_w, LoRA gradients,
+ *    d_topk_w and d_logits are always float32; indices are int32.
+ *  - The caller owns every buffer, including workspaces (size them with the
+ *    *_workspace queries) and `saved`. The library allocates no device
+ *    memory, frees nothing and keeps no pointer after a call returns.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream). Only moe_route with a non-NULL host_counts blocks the host
+ *    (one device->host copy and a stream synchronisation). moe_fwd and
+ *    moe_bwd never synchronise.
+ *  - Errors: arguments are checked on the host before anything is enqueued;
+ *    on any error nothing is launched and outputs are untouched. MOE_E_HIP
+ *    means a HIP call failed after checks passed (outputs then undefined).
+ *    Nothing is printed and no exception crosses the ABI.
+ *  - Limits: 0 <= T; 1 <= k <= E <= 1024; d, F, r >= 8 and multiples of 8;
+ *    T*k*max(d,2F) < 2^31. Logits must be finite (NaN/Inf: undefined order).
+ *  - Gradient outputs are overwritten, never accumulated into.
+ *  - Calls on different streams may run concurrently if they share no
+ *    buffers (workspaces included). The library has no global state.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_ARG = 1,         /* bad dimension, NULL or misaligned pointer */
+    MOE_E_UNSUPPORTED = 2, /* valid but outside the limits above */
+    MOE_E_WORKSPACE = 3,   /* workspace smaller than the *_workspace query */
+    MOE_E_HIP = 4          /* a HIP runtime call failed */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef struct {
+    int32_t T;          /* tokens */
+    int32_t d;          /* model width */
+    int32_t E;          /* experts */
+    int32_t k;          /* experts per token */
+    int32_t F;          /* expert FFN width */
+    int32_t r;          /* LoRA rank */
+    float lora_scale;   /* s = alpha / r */
+    moe_dtype_t dtype;  /* storage of x, W, A, B, activations */
+} moe_problem_t;
+
+typedef struct {
+    int32_t *topk_idx;     /* [T,k]  expert of each slot, j-th best first        */
+    float *topk_w;         /* [T,k]  softmax over the k selected logits          */
+    int32_t *counts;       /* [E]    slots per expert (bincount)                 */
+    int32_t *offsets;      /* [E+1]  exclusive prefix of counts; offsets[E] = S  */
+    int32_t *sorted_slot;  /* [S]    row p -> slot q (stable sort by expert id)  */
+    int32_t *slot_row;     /* [S]    slot q -> row p (inverse permutation)       */
+} moe_routing_t;
+
+typedef struct {
+    const void *w_gate, *w_up, *w_down;              /* frozen base weights      */
+    const void *a_gate, *b_gate, *a_up, *b_up;       /* LoRA factors, gate / up  */
+    const void *a_down, *b_down;                     /* LoRA factors, down       */
+} moe_weights_t;
+
+typedef struct {
+    float *da_gate, *db_gate;   /* [E,r,d], [E,F,r] */
+    float *da_up, *db_up;       /* [E,r,d], [E,F,r] */
+    float *da_down, *db_down;   /* [E,r,F], [E,d,r] */
+} moe_lora_grads_t;
+
+/* Optional per-kernel timing: if a moe_trace_t is passed and start[i] and
+ * stop[i] are both non-NULL hipEvent_t handles, the call records start[i]
+ * before and stop[i] after kernel i on `stream`. Indices: */
+enum {
+    MOE_K_ROUTE_TOPK = 0,   /* top-k + softmax + per-block expert histogram */
+    MOE_K_ROUTE_SCAN,       /* exclusive scan -> counts, offsets, bases     */
+    MOE_K_ROUTE_SCATTER,    /* stable scatter -> sorted_slot, slot_row      */
+    MOE_K_PROJ_GU,          /* LoRA A projection of x (gate|up)             */
+    MOE_K_GATEUP,           /* grouped GEMM gate/up + LoRA + SwiGLU         */
+    MOE_K_PROJ_D,           /* LoRA A projection of h (down)                */
+    MOE_K_DOWN,             /* grouped GEMM down + LoRA                     */
+    MOE_K_COMBINE,          /* weighted combine -> out                      */
+    MOE_K_ROUTER_GRAD,      /* d_topk_w, d_logits                           */
+    MOE_K_PROJ_DOUT,        /* dout B_down projection                       */
+    MOE_K_DOWN_BWD,         /* grouped GEMM dH + LoRA + SwiGLU backward     */
+    MOE_K_PROJ_DGU,         /* dG B_gate | dU B_up projection               */
+    MOE_K_GATEUP_BWD,       /* grouped GEMM dXp + LoRA                      */
+    MOE_K_DX_COMBINE,       /* dX gather-sum                                */
+    MOE_K_LORA_GRAD,        /* all LoRA weight-gradient kernels             */
+    MOE_K_COUNT
+};
+typedef struct {
+    void *start[MOE_K_COUNT];  /* hipEvent_t or NULL */
+    void *stop[MOE_K_COUNT];   /* hipEvent_t or NULL */
+} moe_trace_t;
+
+/* Workspace sizes in bytes (0 is a valid answer). NULL or invalid problem -> 0. */
+size_t moe_route_workspace(const moe_problem_t *pb);
+size_t moe_fwd_workspace(const moe_problem_t *pb, int training, int keep_expert_out);
+size_t moe_bwd_workspace(const moe_problem_t *pb);
+
+/* Bytes of the `saved` buffer that moe_fwd fills for moe_bwd. Layout, each
+ * part starting on a 256-byte boundary: G, U, H [S,F] dtype; Zgu [S,2r]
+ * float32 (x A_gate^T | x A_up^T); Zd [S,r] float32 (h A_down^T); and, if
+ * keep_expert_out, Y [S,d] dtype (expert outputs, needed for d_topk_w).
+ * All indexed by row p. */
+size_t moe_saved_bytes(const moe_problem_t *pb, int keep_expert_out);
+
+/* Routing. logits [T,E] float32 -> rt (all six arrays written).
+ * host_counts: (host) int32[E] that receives counts, or NULL; when non-NULL
+ * the call copies counts to it and synchronises `stream` before returning:
+ * the one device->host crossing of the layer. */
+moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt,
+                       int32_t *host_counts, void *ws, size_t ws_bytes, void *stream,
+                       const moe_trace_t *trace);
+
+/* Forward. x [T,d] -> out [T,d]. saved: NULL for inference (no backward
+ * possible), else moe_saved_bytes(pb, keep_expert_out) bytes that moe_bwd
+ * reads. ws: moe_fwd_workspace(pb, saved != NULL, keep_expert_out) bytes. */
+moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t *rt,
+                     const moe_weights_t *w, void *out, void *saved, int keep_expert_out,
+                     void *ws, size_t ws_bytes, void *stream, const moe_trace_t *trace);
+
+/* Backward. x and dout [T,d]; saved as filled by moe_fwd for the same x,
+ * routing and weights. Writes dx [T,d] and all six LoRA gradients. d_topk_w
+ * [T,k] and d_logits [T,E] are optional (NULL to skip) and need saved to
+ * hold Y (keep_expert_out = 1 in moe_fwd; pass the same flag here). */
+moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout,
+                     const moe_routing_t *rt, const moe_weights_t *w, const void *saved,
+                     int keep_expert_out, void *dx, const moe_lora_grads_t *grads,
+                     float *d_topk_w, float *d_logits, void *ws, size_t ws_bytes,
+                     void *stream, const moe_trace_t *trace);
+
+/* Static string naming a status code. */
+const char *moe_status_str(moe_status_t st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,245 @@
+"""Python binding of libmoe.so, the gfx950 MoE expert layer with Split-LoRA.
+
+Argument marshalling only: every step of routing, forward and backward runs
+in the library's HIP kernels (declared in ``include/moe.h``). PyTorch is
+used for device memory and streams. There is no fallback: if the library
+is missing the import fails.
+
+The three calls keep the C names:
+
+    moe_route(pb, logits, rt, host_counts=None, ws=None, stream=None, trace=None)
+    moe_fwd(pb, x, rt, w, out, saved=None, keep_expert_out=False, ws=None, ...)
+    moe_bwd(pb, x, dout, rt, w, saved, keep_expert_out, dx, grads, d_topk_w=None,
+            d_logits=None, ws=None, ...)
+
+Tensors may be torch tensors (their data_ptr() is passed) or raw integer
+device addresses. ``stream`` is a torch.cuda.Stream, a raw hipStream_t int or
+None for torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import LIB_PATH, build  # noqa: F401
+
+MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+KERNELS = ["route_topk", "route_scan", "route_scatter", "proj_gu", "gateup", "proj_d", "down",
+           "combine", "router_grad", "proj_dout", "down_bwd", "proj_dgu", "gateup_bwd",
+           "dx_combine", "lora_grad"]
+MOE_K_COUNT = len(KERNELS)
+
+EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe_saved_bytes",
+           "moe_route", "moe_fwd", "moe_bwd", "moe_status_str"]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("F", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("lora_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+    @classmethod
+    def from_config(cls, cfg, T=None):
+        return cls(cfg.T if T is None else T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.r, cfg.s,
+                   MOE_BF16 if cfg.dtype == "bf16" else MOE_F32)
+
+    @property
+    def S(self):
+        return self.T * self.k
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "counts", "offsets", "sorted_slot", "slot_row")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down",
+                 "b_down")]
+
+
+class LoraGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("da_gate", "db_gate", "da_up", "db_up", "da_down", "db_down")]
+
+
+class Trace(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p * MOE_K_COUNT), ("stop", ctypes.c_void_p * MOE_K_COUNT)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (or "
+                      "python -m moe_layer_lora_amd._build) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.POINTER
+_vp, _sz, _i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_lib.moe_route_workspace.argtypes = [_P(Problem)]
+_lib.moe_fwd_workspace.argtypes = [_P(Problem), _i32, _i32]
+_lib.moe_bwd_workspace.argtypes = [_P(Problem)]
+_lib.moe_saved_bytes.argtypes = [_P(Problem), _i32]
+for _f in (_lib.moe_route_workspace, _lib.moe_fwd_workspace, _lib.moe_bwd_workspace,
+           _lib.moe_saved_bytes):
+    _f.restype = _sz
+_lib.moe_route.argtypes = [_P(Problem), _vp, _P(Routing), _vp, _vp, _sz, _vp, _P(Trace)]
+_lib.moe_fwd.argtypes = [_P(Problem), _vp, _P(Routing), _P(Weights), _vp, _vp, _i32, _vp, _sz,
+                         _vp, _P(Trace)]
+_lib.moe_bwd.argtypes = [_P(Problem), _vp, _vp, _P(Routing), _P(Weights), _vp, _i32, _vp,
+                         _P(LoraGrads), _vp, _vp, _vp, _sz, _vp, _P(Trace)]
+for _f in (_lib.moe_route, _lib.moe_fwd, _lib.moe_bwd):
+    _f.restype = _i32
+_lib.moe_status_str.argtypes = [_i32]
+_lib.moe_status_str.restype = ctypes.c_char_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {moe_status_str(status)} (status {status})")
+
+
+def lib():
+    return _lib
+
+
+def moe_status_str(st: int) -> str:
+    return _lib.moe_status_str(st).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t):
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        raise TypeError("pass a workspace tensor (its size is needed), not a raw address")
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _struct(cls, d):
+    return cls(*[_ptr(d[n]) for n, _ in cls._fields_])
+
+
+def route_workspace(pb: Problem) -> int:
+    return _lib.moe_route_workspace(ctypes.byref(pb))
+
+
+def fwd_workspace(pb: Problem, training: bool, keep_expert_out: bool) -> int:
+    return _lib.moe_fwd_workspace(ctypes.byref(pb), int(training), int(keep_expert_out))
+
+
+def bwd_workspace(pb: Problem) -> int:
+    return _lib.moe_bwd_workspace(ctypes.byref(pb))
+
+
+def saved_bytes(pb: Problem, keep_expert_out: bool) -> int:
+    return _lib.moe_saved_bytes(ctypes.byref(pb), int(keep_expert_out))
+
+
+def _check(st, what):
+    if st != MOE_OK:
+        raise MoeError(st, what)
+
+
+def moe_route(pb, logits, rt: dict, host_counts=None, ws=None, stream=None, trace=None):
+    """rt: dict of the six routing tensors; host_counts: CPU int32 tensor/array or None."""
+    hc = None
+    if host_counts is not None:
+        hc = host_counts.ctypes.data if hasattr(host_counts, "ctypes") else host_counts.data_ptr()
+    st = _lib.moe_route(ctypes.byref(pb), _ptr(logits), ctypes.byref(_struct(Routing, rt)), hc,
+                        _ptr(ws), _nbytes(ws), _stream(stream),
+                        ctypes.byref(trace) if trace is not None else None)
+    _check(st, "moe_route")
+
+
+def moe_fwd(pb, x, rt: dict, w: dict, out, saved=None, keep_expert_out=False, ws=None,
+            stream=None, trace=None):
+    st = _lib.moe_fwd(ctypes.byref(pb), _ptr(x), ctypes.byref(_struct(Routing, rt)),
+                      ctypes.byref(_struct(Weights, w)), _ptr(out), _ptr(saved),
+                      int(keep_expert_out), _ptr(ws), _nbytes(ws), _stream(stream),
+                      ctypes.byref(trace) if trace is not None else None)
+    _check(st, "moe_fwd")
+
+
+def moe_bwd(pb, x, dout, rt: dict, w: dict, saved, keep_expert_out, dx, grads: dict,
+            d_topk_w=None, d_logits=None, ws=None, stream=None, trace=None):
+    st = _lib.moe_bwd(ctypes.byref(pb), _ptr(x), _ptr(dout), ctypes.byref(_struct(Routing, rt)),
+                      ctypes.byref(_struct(Weights, w)), _ptr(saved), int(keep_expert_out),
+                      _ptr(dx), ctypes.byref(_struct(LoraGrads, grads)), _ptr(d_topk_w),
+                      _ptr(d_logits), _ptr(ws), _nbytes(ws), _stream(stream),
+                      ctypes.byref(trace) if trace is not None else None)
+    _check(st, "moe_bwd")
+
+
+# ---------------------------------------------------------------- allocation helpers
+def alloc_routing(pb: Problem, device):
+    import torch
+    T, E, k = pb.T, pb.E, pb.k
+    i32 = torch.int32
+    return {"topk_idx": torch.empty((T, k), dtype=i32, device=device),
+            "topk_w": torch.empty((T, k), dtype=torch.float32, device=device),
+            "counts": torch.empty(E, dtype=i32, device=device),
+            "offsets": torch.empty(E + 1, dtype=i32, device=device),
+            "sorted_slot": torch.empty(T * k, dtype=i32, device=device),
+            "slot_row": torch.empty(T * k, dtype=i32, device=device)}
+
+
+def alloc_bytes(n: int, device):
+    import torch
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+def alloc_grads(pb: Problem, device):
+    import torch
+    E, d, F, r = pb.E, pb.d, pb.F, pb.r
+    f = torch.float32
+    return {"da_gate": torch.empty((E, r, d), dtype=f, device=device),
+            "db_gate": torch.empty((E, F, r), dtype=f, device=device),
+            "da_up": torch.empty((E, r, d), dtype=f, device=device),
+            "db_up": torch.empty((E, F, r), dtype=f, device=device),
+            "da_down": torch.empty((E, r, F), dtype=f, device=device),
+            "db_down": torch.empty((E, d, r), dtype=f, device=device)}
+
+
+def saved_views(pb: Problem, saved, keep_expert_out: bool) -> dict:
+    """Typed views of the `saved` buffer (layout documented in moe.h)."""
+    import torch
+    S, F, r, d = pb.S, pb.F, pb.r, pb.d
+    dt = torch.bfloat16 if pb.dtype == MOE_BF16 else torch.float32
+    es = 2 if pb.dtype == MOE_BF16 else 4
+
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    out, o = {}, 0
+    for name, n, t, e in (("G", S * F, dt, es), ("U", S * F, dt, es), ("H", S * F, dt, es),
+                          ("Zgu", S * 2 * r, torch.float32, 4), ("Zd", S * r, torch.float32, 4)) + (
+            (("Y", S * d, dt, es),) if keep_expert_out else ()):
+        out[name] = saved[o:o + n * e].view(t)
+        o += al(n * e)
+    out["G"] = out["G"].view(S, F)
+    out["U"] = out["U"].view(S, F)
+    out["H"] = out["H"].view(S, F)
+    out["Zgu"] = out["Zgu"].view(S, 2 * r)
+    out["Zd"] = out["Zd"].view(S, r)
+    if keep_expert_out:
+        out["Y"] = out["Y"].view(S, d)
+    return out

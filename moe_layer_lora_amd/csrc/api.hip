@@ -1,0 +1,291 @@
+// api.hip - the C ABI declared in include/moe.h: argument checks, workspace
+// and saved-buffer layouts, and the launch sequence on the caller's stream.
+#include "moe.h"
+#include "kernels.hpp"
+
+#include <cmath>
+
+namespace {
+
+using moe::Dims;
+
+constexpr size_t kAlign = 256;
+size_t al(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+size_t esize(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks the problem description; MOE_OK if the library supports it.
+moe_status_t check_problem(const moe_problem_t *pb) {
+    if (!pb) return MOE_E_ARG;
+    if (pb->T < 0 || pb->E < 1 || pb->k < 1 || pb->k > pb->E || pb->d < 1 || pb->F < 1 || pb->r < 1)
+        return MOE_E_ARG;
+    if (pb->dtype != MOE_F32 && pb->dtype != MOE_BF16) return MOE_E_ARG;
+    if (!std::isfinite(pb->lora_scale)) return MOE_E_ARG;
+    if (pb->d % 8 || pb->F % 8 || pb->r % 8) return MOE_E_UNSUPPORTED;
+    if (pb->E > 1024 || pb->r > 256) return MOE_E_UNSUPPORTED;
+    const long long S = (long long)pb->T * pb->k;
+    const long long wide = pb->d > 2 * pb->F ? pb->d : 2LL * pb->F;
+    if (S * wide >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+    return MOE_OK;
+}
+
+Dims dims_of(const moe_problem_t *pb) {
+    return Dims{pb->T, pb->d, pb->E, pb->k, pb->F, pb->r, pb->lora_scale};
+}
+
+// ---- layouts -----------------------------------------------------------------
+struct RouteWs { size_t hist, base, total; };
+RouteWs route_ws(const moe_problem_t *pb) {
+    const size_t n = (size_t)pb->E * moe::route_nblk(pb->T, pb->E) * sizeof(int32_t);
+    RouteWs w;
+    w.hist = 0;
+    w.base = al(n);
+    w.total = w.base + al(n);
+    return w;
+}
+
+struct SavedLayout { size_t G, U, H, Zgu, Zd, Y, total; };
+SavedLayout saved_layout(const moe_problem_t *pb, int keep) {
+    const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
+    SavedLayout l;
+    size_t o = 0;
+    l.G = o; o += al(S * pb->F * es);
+    l.U = o; o += al(S * pb->F * es);
+    l.H = o; o += al(S * pb->F * es);
+    l.Zgu = o; o += al(S * 2 * pb->r * sizeof(float));
+    l.Zd = o; o += al(S * pb->r * sizeof(float));
+    l.Y = o; if (keep) o += al(S * pb->d * es);
+    l.total = o;
+    return l;
+}
+
+// forward workspace: what the forward needs that is not kept in `saved`
+struct FwdWs { size_t H, Zgu, Zd, Y, total; };
+FwdWs fwd_ws(const moe_problem_t *pb, int training, int keep) {
+    const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
+    FwdWs w{0, 0, 0, 0, 0};
+    size_t o = 0;
+    if (!training) {
+        w.H = o; o += al(S * pb->F * es);
+        w.Zgu = o; o += al(S * 2 * pb->r * sizeof(float));
+        w.Zd = o; o += al(S * pb->r * sizeof(float));
+    }
+    if (!training || !keep) { w.Y = o; o += al(S * pb->d * es); }
+    w.total = o;
+    return w;
+}
+
+struct BwdWs { size_t Pd, Pgu, dGU, dXp, partial, total; };
+BwdWs bwd_ws(const moe_problem_t *pb) {
+    const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
+    BwdWs w;
+    size_t o = 0;
+    w.Pd = o; o += al(S * pb->r * sizeof(float));
+    w.Pgu = o; o += al(S * 2 * pb->r * sizeof(float));
+    w.dGU = o; o += al(S * 2 * pb->F * es);
+    w.dXp = o; o += al(S * pb->d * es);
+    w.partial = o; o += al(moe::lora_grad_partial_bytes(dims_of(pb)));
+    w.total = o;
+    return w;
+}
+
+char *at(void *base, size_t off) { return static_cast<char *>(base) + off; }
+const char *at(const void *base, size_t off) { return static_cast<const char *>(base) + off; }
+
+// counts and offsets always; the per-slot arrays only when T > 0 (NULL is
+// accepted for an empty batch, where they have no elements)
+bool routing_ok(const moe_routing_t *rt, int T) {
+    if (!rt || !rt->counts || !rt->offsets || !aligned16(rt->counts) || !aligned16(rt->offsets)) return false;
+    const void *p[4] = {rt->topk_idx, rt->topk_w, rt->sorted_slot, rt->slot_row};
+    for (const void *q : p)
+        if ((T > 0 && !q) || !aligned16(q)) return false;
+    return true;
+}
+
+bool weights_ok(const moe_weights_t *w) {
+    if (!w) return false;
+    const void *p[9] = {w->w_gate, w->w_up, w->w_down, w->a_gate, w->b_gate, w->a_up, w->b_up, w->a_down, w->b_down};
+    for (const void *q : p)
+        if (!q || !aligned16(q)) return false;
+    return true;
+}
+
+bool grads_ok(const moe_lora_grads_t *g) {
+    if (!g) return false;
+    const void *p[6] = {g->da_gate, g->db_gate, g->da_up, g->db_up, g->da_down, g->db_down};
+    for (const void *q : p)
+        if (!q || !aligned16(q)) return false;
+    return true;
+}
+
+bool buf_ok(const void *p) { return p && aligned16(p); }
+
+moe::Trace to_trace(const moe_trace_t *t) {
+    moe::Trace tr{};
+    if (t)
+        for (int i = 0; i < MOE_K_COUNT; ++i) {
+            tr.start[i] = static_cast<hipEvent_t>(t->start[i]);
+            tr.stop[i] = static_cast<hipEvent_t>(t->stop[i]);
+        }
+    return tr;
+}
+
+struct Rec {  // event pair around one launch, if the caller asked for it
+    const moe::Trace *tr; int id; hipStream_t st;
+    Rec(const moe::Trace *t, int i, hipStream_t s) : tr(t), id(i), st(s) {
+        if (tr && tr->start[id] && tr->stop[id]) (void)hipEventRecord(tr->start[id], st);
+    }
+    ~Rec() { if (tr && tr->start[id] && tr->stop[id]) (void)hipEventRecord(tr->stop[id], st); }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(moe_status_t st) {
+    switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_E_ARG: return "invalid argument";
+    case MOE_E_UNSUPPORTED: return "unsupported problem";
+    case MOE_E_WORKSPACE: return "workspace too small";
+    case MOE_E_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t moe_route_workspace(const moe_problem_t *pb) {
+    return check_problem(pb) == MOE_OK ? route_ws(pb).total : 0;
+}
+
+size_t moe_fwd_workspace(const moe_problem_t *pb, int training, int keep_expert_out) {
+    return check_problem(pb) == MOE_OK ? fwd_ws(pb, training != 0, keep_expert_out != 0).total : 0;
+}
+
+size_t moe_bwd_workspace(const moe_problem_t *pb) {
+    return check_problem(pb) == MOE_OK ? bwd_ws(pb).total : 0;
+}
+
+size_t moe_saved_bytes(const moe_problem_t *pb, int keep_expert_out) {
+    return check_problem(pb) == MOE_OK ? saved_layout(pb, keep_expert_out != 0).total : 0;
+}
+
+moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt,
+                       int32_t *host_counts, void *ws, size_t ws_bytes, void *stream, const moe_trace_t *trace) {
+    moe_status_t st = check_problem(pb);
+    if (st != MOE_OK) return st;
+    if (!routing_ok(rt, pb->T)) return MOE_E_ARG;
+    if (pb->T > 0 && !buf_ok(logits)) return MOE_E_ARG;
+    const RouteWs w = route_ws(pb);
+    if (ws_bytes < w.total) return MOE_E_WORKSPACE;
+    if (w.total > 0 && !buf_ok(ws)) return MOE_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const moe::Trace tr = to_trace(trace);
+    int32_t *hist = reinterpret_cast<int32_t *>(at(ws, w.hist));
+    int32_t *base = reinterpret_cast<int32_t *>(at(ws, w.base));
+    hipError_t e;
+    {
+        Rec r(&tr, MOE_K_ROUTE_TOPK, s);
+        e = moe::launch_route_topk(logits, pb->T, pb->E, pb->k, rt->topk_idx, rt->topk_w, hist, s);
+    }
+    if (e != hipSuccess) return MOE_E_HIP;
+    {
+        Rec r(&tr, MOE_K_ROUTE_SCAN, s);
+        e = moe::launch_route_scan(hist, pb->T, pb->E, pb->k, base, rt->counts, rt->offsets, s);
+    }
+    if (e != hipSuccess) return MOE_E_HIP;
+    {
+        Rec r(&tr, MOE_K_ROUTE_SCATTER, s);
+        e = moe::launch_route_scatter(rt->topk_idx, base, pb->T, pb->E, pb->k, rt->sorted_slot, rt->slot_row, s);
+    }
+    if (e != hipSuccess) return MOE_E_HIP;
+    if (host_counts) {
+        if (hipMemcpyAsync(host_counts, rt->counts, (size_t)pb->E * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+                hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return MOE_E_HIP;
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t *rt, const moe_weights_t *w,
+                     void *out, void *saved, int keep_expert_out, void *ws, size_t ws_bytes, void *stream,
+                     const moe_trace_t *trace) {
+    moe_status_t st = check_problem(pb);
+    if (st != MOE_OK) return st;
+    if (!routing_ok(rt, pb->T) || !weights_ok(w)) return MOE_E_ARG;
+    if (pb->T > 0 && (!buf_ok(x) || !buf_ok(out))) return MOE_E_ARG;
+    if (saved && !aligned16(saved)) return MOE_E_ARG;
+    const bool training = saved != nullptr, keep = keep_expert_out != 0;
+    const FwdWs fw = fwd_ws(pb, training, keep);
+    if (ws_bytes < fw.total) return MOE_E_WORKSPACE;
+    if (fw.total > 0 && !buf_ok(ws)) return MOE_E_ARG;
+    const SavedLayout sl = saved_layout(pb, keep);
+    moe::FwdBufs b{};
+    b.x = x;
+    b.sorted_slot = rt->sorted_slot; b.offsets = rt->offsets; b.slot_row = rt->slot_row; b.topk_w = rt->topk_w;
+    b.wg = w->w_gate; b.wu = w->w_up; b.wd = w->w_down; b.ag = w->a_gate; b.bg = w->b_gate;
+    b.au = w->a_up; b.bu = w->b_up; b.ad = w->a_down; b.bd = w->b_down;
+    if (training) {
+        b.G = at(saved, sl.G); b.U = at(saved, sl.U); b.H = at(saved, sl.H);
+        b.Zgu = reinterpret_cast<float *>(at(saved, sl.Zgu));
+        b.Zd = reinterpret_cast<float *>(at(saved, sl.Zd));
+        b.Y = keep ? at(saved, sl.Y) : at(ws, fw.Y);
+    } else {
+        b.G = nullptr; b.U = nullptr; b.H = at(ws, fw.H);
+        b.Zgu = reinterpret_cast<float *>(at(ws, fw.Zgu));
+        b.Zd = reinterpret_cast<float *>(at(ws, fw.Zd));
+        b.Y = at(ws, fw.Y);
+    }
+    b.out = out;
+    const moe::Trace tr = to_trace(trace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Dims D = dims_of(pb);
+    const hipError_t e = pb->dtype == MOE_BF16 ? moe::run_fwd<moe::bf16_t>(D, b, s, trace ? &tr : nullptr)
+                                               : moe::run_fwd<float>(D, b, s, trace ? &tr : nullptr);
+    return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout, const moe_routing_t *rt,
+                     const moe_weights_t *w, const void *saved, int keep_expert_out, void *dx,
+                     const moe_lora_grads_t *grads, float *d_topk_w, float *d_logits, void *ws, size_t ws_bytes,
+                     void *stream, const moe_trace_t *trace) {
+    moe_status_t st = check_problem(pb);
+    if (st != MOE_OK) return st;
+    if (!routing_ok(rt, pb->T) || !weights_ok(w) || !grads_ok(grads) || !buf_ok(saved)) return MOE_E_ARG;
+    if (pb->T > 0 && (!buf_ok(x) || !buf_ok(dout) || !buf_ok(dx))) return MOE_E_ARG;
+    const bool keep = keep_expert_out != 0;
+    if ((d_topk_w || d_logits) && !keep) return MOE_E_ARG;
+    if ((d_topk_w && !aligned16(d_topk_w)) || (d_logits && !aligned16(d_logits))) return MOE_E_ARG;
+    const BwdWs bw = bwd_ws(pb);
+    if (ws_bytes < bw.total) return MOE_E_WORKSPACE;
+    if (!buf_ok(ws)) return MOE_E_ARG;
+    const SavedLayout sl = saved_layout(pb, keep);
+    moe::BwdBufs b{};
+    b.x = x; b.dout = dout;
+    b.sorted_slot = rt->sorted_slot; b.offsets = rt->offsets; b.slot_row = rt->slot_row; b.topk_idx = rt->topk_idx;
+    b.topk_w = rt->topk_w;
+    b.wg = w->w_gate; b.wu = w->w_up; b.wd = w->w_down; b.ag = w->a_gate; b.bg = w->b_gate;
+    b.au = w->a_up; b.bu = w->b_up; b.ad = w->a_down; b.bd = w->b_down;
+    b.G = at(saved, sl.G); b.U = at(saved, sl.U); b.H = at(saved, sl.H);
+    b.Y = keep ? at(saved, sl.Y) : nullptr;
+    b.Zgu = reinterpret_cast<const float *>(at(saved, sl.Zgu));
+    b.Zd = reinterpret_cast<const float *>(at(saved, sl.Zd));
+    b.Pd = reinterpret_cast<float *>(at(ws, bw.Pd));
+    b.Pgu = reinterpret_cast<float *>(at(ws, bw.Pgu));
+    b.dGU = at(ws, bw.dGU); b.dXp = at(ws, bw.dXp);
+    b.partial = reinterpret_cast<float *>(at(ws, bw.partial));
+    b.dx = dx;
+    b.da_g = grads->da_gate; b.db_g = grads->db_gate; b.da_u = grads->da_up; b.db_u = grads->db_up;
+    b.da_d = grads->da_down; b.db_d = grads->db_down;
+    b.d_topk_w = d_topk_w; b.d_logits = d_logits;
+    const moe::Trace tr = to_trace(trace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Dims D = dims_of(pb);
+    const hipError_t e = pb->dtype == MOE_BF16 ? moe::run_bwd<moe::bf16_t>(D, b, s, trace ? &tr : nullptr)
+                                               : moe::run_bwd<float>(D, b, s, trace ? &tr : nullptr);
+    return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+}  // extern "C"

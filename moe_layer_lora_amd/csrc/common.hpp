@@ -1,0 +1,164 @@
+// common.hpp - element types, MFMA fragments and the grouped-tile scheduler
+// shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// ---------------------------------------------------------------------------
+// Element traits. A "chunk" is 16 bytes: VEC elements. Both MFMA operands
+// are read from LDS one chunk per lane: lane l holds VEC consecutive k of
+// row (l % 32), at k offset (l / 32) * VEC within a k-group of 2*VEC.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static constexpr int VEC = 4;
+    __device__ static float load_f32(const float *p, int i) { return p[i]; }
+    __device__ static float to_f32(float v) { return v; }
+    __device__ static float from_f32(float v) { return v; }
+    // acc(32x32) += A(32 x 8) * B(8 x 32); the 8 k of a group are split as
+    // lane-half h holding k = 4h .. 4h+3; instruction i takes element i of
+    // both chunks, so it covers k in {i, 4+i}: the same k-permutation on both
+    // operands, hence the exact sum over the group.
+    __device__ static void mma(f32x16_t &acc, const chunk_t &a, const chunk_t &b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]), acc, 0, 0, 0);
+    }
+    // VEC fp32 values -> one chunk
+    __device__ static chunk_t pack(const float *v) {
+        return chunk_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                       __float_as_uint(v[3])};
+    }
+};
+
+template <> struct Elem<bf16_t> {
+    static constexpr int VEC = 8;
+    __device__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+    __device__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+    // acc(32x32) += A(32 x 16) * B(16 x 32), one v_mfma_f32_32x32x16_bf16
+    __device__ static void mma(f32x16_t &acc, const chunk_t &a, const chunk_t &b) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+    }
+    __device__ static chunk_t pack(const float *v) {
+        chunk_t c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            c[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+        return c;
+    }
+};
+
+// unpack one chunk into VEC floats
+template <typename T> __device__ __forceinline__ void unpack(const chunk_t &c, float *v);
+template <> __device__ __forceinline__ void unpack<float>(const chunk_t &c, float *v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(c[i]);
+}
+template <> __device__ __forceinline__ void unpack<bf16_t>(const chunk_t &c, float *v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(c[i] << 16);
+        v[2 * i + 1] = __uint_as_float(c[i] & 0xffff0000u);
+    }
+}
+
+// Row and column of accumulator register i of a 32x32 MFMA tile held by `lane`.
+__device__ __forceinline__ int acc_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+// ---------------------------------------------------------------------------
+// Grouped-tile scheduler. Expert e owns rows offsets[e] .. offsets[e+1]-1,
+// cut into mt_e = ceil(n_e / BM) row tiles; each row tile is crossed with NT
+// column tiles. Work items are ordered expert-major, then column tile, then
+// row tile, so the row tiles that share one expert weight strip are
+// consecutive. Hardware hands workgroups to the 8 XCDs round-robin by block
+// id; the remap below gives each XCD a contiguous range of work items, so a
+// weight strip (and an expert's rows) is fetched into one XCD's L2 and
+// reused there. Empty experts own no work and their weights are never read.
+struct Tile {
+    int e;      // expert
+    int mt;     // row tile within the expert
+    int nt;     // column tile
+    int row0;   // first row p of the tile
+    int rows;   // valid rows in the tile (1..BM)
+    int gmt;    // row tile index over all experts (expert-major)
+};
+
+// s_start: __shared__ int[E+1] scratch. Returns false if block b has no work.
+template <int BM, int NTHREADS>
+__device__ bool schedule_tile(const int *__restrict__ offsets, int E, int NT, int b, int *s_start,
+                              Tile &tile) {
+    const int tid = threadIdx.x;
+    // per-expert row-tile counts, then an inclusive scan (E <= 1024)
+    for (int e = tid; e < E; e += NTHREADS) {
+        const int n = offsets[e + 1] - offsets[e];
+        s_start[e + 1] = (n + BM - 1) / BM;
+    }
+    if (tid == 0) s_start[0] = 0;
+    __syncthreads();
+    if (tid < kWave) {
+        // one wave scans sequential segments of up to 16 entries per lane
+        const int per = (E + kWave - 1) / kWave;
+        const int lo = 1 + tid * per, hi = min(E + 1, lo + per);
+        int sum = 0;
+        for (int i = lo; i < hi; ++i) sum += s_start[i];
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(incl, off, kWave);
+            if (tid >= off) incl += v;
+        }
+        int run = incl - sum;
+        for (int i = lo; i < hi; ++i) {
+            run += s_start[i];
+            s_start[i] = run;
+        }
+    }
+    __syncthreads();
+    const int total = s_start[E] * NT;
+    if (b >= total) return false;
+    // XCD-contiguous remap of block ids (a bijection on [0, total))
+    const int xcd = b & 7, local = b >> 3;
+    const int q = total >> 3, rem = total & 7;
+    const int lam = xcd * q + min(xcd, rem) + local;
+    // find expert: largest e with s_start[e] * NT <= lam
+    int lo = 0, hi = E;  // invariant: s_start[lo]*NT <= lam < s_start[hi]*NT
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_start[mid] * NT <= lam) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int mte = s_start[e + 1] - s_start[e];
+    const int rem2 = lam - s_start[e] * NT;
+    tile.e = e;
+    tile.nt = rem2 / mte;
+    tile.mt = rem2 % mte;
+    tile.row0 = offsets[e] + tile.mt * BM;
+    tile.rows = min(BM, offsets[e + 1] - tile.row0);
+    tile.gmt = s_start[e] + tile.mt;
+    return true;
+}
+
+// Upper bound on the number of row tiles over all experts (a launch size
+// chosen before the counts are known on the host).
+__host__ __device__ inline int max_row_tiles(int S, int E, int BM) { return (S + BM - 1) / BM + E; }
+
+}  // namespace moe

@@ -1,0 +1,70 @@
+// kernels.hpp - host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+
+struct Dims {
+    int T, d, E, k, F, r;
+    float s;  // LoRA scale
+    int S() const { return T * k; }
+};
+
+// ---- routing ---------------------------------------------------------------
+// tokens per routing block: keeps the [E x nblk] histogram at <= 64K entries
+int route_tokens_per_block(int T, int E);
+inline int route_nblk(int T, int E) {
+    const int tpb = route_tokens_per_block(T, E);
+    return T > 0 ? (T + tpb - 1) / tpb : 0;
+}
+hipError_t launch_route_topk(const float *logits, int T, int E, int k, int32_t *topk_idx, float *topk_w,
+                             int32_t *hist, hipStream_t st);
+hipError_t launch_route_scan(const int32_t *hist, int T, int E, int k, int32_t *base, int32_t *counts,
+                             int32_t *offsets, hipStream_t st);
+hipError_t launch_route_scatter(const int32_t *topk_idx, const int32_t *base, int T, int E, int k,
+                                int32_t *sorted_slot, int32_t *slot_row, hipStream_t st);
+
+// ---- forward / backward (T = float or bf16 bits) -----------------------------
+struct FwdBufs {
+    const void *x;
+    const int32_t *sorted_slot, *offsets, *slot_row;
+    const float *topk_w;
+    const void *wg, *wu, *wd, *ag, *bg, *au, *bu, *ad, *bd;
+    void *G, *U, *H;      // G, U may be null (inference)
+    float *Zgu, *Zd;      // [S,2r], [S,r]
+    void *Y;              // [S,d]
+    void *out;            // [T,d]
+};
+
+struct BwdBufs {
+    const void *x, *dout;
+    const int32_t *sorted_slot, *offsets, *slot_row, *topk_idx;
+    const float *topk_w;
+    const void *wg, *wu, *wd, *ag, *bg, *au, *bu, *ad, *bd;
+    const void *G, *U, *H, *Y;   // saved (Y may be null)
+    const float *Zgu, *Zd;       // saved
+    float *Pd, *Pgu;             // workspace [S,r], [S,2r]
+    void *dGU, *dXp;             // workspace [S,2F], [S,d]
+    float *partial;              // workspace for LoRA-gradient partial sums
+    void *dx;
+    float *da_g, *db_g, *da_u, *db_u, *da_d, *db_d;
+    float *d_topk_w, *d_logits;  // optional
+};
+
+// per-kernel timing events (hipEvent_t or null), indexed like MOE_K_*
+struct Trace {
+    hipEvent_t start[32], stop[32];
+};
+
+template <typename T> hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace *tr);
+template <typename T> hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace *tr);
+
+// bytes of LoRA-gradient partial sums the backward may need
+size_t lora_grad_partial_bytes(const Dims &D);
+
+}  // namespace moe

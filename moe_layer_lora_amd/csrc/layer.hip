@@ -1,0 +1,773 @@
+// layer.hip - expert-layer kernels on gfx950: grouped GEMMs with Split-LoRA,
+// SwiGLU epilogues, combines, router-weight gradient and LoRA weight
+// gradients, plus the forward / backward drivers.
+//
+// All experts run in ONE launch per projection (the grouped_mm form of the
+// Unsloth 2026 wiki chapter, "Optimisation 3: grouped_mm and Split-LoRA in
+// MoE training"): a block picks an (expert, row tile, column tile) from the
+// device-side offsets, so no per-expert launch and no host sync exist.
+// Split-LoRA (same chapter, Split-LoRA subsection): each projection runs the
+// frozen W first and adds s * (x A^T) B^T as a second K segment of the same
+// accumulation; W + s B A is never formed.
+#include "kernels.hpp"
+#include "gemm.hpp"
+#include "moe.h"
+
+#include <algorithm>
+
+namespace moe {
+
+constexpr int kMaxE = 1024;
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Main grouped-GEMM tile shapes.
+template <typename T> struct MainCfg;
+template <> struct MainCfg<bf16_t> { using type = GemmCfg<bf16_t, 128, 128, 32, 2, 2>; };
+template <> struct MainCfg<float> { using type = GemmCfg<float, 128, 128, 16, 2, 2>; };
+// Skinny projections (N = r or 2r) and LoRA weight gradients (N = r or 2r).
+template <typename T, int BN> struct SkinnyCfg;
+template <int BN> struct SkinnyCfg<bf16_t, BN> { using type = GemmCfg<bf16_t, 128, BN, 32, 4 / (BN / 32), BN / 32>; };
+template <int BN> struct SkinnyCfg<float, BN> { using type = GemmCfg<float, 128, BN, 16, 4 / (BN / 32), BN / 32>; };
+
+template <class Cfg> struct Smem {
+    __align__(16) typename Cfg::T a[2 * Cfg::A_ELEMS];
+    __align__(16) typename Cfg::T b[2 * Cfg::B_ELEMS];
+    int start[kMaxE + 1];
+};
+
+__device__ __forceinline__ int token_of(const int32_t *sorted_slot, int p, int k) { return sorted_slot[p] / k; }
+
+// ===========================================================================
+// Gate/up grouped GEMM: G = Xp W_g^T + s Zg B_g^T, U likewise, H = silu(G) U.
+// The B tile interleaves 32-column blocks of gate and up rows for the same f,
+// so each lane holds g and u of one element and the SwiGLU is fused.
+// ===========================================================================
+struct GateUpP {
+    const void *x, *wg, *wu, *bg, *bu;
+    const float *zgu;
+    const int32_t *sorted_slot, *offsets;
+    void *G, *U, *H;
+    int E, k, d, F, r;
+    float s;
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_gateup(GateUpP p) {
+    using T = typename Cfg::T;
+    __shared__ Smem<Cfg> sm;
+    constexpr int HALF = Cfg::BN / 2;
+    static_assert(Cfg::TN % 2 == 0, "gate/up pairs");
+    Tile tl;
+    if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(p.F, HALF), blockIdx.x, sm.start, tl)) return;
+    const int f_base = tl.nt * HALF;
+    const int nk0 = cdiv(p.d, Cfg::BK), nk = nk0 + cdiv(2 * p.r, Cfg::BK);
+
+    KLoader<Cfg, Cfg::BM, true> la;
+    la.K0 = p.d; la.K1 = 2 * p.r; la.nk0 = nk0; la.scale1 = p.s;
+#pragma unroll
+    for (int i = 0; i < la.PER; ++i) {
+        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
+        if (!la.active(i)) continue;
+        const int m = la.row_of(i);
+        if (m < tl.rows) {
+            const int pr = tl.row0 + m;
+            la.p0[i] = static_cast<const T *>(p.x) + (size_t)token_of(p.sorted_slot, pr, p.k) * p.d;
+            la.p1[i] = p.zgu + (size_t)pr * 2 * p.r;
+        }
+    }
+    KLoader<Cfg, Cfg::BN, false> lb;
+    lb.K0 = p.d; lb.K1 = 2 * p.r; lb.nk0 = nk0; lb.scale1 = 1.0f;
+#pragma unroll
+    for (int i = 0; i < lb.PER; ++i) {
+        lb.p0[i] = nullptr; lb.p1[i] = nullptr; lb.klo1[i] = 0; lb.khi1[i] = 0;
+        if (!lb.active(i)) continue;
+        const int n = lb.row_of(i);
+        const int wn = n / Cfg::WTN, ni = (n % Cfg::WTN) / 32;
+        const int f = f_base + wn * (Cfg::WTN / 2) + (ni / 2) * 32 + (n % 32);
+        const bool gate = (ni & 1) == 0;
+        if (f < p.F) {
+            const size_t row = (size_t)tl.e * p.F + f;
+            lb.p0[i] = static_cast<const T *>(gate ? p.wg : p.wu) + row * p.d;
+            lb.p1[i] = static_cast<const T *>(gate ? p.bg : p.bu) + row * p.r;
+            lb.klo1[i] = gate ? 0 : p.r;
+            lb.khi1[i] = gate ? p.r : 2 * p.r;
+        }
+    }
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    T *G = static_cast<T *>(p.G), *U = static_cast<T *>(p.U), *H = static_cast<T *>(p.H);
+#pragma unroll
+    for (int mi = 0; mi < Cfg::TM; ++mi)
+#pragma unroll
+        for (int c = 0; c < Cfg::TN / 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = wm * Cfg::WTM + mi * 32 + acc_row(i, lane);
+                const int f = f_base + wn * (Cfg::WTN / 2) + c * 32 + acc_col(lane);
+                if (m < tl.rows && f < p.F) {
+                    const float g = acc[mi][2 * c][i], u = acc[mi][2 * c + 1][i];
+                    const size_t o = (size_t)(tl.row0 + m) * p.F + f;
+                    if (G) G[o] = Elem<T>::from_f32(g);
+                    if (U) U[o] = Elem<T>::from_f32(u);
+                    H[o] = Elem<T>::from_f32(g / (1.0f + expf(-g)) * u);
+                }
+            }
+}
+
+// ===========================================================================
+// Down grouped GEMM: Y = H W_d^T + s Zd B_d^T.
+// ===========================================================================
+struct DownP {
+    const void *H, *wd, *bd;
+    const float *zd;
+    const int32_t *offsets;
+    void *Y;
+    int E, d, F, r;
+    float s;
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_down(DownP p) {
+    using T = typename Cfg::T;
+    __shared__ Smem<Cfg> sm;
+    Tile tl;
+    if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(p.d, Cfg::BN), blockIdx.x, sm.start, tl)) return;
+    const int n_base = tl.nt * Cfg::BN;
+    const int nk0 = cdiv(p.F, Cfg::BK), nk = nk0 + cdiv(p.r, Cfg::BK);
+    KLoader<Cfg, Cfg::BM, true> la;
+    la.K0 = p.F; la.K1 = p.r; la.nk0 = nk0; la.scale1 = p.s;
+#pragma unroll
+    for (int i = 0; i < la.PER; ++i) {
+        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
+        if (!la.active(i)) continue;
+        const int m = la.row_of(i);
+        if (m < tl.rows) {
+            const int pr = tl.row0 + m;
+            la.p0[i] = static_cast<const T *>(p.H) + (size_t)pr * p.F;
+            la.p1[i] = p.zd + (size_t)pr * p.r;
+        }
+    }
+    KLoader<Cfg, Cfg::BN, false> lb;
+    lb.K0 = p.F; lb.K1 = p.r; lb.nk0 = nk0; lb.scale1 = 1.0f;
+#pragma unroll
+    for (int i = 0; i < lb.PER; ++i) {
+        lb.p0[i] = nullptr; lb.p1[i] = nullptr; lb.klo1[i] = 0; lb.khi1[i] = p.r;
+        if (!lb.active(i)) continue;
+        const int n = n_base + lb.row_of(i);
+        if (n < p.d) {
+            const size_t row = (size_t)tl.e * p.d + n;
+            lb.p0[i] = static_cast<const T *>(p.wd) + row * p.F;
+            lb.p1[i] = static_cast<const T *>(p.bd) + row * p.r;
+        }
+    }
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    T *Y = static_cast<T *>(p.Y);
+    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+        if (m < tl.rows && n_base + n < p.d) Y[(size_t)(tl.row0 + m) * p.d + n_base + n] = Elem<T>::from_f32(v);
+    });
+}
+
+// ===========================================================================
+// Down backward: dH = w * (dout W_d + s P'd A_d), with P'd = dout B_d, then
+// the SwiGLU backward  dG = dH u sig(g) (1 + g (1 - sig(g))),  dU = dH silu(g).
+// The row scale w (combine weight of the slot) is applied in the epilogue.
+// ===========================================================================
+struct DownBwdP {
+    const void *dout, *wd, *ad, *G, *U;
+    const float *pd, *topk_w;
+    const int32_t *sorted_slot, *offsets;
+    void *dGU;
+    int E, k, d, F, r;
+    float s;
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_down_bwd(DownBwdP p) {
+    using T = typename Cfg::T;
+    __shared__ Smem<Cfg> sm;
+    Tile tl;
+    if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(p.F, Cfg::BN), blockIdx.x, sm.start, tl)) return;
+    const int n_base = tl.nt * Cfg::BN;
+    const int ncol = min(Cfg::BN, p.F - n_base);
+    const int nk0 = cdiv(p.d, Cfg::BK), nk = nk0 + cdiv(p.r, Cfg::BK);
+    KLoader<Cfg, Cfg::BM, true> la;
+    la.K0 = p.d; la.K1 = p.r; la.nk0 = nk0; la.scale1 = p.s;
+#pragma unroll
+    for (int i = 0; i < la.PER; ++i) {
+        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
+        if (!la.active(i)) continue;
+        const int m = la.row_of(i);
+        if (m < tl.rows) {
+            const int pr = tl.row0 + m;
+            la.p0[i] = static_cast<const T *>(p.dout) + (size_t)token_of(p.sorted_slot, pr, p.k) * p.d;
+            la.p1[i] = p.pd + (size_t)pr * p.r;
+        }
+    }
+    NLoader<Cfg, Cfg::BN> lb;
+    lb.nk0 = nk0;
+    lb.s0 = NSeg{static_cast<const T *>(p.wd) + (size_t)tl.e * p.d * p.F + n_base, nullptr, p.d, p.d, p.F,
+                 0, ncol, 0, 0};
+    lb.s1 = NSeg{static_cast<const T *>(p.ad) + (size_t)tl.e * p.r * p.F + n_base, nullptr, p.r, p.r, p.F,
+                 0, ncol, 0, 0};
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    const T *G = static_cast<const T *>(p.G), *U = static_cast<const T *>(p.U);
+    T *dGU = static_cast<T *>(p.dGU);
+    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+        const int f = n_base + n;
+        if (m < tl.rows && f < p.F) {
+            const int pr = tl.row0 + m;
+            const float w = p.topk_w[p.sorted_slot[pr]];
+            const float dh = w * v;
+            const size_t o = (size_t)pr * p.F + f;
+            const float g = Elem<T>::to_f32(G[o]), u = Elem<T>::to_f32(U[o]);
+            const float sg = 1.0f / (1.0f + expf(-g));
+            dGU[(size_t)pr * 2 * p.F + f] = Elem<T>::from_f32(dh * u * sg * (1.0f + g * (1.0f - sg)));
+            dGU[(size_t)pr * 2 * p.F + p.F + f] = Elem<T>::from_f32(dh * g * sg);
+        }
+    });
+}
+
+// ===========================================================================
+// Gate/up backward: dXp = [dG | dU] [W_g ; W_u] + s [Pg | Pu] [A_g ; A_u].
+// ===========================================================================
+struct GateUpBwdP {
+    const void *dGU, *wg, *wu, *ag, *au;
+    const float *pgu;
+    const int32_t *offsets;
+    void *dXp;
+    int E, d, F, r;
+    float s;
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_gateup_bwd(GateUpBwdP p) {
+    using T = typename Cfg::T;
+    __shared__ Smem<Cfg> sm;
+    Tile tl;
+    if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(p.d, Cfg::BN), blockIdx.x, sm.start, tl)) return;
+    const int n_base = tl.nt * Cfg::BN;
+    const int ncol = min(Cfg::BN, p.d - n_base);
+    const int nk0 = cdiv(2 * p.F, Cfg::BK), nk = nk0 + cdiv(2 * p.r, Cfg::BK);
+    KLoader<Cfg, Cfg::BM, true> la;
+    la.K0 = 2 * p.F; la.K1 = 2 * p.r; la.nk0 = nk0; la.scale1 = p.s;
+#pragma unroll
+    for (int i = 0; i < la.PER; ++i) {
+        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
+        if (!la.active(i)) continue;
+        const int m = la.row_of(i);
+        if (m < tl.rows) {
+            const int pr = tl.row0 + m;
+            la.p0[i] = static_cast<const T *>(p.dGU) + (size_t)pr * 2 * p.F;
+            la.p1[i] = p.pgu + (size_t)pr * 2 * p.r;
+        }
+    }
+    NLoader<Cfg, Cfg::BN> lb;
+    lb.nk0 = nk0;
+    const size_t wofs = (size_t)tl.e * p.F * p.d + n_base, aofs = (size_t)tl.e * p.r * p.d + n_base;
+    lb.s0 = NSeg{static_cast<const T *>(p.wg) + wofs, static_cast<const T *>(p.wu) + wofs, p.F, 2 * p.F, p.d,
+                 0, ncol, 0, ncol};
+    lb.s1 = NSeg{static_cast<const T *>(p.ag) + aofs, static_cast<const T *>(p.au) + aofs, p.r, 2 * p.r, p.d,
+                 0, ncol, 0, ncol};
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    T *dXp = static_cast<T *>(p.dXp);
+    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+        if (m < tl.rows && n_base + n < p.d) dXp[(size_t)(tl.row0 + m) * p.d + n_base + n] = Elem<T>::from_f32(v);
+    });
+}
+
+// ===========================================================================
+// Skinny projections onto the LoRA rank (fp32 out [S, nr]):
+//   PROJ_GU:   Zgu = Xp [A_g ; A_u]^T            (B rows K-contiguous)
+//   PROJ_D:    Zd  = H A_d^T                     (B rows K-contiguous)
+//   PROJ_DOUT: P'd = dout_gathered B_d           (B N-contiguous)
+//   PROJ_DGU:  Pgu = [dG B_g | dU B_u]           (B N-contiguous, block-diagonal)
+// ===========================================================================
+enum ProjKind { PROJ_GU = 0, PROJ_D = 1, PROJ_DOUT = 2, PROJ_DGU = 3 };
+
+struct ProjP {
+    const void *a;            // x, H, dout or dGU
+    const void *b0, *b1;      // A_g/A_u, A_d, B_d, B_g/B_u
+    const int32_t *sorted_slot, *offsets;
+    float *out;
+    int E, k, d, F, r;
+};
+
+template <class Cfg, int KIND>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_proj(ProjP p) {
+    using T = typename Cfg::T;
+    __shared__ Smem<Cfg> sm;
+    constexpr bool GATHER = KIND == PROJ_GU || KIND == PROJ_DOUT;
+    constexpr bool BN_CONTIG = KIND == PROJ_DOUT || KIND == PROJ_DGU;
+    const int nr = (KIND == PROJ_GU || KIND == PROJ_DGU) ? 2 * p.r : p.r;
+    const int K = (KIND == PROJ_GU || KIND == PROJ_DOUT) ? p.d : (KIND == PROJ_D ? p.F : 2 * p.F);
+    Tile tl;
+    if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(nr, Cfg::BN), blockIdx.x, sm.start, tl)) return;
+    const int n_base = tl.nt * Cfg::BN;
+    const int nk = cdiv(K, Cfg::BK);
+    KLoader<Cfg, Cfg::BM, true> la;
+    la.K0 = K; la.K1 = 0; la.nk0 = nk; la.scale1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < la.PER; ++i) {
+        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
+        if (!la.active(i)) continue;
+        const int m = la.row_of(i);
+        if (m < tl.rows) {
+            const int pr = tl.row0 + m;
+            const size_t row = GATHER ? (size_t)token_of(p.sorted_slot, pr, p.k) : (size_t)pr;
+            la.p0[i] = static_cast<const T *>(p.a) + row * K;
+        }
+    }
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    if constexpr (!BN_CONTIG) {
+        KLoader<Cfg, Cfg::BN, false> lb;
+        lb.K0 = K; lb.K1 = 0; lb.nk0 = nk; lb.scale1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < lb.PER; ++i) {
+            lb.p0[i] = nullptr; lb.p1[i] = nullptr; lb.klo1[i] = 0; lb.khi1[i] = 0;
+            if (!lb.active(i)) continue;
+            const int n = n_base + lb.row_of(i);
+            if (n < nr) {
+                if (KIND == PROJ_GU)
+                    lb.p0[i] = static_cast<const T *>(n < p.r ? p.b0 : p.b1) +
+                               ((size_t)tl.e * p.r + (n < p.r ? n : n - p.r)) * K;
+                else
+                    lb.p0[i] = static_cast<const T *>(p.b0) + ((size_t)tl.e * p.r + n) * K;
+            }
+        }
+        gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    } else {
+        NLoader<Cfg, Cfg::BN> lb;
+        lb.nk0 = nk;
+        if (KIND == PROJ_DOUT) {
+            // B_d[e] is [d, r]: element (k = model dim, n = rank)
+            lb.s0 = NSeg{static_cast<const T *>(p.b0) + (size_t)tl.e * p.d * p.r, nullptr, p.d, p.d, p.r,
+                         -n_base, p.r - n_base, 0, 0};
+        } else {
+            // rows f < F from B_g (columns [0, r)), rows f >= F from B_u (columns [r, 2r))
+            const size_t o = (size_t)tl.e * p.F * p.r;
+            lb.s0 = NSeg{static_cast<const T *>(p.b0) + o, static_cast<const T *>(p.b1) + o, p.F, 2 * p.F, p.r,
+                         -n_base, p.r - n_base, p.r - n_base, 2 * p.r - n_base};
+        }
+        lb.s1 = lb.s0;
+        gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    }
+    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+        if (m < tl.rows && n_base + n < nr) p.out[(size_t)(tl.row0 + m) * nr + n_base + n] = v;
+    });
+}
+
+// ===========================================================================
+// Weighted combine / dX gather-sum: out[t] = sum_j w[t,j] Y[slot_row[t*k+j]]
+// (w = 1 for dX), fp32 accumulation in ascending j.
+// ===========================================================================
+template <typename T>
+__global__ __launch_bounds__(128) void k_combine(const T *__restrict__ Y, const int32_t *__restrict__ slot_row,
+                                                 const float *__restrict__ w, int k, int d, T *__restrict__ out) {
+    constexpr int VEC = Elem<T>::VEC;
+    const int t = blockIdx.x;
+    for (int c = threadIdx.x; c < d / VEC; c += blockDim.x) {
+        float acc[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int q = t * k + j;
+            const float wj = w ? w[q] : 1.0f;
+            const chunk_t ch = *reinterpret_cast<const chunk_t *>(Y + (size_t)slot_row[q] * d + c * VEC);
+            float y[VEC];
+            unpack<T>(ch, y);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] += wj * y[v];
+        }
+        *reinterpret_cast<chunk_t *>(out + (size_t)t * d + c * VEC) = Elem<T>::pack(acc);
+    }
+}
+
+// ===========================================================================
+// Router-weight gradient: d_topk_w[t,j] = <dout[t], Y[row of (t,j)]>, and
+// its chain through the softmax over the selected logits:
+// d_logits[t, e_j] = w_j (dw_j - sum_i w_i dw_i); zero for unselected experts.
+// One wave per token.
+// ===========================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void k_router_grad(const T *__restrict__ dout, const T *__restrict__ Y,
+                                                     const int32_t *__restrict__ slot_row,
+                                                     const int32_t *__restrict__ topk_idx,
+                                                     const float *__restrict__ topk_w, int Tn, int E, int k, int d,
+                                                     float *__restrict__ d_topk_w, float *__restrict__ d_logits) {
+    constexpr int VEC = Elem<T>::VEC;
+    __shared__ float s_dw[4][kMaxE];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int t = blockIdx.x * 4 + wave;
+    const bool valid = t < Tn;
+    float dot = 0.0f;
+    if (valid) {
+        for (int j = 0; j < k; ++j) {
+            const int q = t * k + j;
+            const T *yr = Y + (size_t)slot_row[q] * d;
+            const T *gr = dout + (size_t)t * d;
+            float acc = 0.0f;
+            for (int c = lane; c < d / VEC; c += kWave) {
+                float a[VEC], b[VEC];
+                unpack<T>(*reinterpret_cast<const chunk_t *>(gr + c * VEC), a);
+                unpack<T>(*reinterpret_cast<const chunk_t *>(yr + c * VEC), b);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc += a[v] * b[v];
+            }
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+            if (lane == 0) s_dw[wave][j] = acc;
+            dot += topk_w[q] * acc;
+        }
+    }
+    __syncthreads();
+    if (!valid) return;
+    if (d_topk_w)
+        for (int j = lane; j < k; j += kWave) d_topk_w[(size_t)t * k + j] = s_dw[wave][j];
+    if (d_logits)
+        for (int e = lane; e < E; e += kWave) {
+            float v = 0.0f;
+            for (int j = 0; j < k; ++j)
+                if (topk_idx[(size_t)t * k + j] == e) v = topk_w[(size_t)t * k + j] * (s_dw[wave][j] - dot);
+            d_logits[(size_t)t * E + e] = v;
+        }
+}
+
+// ===========================================================================
+// LoRA weight gradients, reduced over each expert's rows (K = rows):
+//   mode 0: [dA_g ; dA_u]^T = s Xp^T [Pg | Pu]        (D = d,  nr = 2r)
+//   mode 1: [dB_g , dB_u]   = s [dG | dU]^T [Zg | Zu] (D = 2F, nr = 2r, diagonal blocks kept)
+//   mode 2: dA_d^T          = s H^T (w P'd)           (D = F,  nr = r)
+//   mode 3: dB_d            = s (w dout)^T Zd         (D = d,  nr = r)
+// A block takes (expert, chunk of RC rows, D tile); an expert with one chunk
+// writes its gradient directly, larger experts write partial sums that the
+// finalize kernel adds in chunk order (deterministic). Experts with no rows
+// get exact zeros from the finalize kernel.
+// ===========================================================================
+constexpr int kLoraRC = 1024;  // rows per chunk
+
+struct LGradP {
+    const void *big;                 // [*, ldbig] rows (gathered by token if gather)
+    const float *small;              // [S, ldsmall] fp32
+    const int32_t *sorted_slot, *offsets;
+    const float *topk_w;
+    float *partial;
+    float *out0, *out1;
+    int E, k, d, F, r, D, nr, ldbig, ldsmall;
+    float s;
+};
+
+__device__ __forceinline__ void lgrad_store(int mode, const LGradP &p, int e, int m, int n, float v) {
+    switch (mode) {
+    case 0:
+        if (n < p.r) p.out0[((size_t)e * p.r + n) * p.d + m] = v;
+        else p.out1[((size_t)e * p.r + n - p.r) * p.d + m] = v;
+        break;
+    case 1:
+        if (m < p.F && n < p.r) p.out0[((size_t)e * p.F + m) * p.r + n] = v;
+        else if (m >= p.F && n >= p.r) p.out1[((size_t)e * p.F + m - p.F) * p.r + n - p.r] = v;
+        break;
+    case 2: p.out0[((size_t)e * p.r + n) * p.F + m] = v; break;
+    default: p.out0[((size_t)e * p.d + m) * p.r + n] = v; break;
+    }
+}
+
+// Transposing loader whose k index is a row p of the current chunk:
+// element (k = row, col) is src_row(p)[col], for ROWS tile columns.
+template <class Cfg, int ROWS, typename SrcT>
+struct RowTLoader {
+    using T = typename Cfg::T;
+    static constexpr int VEC = Cfg::VEC, NT = Cfg::NTHREADS, BK = Cfg::BK;
+    static constexpr int KB = BK / VEC, NB = ROWS / VEC, NBLK = KB * NB;
+    static constexpr int PER = (NBLK + NT - 1) / NT;
+    const void *base;
+    int ld, col0, ncol;          // columns [col0, col0 + ROWS) of rows of length ld; valid < ncol
+    int row0, rows, k;           // chunk rows p in [row0, row0 + rows)
+    bool gather, wscale;
+    const int32_t *sorted_slot;
+    const float *topk_w;
+    struct Regs { chunk_t c[PER][VEC]; };
+    __device__ void load(int kt, Regs &r) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int b = (int)threadIdx.x + i * NT;
+            if (b >= NBLK) continue;
+            const int nb = b % NB, kb = b / NB;
+            const int c = col0 + nb * VEC;
+#pragma unroll
+            for (int ii = 0; ii < VEC; ++ii) {
+                const int pl = kt * BK + kb * VEC + ii;
+                chunk_t v = zero4();
+                if (pl < rows && c + VEC <= ncol) {
+                    const int pr = row0 + pl;
+                    const size_t row = gather ? (size_t)(sorted_slot[pr] / k) : (size_t)pr;
+                    if constexpr (sizeof(SrcT) == sizeof(T)) {
+                        v = *reinterpret_cast<const chunk_t *>(static_cast<const SrcT *>(base) + row * ld + c);
+                    } else {  // fp32 source, T = bf16: 32 bytes -> one chunk
+                        const float *src = static_cast<const float *>(base) + row * ld + c;
+                        const float sc = wscale ? topk_w[sorted_slot[pr]] : 1.0f;
+                        float f[VEC];
+#pragma unroll
+                        for (int h = 0; h < VEC; ++h) f[h] = src[h] * sc;
+                        v = Elem<T>::pack(f);
+                    }
+                    if constexpr (sizeof(SrcT) == sizeof(T)) {
+                        if (wscale) {
+                            float f[VEC];
+                            unpack<T>(v, f);
+                            const float sc = topk_w[sorted_slot[pr]];
+#pragma unroll
+                            for (int h = 0; h < VEC; ++h) f[h] *= sc;
+                            v = Elem<T>::pack(f);
+                        }
+                    }
+                }
+                r.c[i][ii] = v;
+            }
+        }
+    }
+    __device__ void store(const Regs &r, T *lds) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int b = (int)threadIdx.x + i * NT;
+            if (b >= NBLK) continue;
+            const int nb = b % NB, kb = b / NB;
+            chunk_t o[VEC];
+            NLoader<Cfg, ROWS>::transpose(r.c[i], o);
+#pragma unroll
+            for (int jj = 0; jj < VEC; ++jj)
+                *reinterpret_cast<chunk_t *>(lds + (nb * VEC + jj) * Cfg::LDK + kb * VEC) = o[jj];
+        }
+    }
+};
+
+template <class Cfg, int MODE>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_lora_grad(LGradP p) {
+    using T = typename Cfg::T;
+    __shared__ Smem<Cfg> sm;
+    const int ntm = cdiv(p.D, Cfg::BM), ntn = cdiv(p.nr, Cfg::BN);
+    Tile tl;
+    if (!schedule_tile<kLoraRC, Cfg::NTHREADS>(p.offsets, p.E, ntm * ntn, blockIdx.x, sm.start, tl)) return;
+    const int m_base = (tl.nt % ntm) * Cfg::BM, n_base = (tl.nt / ntm) * Cfg::BN;
+    constexpr bool BIG_GATHER = MODE == 0 || MODE == 3;
+    constexpr bool SMALL_W = MODE == 2 || MODE == 3;
+    RowTLoader<Cfg, Cfg::BM, T> la;
+    la.base = p.big; la.ld = p.ldbig; la.col0 = m_base; la.ncol = p.D;
+    la.row0 = tl.row0; la.rows = tl.rows; la.k = p.k; la.gather = BIG_GATHER; la.wscale = MODE == 3;
+    la.sorted_slot = p.sorted_slot; la.topk_w = p.topk_w;
+    RowTLoader<Cfg, Cfg::BN, float> lb;
+    lb.base = p.small; lb.ld = p.ldsmall; lb.col0 = n_base; lb.ncol = p.nr;
+    lb.row0 = tl.row0; lb.rows = tl.rows; lb.k = p.k; lb.gather = false; lb.wscale = MODE == 2;
+    lb.sorted_slot = p.sorted_slot; lb.topk_w = p.topk_w;
+    (void)SMALL_W;
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    gemm_mainloop<Cfg>(la, lb, cdiv(tl.rows, Cfg::BK), sm.a, sm.b, acc);
+    const bool single = (p.offsets[tl.e + 1] - p.offsets[tl.e]) <= kLoraRC;
+    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+        const int gm = m_base + m, gn = n_base + n;
+        if (gm < p.D && gn < p.nr) {
+            if (single) lgrad_store(MODE, p, tl.e, gm, gn, p.s * v);
+            else p.partial[((size_t)tl.gmt * p.D + gm) * p.nr + gn] = v;
+        }
+    });
+}
+
+// Finalize: zeros for empty experts, chunk-ordered sums for multi-chunk experts.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_lora_grad_finalize(LGradP p) {
+    __shared__ int s_start[kMaxE + 1];
+    const int e = blockIdx.y;
+    const int ne = p.offsets[e + 1] - p.offsets[e];
+    if (ne > 0 && ne <= kLoraRC) return;  // written by the GEMM directly
+    // chunk start of expert e: sum of ceil(n/RC) over earlier experts
+    for (int x = threadIdx.x; x < p.E; x += 256)
+        s_start[x] = (p.offsets[x + 1] - p.offsets[x] + kLoraRC - 1) / kLoraRC;
+    __syncthreads();
+    int c0 = 0;
+    for (int x = 0; x < e; ++x) c0 += s_start[x];
+    const int nch = s_start[e];
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= p.D * p.nr) return;
+    const int m = idx / p.nr, n = idx % p.nr;
+    float v = 0.0f;
+    for (int c = 0; c < nch; ++c) v += p.partial[((size_t)(c0 + c) * p.D + m) * p.nr + n];
+    lgrad_store(MODE, p, e, m, n, p.s * v);
+}
+
+size_t lora_grad_partial_bytes(const Dims &D) {
+    const size_t tiles = (size_t)max_row_tiles(D.S(), D.E, kLoraRC);
+    const size_t w = std::max<size_t>((size_t)D.d * 2 * D.r, (size_t)2 * D.F * 2 * D.r);
+    return tiles * w * sizeof(float);
+}
+
+// ===========================================================================
+// drivers
+// ===========================================================================
+struct TraceScope {
+    const Trace *tr;
+    int id;
+    hipStream_t st;
+    TraceScope(const Trace *t, int i, hipStream_t s) : tr(t), id(i), st(s) {
+        if (tr && tr->start[id] && tr->stop[id]) (void)hipEventRecord(tr->start[id], st);
+    }
+    ~TraceScope() {
+        if (tr && tr->start[id] && tr->stop[id]) (void)hipEventRecord(tr->stop[id], st);
+    }
+};
+
+enum {
+    K_PROJ_GU = MOE_K_PROJ_GU, K_GATEUP = MOE_K_GATEUP, K_PROJ_D = MOE_K_PROJ_D, K_DOWN = MOE_K_DOWN,
+    K_COMBINE = MOE_K_COMBINE, K_ROUTER_GRAD = MOE_K_ROUTER_GRAD, K_PROJ_DOUT = MOE_K_PROJ_DOUT,
+    K_DOWN_BWD = MOE_K_DOWN_BWD, K_PROJ_DGU = MOE_K_PROJ_DGU, K_GATEUP_BWD = MOE_K_GATEUP_BWD,
+    K_DX_COMBINE = MOE_K_DX_COMBINE, K_LORA_GRAD = MOE_K_LORA_GRAD
+};
+
+template <class Cfg> static int grid_for(const Dims &D, int BM, int NT) { return max_row_tiles(D.S(), D.E, BM) * NT; }
+
+#define MOE_LAUNCH(kern, grid, block, ...)                   \
+    do {                                                     \
+        if ((grid) > 0) {                                    \
+            kern<<<dim3(grid), dim3(block), 0, st>>>(__VA_ARGS__); \
+            hipError_t _e = hipGetLastError();               \
+            if (_e != hipSuccess) return _e;                 \
+        }                                                    \
+    } while (0)
+
+template <typename T, int KIND>
+static hipError_t launch_proj(const Dims &D, const ProjP &pp, hipStream_t st) {
+    const int nr = (KIND == PROJ_GU || KIND == PROJ_DGU) ? 2 * D.r : D.r;
+    if (nr <= 32) {
+        using Cfg = typename SkinnyCfg<T, 32>::type;
+        MOE_LAUNCH((k_proj<Cfg, KIND>), grid_for<Cfg>(D, Cfg::BM, cdiv(nr, Cfg::BN)), Cfg::NTHREADS, pp);
+    } else {
+        using Cfg = typename SkinnyCfg<T, 64>::type;
+        MOE_LAUNCH((k_proj<Cfg, KIND>), grid_for<Cfg>(D, Cfg::BM, cdiv(nr, Cfg::BN)), Cfg::NTHREADS, pp);
+    }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace *tr) {
+    using Cfg = typename MainCfg<T>::type;
+    if (D.T == 0) return hipSuccess;
+    {
+        TraceScope ts(tr, K_PROJ_GU, st);
+        ProjP pp{b.x, b.ag, b.au, b.sorted_slot, b.offsets, b.Zgu, D.E, D.k, D.d, D.F, D.r};
+        hipError_t e = launch_proj<T, PROJ_GU>(D, pp, st);
+        if (e != hipSuccess) return e;
+    }
+    {
+        TraceScope ts(tr, K_GATEUP, st);
+        GateUpP gp{b.x, b.wg, b.wu, b.bg, b.bu, b.Zgu, b.sorted_slot, b.offsets, b.G, b.U, b.H,
+                   D.E, D.k, D.d, D.F, D.r, D.s};
+        MOE_LAUNCH(k_gateup<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN / 2)), Cfg::NTHREADS, gp);
+    }
+    {
+        TraceScope ts(tr, K_PROJ_D, st);
+        ProjP pp{b.H, b.ad, nullptr, b.sorted_slot, b.offsets, b.Zd, D.E, D.k, D.d, D.F, D.r};
+        hipError_t e = launch_proj<T, PROJ_D>(D, pp, st);
+        if (e != hipSuccess) return e;
+    }
+    {
+        TraceScope ts(tr, K_DOWN, st);
+        DownP dp{b.H, b.wd, b.bd, b.Zd, b.offsets, b.Y, D.E, D.d, D.F, D.r, D.s};
+        MOE_LAUNCH(k_down<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, dp);
+    }
+    {
+        TraceScope ts(tr, K_COMBINE, st);
+        MOE_LAUNCH(k_combine<T>, D.T, 128, static_cast<const T *>(b.Y), b.slot_row, b.topk_w, D.k, D.d,
+                   static_cast<T *>(b.out));
+    }
+    return hipSuccess;
+}
+
+template <typename T, int MODE>
+static hipError_t launch_lgrad(const Dims &D, const LGradP &lp, hipStream_t st) {
+    const int ntm = cdiv(lp.D, 128);
+    if (lp.nr <= 32) {
+        using Cfg = typename SkinnyCfg<T, 32>::type;
+        MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
+                   Cfg::NTHREADS, lp);
+    } else {
+        using Cfg = typename SkinnyCfg<T, 64>::type;
+        MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
+                   Cfg::NTHREADS, lp);
+    }
+    k_lora_grad_finalize<MODE><<<dim3(cdiv(lp.D * lp.nr, 256), D.E), dim3(256), 0, st>>>(lp);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace *tr) {
+    using Cfg = typename MainCfg<T>::type;
+    const int S = D.S();
+    if (D.T > 0 && (b.d_topk_w || b.d_logits)) {
+        TraceScope ts(tr, K_ROUTER_GRAD, st);
+        MOE_LAUNCH(k_router_grad<T>, cdiv(D.T, 4), 256, static_cast<const T *>(b.dout),
+                   static_cast<const T *>(b.Y), b.slot_row, b.topk_idx, b.topk_w, D.T, D.E, D.k, D.d, b.d_topk_w,
+                   b.d_logits);
+    }
+    if (D.T > 0) {
+        {
+            TraceScope ts(tr, K_PROJ_DOUT, st);
+            ProjP pp{b.dout, b.bd, nullptr, b.sorted_slot, b.offsets, b.Pd, D.E, D.k, D.d, D.F, D.r};
+            hipError_t e = launch_proj<T, PROJ_DOUT>(D, pp, st);
+            if (e != hipSuccess) return e;
+        }
+        {
+            TraceScope ts(tr, K_DOWN_BWD, st);
+            DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
+                        D.E, D.k, D.d, D.F, D.r, D.s};
+            MOE_LAUNCH(k_down_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN)), Cfg::NTHREADS, dp);
+        }
+        {
+            TraceScope ts(tr, K_PROJ_DGU, st);
+            ProjP pp{b.dGU, b.bg, b.bu, b.sorted_slot, b.offsets, b.Pgu, D.E, D.k, D.d, D.F, D.r};
+            hipError_t e = launch_proj<T, PROJ_DGU>(D, pp, st);
+            if (e != hipSuccess) return e;
+        }
+        {
+            TraceScope ts(tr, K_GATEUP_BWD, st);
+            GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.E, D.d, D.F, D.r, D.s};
+            MOE_LAUNCH(k_gateup_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, gp);
+        }
+        {
+            TraceScope ts(tr, K_DX_COMBINE, st);
+            MOE_LAUNCH(k_combine<T>, D.T, 128, static_cast<const T *>(b.dXp), b.slot_row,
+                       static_cast<const float *>(nullptr), D.k, D.d, static_cast<T *>(b.dx));
+        }
+    }
+    {
+        TraceScope ts(tr, K_LORA_GRAD, st);
+        (void)S;
+        LGradP l0{b.x, b.Pgu, b.sorted_slot, b.offsets, b.topk_w, b.partial, b.da_g, b.da_u,
+                  D.E, D.k, D.d, D.F, D.r, D.d, 2 * D.r, D.d, 2 * D.r, D.s};
+        hipError_t e = launch_lgrad<T, 0>(D, l0, st);
+        if (e != hipSuccess) return e;
+        LGradP l1{b.dGU, b.Zgu, b.sorted_slot, b.offsets, b.topk_w, b.partial, b.db_g, b.db_u,
+                  D.E, D.k, D.d, D.F, D.r, 2 * D.F, 2 * D.r, 2 * D.F, 2 * D.r, D.s};
+        e = launch_lgrad<T, 1>(D, l1, st);
+        if (e != hipSuccess) return e;
+        LGradP l2{b.H, b.Pd, b.sorted_slot, b.offsets, b.topk_w, b.partial, b.da_d, nullptr,
+                  D.E, D.k, D.d, D.F, D.r, D.F, D.r, D.F, D.r, D.s};
+        e = launch_lgrad<T, 2>(D, l2, st);
+        if (e != hipSuccess) return e;
+        LGradP l3{b.dout, b.Zd, b.sorted_slot, b.offsets, b.topk_w, b.partial, b.db_d, nullptr,
+                  D.E, D.k, D.d, D.F, D.r, D.d, D.r, D.d, D.r, D.s};
+        e = launch_lgrad<T, 3>(D, l3, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template hipError_t run_fwd<float>(const Dims &, const FwdBufs &, hipStream_t, const Trace *);
+template hipError_t run_fwd<bf16_t>(const Dims &, const FwdBufs &, hipStream_t, const Trace *);
+template hipError_t run_bwd<float>(const Dims &, const BwdBufs &, hipStream_t, const Trace *);
+template hipError_t run_bwd<bf16_t>(const Dims &, const BwdBufs &, hipStream_t, const Trace *);
+
+}  // namespace moe

@@ -1,0 +1,247 @@
+// route.hip - top-k routing and expert grouping on gfx950.
+//
+// The grouping follows the flatten / stable sort by expert id / bincount /
+// offset-slice formulation of the Unsloth x NVIDIA blog (d9249.github.io,
+// section "core idea / structure / how it works", MoE routing paragraph), as
+// three kernels with no host synchronisation:
+//   1. topk:    per token, top-k experts by (logit desc, id asc) and softmax
+//               over the k selected logits; per-block expert histogram in
+//               LDS (the bincount, split over token blocks).
+//   2. scan:    one exclusive scan over the expert-major [E x nblk]
+//               histogram gives every (expert, block) its first output row;
+//               counts and offsets fall out of the same pass.
+//   3. scatter: each block ranks its slots within their expert with wave64
+//               ballots (match on the expert-id bits, popcount below the
+//               lane) plus a cross-wave prefix in LDS; the rank is stable
+//               (slot order = token order), so the result is the stable sort.
+#include "kernels.hpp"
+#include "common.hpp"
+
+#include <climits>
+
+namespace moe {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kMaxE = 1024;
+constexpr int kMaxPerLane = kMaxE / kWave;  // 16 logits per lane
+
+int route_tokens_per_block(int T, int E) {
+    int tpb = 64;
+    while ((long long)E * ((T + tpb - 1) / tpb) > 65536) tpb *= 2;
+    return tpb;
+}
+
+// (v, id) ordering of the router: larger logit first, ties to the lower id.
+// Float comparison makes -0.0 equal to +0.0.
+__device__ __forceinline__ bool route_better(float ov, int oid, float bv, int bid) {
+    return oid != INT_MAX && (bid == INT_MAX || ov > bv || (ov == bv && oid < bid));
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float *__restrict__ logits, int T, int E,
+                                                              int k, int tpb, int nblk,
+                                                              int32_t *__restrict__ topk_idx,
+                                                              float *__restrict__ topk_w,
+                                                              int32_t *__restrict__ hist) {
+    __shared__ int s_hist[kMaxE];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    for (int e = tid; e < E; e += kRouteThreads) s_hist[e] = 0;
+    __syncthreads();
+    const int b = blockIdx.x;
+    const int t0 = b * tpb, t1 = min(T, t0 + tpb);
+    for (int t = t0 + wave; t < t1; t += kRouteWaves) {
+        const float *row = logits + (size_t)t * E;
+        float v[kMaxPerLane];
+        uint32_t avail = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) {
+            const int e = lane + kWave * i;
+            v[i] = e < E ? row[e] : 0.0f;
+            if (e < E) avail |= 1u << i;
+        }
+        int my_idx[kMaxPerLane];
+        float my_val[kMaxPerLane];
+        float v0 = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            float bv = 0.0f;
+            int bid = INT_MAX;
+#pragma unroll
+            for (int i = 0; i < kMaxPerLane; ++i)  // ids rise with i: a tie keeps the lower id
+                if (((avail >> i) & 1u) && (bid == INT_MAX || v[i] > bv)) {
+                    bv = v[i];
+                    bid = lane + kWave * i;
+                }
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) {
+                const float ov = __shfl_xor(bv, off, kWave);
+                const int oid = __shfl_xor(bid, off, kWave);
+                if (route_better(ov, oid, bv, bid)) {
+                    bv = ov;
+                    bid = oid;
+                }
+            }
+            // every lane now holds the winner
+            if ((bid & (kWave - 1)) == lane) avail &= ~(1u << (bid / kWave));
+            if (j == 0) v0 = bv;
+#pragma unroll
+            for (int s = 0; s < kMaxPerLane; ++s)
+                if (s == (j / kWave) && lane == (j & (kWave - 1))) {
+                    my_idx[s] = bid;
+                    my_val[s] = bv;
+                }
+            if (lane == 0) atomicAdd(&s_hist[bid], 1);
+        }
+        // softmax over the k selected logits, shifted by the largest
+        float sum = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kMaxPerLane; ++s)
+            if (s * kWave + lane < k) sum += expf(my_val[s] - v0);
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+#pragma unroll
+        for (int s = 0; s < kMaxPerLane; ++s) {
+            const int j = s * kWave + lane;
+            if (j < k) {
+                topk_idx[(size_t)t * k + j] = my_idx[s];
+                topk_w[(size_t)t * k + j] = expf(my_val[s] - v0) / sum;
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kRouteThreads) hist[(size_t)e * nblk + b] = s_hist[e];
+}
+
+// exclusive scan of one value per thread over a 1024-thread block
+__device__ int block_excl_scan_1024(int v, int *s_wsum) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < 16 ? s_wsum[lane] : 0;
+        int wi = w;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int o = __shfl_up(wi, off, kWave);
+            if (lane >= off) wi += o;
+        }
+        if (lane < 16) s_wsum[lane] = wi - w;  // exclusive over waves
+    }
+    __syncthreads();
+    const int r = s_wsum[wave] + incl - v;
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(1024) void k_route_scan(const int32_t *__restrict__ hist, int E, int nblk, int S,
+                                                     int32_t *__restrict__ base, int32_t *__restrict__ counts,
+                                                     int32_t *__restrict__ offsets) {
+    __shared__ int s_wsum[16];
+    const int tid = threadIdx.x;
+    const int N = E * nblk;
+    const int per = (N + 1023) / 1024;
+    const int lo = min(N, tid * per), hi = min(N, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += hist[i];
+    int run = block_excl_scan_1024(sum, s_wsum);
+    for (int i = lo; i < hi; ++i) {
+        base[i] = run;
+        run += hist[i];
+    }
+    // counts (bincount) and offsets (their exclusive scan), one expert per thread
+    int c = 0;
+    if (tid < E)
+        for (int b = 0; b < nblk; ++b) c += hist[(size_t)tid * nblk + b];
+    const int off = block_excl_scan_1024(c, s_wsum);
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = off;
+    }
+    if (tid == 0) offsets[E] = S;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t *__restrict__ topk_idx,
+                                                                 const int32_t *__restrict__ base, int T, int E,
+                                                                 int k, int tpb, int nblk,
+                                                                 int32_t *__restrict__ sorted_slot,
+                                                                 int32_t *__restrict__ slot_row) {
+    __shared__ int s_base[kMaxE], s_run[kMaxE], s_wcnt[kRouteWaves][kMaxE];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int b = blockIdx.x;
+    for (int e = tid; e < E; e += kRouteThreads) {
+        s_base[e] = base[(size_t)e * nblk + b];
+        s_run[e] = 0;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) s_wcnt[w][e] = 0;
+    }
+    __syncthreads();
+    const int q0 = b * tpb * k, q1 = min(T, (b + 1) * tpb) * k;
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int rb = q0; rb < q1; rb += kRouteThreads) {
+        const int q = rb + tid;
+        const bool valid = q < q1;
+        const int e = valid ? topk_idx[q] : 0;
+        unsigned long long m = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool set = (e >> bit) & 1;
+            const unsigned long long bb = __ballot(valid && set);
+            m &= set ? bb : ~bb;
+        }
+        const int rank_w = __popcll(m & below);
+        if (valid && rank_w == 0) s_wcnt[wave][e] = __popcll(m);
+        __syncthreads();
+        if (valid) {
+            int pre = 0;
+            for (int w = 0; w < wave; ++w) pre += s_wcnt[w][e];
+            const int pos = s_base[e] + s_run[e] + pre + rank_w;
+            sorted_slot[pos] = q;
+            slot_row[q] = pos;
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += kRouteThreads) {
+            int add = 0;
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w) {
+                add += s_wcnt[w][x];
+                s_wcnt[w][x] = 0;
+            }
+            s_run[x] += add;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_route_topk(const float *logits, int T, int E, int k, int32_t *topk_idx, float *topk_w,
+                             int32_t *hist, hipStream_t st) {
+    const int nblk = route_nblk(T, E);
+    if (nblk == 0) return hipSuccess;
+    const int tpb = route_tokens_per_block(T, E);
+    hipLaunchKernelGGL(k_route_topk, dim3(nblk), dim3(kRouteThreads), 0, st, logits, T, E, k, tpb, nblk, topk_idx,
+                       topk_w, hist);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_scan(const int32_t *hist, int T, int E, int k, int32_t *base, int32_t *counts,
+                             int32_t *offsets, hipStream_t st) {
+    const int nblk = route_nblk(T, E);
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, hist, E, nblk, T * k, base, counts, offsets);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_scatter(const int32_t *topk_idx, const int32_t *base, int T, int E, int k,
+                                int32_t *sorted_slot, int32_t *slot_row, hipStream_t st) {
+    const int nblk = route_nblk(T, E);
+    if (nblk == 0) return hipSuccess;
+    const int tpb = route_tokens_per_block(T, E);
+    hipLaunchKernelGGL(k_route_scatter, dim3(nblk), dim3(kRouteThreads), 0, st, topk_idx, base, T, E, k, tpb, nblk,
+                       sorted_slot, slot_row);
+    return hipGetLastError();
+}
+
+}  // namespace moe

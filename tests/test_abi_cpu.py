@@ -1,0 +1,147 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/moe.h
+declares, sizes its buffers as documented and rejects bad arguments before
+enqueuing anything. No kernel is launched by these tests: every call that is
+not a size query fails a host-side check (and, as a second guard, passes no
+workspace where one is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import moe_layer_lora_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS)
+    for n in names:
+        assert hasattr(moe.lib(), n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)$", out, flags=re.M))
+    assert set(names) <= exported  # unmangled (extern "C")
+
+
+def test_trace_indices_match_header():
+    src = open(HEADER).read()
+    body = re.search(r"enum \{(.*?)\};", src, flags=re.S).group(1)
+    ids = re.findall(r"MOE_K_(\w+)", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert ids[-1] == "COUNT"
+    assert [i.lower() for i in ids[:-1]] == moe.KERNELS
+
+
+def test_status_strings():
+    assert moe.moe_status_str(moe.MOE_OK) == "ok"
+    assert moe.moe_status_str(moe.MOE_E_WORKSPACE) == "workspace too small"
+    assert moe.moe_status_str(99) == "unknown status"
+
+
+def pb(**kw):
+    base = dict(T=512, d=256, E=16, k=4, F=128, r=16, lora_scale=2.0, dtype=moe.MOE_BF16)
+    base.update(kw)
+    return moe.Problem(**base)
+
+
+def al(x):
+    return (x + 255) // 256 * 256
+
+
+def test_saved_and_workspace_sizes():
+    p = pb()
+    S, es = p.T * p.k, 2
+    want = 3 * al(S * p.F * es) + al(S * 2 * p.r * 4) + al(S * p.r * 4)
+    assert moe.saved_bytes(p, False) == want
+    assert moe.saved_bytes(p, True) == want + al(S * p.d * es)
+    assert moe.fwd_workspace(p, True, True) == 0
+    assert moe.fwd_workspace(p, True, False) == al(S * p.d * es)
+    assert moe.fwd_workspace(p, False, False) == (al(S * p.F * es) + al(S * 2 * p.r * 4)
+                                                  + al(S * p.r * 4) + al(S * p.d * es))
+    assert moe.route_workspace(p) > 0 and moe.bwd_workspace(p) > 0
+    p32 = pb(dtype=moe.MOE_F32)
+    assert moe.saved_bytes(p32, False) == 3 * al(S * p.F * 4) + al(S * 2 * p.r * 4) + al(S * p.r * 4)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), moe.MOE_E_ARG), (dict(k=17), moe.MOE_E_ARG), (dict(T=-1), moe.MOE_E_ARG),
+    (dict(dtype=7), moe.MOE_E_ARG), (dict(lora_scale=float("nan")), moe.MOE_E_ARG),
+    (dict(d=100), moe.MOE_E_UNSUPPORTED), (dict(F=36), moe.MOE_E_UNSUPPORTED),
+    (dict(r=12), moe.MOE_E_UNSUPPORTED), (dict(E=1025, k=2), moe.MOE_E_UNSUPPORTED),
+    (dict(T=1 << 20, d=4096, k=8), moe.MOE_E_UNSUPPORTED),
+])
+def test_bad_problems_rejected(kw, code):
+    p = pb(**kw)
+    assert moe.route_workspace(p) == 0 and moe.saved_bytes(p, True) == 0
+    fake = 1 << 20  # aligned, never dereferenced: the call fails before any launch
+    st = moe.lib().moe_route(ctypes.byref(p), fake, ctypes.byref(_routing(fake)), None, None, 0,
+                             None, None)
+    assert st == code
+
+
+def _routing(ptr):
+    return moe.Routing(*([ptr] * 6))
+
+
+def _weights(ptr):
+    return moe.Weights(*([ptr] * 9))
+
+
+def _grads(ptr):
+    return moe.LoraGrads(*([ptr] * 6))
+
+
+def test_argument_errors_before_launch():
+    p = pb()
+    L = moe.lib()
+    A = 1 << 20
+    ok_rt, w, g = _routing(A), _weights(A), _grads(A)
+    # null / misaligned pointers
+    assert L.moe_route(ctypes.byref(p), A, None, None, None, 0, None, None) == moe.MOE_E_ARG
+    assert L.moe_route(ctypes.byref(p), A + 4, ctypes.byref(ok_rt), None, None, 0, None,
+                       None) == moe.MOE_E_ARG
+    bad_rt = _routing(A)
+    bad_rt.sorted_slot = None
+    assert L.moe_route(ctypes.byref(p), A, ctypes.byref(bad_rt), None, None, 0, None,
+                       None) == moe.MOE_E_ARG
+    # workspace too small
+    assert L.moe_route(ctypes.byref(p), A, ctypes.byref(ok_rt), None, A, 16, None,
+                       None) == moe.MOE_E_WORKSPACE
+    # forward: missing weight, misaligned out, short workspace
+    w2 = _weights(A)
+    w2.b_down = None
+    assert L.moe_fwd(ctypes.byref(p), A, ctypes.byref(ok_rt), ctypes.byref(w2), A, A, 0, A, 0,
+                     None, None) == moe.MOE_E_ARG
+    assert L.moe_fwd(ctypes.byref(p), A, ctypes.byref(ok_rt), ctypes.byref(w), A + 8, A, 0, A, 0,
+                     None, None) == moe.MOE_E_ARG
+    assert L.moe_fwd(ctypes.byref(p), A, ctypes.byref(ok_rt), ctypes.byref(w), A, A, 0, A, 0,
+                     None, None) == moe.MOE_E_WORKSPACE
+    # backward: saved is required; router gradients need the kept expert outputs
+    assert L.moe_bwd(ctypes.byref(p), A, A, ctypes.byref(ok_rt), ctypes.byref(w), None, 1, A,
+                     ctypes.byref(g), None, None, A, 0, None, None) == moe.MOE_E_ARG
+    assert L.moe_bwd(ctypes.byref(p), A, A, ctypes.byref(ok_rt), ctypes.byref(w), A, 0, A,
+                     ctypes.byref(g), A, None, A, 0, None, None) == moe.MOE_E_ARG
+    g2 = _grads(A)
+    g2.da_up = A + 2
+    assert L.moe_bwd(ctypes.byref(p), A, A, ctypes.byref(ok_rt), ctypes.byref(w), A, 1, A,
+                     ctypes.byref(g2), None, None, A, 0, None, None) == moe.MOE_E_ARG
+    assert L.moe_bwd(ctypes.byref(p), A, A, ctypes.byref(ok_rt), ctypes.byref(w), A, 1, A,
+                     ctypes.byref(g), None, None, A, 0, None, None) == moe.MOE_E_WORKSPACE
+
+
+def test_binding_raises_on_error():
+    p = pb(k=99)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(p, 1 << 20, {n: 1 << 20 for n in ("topk_idx", "topk_w", "counts", "offsets",
+                                                         "sorted_slot", "slot_row")},
+                      stream=0)
+    assert ei.value.status == moe.MOE_E_ARG

@@ -1,0 +1,270 @@
+"""GPU parity: the HIP layer (through the C ABI) against the CPU oracle.
+
+Routing outputs must match bit for bit; floating-point outputs within the
+rel-L2 bound of their storage type (1e-5 fp32, 2e-2 bf16), measured over the
+whole tensor (small layers) or over the sampled rows / experts (full-size
+layers, where the oracle computes chosen tokens and experts one by one).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from synth.configs import LayerConfig  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+GRADS = ("da_gate", "db_gate", "da_up", "db_up", "da_down", "db_down")
+
+
+def _runner():
+    import layer_runner
+    return layer_runner
+
+
+def check_routing(r, o, tag=""):
+    for n in ("topk_idx", "counts", "offsets", "sorted_slot", "slot_row"):
+        assert np.array_equal(r[n], o[n]), f"{tag} routing {n} differs"
+    # the weights are fp32 softmax values: fp32 rounding only
+    lr = _runner()
+    assert lr.rel_l2(r["topk_w"], o["topk_w"]) <= 1e-6, tag
+
+
+def check(name, got, want, tol, tag=""):
+    lr = _runner()
+    e = lr.rel_l2(got, want)
+    assert e <= tol, f"{tag} {name}: rel-L2 {e:.3e} > {tol:.1e}"
+    return e
+
+
+SMALL = {
+    "tiny_fp32": synth.get_config("tiny_fp32"),
+    "ragged_bf16": LayerConfig("ragged_bf16", T=300, d=136, E=6, k=3, F=200, r=16, dtype="bf16",
+                               alpha=32.0, router_grad=True),
+    "ragged_f32": LayerConfig("ragged_f32", T=300, d=136, E=6, k=3, F=200, r=16, dtype="f32",
+                              alpha=32.0, router_grad=True),
+    "rank32_bf16": LayerConfig("rank32_bf16", T=200, d=96, E=5, k=2, F=160, r=32, dtype="bf16",
+                               alpha=64.0, router_grad=True),
+    "wide_bf16": LayerConfig("wide_bf16", T=520, d=264, E=4, k=2, F=328, r=8, dtype="bf16",
+                             alpha=16.0, router_grad=True),
+}
+
+
+def run_small(cfg, inputs, keep=True, router_grad=True):
+    lr = _runner()
+    L = lr.Layer(cfg, inputs, keep_expert_out=keep)
+    L.step(backward=True, router_grad=router_grad)
+    return L, L.results(backward=True, router_grad=router_grad, intermediates=True)
+
+
+def oracle_full(cfg, inputs, rt=None):
+    if rt is None:
+        rt = oracle.route(inputs["logits"], cfg.k)
+    L = oracle.Layer.from_config(cfg, inputs)
+    f = oracle.fwd(L, rt, intermediates=True)
+    b = oracle.bwd(L, rt, inputs["dout"], intermediates=True)
+    return rt, f, b
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_full_parity(name):
+    cfg = SMALL[name]
+    print(f"[parity] {name}", flush=True)
+    inputs = synth.make_inputs(cfg, seed=0)
+    _, r = run_small(cfg, inputs)
+    rt, f, b = oracle_full(cfg, inputs)
+    check_routing(r, rt, name)
+    tol = TOL[cfg.dtype]
+    check("G", r["G"], f["G"], tol, name)
+    check("U", r["U"], f["U"], tol, name)
+    check("H", r["H"], f["H"], tol, name)
+    check("Zgu", r["Zgu"], np.concatenate([f["Zg"], f["Zu"]], 1), tol, name)
+    check("Zd", r["Zd"], f["Zd"], tol, name)
+    check("Y", r["Y"], f["Y"], tol, name)
+    check("out", r["out"], f["out"], tol, name)
+    check("dx", r["dx"], b["dx"], tol, name)
+    for g in GRADS:
+        check(g, r[g], b[g], tol, name)
+    check("d_topk_w", r["d_topk_w"], b["d_topk_w"], tol, name)
+    check("d_logits", r["d_logits"], b["d_logits"], tol, name)
+    unselected = b["d_logits"] == 0.0
+    assert np.all(r["d_logits"][unselected] == 0.0)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def edge_case(name):
+    base = dict(d=64, F=64, r=8, dtype="bf16", alpha=16.0, router_grad=True)
+    if name == "one_token":
+        return LayerConfig(name, T=1, E=4, k=2, **base), None
+    if name == "k_equals_E":
+        return LayerConfig(name, T=40, E=4, k=4, **base), None
+    if name == "single_expert":
+        return LayerConfig(name, T=70, E=1, k=1, **base), None
+    if name == "all_to_one_expert":
+        cfg = LayerConfig(name, T=90, E=5, k=1, **base)
+        return cfg, lambda l: l.__setitem__((slice(None), 2), 100.0)
+    if name == "integer_ties":
+        cfg = LayerConfig(name, T=128, E=8, k=3, **base)
+        return cfg, lambda l: l.__setitem__(slice(None), np.floor(l * 0.7))
+    if name == "multi_chunk_expert":  # > 1024 rows on one expert: chunked LoRA gradients
+        cfg = LayerConfig(name, T=2100, E=3, k=1, **base)
+        return cfg, lambda l: l.__setitem__((slice(0, 2050), 0), 50.0)
+    if name == "fp32_ties":
+        cfg = LayerConfig(name, T=64, E=6, k=2, d=32, F=40, r=8, dtype="f32", alpha=16.0,
+                          router_grad=True)
+        return cfg, lambda l: l.__setitem__(slice(None), np.floor(l))
+    raise KeyError(name)
+
+
+EDGE = ["one_token", "k_equals_E", "single_expert", "all_to_one_expert", "integer_ties",
+        "multi_chunk_expert", "fp32_ties"]
+
+
+@pytest.mark.parametrize("name", EDGE)
+def test_edge_cases(name):
+    cfg, mutate = edge_case(name)
+    print(f"[edge] {name}", flush=True)
+    inputs = synth.make_inputs(cfg, seed=1)
+    if mutate is not None:
+        mutate(inputs["logits"])
+        inputs["logits"] = np.ascontiguousarray(inputs["logits"], dtype=np.float32)
+    _, r = run_small(cfg, inputs)
+    rt, f, b = oracle_full(cfg, inputs)
+    check_routing(r, rt, name)
+    tol = TOL[cfg.dtype]
+    check("out", r["out"], f["out"], tol, name)
+    check("dx", r["dx"], b["dx"], tol, name)
+    for g in GRADS:
+        check(g, r[g], b[g], tol, name)
+        empty = rt["counts"] == 0
+        assert np.all(r[g][empty] == 0.0), f"{name} {g}: empty experts must get exact zeros"
+    check("d_topk_w", r["d_topk_w"], b["d_topk_w"], tol, name)
+    check("d_logits", r["d_logits"], b["d_logits"], tol, name)
+
+
+def test_empty_batch():
+    lr = _runner()
+    cfg = LayerConfig("empty", T=0, d=64, E=4, k=2, F=64, r=8, dtype="bf16", alpha=16.0)
+    inputs = synth.make_inputs(cfg.with_(T=1), seed=0)
+    for n in ("x", "logits", "dout"):
+        inputs[n] = inputs[n][:0]
+    L = lr.Layer(cfg, inputs, keep_expert_out=True)
+    for g in L.grads.values():
+        g.fill_(7.0)
+    hc = np.full(cfg.E, -1, np.int32)
+    L.route(host_counts=hc)
+    L.fwd()
+    L.bwd(router_grad=True)
+    torch.cuda.synchronize()
+    assert np.all(hc == 0)
+    assert L.rt["offsets"].cpu().numpy().tolist() == [0] * (cfg.E + 1)
+    for g in L.grads.values():
+        assert torch.all(g == 0.0)
+
+
+def test_host_counts_readback_and_determinism():
+    lr = _runner()
+    cfg = SMALL["ragged_bf16"]
+    inputs = synth.make_inputs(cfg, seed=2)
+    L = lr.Layer(cfg, inputs, keep_expert_out=True)
+    hc = np.zeros(cfg.E, np.int32)
+    L.route(host_counts=hc)
+    L.fwd()
+    L.bwd(router_grad=True)
+    r1 = L.results(router_grad=True, intermediates=True)
+    assert np.array_equal(hc, oracle.route(inputs["logits"], cfg.k)["counts"])
+    L.step(backward=True, router_grad=True)
+    r2 = L.results(router_grad=True, intermediates=True)
+    for n in r1:
+        assert np.array_equal(r1[n], r2[n]), f"{n} not bit-identical across runs"
+
+
+def test_graph_capture_has_no_hidden_sync():
+    """route (no readback) + fwd + bwd captured in one HIP graph, replayed."""
+    lr = _runner()
+    cfg = SMALL["ragged_bf16"]
+    inputs = synth.make_inputs(cfg, seed=3)
+    L = lr.Layer(cfg, inputs, keep_expert_out=True)
+    L.step(backward=True, router_grad=True)
+    ref = L.results(router_grad=True, intermediates=True)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            L.step(backward=True, router_grad=True)
+    torch.cuda.current_stream().wait_stream(s)
+    for it in range(3):
+        L.out.zero_()
+        L.dx.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = L.results(router_grad=True, intermediates=True)
+        for n in ref:
+            assert np.array_equal(got[n], ref[n]), f"replay {it}: {n} differs from eager"
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+FULL = ["gptoss20b", "qwen3_30b_a3b", "qwen3_30b_a3b_skewed", "gptoss120b"]
+
+
+def sample_tokens(T, n=6, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, n - 2)])).astype(np.int32)
+
+
+def sample_experts(counts, multi_chunk=False):
+    ne = [e for e in range(len(counts)) if counts[e] > 0]
+    ex = [min(ne, key=lambda e: counts[e])]
+    empty = [e for e in range(len(counts)) if counts[e] == 0]
+    if empty:
+        ex.append(empty[0])
+    if multi_chunk:
+        big = [e for e in ne if counts[e] > 1024]
+        if big:
+            ex.append(min(big, key=lambda e: counts[e]))
+    return ex
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    lr = _runner()
+    cfg = synth.get_config(name)
+    print(f"[full] {name}: generating inputs", flush=True)
+    inputs = synth.make_inputs(cfg, seed=0, with_dout=cfg.backward)
+    L = lr.Layer(cfg, inputs, keep_expert_out=cfg.router_grad, training=cfg.backward)
+    print(f"[full] {name}: GPU step", flush=True)
+    L.step(backward=cfg.backward, router_grad=cfg.router_grad)
+    r = L.results(backward=cfg.backward, router_grad=cfg.router_grad)
+    del L
+    torch.cuda.empty_cache()
+    print(f"[full] {name}: oracle", flush=True)
+    rt = oracle.route(inputs["logits"], cfg.k)
+    check_routing(r, rt, name)
+    OL = oracle.Layer.from_config(cfg, inputs)
+    toks = sample_tokens(cfg.T)
+    tol = TOL[cfg.dtype]
+    fo = oracle.fwd_tokens(OL, rt, toks)
+    check("out rows", r["out"][toks], fo["out"], tol, name)
+    if cfg.backward:
+        bo = oracle.bwd_tokens(OL, rt, inputs["dout"], toks)
+        check("dx rows", r["dx"][toks], bo["dx"], tol, name)
+        if cfg.router_grad:
+            check("d_topk_w rows", r["d_topk_w"][toks], bo["d_topk_w"], tol, name)
+            check("d_logits rows", r["d_logits"][toks], bo["d_logits"], tol, name)
+        ex = sample_experts(rt["counts"], multi_chunk=name.endswith("skewed"))
+        print(f"[full] {name}: LoRA grads of experts {ex} (rows {rt['counts'][ex].tolist()})",
+              flush=True)
+        go = oracle.lora_grads(OL, rt, inputs["dout"], ex)
+        for g in GRADS:
+            check(g, r[g][ex], go[g], tol, name)
+            for i, e in enumerate(ex):
+                if rt["counts"][e] == 0:
+                    assert np.all(r[g][e] == 0.0)
