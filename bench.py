@@ -1,0 +1,229 @@
+"""Benchmark of the MoE expert layer (routing + grouped GEMMs with Split-LoRA,
+forward + backward) on one MI355X.
+
+A step is one pass of the whole hot path over one batch of the workload:
+moe_route (with the one count readback to the host) + moe_fwd + moe_bwd.
+Inputs are seeded synthetic tensors with the workload's shapes and
+distributions, resident in HBM before timing starts. Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload qwen3_30b_a3b]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA/vector
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "MoE layer fwd+bwd tokens/s; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_a3b")
+    ap.add_argument("--no-readback", action="store_true",
+                    help="route without copying the expert counts to the host")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens of the workload the CPU oracle baseline runs on")
+    ap.add_argument("--skip-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def gemm_flops_per_slot(c):
+    d, F, r = c.d, c.F, c.r
+    return {
+        "proj_gu": 4 * d * r, "gateup": 4 * d * F + 4 * r * F, "proj_d": 2 * F * r,
+        "down": 2 * d * F + 2 * d * r, "proj_dout": 2 * d * r, "down_bwd": 2 * d * F + 2 * r * F,
+        "proj_dgu": 4 * F * r, "gateup_bwd": 4 * d * F + 4 * r * d, "lora_grad": 6 * r * (d + F),
+    }
+
+
+class Hip:
+    """hipEvent_* from the HIP runtime torch has loaded (same soname)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def cpu_baseline(cfg, tokens):
+    import oracle
+    import synth
+    inputs = synth.make_inputs(cfg, seed=0, tokens=tokens)
+    L = oracle.Layer.from_config(cfg, inputs, tokens=tokens)
+    t0 = time.perf_counter()
+    rt = oracle.route(inputs["logits"], cfg.k)
+    oracle.fwd(L, rt)
+    if cfg.backward:
+        oracle.bwd(L, rt, inputs["dout"])
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {tokens} of the {cfg.T} tokens of the same layer (same weights and "
+                      f"generator), route+fwd" + ("+bwd" if cfg.backward else "") +
+                      ", fp64 plain loops, OpenMP over experts"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"{max(args.gpus, world)} GPUs). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_layer_lora_amd as moe
+    import synth
+
+    cfg = synth.get_config(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pb = moe.Problem.from_config(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t_gen = time.perf_counter()
+    inputs = synth.make_inputs(cfg, seed=0, with_dout=cfg.backward)
+    x, logits = up(inputs["x"]), up(inputs["logits"])
+    names = ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
+    w = {n: up(inputs[n]) for n in names}
+    dout = up(inputs["dout"]) if cfg.backward else None
+    del inputs
+    t_gen = time.perf_counter() - t_gen
+
+    keep = cfg.router_grad
+    rt = moe.alloc_routing(pb, dev)
+    ws_r = moe.alloc_bytes(moe.route_workspace(pb), dev)
+    ws_f = moe.alloc_bytes(moe.fwd_workspace(pb, cfg.backward, keep), dev)
+    saved = moe.alloc_bytes(moe.saved_bytes(pb, keep), dev) if cfg.backward else None
+    out = torch.empty((cfg.T, cfg.d), dtype=dt, device=dev)
+    if cfg.backward:
+        ws_b = moe.alloc_bytes(moe.bwd_workspace(pb), dev)
+        dx = torch.empty((cfg.T, cfg.d), dtype=dt, device=dev)
+        grads = moe.alloc_grads(pb, dev)
+        dtw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev) if keep else None
+        dlg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev) if keep else None
+    host_counts = np.zeros(cfg.E, np.int32)
+    stream = torch.cuda.current_stream()
+
+    def step(trace=None):
+        moe.moe_route(pb, logits, rt, host_counts=None if args.no_readback else host_counts,
+                      ws=ws_r, stream=stream, trace=trace)
+        moe.moe_fwd(pb, x, rt, w, out, saved=saved, keep_expert_out=keep, ws=ws_f, stream=stream,
+                    trace=trace)
+        if cfg.backward:
+            moe.moe_bwd(pb, x, dout, rt, w, saved, keep, dx, grads, d_topk_w=dtw, d_logits=dlg,
+                        ws=ws_b, stream=stream, trace=trace)
+
+    hip = Hip()
+    traces, events = [], []
+    for _ in range(args.steps):
+        tr = moe.Trace()
+        for i in range(moe.MOE_K_COUNT):
+            a, b = hip.event(), hip.event()
+            tr.start[i], tr.stop[i] = a, b
+            events += [a, b]
+        traces.append(tr)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel HIP events recorded on the launch stream
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(traces[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    kern_ms = {}
+    for i, name in enumerate(moe.KERNELS):
+        if not cfg.backward and i >= moe.KERNELS.index("router_grad"):
+            continue
+        if name == "router_grad" and not keep:
+            continue
+        v = [hip.elapsed_ms(tr.start[i], tr.stop[i]) for tr in traces]
+        kern_ms[name] = sum(v) / len(v)
+    for ev in events:
+        hip.destroy(ev)
+
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = cfg.T * args.steps / elapsed
+    fps = gemm_flops_per_slot(cfg)
+    S = cfg.S
+    gemm_names = [n for n in fps if n in kern_ms]
+    gemm_flops = sum(fps[n] * S for n in gemm_names)
+    gemm_ms = sum(kern_ms[n] for n in gemm_names)
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    dom = max((n for n in ("gateup", "down", "down_bwd", "gateup_bwd") if n in kern_ms),
+              key=lambda n: kern_ms[n])
+    ach = fps[dom] * S / (kern_ms[dom] * 1e-3) / 1e12
+
+    rec = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name} MoE layer", "T": cfg.T, "d": cfg.d, "E": cfg.E,
+                   "k": cfg.k, "F": cfg.F, "r": cfg.r, "lora_scale": cfg.s,
+                   "step": "route" + ("" if args.no_readback else "(+count readback)") + "+fwd" +
+                           ("+bwd" if cfg.backward else "") +
+                           ("+router-weight grad" if keep else ""),
+                   "parallelism": "single GPU"},
+        "grouped_gemm": {"tflops": round(gemm_tflops, 2),
+                         "frac_of_peak": round(gemm_tflops / peak, 4),
+                         "flops_per_step": gemm_flops, "ms_per_step": round(gemm_ms, 4),
+                         "kernels": gemm_names},
+        "kernels_ms": {n: round(v, 4) for n, v in kern_ms.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                     "flops_per_launch": fps[dom] * S},
+        "input_setup_s": round(t_gen, 2),
+    }
+    if not args.skip_cpu:
+        rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -58,8 +58,15 @@ def _load():
         for f in (lib.orc_route, lib.orc_fwd, lib.orc_bwd, lib.orc_fwd_tokens,
                   lib.orc_bwd_tokens, lib.orc_lora_grads):
             f.restype = ctypes.c_int
+        lib.orc_threads.argtypes = []
+        lib.orc_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_threads())
 
 
 def _p(a):

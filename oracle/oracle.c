@@ -44,6 +44,7 @@
  * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -55,6 +56,9 @@ typedef struct {
     const void *x, *w_gate, *w_up, *w_down;
     const void *a_gate, *b_gate, *a_up, *b_up, *a_down, *b_down;
 } orc_layer_t;
+
+/* threads the parallel loops below will use */
+int orc_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------ */
 /* stored value -> double (exact)                                      */
