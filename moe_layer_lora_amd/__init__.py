@@ -21,6 +21,11 @@ from __future__ import annotations
 import ctypes
 import os
 
+try:  # torch first: libmoe.so then binds to the HIP runtime torch already
+    import torch  # noqa: F401  # loaded, so both share one runtime and its streams
+except ImportError:  # host-only use (size queries, argument checks)
+    torch = None
+
 from ._build import LIB_PATH, build  # noqa: F401
 
 MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
@@ -127,7 +132,6 @@ def _nbytes(t):
 
 def _stream(stream):
     if stream is None:
-        import torch
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream
@@ -191,7 +195,6 @@ def moe_bwd(pb, x, dout, rt: dict, w: dict, saved, keep_expert_out, dx, grads: d
 
 # ---------------------------------------------------------------- allocation helpers
 def alloc_routing(pb: Problem, device):
-    import torch
     T, E, k = pb.T, pb.E, pb.k
     i32 = torch.int32
     return {"topk_idx": torch.empty((T, k), dtype=i32, device=device),
@@ -203,12 +206,10 @@ def alloc_routing(pb: Problem, device):
 
 
 def alloc_bytes(n: int, device):
-    import torch
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
 def alloc_grads(pb: Problem, device):
-    import torch
     E, d, F, r = pb.E, pb.d, pb.F, pb.r
     f = torch.float32
     return {"da_gate": torch.empty((E, r, d), dtype=f, device=device),
@@ -221,7 +222,6 @@ def alloc_grads(pb: Problem, device):
 
 def saved_views(pb: Problem, saved, keep_expert_out: bool) -> dict:
     """Typed views of the `saved` buffer (layout documented in moe.h)."""
-    import torch
     S, F, r, d = pb.S, pb.F, pb.r, pb.d
     dt = torch.bfloat16 if pb.dtype == MOE_BF16 else torch.float32
     es = 2 if pb.dtype == MOE_BF16 else 4

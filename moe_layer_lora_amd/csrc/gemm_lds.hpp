@@ -1,0 +1,410 @@
+// gemm_lds.hpp - bf16 grouped-GEMM engine for gfx950 built on direct
+// global->LDS loads and transposing LDS reads.
+//
+// Tile: BM x BN per workgroup of 4 waves (2 x 2), each wave 128 x 128 for the
+// 256 x 256 shape: 16 v_mfma_f32_32x32x16_bf16 accumulators (256 registers).
+// K advances BK = 32 per step through a ring of NSTAGE LDS stages filled by
+// buffer_load_dwordx4 ... lds (no staging registers): NSTAGE-1 steps are in
+// flight while one is multiplied.
+//
+// LDS layouts (byte offsets inside a stage):
+//  K-contiguous operand [rows][BK]: 64-byte rows of 4 16-byte chunks; chunk c
+//    of row r sits at physical chunk c ^ ((r >> 1) & 3). The 8 rows an MFMA
+//    fragment read touches per LDS cycle then cover all 32 banks.
+//  N-contiguous operand [BK][BN] (k-rows of BN elements): 16-byte chunk c of
+//    k-row k sits at physical chunk c ^ (2 * (k & 3)), so the 4 k-rows a
+//    ds_read_b64_tr_b16 group touches fall in distinct banks.
+// A direct load writes 1 KB contiguous per wave instruction (lane l at 16 l),
+// so each lane loads the global chunk that belongs at its LDS slot.
+#pragma once
+
+#include "gemm.hpp"
+
+namespace moe {
+namespace lds {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+#define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+template <int BM_, int BN_, int NSTAGE_, bool BN_CONTIG_>
+struct Cfg {
+    using T = bf16_t;
+    static constexpr int BM = BM_, BN = BN_, BK = 32, NSTAGE = NSTAGE_;
+    static constexpr bool B_NCONTIG = BN_CONTIG_;
+    static constexpr int WM = 2, WN = 2, NTHREADS = 256, NWAVES = 4;
+    static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+    static constexpr int CPR = BK / 8;                       // 16-byte chunks per K-contig row
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;  // direct loads per wave per step
+    static constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;
+    static constexpr int LOADS_PER_STEP = A_INSTR + B_INSTR;
+    static constexpr int ROWS_PER_INSTR = 1024 / (BK * 2);   // K-contig rows per 1 KB
+    static constexpr int KROWS_PER_INSTR = 1024 / (BN * 2);  // N-contig k-rows per 1 KB
+    static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "whole loads per wave");
+    static_assert(CPR == 4, "the K-contig swizzle assumes 64-byte rows");
+    static_assert(!B_NCONTIG || (BN * 2) % 1024 == 0 || 1024 % (BN * 2) == 0, "k-rows tile 1 KB loads");
+};
+
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int swz_n(int krow) { return 2 * (krow & 3); }
+
+// ---------------------------------------------------------------------------
+// Direct loads of one K-contiguous operand tile (ROWS x BK) into LDS.
+// Each thread owns INSTR rows (one per wave instruction); their byte offsets
+// (row start + segment column base handled by the caller) are fixed for the
+// whole K loop.
+template <int ROWS, int INSTR>
+struct KDirect {
+    uint32_t off[INSTR];   // byte offset of the thread's row, kInvalid if outside
+    int pchunk;            // this lane's physical chunk within its row
+    // chunk of the row this lane fetches: logical = physical ^ swizzle(row)
+    int lchunk[INSTR];
+
+    __device__ void init_rows(int wave, int lane, const uint32_t (&rowoff)[INSTR]) {
+        pchunk = lane & 3;
+#pragma unroll
+        for (int j = 0; j < INSTR; ++j) {
+            const int row = (wave * INSTR + j) * 16 + (lane >> 2);
+            lchunk[j] = pchunk ^ swz_k(row);
+            off[j] = rowoff[j];
+        }
+    }
+    // row (within the tile) that instruction j of this lane covers
+    __device__ static int row_of(int wave, int lane, int j, int instr) { return (wave * instr + j) * 16 + (lane >> 2); }
+
+    // issue the INSTR loads of K-step kstep (k elements [k0, k0 + 32) of the
+    // segment, valid for k < K) into the stage region at `lds`
+    __device__ __forceinline__ void issue(rsrc_t rs, uint32_t colbytes, int k0, int K, char *lds, int wave) const {
+#pragma unroll
+        for (int j = 0; j < INSTR; ++j) {
+            const int k = k0 + lchunk[j] * 8;
+            const uint32_t vo = (off[j] != kInvalid && k < K) ? off[j] + colbytes + (uint32_t)k * 2 : kInvalid;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDS_PTR(lds + (wave * INSTR + j) * 1024), 16, vo, 0, 0, 0);
+        }
+    }
+};
+
+// Direct loads of one N-contiguous operand tile (BK k-rows x BN) into LDS:
+// element (k, n) of the segment at byte k * ldb + n * 2 of the descriptor
+// (the descriptor base already at the tile's first column).
+template <int BN, int INSTR>
+struct NDirect {
+    static constexpr int KR = 1024 / (BN * 2);  // k-rows per 1 KB instruction
+    int krow[INSTR];
+    int ncol_off[INSTR];   // element offset n of this lane's chunk
+    bool nok[INSTR];
+
+    __device__ void init(int wave, int lane, int ncol) {
+#pragma unroll
+        for (int j = 0; j < INSTR; ++j) {
+            const int q = wave * INSTR + j;
+            const int byte = lane * 16;               // within the 1 KB block
+            krow[j] = q * KR + byte / (BN * 2);
+            const int pch = (byte % (BN * 2)) / 16;   // physical chunk in the k-row
+            const int lch = pch ^ swz_n(krow[j]);
+            ncol_off[j] = lch * 8;
+            nok[j] = ncol_off[j] + 8 <= ncol;
+        }
+    }
+    __device__ __forceinline__ void issue(rsrc_t rs, uint32_t ldb, int k0, int K, char *lds, int wave) const {
+#pragma unroll
+        for (int j = 0; j < INSTR; ++j) {
+            const int k = k0 + krow[j];
+            const uint32_t vo = (nok[j] && k < K) ? (uint32_t)k * ldb + (uint32_t)ncol_off[j] * 2 : kInvalid;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDS_PTR(lds + (wave * INSTR + j) * 1024), 16, vo, 0, 0, 0);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Register-staged stores into the same layouts (used for the rank-r LoRA
+// tile, whose A side is fp32 scaled by s and so cannot be loaded directly).
+// K-contiguous: chunk (row, logical c) -> physical c ^ swz_k(row).
+__device__ __forceinline__ void st_kcontig(char *lds, int row, int c, const chunk_t &v) {
+    *reinterpret_cast<chunk_t *>(lds + row * 64 + ((c ^ swz_k(row)) * 16)) = v;
+}
+// N-contiguous: 8 consecutive n at (k, n0) -> physical chunk (n0 / 8) ^ swz_n(k).
+template <int BN>
+__device__ __forceinline__ void st_ncontig(char *lds, int k, int n0, const chunk_t &v) {
+    *reinterpret_cast<chunk_t *>(lds + k * BN * 2 + (((n0 >> 3) ^ swz_n(k)) * 16)) = v;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA work of one K step out of a stage.
+template <class C>
+__device__ __forceinline__ void mma_step(const char *sa, const char *sb, f32x16_t (&acc)[C::TM][C::TN]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    // A fragments: row (wm*WTM + mi*32 + lane%32), logical chunk kg*2 + lane/32
+    const int arow0 = wm * C::WTM + (lane & 31);
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+        chunk_t af[C::TM], bfr[C::TN];
+#pragma unroll
+        for (int mi = 0; mi < C::TM; ++mi) {
+            const int row = arow0 + mi * 32;
+            const int c = kg * 2 + (lane >> 5);
+            af[mi] = *reinterpret_cast<const chunk_t *>(sa + row * 64 + ((c ^ swz_k(row)) * 16));
+        }
+        if constexpr (!C::B_NCONTIG) {
+            const int brow0 = wn * C::WTN + (lane & 31);
+#pragma unroll
+            for (int ni = 0; ni < C::TN; ++ni) {
+                const int row = brow0 + ni * 32;
+                const int c = kg * 2 + (lane >> 5);
+                bfr[ni] = *reinterpret_cast<const chunk_t *>(sb + row * 64 + ((c ^ swz_k(row)) * 16));
+            }
+        } else {
+            // transposing reads: 16-lane group g gets 4 k of 16 columns per read
+            const int g = lane >> 4, s = lane & 15;
+            const int kbase = kg * 16 + (g >> 1) * 8 + (s >> 2);
+#pragma unroll
+            for (int ni = 0; ni < C::TN; ++ni) {
+                const int n = wn * C::WTN + ni * 32 + (g & 1) * 16 + 4 * (s & 3);
+                s16x4_t h[2];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int k = kbase + 4 * half;
+                    const char *p = sb + k * C::BN * 2 + (((n >> 3) ^ swz_n(k)) * 16) + (n & 7) * 2;
+                    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4_t *)(p));
+                }
+                bfr[ni] = chunk_t{(uint32_t)(uint16_t)h[0].x | ((uint32_t)(uint16_t)h[0].y << 16),
+                                  (uint32_t)(uint16_t)h[0].z | ((uint32_t)(uint16_t)h[0].w << 16),
+                                  (uint32_t)(uint16_t)h[1].x | ((uint32_t)(uint16_t)h[1].y << 16),
+                                  (uint32_t)(uint16_t)h[1].z | ((uint32_t)(uint16_t)h[1].w << 16)};
+            }
+        }
+#pragma unroll
+        for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::TN; ++ni)
+                Elem<bf16_t>::mma(acc[mi][ni], af[mi], bfr[ni]);
+    }
+}
+
+// wait until at most N direct loads of this wave are outstanding
+template <int N> __device__ __forceinline__ void wait_vm() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else static_assert(N < 0, "unsupported wait count");
+}
+
+}  // namespace lds
+}  // namespace moe
+
+namespace moe {
+namespace lds {
+
+// Operands of one grouped-GEMM tile for the ring driver below. Up to two K
+// segments; step t < nt0 is segment 0 at k = 32 t, else segment 1.
+template <class C>
+struct Operands {
+    KDirect<C::BM, C::A_INSTR> a;
+    rsrc_t ra[2];
+    uint32_t acol[2] = {0, 0};     // byte column base of the A rows per segment
+    int K[2] = {0, 0};
+    int nt0 = 0, nt = 0;
+    // B, K-contiguous: rows through rb[seg][sel] with sel a per-instruction
+    // choice (bit j of bsel_mask for this wave)
+    KDirect<C::BN, C::B_INSTR> bk;
+    uint32_t bsel_mask = 0;
+    // B, N-contiguous
+    NDirect<C::BN, C::B_INSTR> bn;
+    uint32_t ldb[2] = {0, 0};
+    rsrc_t rb[2][2];
+
+    __device__ __forceinline__ void issue(int t, char *stage, int wave) const {
+        const bool s1 = t >= nt0;
+        const int k0 = (s1 ? t - nt0 : t) * C::BK;
+        const int Ks = s1 ? K[1] : K[0];
+        a.issue(s1 ? ra[1] : ra[0], s1 ? acol[1] : acol[0], k0, Ks, stage, wave);
+        char *sb = stage + C::A_BYTES;
+        if constexpr (C::B_NCONTIG) {
+            bn.issue(s1 ? rb[1][0] : rb[0][0], s1 ? ldb[1] : ldb[0], k0, Ks, sb, wave);
+        } else {
+#pragma unroll
+            for (int j = 0; j < C::B_INSTR; ++j) {
+                const bool sel = (bsel_mask >> j) & 1u;
+                const rsrc_t d = s1 ? (sel ? rb[1][1] : rb[1][0]) : (sel ? rb[0][1] : rb[0][0]);
+                const int k = k0 + bk.lchunk[j] * 8;
+                const uint32_t vo = (bk.off[j] != kInvalid && k < Ks) ? bk.off[j] + (uint32_t)k * 2 : kInvalid;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(d, MOE_LDS_PTR(sb + (wave * C::B_INSTR + j) * 1024), 16, vo,
+                                                         0, 0, 0);
+            }
+        }
+    }
+};
+
+// Ring driver: LoRA tiles first (stage 0, staged through registers by
+// lora.load / lora.store), then nt steady steps through stages 1.. in a
+// ring. The first LoRA tile's global loads are issued before the ring's, so
+// waiting for them leaves the ring loads in flight.
+template <class C, class Lora>
+__device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora &lora, char *smem,
+                                    f32x16_t (&acc)[C::TM][C::TN]) {
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+    const int wave = threadIdx.x >> 6;
+    auto stage_of = [&](int t) { return smem + ((t + 1) % C::NSTAGE) * C::STAGE_BYTES; };
+    typename Lora::Regs lr;
+    if (nlora > 0) lora.load(0, lr);
+    // keep the LoRA loads ahead of the ring loads: loads complete in order,
+    // so waiting for the LoRA data must not also wait for the ring
+    __builtin_amdgcn_sched_barrier(0);
+    // ring prologue: steps 0 .. NSTAGE-2 in flight
+#pragma unroll
+    for (int t = 0; t < C::NSTAGE - 1; ++t)
+        if (t < op.nt) op.issue(t, stage_of(t), wave);
+    // rank-r LoRA expansion tiles through stage 0 while the ring fills
+    for (int lt = 0; lt < nlora; ++lt) {
+        if (lt > 0) lora.load(lt, lr);
+        lora.store(lr, smem);
+        // LDS writes done, then a bare barrier: the ring loads stay in flight
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        mma_step<C>(smem, smem + C::A_BYTES, acc);
+        if (lt + 1 < nlora) {  // stage 0 is refilled by the next LoRA tile
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+    }
+    for (int t = 0; t < op.nt; ++t) {
+        const int ahead = op.nt - 1 - t;  // steps issued after t that may stay in flight
+        if (ahead >= C::NSTAGE - 2) wait_vm<(C::NSTAGE - 2) * C::LOADS_PER_STEP>();
+        else if (ahead == 1) wait_vm<C::LOADS_PER_STEP>();
+        else wait_vm<0>();
+        // Bare barrier: step t's LDS data is in (the wait above) and every
+        // fragment read of step t-1 was consumed by an MFMA before this point.
+        // __syncthreads() would add a release fence, i.e. a full vmcnt(0)
+        // drain of the steps still in flight. The empty asm keeps the
+        // compiler from moving LDS accesses across the barrier.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (t + C::NSTAGE - 1 < op.nt) op.issue(t + C::NSTAGE - 1, stage_of(t + C::NSTAGE - 1), wave);
+        const char *st = stage_of(t);
+        mma_step<C>(st, st + C::A_BYTES, acc);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// LoRA tile pieces (register-staged). A side: rows p of an fp32 [S, nz]
+// matrix times s, k = 32 lt + ..., into the K-contiguous A tile.
+template <class C>
+struct LoraA {
+    static constexpr int PER = C::BM * 4 / 256;
+    const float *z;
+    int nz, row0, rows;
+    float s;
+    struct Regs { float4 v[PER][2]; uint32_t ok; };
+    // raw loads only (invalid chunks read a valid address); zeroing happens in
+    // store(), so issuing these needs no wait on their data
+    __device__ __forceinline__ void load(int lt, Regs &r) const {
+        r.ok = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = (int)threadIdx.x + 256 * i;
+            const int row = c >> 2, k = lt * 32 + (c & 3) * 8;
+            const bool ok = row < rows && k < nz;
+            const float4 *src = reinterpret_cast<const float4 *>(ok ? z + (size_t)(row0 + row) * nz + k : z);
+            r.v[i][0] = src[0];
+            r.v[i][1] = src[1];
+            r.ok |= (uint32_t)ok << i;
+        }
+    }
+    __device__ __forceinline__ void store(const Regs &r, char *st) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = (int)threadIdx.x + 256 * i;
+            const float m = ((r.ok >> i) & 1u) ? s : 0.0f;
+            const float4 a = r.v[i][0], b = r.v[i][1];
+            const float v[8] = {a.x * m, a.y * m, a.z * m, a.w * m, b.x * m, b.y * m, b.z * m, b.w * m};
+            st_kcontig(st, c >> 2, c & 3, Elem<bf16_t>::pack(v));
+        }
+    }
+};
+
+// B side, K-contiguous rows of rank r: tile row n holds row_of(n) of a [*, r]
+// matrix (a or b) placed at k in [klo, klo + r) of the 32 lt + ... range.
+// The row map comes from the kernel as per-chunk pointers and offsets.
+template <class C>
+struct LoraBK {
+    static constexpr int PER = C::BN * 4 / 256;
+    const bf16_t *rowp[PER];  // row start (element k = klo), nullptr outside
+    int klo[PER];
+    int r;
+    const bf16_t *safe;       // any readable address (loaded, then discarded, for empty chunks)
+    struct Regs { chunk_t v[PER]; uint32_t ok; };
+    __device__ __forceinline__ void load(int lt, Regs &rg) const {
+        rg.ok = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = (int)threadIdx.x + 256 * i;
+            const int k = lt * 32 + (c & 3) * 8 - klo[i];
+            const bool ok = rowp[i] && k >= 0 && k < r;
+            rg.v[i] = *reinterpret_cast<const chunk_t *>(ok ? rowp[i] + k : safe);
+            rg.ok |= (uint32_t)ok << i;
+        }
+    }
+    __device__ __forceinline__ void store(const Regs &rg, char *st) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = (int)threadIdx.x + 256 * i;
+            st_kcontig(st + C::A_BYTES, c >> 2, c & 3, ((rg.ok >> i) & 1u) ? rg.v[i] : zero4());
+        }
+    }
+};
+
+// B side, N-contiguous: k-rows j of up to two stacked [*, ld] matrices (rows
+// < split from a, the rest from b, K rows in all), tile columns [0, ncol).
+template <class C>
+struct LoraBN {
+    static constexpr int PER = 32 * C::BN / 8 / 256;
+    const bf16_t *a, *b;
+    int split, K, ld, ncol;
+    struct Regs { chunk_t v[PER]; uint32_t ok; };
+    __device__ __forceinline__ void load(int lt, Regs &rg) const {
+        rg.ok = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = (int)threadIdx.x + 256 * i;
+            const int kr = c / (C::BN / 8), n = (c % (C::BN / 8)) * 8;
+            const int j = lt * 32 + kr;
+            const bool ok = j < K && n + 8 <= ncol;
+            const bf16_t *src = ok ? (j < split ? a + (size_t)j * ld : b + (size_t)(j - split) * ld) + n : a;
+            rg.v[i] = *reinterpret_cast<const chunk_t *>(src);
+            rg.ok |= (uint32_t)ok << i;
+        }
+    }
+    __device__ __forceinline__ void store(const Regs &rg, char *st) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = (int)threadIdx.x + 256 * i;
+            st_ncontig<C::BN>(st + C::A_BYTES, c / (C::BN / 8), (c % (C::BN / 8)) * 8,
+                              ((rg.ok >> i) & 1u) ? rg.v[i] : zero4());
+        }
+    }
+};
+
+// a LoRA tile = its A piece and its B piece
+template <class PA, class PB>
+struct LoraTile {
+    PA pa;
+    PB pb;
+    struct Regs { typename PA::Regs a; typename PB::Regs b; };
+    __device__ __forceinline__ void load(int lt, Regs &r) const { pa.load(lt, r.a); pb.load(lt, r.b); }
+    __device__ __forceinline__ void store(const Regs &r, char *st) const { pa.store(r.a, st); pb.store(r.b, st); }
+};
+
+}  // namespace lds
+}  // namespace moe

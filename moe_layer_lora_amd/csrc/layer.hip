@@ -11,19 +11,26 @@
 // accumulation; W + s B A is never formed.
 #include "kernels.hpp"
 #include "gemm.hpp"
+#include "gemm_lds.hpp"
 #include "moe.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 
 constexpr int kMaxE = 1024;
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// The large tiles hold a 128x128 fp32 accumulator per wave (256 registers):
+// one wave per SIMD, so the full 512-entry register file (256 VGPR + 256
+// AGPR) is available to it.
+#define MOE_ONE_WAVE_PER_SIMD __attribute__((amdgpu_waves_per_eu(1, 1)))
+
 // Main grouped-GEMM tile shapes.
 template <typename T> struct MainCfg;
-template <> struct MainCfg<bf16_t> { using type = GemmCfg<bf16_t, 128, 128, 32, 2, 2>; };
-template <> struct MainCfg<float> { using type = GemmCfg<float, 128, 128, 16, 2, 2>; };
+template <> struct MainCfg<bf16_t> { using type = GemmCfg<bf16_t, 128, 128, 32, 2, 2>; };  // (bf16 runs the LDS-ring kernels)
+template <> struct MainCfg<float> { using type = GemmCfg<float, 128, 128, 32, 2, 2>; };
 // Skinny projections (N = r or 2r) and LoRA weight gradients (N = r or 2r).
 template <typename T, int BN> struct SkinnyCfg;
 template <int BN> struct SkinnyCfg<bf16_t, BN> { using type = GemmCfg<bf16_t, 128, BN, 32, 4 / (BN / 32), BN / 32>; };
@@ -47,54 +54,65 @@ struct GateUpP {
     const float *zgu;
     const int32_t *sorted_slot, *offsets;
     void *G, *U, *H;
-    int E, k, d, F, r;
+    int T, E, k, d, F, r;
     float s;
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS) void k_gateup(GateUpP p) {
+__global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup(GateUpP p) {
     using T = typename Cfg::T;
     __shared__ Smem<Cfg> sm;
     constexpr int HALF = Cfg::BN / 2;
     static_assert(Cfg::TN % 2 == 0, "gate/up pairs");
+    static_assert(Cfg::NTHREADS / Cfg::CPR == 32, "one 32-row gate or up block per chunk index");
     Tile tl;
     if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(p.F, HALF), blockIdx.x, sm.start, tl)) return;
     const int f_base = tl.nt * HALF;
-    const int nk0 = cdiv(p.d, Cfg::BK), nk = nk0 + cdiv(2 * p.r, Cfg::BK);
 
+    // steady state: x rows (gathered by token) against W_gate / W_up rows
+    BufKLoader<Cfg, Cfg::BM> sa;
+    sa.rs[0][0] = sa.rs[0][1] = make_rsrc(p.x, (uint32_t)p.T * p.d * sizeof(T));
+    sa.K[0] = p.d; sa.nt0 = cdiv(p.d, Cfg::BK);
+#pragma unroll
+    for (int i = 0; i < sa.PER; ++i) {
+        const int m = sa.row_of(i);
+        sa.off[i] = m < tl.rows ? (uint32_t)token_of(p.sorted_slot, tl.row0 + m, p.k) * p.d * sizeof(T) : kInvalid;
+    }
+    BufKLoader<Cfg, Cfg::BN, true> sb;
+    const size_t wofs = (size_t)tl.e * p.F * p.d;
+    sb.rs[0][0] = make_rsrc(static_cast<const T *>(p.wg) + wofs, (uint32_t)p.F * p.d * sizeof(T));
+    sb.rs[0][1] = make_rsrc(static_cast<const T *>(p.wu) + wofs, (uint32_t)p.F * p.d * sizeof(T));
+    sb.K[0] = p.d; sb.nt0 = sa.nt0;
+#pragma unroll
+    for (int i = 0; i < sb.PER; ++i) {
+        const int n = sb.row_of(i);
+        const int wn = n / Cfg::WTN, ni = (n % Cfg::WTN) / 32;
+        const int f = f_base + wn * (Cfg::WTN / 2) + (ni / 2) * 32 + (n % 32);
+        sb.off[i] = f < p.F ? (uint32_t)f * p.d * sizeof(T) : kInvalid;
+    }
+    // LoRA tile: [s Zg | s Zu] rows against [B_g | 0] (gate rows) and [0 | B_u] (up rows)
     KLoader<Cfg, Cfg::BM, true> la;
-    la.K0 = p.d; la.K1 = 2 * p.r; la.nk0 = nk0; la.scale1 = p.s;
+    la.K1 = 2 * p.r; la.nk0 = 0; la.scale1 = p.s;
+    la.b1[0] = la.b1[1] = p.zgu;
 #pragma unroll
     for (int i = 0; i < la.PER; ++i) {
-        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
-        if (!la.active(i)) continue;
         const int m = la.row_of(i);
-        if (m < tl.rows) {
-            const int pr = tl.row0 + m;
-            la.p0[i] = static_cast<const T *>(p.x) + (size_t)token_of(p.sorted_slot, pr, p.k) * p.d;
-            la.p1[i] = p.zgu + (size_t)pr * 2 * p.r;
-        }
+        if (la.active(i) && m < tl.rows) la.set1(i, (uint32_t)(tl.row0 + m) * 2 * p.r, 0);
     }
     KLoader<Cfg, Cfg::BN, false> lb;
-    lb.K0 = p.d; lb.K1 = 2 * p.r; lb.nk0 = nk0; lb.scale1 = 1.0f;
+    lb.K1 = 2 * p.r; lb.nk0 = 0;
+    lb.b1[0] = static_cast<const T *>(p.bg) + (size_t)tl.e * p.F * p.r;
+    lb.b1[1] = static_cast<const T *>(p.bu) + (size_t)tl.e * p.F * p.r;
+    lb.wlo[0] = 0; lb.wlo[1] = p.r; lb.wwidth = p.r;
 #pragma unroll
     for (int i = 0; i < lb.PER; ++i) {
-        lb.p0[i] = nullptr; lb.p1[i] = nullptr; lb.klo1[i] = 0; lb.khi1[i] = 0;
-        if (!lb.active(i)) continue;
         const int n = lb.row_of(i);
         const int wn = n / Cfg::WTN, ni = (n % Cfg::WTN) / 32;
         const int f = f_base + wn * (Cfg::WTN / 2) + (ni / 2) * 32 + (n % 32);
-        const bool gate = (ni & 1) == 0;
-        if (f < p.F) {
-            const size_t row = (size_t)tl.e * p.F + f;
-            lb.p0[i] = static_cast<const T *>(gate ? p.wg : p.wu) + row * p.d;
-            lb.p1[i] = static_cast<const T *>(gate ? p.bg : p.bu) + row * p.r;
-            lb.klo1[i] = gate ? 0 : p.r;
-            lb.khi1[i] = gate ? p.r : 2 * p.r;
-        }
+        if (lb.active(i) && f < p.F) lb.set1(i, (uint32_t)f * p.r, ni & 1);
     }
     f32x16_t acc[Cfg::TM][Cfg::TN];
-    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    gemm_pipeline<Cfg>(sa, sb, sa.nt0, la, lb, cdiv(2 * p.r, Cfg::BK), sm.a, sm.b, acc);
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
@@ -125,46 +143,52 @@ struct DownP {
     const float *zd;
     const int32_t *offsets;
     void *Y;
-    int E, d, F, r;
+    int S, E, d, F, r;
     float s;
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS) void k_down(DownP p) {
+__global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_down(DownP p) {
     using T = typename Cfg::T;
     __shared__ Smem<Cfg> sm;
     Tile tl;
     if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(p.d, Cfg::BN), blockIdx.x, sm.start, tl)) return;
     const int n_base = tl.nt * Cfg::BN;
-    const int nk0 = cdiv(p.F, Cfg::BK), nk = nk0 + cdiv(p.r, Cfg::BK);
+    BufKLoader<Cfg, Cfg::BM> sa;
+    sa.rs[0][0] = sa.rs[0][1] = make_rsrc(p.H, (uint32_t)p.S * p.F * sizeof(T));
+    sa.K[0] = p.F; sa.nt0 = cdiv(p.F, Cfg::BK);
+#pragma unroll
+    for (int i = 0; i < sa.PER; ++i) {
+        const int m = sa.row_of(i);
+        sa.off[i] = m < tl.rows ? (uint32_t)(tl.row0 + m) * p.F * sizeof(T) : kInvalid;
+    }
+    BufKLoader<Cfg, Cfg::BN> sb;
+    sb.rs[0][0] = sb.rs[0][1] = make_rsrc(static_cast<const T *>(p.wd) + (size_t)tl.e * p.d * p.F,
+                                          (uint32_t)p.d * p.F * sizeof(T));
+    sb.K[0] = p.F; sb.nt0 = sa.nt0;
+#pragma unroll
+    for (int i = 0; i < sb.PER; ++i) {
+        const int n = n_base + sb.row_of(i);
+        sb.off[i] = n < p.d ? (uint32_t)n * p.F * sizeof(T) : kInvalid;
+    }
     KLoader<Cfg, Cfg::BM, true> la;
-    la.K0 = p.F; la.K1 = p.r; la.nk0 = nk0; la.scale1 = p.s;
+    la.K1 = p.r; la.nk0 = 0; la.scale1 = p.s;
+    la.b1[0] = la.b1[1] = p.zd;
 #pragma unroll
     for (int i = 0; i < la.PER; ++i) {
-        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
-        if (!la.active(i)) continue;
         const int m = la.row_of(i);
-        if (m < tl.rows) {
-            const int pr = tl.row0 + m;
-            la.p0[i] = static_cast<const T *>(p.H) + (size_t)pr * p.F;
-            la.p1[i] = p.zd + (size_t)pr * p.r;
-        }
+        if (la.active(i) && m < tl.rows) la.set1(i, (uint32_t)(tl.row0 + m) * p.r, 0);
     }
     KLoader<Cfg, Cfg::BN, false> lb;
-    lb.K0 = p.F; lb.K1 = p.r; lb.nk0 = nk0; lb.scale1 = 1.0f;
+    lb.K1 = p.r; lb.nk0 = 0; lb.wwidth = p.r;
+    lb.b1[0] = lb.b1[1] = static_cast<const T *>(p.bd) + (size_t)tl.e * p.d * p.r;
 #pragma unroll
     for (int i = 0; i < lb.PER; ++i) {
-        lb.p0[i] = nullptr; lb.p1[i] = nullptr; lb.klo1[i] = 0; lb.khi1[i] = p.r;
-        if (!lb.active(i)) continue;
         const int n = n_base + lb.row_of(i);
-        if (n < p.d) {
-            const size_t row = (size_t)tl.e * p.d + n;
-            lb.p0[i] = static_cast<const T *>(p.wd) + row * p.F;
-            lb.p1[i] = static_cast<const T *>(p.bd) + row * p.r;
-        }
+        if (lb.active(i) && n < p.d) lb.set1(i, (uint32_t)n * p.r, 0);
     }
     f32x16_t acc[Cfg::TM][Cfg::TN];
-    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    gemm_pipeline<Cfg>(sa, sb, sa.nt0, la, lb, cdiv(p.r, Cfg::BK), sm.a, sm.b, acc);
     T *Y = static_cast<T *>(p.Y);
     for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
         if (m < tl.rows && n_base + n < p.d) Y[(size_t)(tl.row0 + m) * p.d + n_base + n] = Elem<T>::from_f32(v);
@@ -181,55 +205,72 @@ struct DownBwdP {
     const float *pd, *topk_w;
     const int32_t *sorted_slot, *offsets;
     void *dGU;
-    int E, k, d, F, r;
+    int T, E, k, d, F, r;
     float s;
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS) void k_down_bwd(DownBwdP p) {
+__global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_down_bwd(DownBwdP p) {
     using T = typename Cfg::T;
     __shared__ Smem<Cfg> sm;
     Tile tl;
     if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(p.F, Cfg::BN), blockIdx.x, sm.start, tl)) return;
     const int n_base = tl.nt * Cfg::BN;
     const int ncol = min(Cfg::BN, p.F - n_base);
-    const int nk0 = cdiv(p.d, Cfg::BK), nk = nk0 + cdiv(p.r, Cfg::BK);
+    BufKLoader<Cfg, Cfg::BM> sa;
+    sa.rs[0][0] = sa.rs[0][1] = make_rsrc(p.dout, (uint32_t)p.T * p.d * sizeof(T));
+    sa.K[0] = p.d; sa.nt0 = cdiv(p.d, Cfg::BK);
+#pragma unroll
+    for (int i = 0; i < sa.PER; ++i) {
+        const int m = sa.row_of(i);
+        sa.off[i] = m < tl.rows ? (uint32_t)token_of(p.sorted_slot, tl.row0 + m, p.k) * p.d * sizeof(T) : kInvalid;
+    }
+    // W_d[e] is [d, F]: element (k = model dim, n = f)
+    BufNLoader<Cfg, Cfg::BN> sb;
+    sb.rs[0] = sb.rs[1] = make_rsrc(static_cast<const T *>(p.wd) + (size_t)tl.e * p.d * p.F + n_base,
+                                    (uint32_t)((size_t)p.d * p.F - n_base) * sizeof(T));
+    sb.K[0] = p.d; sb.ld[0] = p.F; sb.ncol = ncol; sb.nt0 = sa.nt0;
     KLoader<Cfg, Cfg::BM, true> la;
-    la.K0 = p.d; la.K1 = p.r; la.nk0 = nk0; la.scale1 = p.s;
+    la.K1 = p.r; la.nk0 = 0; la.scale1 = p.s;
+    la.b1[0] = la.b1[1] = p.pd;
 #pragma unroll
     for (int i = 0; i < la.PER; ++i) {
-        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
-        if (!la.active(i)) continue;
         const int m = la.row_of(i);
-        if (m < tl.rows) {
-            const int pr = tl.row0 + m;
-            la.p0[i] = static_cast<const T *>(p.dout) + (size_t)token_of(p.sorted_slot, pr, p.k) * p.d;
-            la.p1[i] = p.pd + (size_t)pr * p.r;
-        }
+        if (la.active(i) && m < tl.rows) la.set1(i, (uint32_t)(tl.row0 + m) * p.r, 0);
     }
     NLoader<Cfg, Cfg::BN> lb;
-    lb.nk0 = nk0;
-    lb.s0 = NSeg{static_cast<const T *>(p.wd) + (size_t)tl.e * p.d * p.F + n_base, nullptr, p.d, p.d, p.F,
+    lb.nk0 = 1 << 30;
+    lb.s0 = NSeg{static_cast<const T *>(p.ad) + (size_t)tl.e * p.r * p.F + n_base, nullptr, p.r, p.r, p.F,
                  0, ncol, 0, 0};
-    lb.s1 = NSeg{static_cast<const T *>(p.ad) + (size_t)tl.e * p.r * p.F + n_base, nullptr, p.r, p.r, p.F,
-                 0, ncol, 0, 0};
+    lb.s1 = lb.s0;
     f32x16_t acc[Cfg::TM][Cfg::TN];
-    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    gemm_pipeline<Cfg>(sa, sb, sa.nt0, la, lb, cdiv(p.r, Cfg::BK), sm.a, sm.b, acc);
     const T *G = static_cast<const T *>(p.G), *U = static_cast<const T *>(p.U);
     T *dGU = static_cast<T *>(p.dGU);
-    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
-        const int f = n_base + n;
-        if (m < tl.rows && f < p.F) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+#pragma unroll
+    for (int mi = 0; mi < Cfg::TM; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = wm * Cfg::WTM + mi * 32 + acc_row(i, lane);
+            if (m >= tl.rows) continue;
             const int pr = tl.row0 + m;
             const float w = p.topk_w[p.sorted_slot[pr]];
-            const float dh = w * v;
-            const size_t o = (size_t)pr * p.F + f;
-            const float g = Elem<T>::to_f32(G[o]), u = Elem<T>::to_f32(U[o]);
-            const float sg = 1.0f / (1.0f + expf(-g));
-            dGU[(size_t)pr * 2 * p.F + f] = Elem<T>::from_f32(dh * u * sg * (1.0f + g * (1.0f - sg)));
-            dGU[(size_t)pr * 2 * p.F + p.F + f] = Elem<T>::from_f32(dh * g * sg);
+#pragma unroll
+            for (int ni = 0; ni < Cfg::TN; ++ni) {
+                const int f = n_base + wn * Cfg::WTN + ni * 32 + acc_col(lane);
+                if (f < p.F) {
+                    const float dh = w * acc[mi][ni][i];
+                    const size_t o = (size_t)pr * p.F + f;
+                    const float g = Elem<T>::to_f32(G[o]), u = Elem<T>::to_f32(U[o]);
+                    const float sg = 1.0f / (1.0f + expf(-g));
+                    dGU[(size_t)pr * 2 * p.F + f] = Elem<T>::from_f32(dh * u * sg * (1.0f + g * (1.0f - sg)));
+                    dGU[(size_t)pr * 2 * p.F + p.F + f] = Elem<T>::from_f32(dh * g * sg);
+                }
+            }
         }
-    });
+    }
 }
 
 // ===========================================================================
@@ -240,44 +281,284 @@ struct GateUpBwdP {
     const float *pgu;
     const int32_t *offsets;
     void *dXp;
-    int E, d, F, r;
+    int S, E, d, F, r;
     float s;
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS) void k_gateup_bwd(GateUpBwdP p) {
+__global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd(GateUpBwdP p) {
     using T = typename Cfg::T;
     __shared__ Smem<Cfg> sm;
     Tile tl;
     if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(p.d, Cfg::BN), blockIdx.x, sm.start, tl)) return;
     const int n_base = tl.nt * Cfg::BN;
     const int ncol = min(Cfg::BN, p.d - n_base);
-    const int nk0 = cdiv(2 * p.F, Cfg::BK), nk = nk0 + cdiv(2 * p.r, Cfg::BK);
+    const int ntf = cdiv(p.F, Cfg::BK);
+    // two K segments: dG (columns 0..F of dGU) against W_g, then dU (F..2F) against W_u
+    BufKLoader<Cfg, Cfg::BM> sa;
+    sa.rs[0][0] = sa.rs[0][1] = sa.rs[1][0] = sa.rs[1][1] =
+        make_rsrc(p.dGU, (uint32_t)p.S * 2 * p.F * sizeof(T));
+    sa.K[0] = sa.K[1] = p.F; sa.col[0] = 0; sa.col[1] = p.F; sa.nt0 = ntf;
+#pragma unroll
+    for (int i = 0; i < sa.PER; ++i) {
+        const int m = sa.row_of(i);
+        sa.off[i] = m < tl.rows ? (uint32_t)(tl.row0 + m) * 2 * p.F * sizeof(T) : kInvalid;
+    }
+    // W_g[e], W_u[e] are [F, d]: element (k = f, n = model dim)
+    BufNLoader<Cfg, Cfg::BN> sb;
+    const size_t wofs = (size_t)tl.e * p.F * p.d + n_base;
+    const uint32_t wbytes = (uint32_t)((size_t)p.F * p.d - n_base) * sizeof(T);
+    sb.rs[0] = make_rsrc(static_cast<const T *>(p.wg) + wofs, wbytes);
+    sb.rs[1] = make_rsrc(static_cast<const T *>(p.wu) + wofs, wbytes);
+    sb.K[0] = sb.K[1] = p.F; sb.ld[0] = sb.ld[1] = p.d; sb.ncol = ncol; sb.nt0 = ntf;
     KLoader<Cfg, Cfg::BM, true> la;
-    la.K0 = 2 * p.F; la.K1 = 2 * p.r; la.nk0 = nk0; la.scale1 = p.s;
+    la.K1 = 2 * p.r; la.nk0 = 0; la.scale1 = p.s;
+    la.b1[0] = la.b1[1] = p.pgu;
 #pragma unroll
     for (int i = 0; i < la.PER; ++i) {
-        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
-        if (!la.active(i)) continue;
         const int m = la.row_of(i);
-        if (m < tl.rows) {
-            const int pr = tl.row0 + m;
-            la.p0[i] = static_cast<const T *>(p.dGU) + (size_t)pr * 2 * p.F;
-            la.p1[i] = p.pgu + (size_t)pr * 2 * p.r;
-        }
+        if (la.active(i) && m < tl.rows) la.set1(i, (uint32_t)(tl.row0 + m) * 2 * p.r, 0);
     }
     NLoader<Cfg, Cfg::BN> lb;
-    lb.nk0 = nk0;
-    const size_t wofs = (size_t)tl.e * p.F * p.d + n_base, aofs = (size_t)tl.e * p.r * p.d + n_base;
-    lb.s0 = NSeg{static_cast<const T *>(p.wg) + wofs, static_cast<const T *>(p.wu) + wofs, p.F, 2 * p.F, p.d,
+    lb.nk0 = 1 << 30;
+    const size_t aofs = (size_t)tl.e * p.r * p.d + n_base;
+    lb.s0 = NSeg{static_cast<const T *>(p.ag) + aofs, static_cast<const T *>(p.au) + aofs, p.r, 2 * p.r, p.d,
                  0, ncol, 0, ncol};
-    lb.s1 = NSeg{static_cast<const T *>(p.ag) + aofs, static_cast<const T *>(p.au) + aofs, p.r, 2 * p.r, p.d,
-                 0, ncol, 0, ncol};
+    lb.s1 = lb.s0;
     f32x16_t acc[Cfg::TM][Cfg::TN];
-    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    gemm_pipeline<Cfg>(sa, sb, 2 * ntf, la, lb, cdiv(2 * p.r, Cfg::BK), sm.a, sm.b, acc);
     T *dXp = static_cast<T *>(p.dXp);
     for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
         if (m < tl.rows && n_base + n < p.d) dXp[(size_t)(tl.row0 + m) * p.d + n_base + n] = Elem<T>::from_f32(v);
+    });
+}
+
+// ===========================================================================
+// bf16 versions of the four grouped GEMMs on the direct-to-LDS ring engine
+// (gemm_lds.hpp). Same math and epilogues as the kernels above.
+// ===========================================================================
+using LdsNT = lds::Cfg<256, 256, 4, false>;  // both operands K-contiguous
+using LdsNN = lds::Cfg<256, 256, 4, true>;   // B N-contiguous (transposing reads)
+
+template <class C> struct LdsSmem {
+    __align__(16) char ring[C::NSTAGE * C::STAGE_BYTES];
+    int start[kMaxE + 1];
+};
+
+__device__ __forceinline__ int lds_row(int wave, int lane, int j, int instr) { return (wave * instr + j) * 16 + (lane >> 2); }
+
+template <class C>
+__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUpP p) {
+    __shared__ LdsSmem<C> sm;
+    constexpr int HALF = C::BN / 2;
+    Tile tl;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, HALF), blockIdx.x, sm.start, tl)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int f_base = tl.nt * HALF;
+    lds::Operands<C> op;
+    uint32_t aro[C::A_INSTR], bro[C::B_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::A_INSTR; ++j) {
+        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        aro[j] = m < tl.rows ? (uint32_t)token_of(p.sorted_slot, tl.row0 + m, p.k) * p.d * 2 : kInvalid;
+    }
+    op.a.init_rows(wave, lane, aro);
+    op.ra[0] = op.ra[1] = make_rsrc(p.x, (uint32_t)p.T * p.d * 2);
+    op.K[0] = op.K[1] = p.d;
+    op.nt0 = op.nt = cdiv(p.d, C::BK);
+    // B rows interleave gate / up in 32-row blocks; one load covers 16 rows of one block
+#pragma unroll
+    for (int j = 0; j < C::B_INSTR; ++j) {
+        const int n = lds_row(wave, lane, j, C::B_INSTR);
+        const int wn = n / C::WTN, ni = (n % C::WTN) / 32;
+        const int f = f_base + wn * (C::WTN / 2) + (ni / 2) * 32 + (n % 32);
+        bro[j] = f < p.F ? (uint32_t)f * p.d * 2 : kInvalid;
+        const int n0 = (wave * C::B_INSTR + j) * 16;  // first row of the load (same block for every lane)
+        op.bsel_mask |= (uint32_t)(((n0 % C::WTN) / 32) & 1) << j;
+    }
+    op.bk.init_rows(wave, lane, bro);
+    const size_t wofs = (size_t)tl.e * p.F * p.d;
+    op.rb[0][0] = op.rb[1][0] = make_rsrc(static_cast<const bf16_t *>(p.wg) + wofs, (uint32_t)p.F * p.d * 2);
+    op.rb[0][1] = op.rb[1][1] = make_rsrc(static_cast<const bf16_t *>(p.wu) + wofs, (uint32_t)p.F * p.d * 2);
+    const bf16_t *bg = static_cast<const bf16_t *>(p.bg) + (size_t)tl.e * p.F * p.r;
+    const bf16_t *bu = static_cast<const bf16_t *>(p.bu) + (size_t)tl.e * p.F * p.r;
+    // LoRA tile: [s Zg | s Zu] rows against [B_g | 0] (gate rows) and [0 | B_u] (up rows)
+    lds::LoraTile<lds::LoraA<C>, lds::LoraBK<C>> lora;
+    lora.pa = {p.zgu, 2 * p.r, tl.row0, tl.rows, p.s};
+    lora.pb.r = p.r;
+    lora.pb.safe = bg;
+#pragma unroll
+    for (int i = 0; i < lds::LoraBK<C>::PER; ++i) {
+        const int n = ((int)threadIdx.x + 256 * i) >> 2;
+        const int wn = n / C::WTN, ni = (n % C::WTN) / 32;
+        const int f = f_base + wn * (C::WTN / 2) + (ni / 2) * 32 + (n % 32);
+        const bool up = ni & 1;
+        lora.pb.rowp[i] = f < p.F ? (up ? bu : bg) + (size_t)f * p.r : nullptr;
+        lora.pb.klo[i] = up ? p.r : 0;
+    }
+    f32x16_t acc[C::TM][C::TN];
+    lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, sm.ring, acc);
+
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    bf16_t *G = static_cast<bf16_t *>(p.G), *U = static_cast<bf16_t *>(p.U), *H = static_cast<bf16_t *>(p.H);
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+        for (int c = 0; c < C::TN / 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = wm * C::WTM + mi * 32 + acc_row(i, lane);
+                const int f = f_base + wn * (C::WTN / 2) + c * 32 + acc_col(lane);
+                if (m < tl.rows && f < p.F) {
+                    const float g = acc[mi][2 * c][i], u = acc[mi][2 * c + 1][i];
+                    const size_t o = (size_t)(tl.row0 + m) * p.F + f;
+                    if (G) G[o] = f32_to_bf16(g);
+                    if (U) U[o] = f32_to_bf16(u);
+                    H[o] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+                }
+            }
+}
+
+template <class C>
+__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_lds(DownP p) {
+    __shared__ LdsSmem<C> sm;
+    Tile tl;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_base = tl.nt * C::BN;
+    lds::Operands<C> op;
+    uint32_t aro[C::A_INSTR], bro[C::B_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::A_INSTR; ++j) {
+        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        aro[j] = m < tl.rows ? (uint32_t)(tl.row0 + m) * p.F * 2 : kInvalid;
+    }
+    op.a.init_rows(wave, lane, aro);
+    op.ra[0] = op.ra[1] = make_rsrc(p.H, (uint32_t)p.S * p.F * 2);
+    op.K[0] = op.K[1] = p.F;
+    op.nt0 = op.nt = cdiv(p.F, C::BK);
+#pragma unroll
+    for (int j = 0; j < C::B_INSTR; ++j) {
+        const int n = n_base + lds_row(wave, lane, j, C::B_INSTR);
+        bro[j] = n < p.d ? (uint32_t)n * p.F * 2 : kInvalid;
+    }
+    op.bk.init_rows(wave, lane, bro);
+    op.rb[0][0] = op.rb[0][1] = op.rb[1][0] = op.rb[1][1] =
+        make_rsrc(static_cast<const bf16_t *>(p.wd) + (size_t)tl.e * p.d * p.F, (uint32_t)p.d * p.F * 2);
+    const bf16_t *bd = static_cast<const bf16_t *>(p.bd) + (size_t)tl.e * p.d * p.r;
+    lds::LoraTile<lds::LoraA<C>, lds::LoraBK<C>> lora;
+    lora.pa = {p.zd, p.r, tl.row0, tl.rows, p.s};
+    lora.pb.r = p.r;
+    lora.pb.safe = bd;
+#pragma unroll
+    for (int i = 0; i < lds::LoraBK<C>::PER; ++i) {
+        const int n = n_base + (((int)threadIdx.x + 256 * i) >> 2);
+        lora.pb.rowp[i] = n < p.d ? bd + (size_t)n * p.r : nullptr;
+        lora.pb.klo[i] = 0;
+    }
+    f32x16_t acc[C::TM][C::TN];
+    lds::run<C>(op, cdiv(p.r, C::BK), lora, sm.ring, acc);
+    bf16_t *Y = static_cast<bf16_t *>(p.Y);
+    for_each_acc<C>(acc, [&](int m, int n, int, int, int, float v) {
+        if (m < tl.rows && n_base + n < p.d) Y[(size_t)(tl.row0 + m) * p.d + n_base + n] = f32_to_bf16(v);
+    });
+}
+
+template <class C>
+__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(DownBwdP p) {
+    __shared__ LdsSmem<C> sm;
+    Tile tl;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, C::BN), blockIdx.x, sm.start, tl)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_base = tl.nt * C::BN;
+    const int ncol = min(C::BN, p.F - n_base);
+    lds::Operands<C> op;
+    uint32_t aro[C::A_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::A_INSTR; ++j) {
+        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        aro[j] = m < tl.rows ? (uint32_t)token_of(p.sorted_slot, tl.row0 + m, p.k) * p.d * 2 : kInvalid;
+    }
+    op.a.init_rows(wave, lane, aro);
+    op.ra[0] = op.ra[1] = make_rsrc(p.dout, (uint32_t)p.T * p.d * 2);
+    op.K[0] = op.K[1] = p.d;
+    op.nt0 = op.nt = cdiv(p.d, C::BK);
+    // W_d[e] is [d, F]: k = model dim, n = f
+    op.bn.init(wave, lane, ncol);
+    op.rb[0][0] = op.rb[1][0] = make_rsrc(static_cast<const bf16_t *>(p.wd) + (size_t)tl.e * p.d * p.F + n_base,
+                                          (uint32_t)((size_t)p.d * p.F - n_base) * 2);
+    op.ldb[0] = op.ldb[1] = (uint32_t)p.F * 2;
+    const bf16_t *ad = static_cast<const bf16_t *>(p.ad) + (size_t)tl.e * p.r * p.F + n_base;
+    lds::LoraTile<lds::LoraA<C>, lds::LoraBN<C>> lora;
+    lora.pa = {p.pd, p.r, tl.row0, tl.rows, p.s};
+    lora.pb = {ad, ad, p.r, p.r, p.F, ncol};
+    f32x16_t acc[C::TM][C::TN];
+    lds::run<C>(op, cdiv(p.r, C::BK), lora, sm.ring, acc);
+    const bf16_t *G = static_cast<const bf16_t *>(p.G), *U = static_cast<const bf16_t *>(p.U);
+    bf16_t *dGU = static_cast<bf16_t *>(p.dGU);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = wm * C::WTM + mi * 32 + acc_row(i, lane);
+            if (m >= tl.rows) continue;
+            const int pr = tl.row0 + m;
+            const float w = p.topk_w[p.sorted_slot[pr]];
+#pragma unroll
+            for (int ni = 0; ni < C::TN; ++ni) {
+                const int f = n_base + wn * C::WTN + ni * 32 + acc_col(lane);
+                if (f < p.F) {
+                    const float dh = w * acc[mi][ni][i];
+                    const size_t o = (size_t)pr * p.F + f;
+                    const float g = bf16_to_f32(G[o]), u = bf16_to_f32(U[o]);
+                    const float sg = 1.0f / (1.0f + expf(-g));
+                    dGU[(size_t)pr * 2 * p.F + f] = f32_to_bf16(dh * u * sg * (1.0f + g * (1.0f - sg)));
+                    dGU[(size_t)pr * 2 * p.F + p.F + f] = f32_to_bf16(dh * g * sg);
+                }
+            }
+        }
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd_lds(GateUpBwdP p) {
+    __shared__ LdsSmem<C> sm;
+    Tile tl;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_base = tl.nt * C::BN;
+    const int ncol = min(C::BN, p.d - n_base);
+    lds::Operands<C> op;
+    uint32_t aro[C::A_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::A_INSTR; ++j) {
+        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        aro[j] = m < tl.rows ? (uint32_t)(tl.row0 + m) * 2 * p.F * 2 : kInvalid;
+    }
+    op.a.init_rows(wave, lane, aro);
+    // segment 0: dG (columns 0..F) x W_g ; segment 1: dU (columns F..2F) x W_u
+    op.ra[0] = op.ra[1] = make_rsrc(p.dGU, (uint32_t)p.S * 2 * p.F * 2);
+    op.acol[0] = 0; op.acol[1] = (uint32_t)p.F * 2;
+    op.K[0] = op.K[1] = p.F;
+    op.nt0 = cdiv(p.F, C::BK);
+    op.nt = 2 * op.nt0;
+    op.bn.init(wave, lane, ncol);
+    const size_t wofs = (size_t)tl.e * p.F * p.d + n_base;
+    const uint32_t wbytes = (uint32_t)((size_t)p.F * p.d - n_base) * 2;
+    op.rb[0][0] = make_rsrc(static_cast<const bf16_t *>(p.wg) + wofs, wbytes);
+    op.rb[1][0] = make_rsrc(static_cast<const bf16_t *>(p.wu) + wofs, wbytes);
+    op.ldb[0] = op.ldb[1] = (uint32_t)p.d * 2;
+    const size_t aofs = (size_t)tl.e * p.r * p.d + n_base;
+    const bf16_t *ag = static_cast<const bf16_t *>(p.ag) + aofs, *au = static_cast<const bf16_t *>(p.au) + aofs;
+    lds::LoraTile<lds::LoraA<C>, lds::LoraBN<C>> lora;
+    lora.pa = {p.pgu, 2 * p.r, tl.row0, tl.rows, p.s};
+    lora.pb = {ag, au, p.r, 2 * p.r, p.d, ncol};
+    f32x16_t acc[C::TM][C::TN];
+    lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, sm.ring, acc);
+    bf16_t *dXp = static_cast<bf16_t *>(p.dXp);
+    for_each_acc<C>(acc, [&](int m, int n, int, int, int, float v) {
+        if (m < tl.rows && n_base + n < p.d) dXp[(size_t)(tl.row0 + m) * p.d + n_base + n] = f32_to_bf16(v);
     });
 }
 
@@ -312,32 +593,31 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_proj(ProjP p) {
     const int nk = cdiv(K, Cfg::BK);
     KLoader<Cfg, Cfg::BM, true> la;
     la.K0 = K; la.K1 = 0; la.nk0 = nk; la.scale1 = 0.0f;
+    la.b0[0] = la.b0[1] = static_cast<const T *>(p.a);
+    la.b1[0] = la.b1[1] = nullptr;
 #pragma unroll
     for (int i = 0; i < la.PER; ++i) {
-        la.p0[i] = nullptr; la.p1[i] = nullptr; la.klo1[i] = 0; la.khi1[i] = 0;
-        if (!la.active(i)) continue;
         const int m = la.row_of(i);
-        if (m < tl.rows) {
+        if (la.active(i) && m < tl.rows) {
             const int pr = tl.row0 + m;
-            const size_t row = GATHER ? (size_t)token_of(p.sorted_slot, pr, p.k) : (size_t)pr;
-            la.p0[i] = static_cast<const T *>(p.a) + row * K;
+            const uint32_t row = GATHER ? (uint32_t)token_of(p.sorted_slot, pr, p.k) : (uint32_t)pr;
+            la.set0(i, row * K, 0);
         }
     }
     f32x16_t acc[Cfg::TM][Cfg::TN];
     if constexpr (!BN_CONTIG) {
         KLoader<Cfg, Cfg::BN, false> lb;
-        lb.K0 = K; lb.K1 = 0; lb.nk0 = nk; lb.scale1 = 0.0f;
+        lb.K0 = K; lb.K1 = 0; lb.nk0 = nk;
+        // rows n < r from b0 (A_gate or A_down), rows r..2r from b1 (A_up)
+        lb.b0[0] = static_cast<const T *>(p.b0) + (size_t)tl.e * p.r * K;
+        lb.b0[1] = KIND == PROJ_GU ? static_cast<const T *>(p.b1) + (size_t)tl.e * p.r * K : lb.b0[0];
+        lb.b1[0] = lb.b1[1] = nullptr;
 #pragma unroll
         for (int i = 0; i < lb.PER; ++i) {
-            lb.p0[i] = nullptr; lb.p1[i] = nullptr; lb.klo1[i] = 0; lb.khi1[i] = 0;
-            if (!lb.active(i)) continue;
             const int n = n_base + lb.row_of(i);
-            if (n < nr) {
-                if (KIND == PROJ_GU)
-                    lb.p0[i] = static_cast<const T *>(n < p.r ? p.b0 : p.b1) +
-                               ((size_t)tl.e * p.r + (n < p.r ? n : n - p.r)) * K;
-                else
-                    lb.p0[i] = static_cast<const T *>(p.b0) + ((size_t)tl.e * p.r + n) * K;
+            if (lb.active(i) && n < nr) {
+                const int hi = n >= p.r;
+                lb.set0(i, (uint32_t)(hi ? n - p.r : n) * K, hi);
             }
         }
         gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
@@ -664,8 +944,11 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
     {
         TraceScope ts(tr, K_GATEUP, st);
         GateUpP gp{b.x, b.wg, b.wu, b.bg, b.bu, b.Zgu, b.sorted_slot, b.offsets, b.G, b.U, b.H,
-                   D.E, D.k, D.d, D.F, D.r, D.s};
-        MOE_LAUNCH(k_gateup<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN / 2)), Cfg::NTHREADS, gp);
+                   D.T, D.E, D.k, D.d, D.F, D.r, D.s};
+        if constexpr (std::is_same<T, bf16_t>::value)
+            MOE_LAUNCH(k_gateup_lds<LdsNT>, grid_for<Cfg>(D, LdsNT::BM, cdiv(D.F, LdsNT::BN / 2)), 256, gp);
+        else
+            MOE_LAUNCH(k_gateup<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN / 2)), Cfg::NTHREADS, gp);
     }
     {
         TraceScope ts(tr, K_PROJ_D, st);
@@ -675,8 +958,11 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
     }
     {
         TraceScope ts(tr, K_DOWN, st);
-        DownP dp{b.H, b.wd, b.bd, b.Zd, b.offsets, b.Y, D.E, D.d, D.F, D.r, D.s};
-        MOE_LAUNCH(k_down<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, dp);
+        DownP dp{b.H, b.wd, b.bd, b.Zd, b.offsets, b.Y, D.S(), D.E, D.d, D.F, D.r, D.s};
+        if constexpr (std::is_same<T, bf16_t>::value)
+            MOE_LAUNCH(k_down_lds<LdsNT>, grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)), 256, dp);
+        else
+            MOE_LAUNCH(k_down<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, dp);
     }
     {
         TraceScope ts(tr, K_COMBINE, st);
@@ -722,8 +1008,11 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         {
             TraceScope ts(tr, K_DOWN_BWD, st);
             DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
-                        D.E, D.k, D.d, D.F, D.r, D.s};
-            MOE_LAUNCH(k_down_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN)), Cfg::NTHREADS, dp);
+                        D.T, D.E, D.k, D.d, D.F, D.r, D.s};
+            if constexpr (std::is_same<T, bf16_t>::value)
+                MOE_LAUNCH(k_down_bwd_lds<LdsNN>, grid_for<Cfg>(D, LdsNN::BM, cdiv(D.F, LdsNN::BN)), 256, dp);
+            else
+                MOE_LAUNCH(k_down_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN)), Cfg::NTHREADS, dp);
         }
         {
             TraceScope ts(tr, K_PROJ_DGU, st);
@@ -733,8 +1022,11 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         }
         {
             TraceScope ts(tr, K_GATEUP_BWD, st);
-            GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.E, D.d, D.F, D.r, D.s};
-            MOE_LAUNCH(k_gateup_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, gp);
+            GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.S(), D.E, D.d, D.F, D.r, D.s};
+            if constexpr (std::is_same<T, bf16_t>::value)
+                MOE_LAUNCH(k_gateup_bwd_lds<LdsNN>, grid_for<Cfg>(D, LdsNN::BM, cdiv(D.d, LdsNN::BN)), 256, gp);
+            else
+                MOE_LAUNCH(k_gateup_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, gp);
         }
         {
             TraceScope ts(tr, K_DX_COMBINE, st);
