@@ -186,11 +186,8 @@ __device__ __forceinline__ void mma_step(const char *sa, const char *sb, f32x16_
 
 // wait until at most N direct loads of this wave are outstanding
 template <int N> __device__ __forceinline__ void wait_vm() {
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-    else static_assert(N < 0, "unsupported wait count");
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 }  // namespace lds
@@ -405,6 +402,41 @@ struct LoraTile {
     __device__ __forceinline__ void load(int lt, Regs &r) const { pa.load(lt, r.a); pb.load(lt, r.b); }
     __device__ __forceinline__ void store(const Regs &r, char *st) const { pa.store(r.a, st); pb.store(r.b, st); }
 };
+
+// ---------------------------------------------------------------------------
+// Epilogue through LDS: the accumulators of one wave, 32 rows at a time, are
+// parked in the wave's own LDS region (32 x WTN fp32, 16 KB for WTN = 128)
+// and read back row-major, so each lane holds 8 consecutive columns of one
+// row and global traffic uses 16-byte accesses. fn(tile_row, tile_col, v[8])
+// is called for every (row, 8-column group) of the wave's sub-tile. Call
+// after the K loop on all threads (the ring is reused: one barrier first).
+template <class C, class Fn>
+__device__ __forceinline__ void epilogue_rows(const f32x16_t (&acc)[C::TM][C::TN], char *smem, Fn &&fn) {
+    static_assert(C::WTN % 64 == 0, "8-column groups per 16 lanes");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    float *buf = reinterpret_cast<float *>(smem) + wave * 32 * C::WTN;
+    __syncthreads();  // every wave is done with the ring
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) buf[acc_row(i, lane) * C::WTN + ni * 32 + acc_col(lane)] = acc[mi][ni][i];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        constexpr int LPR = C::WTN / 8;  // lanes per row
+        constexpr int RPP = 64 / LPR;    // rows per pass
+#pragma unroll
+        for (int pass = 0; pass < 32 / RPP; ++pass) {
+            const int r = pass * RPP + lane / LPR, c8 = (lane % LPR) * 8;
+            const float4 a = *reinterpret_cast<const float4 *>(buf + r * C::WTN + c8);
+            const float4 b = *reinterpret_cast<const float4 *>(buf + r * C::WTN + c8 + 4);
+            const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            fn(wm * C::WTM + mi * 32 + r, wn * C::WTN + c8, v);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next slab overwrites
+    }
+}
 
 }  // namespace lds
 }  // namespace moe

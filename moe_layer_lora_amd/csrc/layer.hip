@@ -399,24 +399,46 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUp
     f32x16_t acc[C::TM][C::TN];
     lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, sm.ring, acc);
 
-    const int wm = wave / C::WN, wn = wave % C::WN;
+    // wave columns: [gate 32 | up 32 | gate 32 | up 32] for f = f_base + wn*64 + (0..63)
     bf16_t *G = static_cast<bf16_t *>(p.G), *U = static_cast<bf16_t *>(p.U), *H = static_cast<bf16_t *>(p.H);
+    {
+        const int wn = wave % C::WN, wm = wave / C::WN;
+        float *buf = reinterpret_cast<float *>(sm.ring) + wave * 32 * C::WTN;
+        __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < C::TM; ++mi)
+        for (int mi = 0; mi < C::TM; ++mi) {
 #pragma unroll
-        for (int c = 0; c < C::TN / 2; ++c)
+            for (int ni = 0; ni < C::TN; ++ni)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = wm * C::WTM + mi * 32 + acc_row(i, lane);
-                const int f = f_base + wn * (C::WTN / 2) + c * 32 + acc_col(lane);
+                for (int i = 0; i < 16; ++i)
+                    buf[acc_row(i, lane) * C::WTN + ni * 32 + acc_col(lane)] = acc[mi][ni][i];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // 64 f per row = 8 lanes x 8 f; 8 rows per pass
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {
+                const int r = pass * 8 + lane / 8, q = lane % 8;  // q: 8-f group
+                const int gc = (q / 4) * 64 + (q % 4) * 8;       // gate column in the wave tile
+                const float4 g0 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc);
+                const float4 g1 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 4);
+                const float4 u0 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 32);
+                const float4 u1 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 36);
+                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                const int m = wm * C::WTM + mi * 32 + r;
+                const int f = f_base + wn * (C::WTN / 2) + (q / 4) * 32 + (q % 4) * 8;
                 if (m < tl.rows && f < p.F) {
-                    const float g = acc[mi][2 * c][i], u = acc[mi][2 * c + 1][i];
+                    float h[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) h[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
                     const size_t o = (size_t)(tl.row0 + m) * p.F + f;
-                    if (G) G[o] = f32_to_bf16(g);
-                    if (U) U[o] = f32_to_bf16(u);
-                    H[o] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+                    if (G) *reinterpret_cast<chunk_t *>(G + o) = Elem<bf16_t>::pack(g);
+                    if (U) *reinterpret_cast<chunk_t *>(U + o) = Elem<bf16_t>::pack(u);
+                    *reinterpret_cast<chunk_t *>(H + o) = Elem<bf16_t>::pack(h);
                 }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+    }
 }
 
 template <class C>
@@ -459,8 +481,9 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_lds(DownP p)
     f32x16_t acc[C::TM][C::TN];
     lds::run<C>(op, cdiv(p.r, C::BK), lora, sm.ring, acc);
     bf16_t *Y = static_cast<bf16_t *>(p.Y);
-    for_each_acc<C>(acc, [&](int m, int n, int, int, int, float v) {
-        if (m < tl.rows && n_base + n < p.d) Y[(size_t)(tl.row0 + m) * p.d + n_base + n] = f32_to_bf16(v);
+    lds::epilogue_rows<C>(acc, sm.ring, [&](int m, int n, const float *v) {
+        if (m < tl.rows && n_base + n < p.d)
+            *reinterpret_cast<chunk_t *>(Y + (size_t)(tl.row0 + m) * p.d + n_base + n) = Elem<bf16_t>::pack(v);
     });
 }
 
@@ -496,29 +519,26 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(Down
     lds::run<C>(op, cdiv(p.r, C::BK), lora, sm.ring, acc);
     const bf16_t *G = static_cast<const bf16_t *>(p.G), *U = static_cast<const bf16_t *>(p.U);
     bf16_t *dGU = static_cast<bf16_t *>(p.dGU);
-    const int wm = wave / C::WN, wn = wave % C::WN;
-#pragma unroll
-    for (int mi = 0; mi < C::TM; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = wm * C::WTM + mi * 32 + acc_row(i, lane);
-            if (m >= tl.rows) continue;
+    lds::epilogue_rows<C>(acc, sm.ring, [&](int m, int n, const float *v) {
+        const int f = n_base + n;
+        if (m < tl.rows && f < p.F) {
             const int pr = tl.row0 + m;
             const float w = p.topk_w[p.sorted_slot[pr]];
+            const size_t o = (size_t)pr * p.F + f;
+            float g[8], u[8], dg[8], du[8];
+            unpack<bf16_t>(*reinterpret_cast<const chunk_t *>(G + o), g);
+            unpack<bf16_t>(*reinterpret_cast<const chunk_t *>(U + o), u);
 #pragma unroll
-            for (int ni = 0; ni < C::TN; ++ni) {
-                const int f = n_base + wn * C::WTN + ni * 32 + acc_col(lane);
-                if (f < p.F) {
-                    const float dh = w * acc[mi][ni][i];
-                    const size_t o = (size_t)pr * p.F + f;
-                    const float g = bf16_to_f32(G[o]), u = bf16_to_f32(U[o]);
-                    const float sg = 1.0f / (1.0f + expf(-g));
-                    dGU[(size_t)pr * 2 * p.F + f] = f32_to_bf16(dh * u * sg * (1.0f + g * (1.0f - sg)));
-                    dGU[(size_t)pr * 2 * p.F + p.F + f] = f32_to_bf16(dh * g * sg);
-                }
+            for (int h = 0; h < 8; ++h) {
+                const float dh = w * v[h];
+                const float sg = 1.0f / (1.0f + __expf(-g[h]));
+                dg[h] = dh * u[h] * sg * (1.0f + g[h] * (1.0f - sg));
+                du[h] = dh * g[h] * sg;
             }
+            *reinterpret_cast<chunk_t *>(dGU + (size_t)pr * 2 * p.F + f) = Elem<bf16_t>::pack(dg);
+            *reinterpret_cast<chunk_t *>(dGU + (size_t)pr * 2 * p.F + p.F + f) = Elem<bf16_t>::pack(du);
         }
-    }
+    });
 }
 
 template <class C>
@@ -557,8 +577,9 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd_lds(Ga
     f32x16_t acc[C::TM][C::TN];
     lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, sm.ring, acc);
     bf16_t *dXp = static_cast<bf16_t *>(p.dXp);
-    for_each_acc<C>(acc, [&](int m, int n, int, int, int, float v) {
-        if (m < tl.rows && n_base + n < p.d) dXp[(size_t)(tl.row0 + m) * p.d + n_base + n] = f32_to_bf16(v);
+    lds::epilogue_rows<C>(acc, sm.ring, [&](int m, int n, const float *v) {
+        if (m < tl.rows && n_base + n < p.d)
+            *reinterpret_cast<chunk_t *>(dXp + (size_t)(tl.row0 + m) * p.d + n_base + n) = Elem<bf16_t>::pack(v);
     });
 }
 
@@ -857,16 +878,176 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_lora_grad(LGradP p) {
     });
 }
 
+// bf16 LoRA weight gradients on the LDS ring. Per block: expert e, a chunk
+// of up to kLgRC of its rows, 256 columns of the big operand. The product is
+// formed transposed, out^T[j][c] = sum_p Small[p][j] * Big[p][c]:
+//  - Small (fp32 [S, nr], times w for modes 2, 3) is staged once per block
+//    into LDS as bf16 Small^T in K-contiguous 32-row steps;
+//  - Big rows (gathered by token for modes 0, 3) stream through a 4-stage
+//    ring of direct loads, 32 rows x 256 columns per step (N-contiguous),
+//    read back with transposing LDS reads.
+constexpr int kLgRC = 512;            // rows per chunk
+constexpr int kLgSteps = kLgRC / 32;  // K steps per chunk
+constexpr int kLgBN = 256, kLgStage = 32 * kLgBN * 2, kLgNStage = 4;
+
+template <int NR>
+struct LgSmem {
+    __align__(16) char ring[kLgNStage * kLgStage];  // 64 KB
+    __align__(16) char small[kLgSteps * NR * 64];   // Small^T, 32 or 64 KB
+    uint32_t rowoff[kLgRC];                         // byte offset of each chunk row in Big
+    int start[kMaxE + 1];
+};
+
+template <int NR, int MODE>
+__global__ __launch_bounds__(256) void k_lgrad_lds(LGradP p) {
+    __shared__ LgSmem<NR> sm;
+    constexpr bool GATHER = MODE == 0 || MODE == 3;
+    constexpr bool WSCALE = MODE == 2 || MODE == 3;
+    const int ntn = cdiv(p.D, kLgBN);
+    Tile tl;
+    if (!schedule_tile<kLgRC, 256>(p.offsets, p.E, ntn, blockIdx.x, sm.start, tl)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c_base = tl.nt * kLgBN;
+    const int ncol = min(kLgBN, p.D - c_base);
+    // row offsets of Big for this chunk
+    for (int i = tid; i < kLgRC; i += 256) {
+        uint32_t o = kInvalid;
+        if (i < tl.rows) {
+            const int pr = tl.row0 + i;
+            o = (GATHER ? (uint32_t)(p.sorted_slot[pr] / p.k) : (uint32_t)pr) * (uint32_t)p.ldbig * 2u;
+        }
+        sm.rowoff[i] = o;
+    }
+    // Small^T: thread takes an 8-row x 8-column block, transposes it to 8 chunks of 8 rows
+    for (int b = tid; b < kLgRC / 8 * (NR / 8); b += 256) {
+        const int rb = b / (NR / 8), jb = b % (NR / 8);
+        const int p0 = rb * 8;
+        chunk_t in[8];
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+            const int pl = p0 + ii;
+            float v[8];
+            if (pl < tl.rows && jb * 8 < p.nr) {
+                const int pr = tl.row0 + pl;
+                const float sc = WSCALE ? p.topk_w[p.sorted_slot[pr]] : 1.0f;
+                const float4 *src = reinterpret_cast<const float4 *>(p.small + (size_t)pr * p.ldsmall + jb * 8);
+                const float4 a = src[0], c = src[1];
+                v[0] = a.x * sc; v[1] = a.y * sc; v[2] = a.z * sc; v[3] = a.w * sc;
+                v[4] = c.x * sc; v[5] = c.y * sc; v[6] = c.z * sc; v[7] = c.w * sc;
+            } else {
+#pragma unroll
+                for (int h = 0; h < 8; ++h) v[h] = 0.0f;
+            }
+            in[ii] = Elem<bf16_t>::pack(v);
+        }
+        chunk_t out[8];
+        NLoader<GemmCfg<bf16_t, 32, 32, 32, 1, 1>, 32>::transpose(in, out);
+        // out[jj] = rows p0..p0+7 of column j = jb*8 + jj: step p0/32, chunk (p0%32)/8
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            lds::st_kcontig(sm.small + (p0 / 32) * NR * 64, jb * 8 + jj, (p0 % 32) / 8, out[jj]);
+    }
+    __syncthreads();
+
+    const rsrc_t rs = make_rsrc(p.big, 0x7fffffff);  // offsets are row-checked below
+    const int nsteps = cdiv(tl.rows, 32);
+    auto issue = [&](int t) {
+        char *st = sm.ring + (t % kLgNStage) * kLgStage;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = wave * 4 + j;
+            const int kr = q * 2 + (lane >> 5);       // row of the step (2 rows per 1 KB)
+            const int lch = (lane & 31) ^ lds::swz_n(kr);
+            const int col = c_base + lch * 8;
+            const uint32_t ro = sm.rowoff[t * 32 + kr];
+            const uint32_t vo = (ro != kInvalid && lch * 8 + 8 <= ncol) ? ro + (uint32_t)col * 2 : kInvalid;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDS_PTR(st + q * 1024), 16, vo, 0, 0, 0);
+        }
+    };
+    constexpr int TM = NR / 32;
+    f32x16_t acc[TM][2];
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kLgNStage - 1; ++t)
+        if (t < nsteps) issue(t);
+    const int g = lane >> 4, sl = lane & 15;
+    for (int t = 0; t < nsteps; ++t) {
+        const int ahead = nsteps - 1 - t;
+        if (ahead >= 2) lds::wait_vm<8>();
+        else if (ahead == 1) lds::wait_vm<4>();
+        else lds::wait_vm<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (t + kLgNStage - 1 < nsteps) issue(t + kLgNStage - 1);
+        const char *st = sm.ring + (t % kLgNStage) * kLgStage;
+        const char *sa = sm.small + t * NR * 64;
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg) {
+            chunk_t af[TM], bfr[2];
+#pragma unroll
+            for (int mi = 0; mi < TM; ++mi) {
+                const int row = mi * 32 + (lane & 31);
+                const int c = kg * 2 + (lane >> 5);
+                af[mi] = *reinterpret_cast<const chunk_t *>(sa + row * 64 + ((c ^ lds::swz_k(row)) * 16));
+            }
+            const int kbase = kg * 16 + (g >> 1) * 8 + (sl >> 2);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const int n = wave * 64 + ni * 32 + (g & 1) * 16 + 4 * (sl & 3);
+                lds::s16x4_t h[2];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int k = kbase + 4 * half;
+                    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) lds::s16x4_t *)(st + k * kLgBN * 2 +
+                                                                           (((n >> 3) ^ lds::swz_n(k)) * 16) +
+                                                                           (n & 7) * 2));
+                }
+                bfr[ni] = chunk_t{(uint32_t)(uint16_t)h[0].x | ((uint32_t)(uint16_t)h[0].y << 16),
+                                  (uint32_t)(uint16_t)h[0].z | ((uint32_t)(uint16_t)h[0].w << 16),
+                                  (uint32_t)(uint16_t)h[1].x | ((uint32_t)(uint16_t)h[1].y << 16),
+                                  (uint32_t)(uint16_t)h[1].z | ((uint32_t)(uint16_t)h[1].w << 16)};
+            }
+#pragma unroll
+            for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) Elem<bf16_t>::mma(acc[mi][ni], af[mi], bfr[ni]);
+        }
+    }
+    // acc[mi][ni] holds out^T rows j = mi*32 + .., columns c = wave*64 + ni*32 + ..
+    const bool single = (p.offsets[tl.e + 1] - p.offsets[tl.e]) <= kLgRC;
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = mi * 32 + acc_row(i, lane);
+                const int cl = wave * 64 + ni * 32 + acc_col(lane);
+                if (j < p.nr && cl < ncol) {
+                    const int m = c_base + cl;
+                    if (single) lgrad_store(MODE, p, tl.e, m, j, p.s * acc[mi][ni][i]);
+                    else p.partial[((size_t)tl.gmt * p.D + m) * p.nr + j] = acc[mi][ni][i];
+                }
+            }
+}
+
 // Finalize: zeros for empty experts, chunk-ordered sums for multi-chunk experts.
-template <int MODE>
+template <int MODE, int RC>
 __global__ __launch_bounds__(256) void k_lora_grad_finalize(LGradP p) {
     __shared__ int s_start[kMaxE + 1];
     const int e = blockIdx.y;
     const int ne = p.offsets[e + 1] - p.offsets[e];
-    if (ne > 0 && ne <= kLoraRC) return;  // written by the GEMM directly
+    if (ne > 0 && ne <= RC) return;  // written by the GEMM directly
     // chunk start of expert e: sum of ceil(n/RC) over earlier experts
     for (int x = threadIdx.x; x < p.E; x += 256)
-        s_start[x] = (p.offsets[x + 1] - p.offsets[x] + kLoraRC - 1) / kLoraRC;
+        s_start[x] = (p.offsets[x + 1] - p.offsets[x] + RC - 1) / RC;
     __syncthreads();
     int c0 = 0;
     for (int x = 0; x < e; ++x) c0 += s_start[x];
@@ -880,7 +1061,7 @@ __global__ __launch_bounds__(256) void k_lora_grad_finalize(LGradP p) {
 }
 
 size_t lora_grad_partial_bytes(const Dims &D) {
-    const size_t tiles = (size_t)max_row_tiles(D.S(), D.E, kLoraRC);
+    const size_t tiles = (size_t)max_row_tiles(D.S(), D.E, std::min(kLoraRC, kLgRC));
     const size_t w = std::max<size_t>((size_t)D.d * 2 * D.r, (size_t)2 * D.F * 2 * D.r);
     return tiles * w * sizeof(float);
 }
@@ -974,18 +1155,27 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
 
 template <typename T, int MODE>
 static hipError_t launch_lgrad(const Dims &D, const LGradP &lp, hipStream_t st) {
-    const int ntm = cdiv(lp.D, 128);
-    if (lp.nr <= 32) {
-        using Cfg = typename SkinnyCfg<T, 32>::type;
-        MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
-                   Cfg::NTHREADS, lp);
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        const int grid = max_row_tiles(D.S(), D.E, kLgRC) * cdiv(lp.D, kLgBN);
+        if (lp.nr <= 32) MOE_LAUNCH((k_lgrad_lds<32, MODE>), grid, 256, lp);
+        else if (lp.nr <= 64) MOE_LAUNCH((k_lgrad_lds<64, MODE>), grid, 256, lp);
+        else return hipErrorInvalidValue;
+        k_lora_grad_finalize<MODE, kLgRC><<<dim3(cdiv(lp.D * lp.nr, 256), D.E), dim3(256), 0, st>>>(lp);
+        return hipGetLastError();
     } else {
-        using Cfg = typename SkinnyCfg<T, 64>::type;
-        MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
-                   Cfg::NTHREADS, lp);
+        const int ntm = cdiv(lp.D, 128);
+        if (lp.nr <= 32) {
+            using Cfg = typename SkinnyCfg<T, 32>::type;
+            MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
+                       Cfg::NTHREADS, lp);
+        } else {
+            using Cfg = typename SkinnyCfg<T, 64>::type;
+            MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
+                       Cfg::NTHREADS, lp);
+        }
+        k_lora_grad_finalize<MODE, kLoraRC><<<dim3(cdiv(lp.D * lp.nr, 256), D.E), dim3(256), 0, st>>>(lp);
+        return hipGetLastError();
     }
-    k_lora_grad_finalize<MODE><<<dim3(cdiv(lp.D * lp.nr, 256), D.E), dim3(256), 0, st>>>(lp);
-    return hipGetLastError();
 }
 
 template <typename T>
