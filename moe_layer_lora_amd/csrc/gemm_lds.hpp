@@ -9,11 +9,15 @@
 //
 // LDS layouts (byte offsets inside a stage):
 //  K-contiguous operand [rows][BK]: 64-byte rows of 4 16-byte chunks; chunk c
-//    of row r sits at physical chunk c ^ ((r >> 1) & 3). The 8 rows an MFMA
-//    fragment read touches per LDS cycle then cover all 32 banks.
+//    of row r sits at physical chunk c ^ ((r >> 2) & 3). The LDS serves a
+//    16-byte read for 16 lanes (16 consecutive rows, one chunk column) per
+//    cycle across 64 banks; with this swizzle those 16 rows hit 16 distinct
+//    16-byte bank groups (measured: half of all LDS cycles were conflicts
+//    with a swizzle that only separated 8 rows).
 //  N-contiguous operand [BK][BN] (k-rows of BN elements): 16-byte chunk c of
-//    k-row k sits at physical chunk c ^ (2 * (k & 3)), so the 4 k-rows a
-//    ds_read_b64_tr_b16 group touches fall in distinct banks.
+//    k-row k sits at physical chunk c ^ (4 * (k & 3)). A ds_read_b64_tr_b16
+//    cycle serves 32 lanes = 4 k-rows x 4 chunks; the XOR puts them in 16
+//    distinct 16-byte bank groups.
 // A direct load writes 1 KB contiguous per wave instruction (lane l at 16 l),
 // so each lane loads the global chunk that belongs at its LDS slot.
 #pragma once
@@ -46,8 +50,8 @@ struct Cfg {
     static_assert(!B_NCONTIG || (BN * 2) % 1024 == 0 || 1024 % (BN * 2) == 0, "k-rows tile 1 KB loads");
 };
 
-__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 3; }
-__device__ __forceinline__ int swz_n(int krow) { return 2 * (krow & 3); }
+__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz_n(int krow) { return 4 * (krow & 3); }
 
 // ---------------------------------------------------------------------------
 // Direct loads of one K-contiguous operand tile (ROWS x BK) into LDS.

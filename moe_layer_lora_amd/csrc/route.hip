@@ -27,7 +27,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / kWave;  // 16 logits per lane
 
 int route_tokens_per_block(int T, int E) {
-    int tpb = 64;
+    int tpb = 16;  // 4 tokens per wave: enough waves to fill the chip at a few thousand tokens
     while ((long long)E * ((T + tpb - 1) / tpb) > 65536) tpb *= 2;
     return tpb;
 }
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float *__res
         }
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kRouteThreads) hist[(size_t)e * nblk + b] = s_hist[e];
+    for (int e = tid; e < E; e += kRouteThreads) hist[(size_t)b * E + e] = s_hist[e];  // block-major
 }
 
 // exclusive scan of one value per thread over a 1024-thread block
@@ -138,31 +138,47 @@ __device__ int block_excl_scan_1024(int v, int *s_wsum) {
     return r;
 }
 
+// Scan of the block-major [nblk x E] histogram. Thread (g, e) owns expert e
+// over the g-th range of token blocks; per-column passes are coalesced across
+// the lanes (consecutive experts).
 __global__ __launch_bounds__(1024) void k_route_scan(const int32_t *__restrict__ hist, int E, int nblk, int S,
                                                      int32_t *__restrict__ base, int32_t *__restrict__ counts,
                                                      int32_t *__restrict__ offsets) {
     __shared__ int s_wsum[16];
+    __shared__ int s_part[1024];
     const int tid = threadIdx.x;
-    const int N = E * nblk;
-    const int per = (N + 1023) / 1024;
-    const int lo = min(N, tid * per), hi = min(N, lo + per);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += hist[i];
-    int run = block_excl_scan_1024(sum, s_wsum);
-    for (int i = lo; i < hi; ++i) {
-        base[i] = run;
-        run += hist[i];
-    }
-    // counts (bincount) and offsets (their exclusive scan), one expert per thread
+    const int G = max(1, 1024 / E);            // block ranges
+    const int g = tid / E, e = tid % E;
+    const bool act = g < G;
+    const int per = (nblk + G - 1) / G;
+    const int b0 = min(nblk, g * per), b1 = min(nblk, b0 + per);
+    int part = 0;
+    if (act)
+        for (int b = b0; b < b1; ++b) part += hist[(size_t)b * E + e];
+    s_part[tid] = act ? part : 0;
+    __syncthreads();
     int c = 0;
     if (tid < E)
-        for (int b = 0; b < nblk; ++b) c += hist[(size_t)tid * nblk + b];
-    const int off = block_excl_scan_1024(c, s_wsum);
+        for (int q = 0; q < G; ++q) c += s_part[q * E + tid];
+    const int off = block_excl_scan_1024(tid < E ? c : 0, s_wsum);
     if (tid < E) {
         counts[tid] = c;
         offsets[tid] = off;
     }
     if (tid == 0) offsets[E] = S;
+    // bases: offset of e plus the counts of e in earlier blocks
+    __shared__ int s_off[1024];
+    if (tid < E) s_off[tid] = off;
+    __syncthreads();
+    if (act) {
+        int run = s_off[e];
+        for (int q = 0; q < g; ++q) run += s_part[q * E + e];
+        for (int b = b0; b < b1; ++b) {
+            const int h = hist[(size_t)b * E + e];
+            base[(size_t)b * E + e] = run;
+            run += h;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t *__restrict__ topk_idx,
@@ -174,7 +190,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t *
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int b = blockIdx.x;
     for (int e = tid; e < E; e += kRouteThreads) {
-        s_base[e] = base[(size_t)e * nblk + b];
+        s_base[e] = base[(size_t)b * E + e];  // block-major
         s_run[e] = 0;
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) s_wcnt[w][e] = 0;
