@@ -337,8 +337,10 @@ __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup_
 // bf16 versions of the four grouped GEMMs on the direct-to-LDS ring engine
 // (gemm_lds.hpp). Same math and epilogues as the kernels above.
 // ===========================================================================
-using LdsNT = lds::Cfg<256, 256, 4, false>;  // both operands K-contiguous
-using LdsNN = lds::Cfg<256, 256, 4, true>;   // B N-contiguous (transposing reads)
+using LdsNT = lds::Cfg<256, 256, 4, false>;   // both operands K-contiguous
+using LdsNN = lds::Cfg<256, 256, 4, true>;    // B N-contiguous (transposing reads)
+using LdsNTh = lds::Cfg<128, 256, 4, false>;  // 128-row tail tiles
+using LdsNNh = lds::Cfg<128, 256, 4, true>;
 
 template <class C> struct LdsSmem {
     __align__(16) char ring[C::NSTAGE * C::STAGE_BYTES];
@@ -348,13 +350,9 @@ template <class C> struct LdsSmem {
 __device__ __forceinline__ int lds_row(int wave, int lane, int j, int instr) { return (wave * instr + j) * 16 + (lane >> 2); }
 
 template <class C>
-__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUpP p) {
-    __shared__ LdsSmem<C> sm;
-    constexpr int HALF = C::BN / 2;
-    Tile tl;
-    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, HALF), blockIdx.x, sm.start, tl)) return;
+__device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, char *ring) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int f_base = tl.nt * HALF;
+    const int f_base = tl.nt * (C::BN / 2);
     lds::Operands<C> op;
     uint32_t aro[C::A_INSTR], bro[C::B_INSTR];
 #pragma unroll
@@ -397,13 +395,13 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUp
         lora.pb.klo[i] = up ? p.r : 0;
     }
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, sm.ring, acc);
+    lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, ring, acc);
 
     // wave columns: [gate 32 | up 32 | gate 32 | up 32] for f = f_base + wn*64 + (0..63)
     bf16_t *G = static_cast<bf16_t *>(p.G), *U = static_cast<bf16_t *>(p.U), *H = static_cast<bf16_t *>(p.H);
     {
         const int wn = wave % C::WN, wm = wave / C::WN;
-        float *buf = reinterpret_cast<float *>(sm.ring) + wave * 32 * C::WTN;
+        float *buf = reinterpret_cast<float *>(ring) + wave * 32 * C::WTN;
         __syncthreads();
 #pragma unroll
         for (int mi = 0; mi < C::TM; ++mi) {
@@ -441,11 +439,18 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUp
     }
 }
 
-template <class C>
-__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_lds(DownP p) {
+// full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
+template <class C, class CH>
+__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUpP p) {
     __shared__ LdsSmem<C> sm;
     Tile tl;
-    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, C::BN / 2), blockIdx.x, sm.start, tl)) return;
+    if (tl.rows > CH::BM) gateup_tile<C>(p, tl, sm.ring);
+    else gateup_tile<CH>(p, tl, sm.ring);
+}
+
+template <class C>
+__device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *ring) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_base = tl.nt * C::BN;
     lds::Operands<C> op;
@@ -479,19 +484,26 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_lds(DownP p)
         lora.pb.klo[i] = 0;
     }
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(p.r, C::BK), lora, sm.ring, acc);
+    lds::run<C>(op, cdiv(p.r, C::BK), lora, ring, acc);
     bf16_t *Y = static_cast<bf16_t *>(p.Y);
-    lds::epilogue_rows<C>(acc, sm.ring, [&](int m, int n, const float *v) {
+    lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
         if (m < tl.rows && n_base + n < p.d)
             *reinterpret_cast<chunk_t *>(Y + (size_t)(tl.row0 + m) * p.d + n_base + n) = Elem<bf16_t>::pack(v);
     });
 }
 
-template <class C>
-__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(DownBwdP p) {
+// full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
+template <class C, class CH>
+__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_lds(DownP p) {
     __shared__ LdsSmem<C> sm;
     Tile tl;
-    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, C::BN), blockIdx.x, sm.start, tl)) return;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
+    if (tl.rows > CH::BM) down_tile<C>(p, tl, sm.ring);
+    else down_tile<CH>(p, tl, sm.ring);
+}
+
+template <class C>
+__device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl, char *ring) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_base = tl.nt * C::BN;
     const int ncol = min(C::BN, p.F - n_base);
@@ -516,10 +528,10 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(Down
     lora.pa = {p.pd, p.r, tl.row0, tl.rows, p.s};
     lora.pb = {ad, ad, p.r, p.r, p.F, ncol};
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(p.r, C::BK), lora, sm.ring, acc);
+    lds::run<C>(op, cdiv(p.r, C::BK), lora, ring, acc);
     const bf16_t *G = static_cast<const bf16_t *>(p.G), *U = static_cast<const bf16_t *>(p.U);
     bf16_t *dGU = static_cast<bf16_t *>(p.dGU);
-    lds::epilogue_rows<C>(acc, sm.ring, [&](int m, int n, const float *v) {
+    lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
         const int f = n_base + n;
         if (m < tl.rows && f < p.F) {
             const int pr = tl.row0 + m;
@@ -541,11 +553,18 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(Down
     });
 }
 
-template <class C>
-__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd_lds(GateUpBwdP p) {
+// full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
+template <class C, class CH>
+__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(DownBwdP p) {
     __shared__ LdsSmem<C> sm;
     Tile tl;
-    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, C::BN), blockIdx.x, sm.start, tl)) return;
+    if (tl.rows > CH::BM) down_bwd_tile<C>(p, tl, sm.ring);
+    else down_bwd_tile<CH>(p, tl, sm.ring);
+}
+
+template <class C>
+__device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile &tl, char *ring) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_base = tl.nt * C::BN;
     const int ncol = min(C::BN, p.d - n_base);
@@ -575,12 +594,22 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd_lds(Ga
     lora.pa = {p.pgu, 2 * p.r, tl.row0, tl.rows, p.s};
     lora.pb = {ag, au, p.r, 2 * p.r, p.d, ncol};
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, sm.ring, acc);
+    lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, ring, acc);
     bf16_t *dXp = static_cast<bf16_t *>(p.dXp);
-    lds::epilogue_rows<C>(acc, sm.ring, [&](int m, int n, const float *v) {
+    lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
         if (m < tl.rows && n_base + n < p.d)
             *reinterpret_cast<chunk_t *>(dXp + (size_t)(tl.row0 + m) * p.d + n_base + n) = Elem<bf16_t>::pack(v);
     });
+}
+
+// full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
+template <class C, class CH>
+__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd_lds(GateUpBwdP p) {
+    __shared__ LdsSmem<C> sm;
+    Tile tl;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
+    if (tl.rows > CH::BM) gateup_bwd_tile<C>(p, tl, sm.ring);
+    else gateup_bwd_tile<CH>(p, tl, sm.ring);
 }
 
 // ===========================================================================
@@ -1127,7 +1156,7 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
         GateUpP gp{b.x, b.wg, b.wu, b.bg, b.bu, b.Zgu, b.sorted_slot, b.offsets, b.G, b.U, b.H,
                    D.T, D.E, D.k, D.d, D.F, D.r, D.s};
         if constexpr (std::is_same<T, bf16_t>::value)
-            MOE_LAUNCH(k_gateup_lds<LdsNT>, grid_for<Cfg>(D, LdsNT::BM, cdiv(D.F, LdsNT::BN / 2)), 256, gp);
+            MOE_LAUNCH((k_gateup_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.F, LdsNT::BN / 2)), 256, gp);
         else
             MOE_LAUNCH(k_gateup<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN / 2)), Cfg::NTHREADS, gp);
     }
@@ -1141,7 +1170,7 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
         TraceScope ts(tr, K_DOWN, st);
         DownP dp{b.H, b.wd, b.bd, b.Zd, b.offsets, b.Y, D.S(), D.E, D.d, D.F, D.r, D.s};
         if constexpr (std::is_same<T, bf16_t>::value)
-            MOE_LAUNCH(k_down_lds<LdsNT>, grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)), 256, dp);
+            MOE_LAUNCH((k_down_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)), 256, dp);
         else
             MOE_LAUNCH(k_down<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, dp);
     }
@@ -1200,7 +1229,7 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
             DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
                         D.T, D.E, D.k, D.d, D.F, D.r, D.s};
             if constexpr (std::is_same<T, bf16_t>::value)
-                MOE_LAUNCH(k_down_bwd_lds<LdsNN>, grid_for<Cfg>(D, LdsNN::BM, cdiv(D.F, LdsNN::BN)), 256, dp);
+                MOE_LAUNCH((k_down_bwd_lds<LdsNN, LdsNNh>), grid_for<Cfg>(D, LdsNN::BM, cdiv(D.F, LdsNN::BN)), 256, dp);
             else
                 MOE_LAUNCH(k_down_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN)), Cfg::NTHREADS, dp);
         }
@@ -1214,7 +1243,7 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
             TraceScope ts(tr, K_GATEUP_BWD, st);
             GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.S(), D.E, D.d, D.F, D.r, D.s};
             if constexpr (std::is_same<T, bf16_t>::value)
-                MOE_LAUNCH(k_gateup_bwd_lds<LdsNN>, grid_for<Cfg>(D, LdsNN::BM, cdiv(D.d, LdsNN::BN)), 256, gp);
+                MOE_LAUNCH((k_gateup_bwd_lds<LdsNN, LdsNNh>), grid_for<Cfg>(D, LdsNN::BM, cdiv(D.d, LdsNN::BN)), 256, gp);
             else
                 MOE_LAUNCH(k_gateup_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, gp);
         }
