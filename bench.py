@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before warm-up, run a plain device copy (y = -x, fp32) of MIB MiB "
+                         "three times: the known-size kernel that scales rocprofv3's "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes")
     return ap.parse_args()
 
 
@@ -76,6 +80,53 @@ class Hip:
 
     def destroy(self, ev):
         self.lib.hipEventDestroy(ev)
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources and build flags: a counter summary taken on other
+    sources no longer describes the kernels being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_layer_lora_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        if n.endswith((".hip", ".hpp")):
+            h.update(n.encode())
+            with open(os.path.join(csrc, n), "rb") as f:
+                h.update(f.read())
+    with open(os.path.join(ROOT, "moe_layer_lora_amd", "_build.py"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel), or None if
+    there is none for these sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, mib, dev):
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(cfg, tokens):
@@ -144,6 +195,8 @@ def main():
         dlg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev) if keep else None
     host_counts = np.zeros(cfg.E, np.int32)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration, dev)
 
     def step(trace=None):
         moe.moe_route(pb, logits, rt, host_counts=None if args.no_readback else host_counts,
@@ -199,6 +252,20 @@ def main():
               key=lambda n: kern_ms[n])
     ach = fps[dom] * S / (kern_ms[dom] * 1e-3) / 1e12
 
+    # HBM-bound kernels: algorithmic bytes / time
+    T, d, k, E = cfg.T, cfg.d, cfg.k, cfg.E
+    es = 2 if cfg.dtype == "bf16" else 4
+    hbm_bytes = {
+        "route_topk": T * E * 4 + T * k * 8,
+        "route_scatter": S * 4 + 2 * S * 4,
+        "combine": T * ((k + 1) * d * es + k * 8),
+        "dx_combine": T * ((k + 1) * d * es + k * 4),
+        "router_grad": T * ((k + 1) * d * es + k * 8 + E * 4),
+    }
+    hbm = {n: {"bytes": b, "GBs": round(b / (kern_ms[n] * 1e-3) / 1e9, 1)}
+           for n, b in hbm_bytes.items() if n in kern_ms}
+    traffic = measured_traffic(dom, cfg.name)
+
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -216,8 +283,10 @@ def main():
                          "kernels": gemm_names},
         "kernels_ms": {n: round(v, 4) for n, v in kern_ms.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                      "flops_per_launch": fps[dom] * S},
+        "hbm_kernels": hbm,
+        "kernel_source_hash": kernel_source_hash(),
         "input_setup_s": round(t_gen, 2),
     }
     if not args.skip_cpu:
