@@ -136,55 +136,70 @@ __device__ __forceinline__ void st_ncontig(char *lds, int k, int n0, const chunk
 
 // ---------------------------------------------------------------------------
 // MFMA work of one K step out of a stage.
+// MFMA operand fragments of one 16-deep k group of a step, for one wave.
+template <class C> struct Frags {
+    chunk_t a[C::TM], b[C::TN];
+};
+
+// LDS reads of the fragments of k group kg (k = 16 kg .. 16 kg + 15 of the step).
 template <class C>
-__device__ __forceinline__ void mma_step(const char *sa, const char *sb, f32x16_t (&acc)[C::TM][C::TN]) {
+__device__ __forceinline__ void read_frags(const char *sa, const char *sb, int kg, Frags<C> &f) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     // A fragments: row (wm*WTM + mi*32 + lane%32), logical chunk kg*2 + lane/32
     const int arow0 = wm * C::WTM + (lane & 31);
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-        chunk_t af[C::TM], bfr[C::TN];
+    for (int mi = 0; mi < C::TM; ++mi) {
+        const int row = arow0 + mi * 32;
+        const int c = kg * 2 + (lane >> 5);
+        f.a[mi] = *reinterpret_cast<const chunk_t *>(sa + row * 64 + ((c ^ swz_k(row)) * 16));
+    }
+    if constexpr (!C::B_NCONTIG) {
+        const int brow0 = wn * C::WTN + (lane & 31);
 #pragma unroll
-        for (int mi = 0; mi < C::TM; ++mi) {
-            const int row = arow0 + mi * 32;
+        for (int ni = 0; ni < C::TN; ++ni) {
+            const int row = brow0 + ni * 32;
             const int c = kg * 2 + (lane >> 5);
-            af[mi] = *reinterpret_cast<const chunk_t *>(sa + row * 64 + ((c ^ swz_k(row)) * 16));
+            f.b[ni] = *reinterpret_cast<const chunk_t *>(sb + row * 64 + ((c ^ swz_k(row)) * 16));
         }
-        if constexpr (!C::B_NCONTIG) {
-            const int brow0 = wn * C::WTN + (lane & 31);
+    } else {
+        // transposing reads: 16-lane group g gets 4 k of 16 columns per read
+        const int g = lane >> 4, s = lane & 15;
+        const int kbase = kg * 16 + (g >> 1) * 8 + (s >> 2);
 #pragma unroll
-            for (int ni = 0; ni < C::TN; ++ni) {
-                const int row = brow0 + ni * 32;
-                const int c = kg * 2 + (lane >> 5);
-                bfr[ni] = *reinterpret_cast<const chunk_t *>(sb + row * 64 + ((c ^ swz_k(row)) * 16));
+        for (int ni = 0; ni < C::TN; ++ni) {
+            const int n = wn * C::WTN + ni * 32 + (g & 1) * 16 + 4 * (s & 3);
+            s16x4_t h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int k = kbase + 4 * half;
+                const char *p = sb + k * C::BN * 2 + (((n >> 3) ^ swz_n(k)) * 16) + (n & 7) * 2;
+                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(p));
             }
-        } else {
-            // transposing reads: 16-lane group g gets 4 k of 16 columns per read
-            const int g = lane >> 4, s = lane & 15;
-            const int kbase = kg * 16 + (g >> 1) * 8 + (s >> 2);
-#pragma unroll
-            for (int ni = 0; ni < C::TN; ++ni) {
-                const int n = wn * C::WTN + ni * 32 + (g & 1) * 16 + 4 * (s & 3);
-                s16x4_t h[2];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int k = kbase + 4 * half;
-                    const char *p = sb + k * C::BN * 2 + (((n >> 3) ^ swz_n(k)) * 16) + (n & 7) * 2;
-                    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4_t *)(p));
-                }
-                bfr[ni] = chunk_t{(uint32_t)(uint16_t)h[0].x | ((uint32_t)(uint16_t)h[0].y << 16),
-                                  (uint32_t)(uint16_t)h[0].z | ((uint32_t)(uint16_t)h[0].w << 16),
-                                  (uint32_t)(uint16_t)h[1].x | ((uint32_t)(uint16_t)h[1].y << 16),
-                                  (uint32_t)(uint16_t)h[1].z | ((uint32_t)(uint16_t)h[1].w << 16)};
-            }
+            f.b[ni] = chunk_t{(uint32_t)(uint16_t)h[0].x | ((uint32_t)(uint16_t)h[0].y << 16),
+                              (uint32_t)(uint16_t)h[0].z | ((uint32_t)(uint16_t)h[0].w << 16),
+                              (uint32_t)(uint16_t)h[1].x | ((uint32_t)(uint16_t)h[1].y << 16),
+                              (uint32_t)(uint16_t)h[1].z | ((uint32_t)(uint16_t)h[1].w << 16)};
         }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void mma_frags(const Frags<C> &f, f32x16_t (&acc)[C::TM][C::TN]) {
 #pragma unroll
-        for (int mi = 0; mi < C::TM; ++mi)
+    for (int mi = 0; mi < C::TM; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < C::TN; ++ni)
-                Elem<bf16_t>::mma(acc[mi][ni], af[mi], bfr[ni]);
+        for (int ni = 0; ni < C::TN; ++ni) Elem<bf16_t>::mma(acc[mi][ni], f.a[mi], f.b[ni]);
+}
+
+// One whole step (both k groups) from one stage.
+template <class C>
+__device__ __forceinline__ void mma_step(const char *sa, const char *sb, f32x16_t (&acc)[C::TM][C::TN]) {
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+        Frags<C> f;
+        read_frags<C>(sa, sb, kg, f);
+        mma_frags<C>(f, acc);
     }
 }
 
@@ -279,23 +294,41 @@ __device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora
             asm volatile("" ::: "memory");
         }
     }
-    for (int t = 0; t < op.nt; ++t) {
+    // Steady loop, skewed by half a step: after the barrier of step t the
+    // wave first issues the LDS reads of step t's first k group and then the
+    // MFMAs of step t-1's second k group (already in registers), so the MFMA
+    // pipe has work while the barrier resolves and the reads are in flight.
+    auto sync_step = [&](int t) {
         const int ahead = op.nt - 1 - t;  // steps issued after t that may stay in flight
         if (ahead >= C::NSTAGE - 2) wait_vm<(C::NSTAGE - 2) * C::LOADS_PER_STEP>();
         else if (ahead == 1) wait_vm<C::LOADS_PER_STEP>();
         else wait_vm<0>();
-        // Bare barrier: step t's LDS data is in (the wait above) and every
-        // fragment read of step t-1 was consumed by an MFMA before this point.
-        // __syncthreads() would add a release fence, i.e. a full vmcnt(0)
-        // drain of the steps still in flight. The empty asm keeps the
-        // compiler from moving LDS accesses across the barrier.
-        asm volatile("" ::: "memory");
+        // Every LDS read of step t-1 has completed (lgkmcnt) before the bare
+        // barrier, so after it step t-1's stage can be refilled. A full
+        // __syncthreads() would add a release fence, i.e. a vmcnt(0) drain of
+        // the steps still in flight. The asm keeps LDS accesses in place.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (t + C::NSTAGE - 1 < op.nt) op.issue(t + C::NSTAGE - 1, stage_of(t + C::NSTAGE - 1), wave);
-        const char *st = stage_of(t);
-        mma_step<C>(st, st + C::A_BYTES, acc);
+    };
+    Frags<C> f0, f1;
+    if (op.nt > 0) {
+        sync_step(0);
+        const char *st = stage_of(0);
+        read_frags<C>(st, st + C::A_BYTES, 0, f0);
+        read_frags<C>(st, st + C::A_BYTES, 1, f1);
+        mma_frags<C>(f0, acc);
     }
+    for (int t = 1; t < op.nt; ++t) {
+        sync_step(t);
+        const char *st = stage_of(t);
+        read_frags<C>(st, st + C::A_BYTES, 0, f0);
+        mma_frags<C>(f1, acc);
+        read_frags<C>(st, st + C::A_BYTES, 1, f1);
+        mma_frags<C>(f0, acc);
+    }
+    if (op.nt > 0) mma_frags<C>(f1, acc);
 }
 
 // ---------------------------------------------------------------------------
