@@ -45,7 +45,7 @@
  *    means a HIP call failed after checks passed (outputs then undefined).
  *    Nothing is printed and no exception crosses the ABI.
  *  - Limits: 0 <= T; 1 <= k <= E <= 1024; d, F, r >= 8 and multiples of 8;
- *    T*k*max(d,2F) < 2^31. Logits must be finite (NaN/Inf: undefined order).
+ *    T*k*max(d,2F,2r) < 2^31. Logits must be finite (NaN/Inf: undefined order).
  *  - Gradient outputs are overwritten, never accumulated into.
  *  - Calls on different streams may run concurrently if they share no
  *    buffers (workspaces included). The library has no global state.
@@ -135,9 +135,11 @@ size_t moe_bwd_workspace(const moe_problem_t *pb);
 
 /* Bytes of the `saved` buffer that moe_fwd fills for moe_bwd. Layout, each
  * part starting on a 256-byte boundary: G, U, H [S,F] dtype; Zgu [S,2r]
- * float32 (x A_gate^T | x A_up^T); Zd [S,r] float32 (h A_down^T); and, if
- * keep_expert_out, Y [S,d] dtype (expert outputs, needed for d_topk_w).
- * All indexed by row p. */
+ * float32 (x A_gate^T | x A_up^T); Zd [S,r] float32 (h A_down^T); for bf16
+ * only, ZguT [2r,ldT] bf16 (Zgu transposed) and wZdT [r,ldT] bf16 (Zd
+ * transposed, row p scaled by its combine weight), ldT = S rounded up to a
+ * multiple of 8, the operands of the LoRA-gradient kernels; and, if keep_expert_out, Y [S,d] dtype (expert outputs, needed
+ * for d_topk_w). Rows are indexed by row p. */
 size_t moe_saved_bytes(const moe_problem_t *pb, int keep_expert_out);
 
 /* Routing. logits [T,E] float32 -> rt (all six arrays written).

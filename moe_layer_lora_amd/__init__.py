@@ -223,23 +223,26 @@ def alloc_grads(pb: Problem, device):
 def saved_views(pb: Problem, saved, keep_expert_out: bool) -> dict:
     """Typed views of the `saved` buffer (layout documented in moe.h)."""
     S, F, r, d = pb.S, pb.F, pb.r, pb.d
-    dt = torch.bfloat16 if pb.dtype == MOE_BF16 else torch.float32
-    es = 2 if pb.dtype == MOE_BF16 else 4
+    bf = pb.dtype == MOE_BF16
+    dt = torch.bfloat16 if bf else torch.float32
+    es = 2 if bf else 4
 
     def al(x):
         return (x + 255) // 256 * 256
 
-    out, o = {}, 0
-    for name, n, t, e in (("G", S * F, dt, es), ("U", S * F, dt, es), ("H", S * F, dt, es),
-                          ("Zgu", S * 2 * r, torch.float32, 4), ("Zd", S * r, torch.float32, 4)) + (
-            (("Y", S * d, dt, es),) if keep_expert_out else ()):
-        out[name] = saved[o:o + n * e].view(t)
-        o += al(n * e)
-    out["G"] = out["G"].view(S, F)
-    out["U"] = out["U"].view(S, F)
-    out["H"] = out["H"].view(S, F)
-    out["Zgu"] = out["Zgu"].view(S, 2 * r)
-    out["Zd"] = out["Zd"].view(S, r)
+    parts = [("G", (S, F), dt, es), ("U", (S, F), dt, es), ("H", (S, F), dt, es),
+             ("Zgu", (S, 2 * r), torch.float32, 4), ("Zd", (S, r), torch.float32, 4)]
+    ldT = (S + 7) // 8 * 8
+    if bf:
+        parts += [("ZguT", (2 * r, ldT), torch.bfloat16, 2), ("wZdT", (r, ldT), torch.bfloat16, 2)]
     if keep_expert_out:
-        out["Y"] = out["Y"].view(S, d)
+        parts += [("Y", (S, d), dt, es)]
+    out, o = {}, 0
+    for name, shape, t, e in parts:
+        n = shape[0] * shape[1]
+        out[name] = saved[o:o + n * e].view(t).view(*shape)
+        o += al(n * e)
+    for name in ("ZguT", "wZdT"):
+        if name in out:
+            out[name] = out[name][:, :S]
     return out

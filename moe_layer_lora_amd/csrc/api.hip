@@ -26,7 +26,8 @@ moe_status_t check_problem(const moe_problem_t *pb) {
     if (pb->d % 8 || pb->F % 8 || pb->r % 8) return MOE_E_UNSUPPORTED;
     if (pb->E > 1024 || pb->r > 256) return MOE_E_UNSUPPORTED;
     const long long S = (long long)pb->T * pb->k;
-    const long long wide = pb->d > 2 * pb->F ? pb->d : 2LL * pb->F;
+    long long wide = pb->d > 2 * pb->F ? pb->d : 2LL * pb->F;
+    if (2LL * pb->r > wide) wide = 2LL * pb->r;
     if (S * wide >= (1LL << 31)) return MOE_E_UNSUPPORTED;
     return MOE_OK;
 }
@@ -46,9 +47,10 @@ RouteWs route_ws(const moe_problem_t *pb) {
     return w;
 }
 
-struct SavedLayout { size_t G, U, H, Zgu, Zd, Y, total; };
+struct SavedLayout { size_t G, U, H, Zgu, Zd, ZguT, wZdT, Y, total; };
 SavedLayout saved_layout(const moe_problem_t *pb, int keep) {
     const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
+    const bool bf = pb->dtype == MOE_BF16;
     SavedLayout l;
     size_t o = 0;
     l.G = o; o += al(S * pb->F * es);
@@ -56,6 +58,9 @@ SavedLayout saved_layout(const moe_problem_t *pb, int keep) {
     l.H = o; o += al(S * pb->F * es);
     l.Zgu = o; o += al(S * 2 * pb->r * sizeof(float));
     l.Zd = o; o += al(S * pb->r * sizeof(float));
+    const size_t ldT = (S + 7) & ~(size_t)7;
+    l.ZguT = o; if (bf) o += al(ldT * 2 * pb->r * 2);
+    l.wZdT = o; if (bf) o += al(ldT * pb->r * 2);
     l.Y = o; if (keep) o += al(S * pb->d * es);
     l.total = o;
     return l;
@@ -77,13 +82,17 @@ FwdWs fwd_ws(const moe_problem_t *pb, int training, int keep) {
     return w;
 }
 
-struct BwdWs { size_t Pd, Pgu, dGU, dXp, partial, total; };
+struct BwdWs { size_t Pd, Pgu, wPdT, PguT, dGU, dXp, partial, total; };
 BwdWs bwd_ws(const moe_problem_t *pb) {
     const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
+    const bool bf = pb->dtype == MOE_BF16;
     BwdWs w;
     size_t o = 0;
     w.Pd = o; o += al(S * pb->r * sizeof(float));
     w.Pgu = o; o += al(S * 2 * pb->r * sizeof(float));
+    const size_t ldT = (S + 7) & ~(size_t)7;
+    w.wPdT = o; if (bf) o += al(ldT * pb->r * 2);
+    w.PguT = o; if (bf) o += al(ldT * 2 * pb->r * 2);
     w.dGU = o; o += al(S * 2 * pb->F * es);
     w.dXp = o; o += al(S * pb->d * es);
     w.partial = o; o += al(moe::lora_grad_partial_bytes(dims_of(pb)));
@@ -231,6 +240,7 @@ moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t
         b.G = at(saved, sl.G); b.U = at(saved, sl.U); b.H = at(saved, sl.H);
         b.Zgu = reinterpret_cast<float *>(at(saved, sl.Zgu));
         b.Zd = reinterpret_cast<float *>(at(saved, sl.Zd));
+        if (pb->dtype == MOE_BF16) { b.ZguT = at(saved, sl.ZguT); b.wZdT = at(saved, sl.wZdT); }
         b.Y = keep ? at(saved, sl.Y) : at(ws, fw.Y);
     } else {
         b.G = nullptr; b.U = nullptr; b.H = at(ws, fw.H);
@@ -274,6 +284,10 @@ moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout, c
     b.Zd = reinterpret_cast<const float *>(at(saved, sl.Zd));
     b.Pd = reinterpret_cast<float *>(at(ws, bw.Pd));
     b.Pgu = reinterpret_cast<float *>(at(ws, bw.Pgu));
+    if (pb->dtype == MOE_BF16) {
+        b.ZguT = at(saved, sl.ZguT); b.wZdT = at(saved, sl.wZdT);
+        b.wPdT = at(ws, bw.wPdT); b.PguT = at(ws, bw.PguT);
+    }
     b.dGU = at(ws, bw.dGU); b.dXp = at(ws, bw.dXp);
     b.partial = reinterpret_cast<float *>(at(ws, bw.partial));
     b.dx = dx;

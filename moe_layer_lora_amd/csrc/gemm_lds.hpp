@@ -233,10 +233,12 @@ struct Operands {
     uint32_t ldb[2] = {0, 0};
     rsrc_t rb[2][2];
 
+    // Loads of step t into `stage`. Steps at or beyond nt load zeros (every
+    // offset out of range), so the steady loop can issue unconditionally.
     __device__ __forceinline__ void issue(int t, char *stage, int wave) const {
         const bool s1 = t >= nt0;
         const int k0 = (s1 ? t - nt0 : t) * C::BK;
-        const int Ks = s1 ? K[1] : K[0];
+        const int Ks = t < nt ? (s1 ? K[1] : K[0]) : 0;
         a.issue(s1 ? ra[1] : ra[0], s1 ? acol[1] : acol[0], k0, Ks, stage, wave);
         char *sb = stage + C::A_BYTES;
         if constexpr (C::B_NCONTIG) {
@@ -255,6 +257,40 @@ struct Operands {
     }
 };
 
+// One steady iteration: the loads of step t_issue into `dst` and the MFMA
+// work of the step in `src`. The two stages are distinct ring slots, which
+// the restrict qualifiers state: the compiler then knows the LDS reads of
+// `src` cannot see the direct loads into `dst` and inserts no vmcnt drain
+// before them (the loop's own vmcnt waits order the stages).
+template <class C>
+__device__ __forceinline__ void ring_iter(const Operands<C> &op, int t_issue, char *__restrict__ dst,
+                                          const char *__restrict__ src, int wave, Frags<C> &f0, Frags<C> &f1,
+                                          f32x16_t (&acc)[C::TM][C::TN]) {
+    op.issue(t_issue, dst, wave);
+    constexpr int NMMA = C::TM * C::TN, NRD = C::TM + (C::B_NCONTIG ? 2 : 1) * C::TN;
+    constexpr int L = C::LOADS_PER_STEP;
+    // phase 1: loads of the later step and reads of f0 under the MFMAs of f1
+    read_frags<C>(src, src + C::A_BYTES, 0, f0);
+    mma_frags<C>(f1, acc);  // zeros in the first iteration
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                // direct load
+        __builtin_amdgcn_sched_group_barrier(0x100, (NRD + L - 1) / L, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMMA - L, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 2: reads of f1 under the MFMAs of f0
+    read_frags<C>(src, src + C::A_BYTES, 1, f1);
+    mma_frags<C>(f0, acc);
+#pragma unroll
+    for (int i = 0; i < NMMA / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, (NRD + NMMA / 2 - 1) / (NMMA / 2), 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMMA / 2, 1);
+}
+
 // Ring driver: LoRA tiles first (stage 0, staged through registers by
 // lora.load / lora.store), then nt steady steps through stages 1.. in a
 // ring. The first LoRA tile's global loads are issued before the ring's, so
@@ -268,7 +304,7 @@ __device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora
         for (int ni = 0; ni < C::TN; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     auto stage_of = [&](int t) { return smem + ((t + 1) % C::NSTAGE) * C::STAGE_BYTES; };
     typename Lora::Regs lr;
     if (nlora > 0) lora.load(0, lr);
@@ -295,14 +331,19 @@ __device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora
         }
     }
     // Steady loop, skewed by half a step: after the barrier of step t the
-    // wave first issues the LDS reads of step t's first k group and then the
-    // MFMAs of step t-1's second k group (already in registers), so the MFMA
-    // pipe has work while the barrier resolves and the reads are in flight.
-    auto sync_step = [&](int t) {
-        const int ahead = op.nt - 1 - t;  // steps issued after t that may stay in flight
-        if (ahead >= C::NSTAGE - 2) wait_vm<(C::NSTAGE - 2) * C::LOADS_PER_STEP>();
-        else if (ahead == 1) wait_vm<C::LOADS_PER_STEP>();
-        else wait_vm<0>();
+    // wave issues the loads of step t + NSTAGE - 1 and the LDS reads of step
+    // t's first k group interleaved with the MFMAs of step t-1's second k
+    // group (already in registers), then step t's second-group reads with
+    // its first-group MFMAs. Every iteration issues one step of loads (zeros
+    // past the end), so the wait count is the same in every iteration and
+    // the loop body is a single block the scheduler can interleave.
+    Frags<C> f0, f1;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) f1.a[i] = chunk_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < C::TN; ++i) f1.b[i] = chunk_t{0u, 0u, 0u, 0u};
+    for (int t = 0; t < op.nt; ++t) {
+        wait_vm<(C::NSTAGE - 2) * C::LOADS_PER_STEP>();
         // Every LDS read of step t-1 has completed (lgkmcnt) before the bare
         // barrier, so after it step t-1's stage can be refilled. A full
         // __syncthreads() would add a release fence, i.e. a vmcnt(0) drain of
@@ -310,25 +351,13 @@ __device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (t + C::NSTAGE - 1 < op.nt) op.issue(t + C::NSTAGE - 1, stage_of(t + C::NSTAGE - 1), wave);
-    };
-    Frags<C> f0, f1;
-    if (op.nt > 0) {
-        sync_step(0);
-        const char *st = stage_of(0);
-        read_frags<C>(st, st + C::A_BYTES, 0, f0);
-        read_frags<C>(st, st + C::A_BYTES, 1, f1);
-        mma_frags<C>(f0, acc);
-    }
-    for (int t = 1; t < op.nt; ++t) {
-        sync_step(t);
-        const char *st = stage_of(t);
-        read_frags<C>(st, st + C::A_BYTES, 0, f0);
-        mma_frags<C>(f1, acc);
-        read_frags<C>(st, st + C::A_BYTES, 1, f1);
-        mma_frags<C>(f0, acc);
+        ring_iter<C>(op, t + C::NSTAGE - 1, stage_of(t + C::NSTAGE - 1), stage_of(t), wave, f0, f1, acc);
     }
     if (op.nt > 0) mma_frags<C>(f1, acc);
+    // the zero loads of the last iterations land in the ring: drain them
+    // before the epilogue reuses its memory
+    wait_vm<0>();
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------

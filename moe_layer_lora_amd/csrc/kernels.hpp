@@ -37,6 +37,7 @@ struct FwdBufs {
     const void *wg, *wu, *wd, *ag, *bg, *au, *bu, *ad, *bd;
     void *G, *U, *H;      // G, U may be null (inference)
     float *Zgu, *Zd;      // [S,2r], [S,r]
+    void *ZguT, *wZdT;    // bf16 training only: [2r,S] Zgu^T, [r,S] (w Zd)^T; else null
     void *Y;              // [S,d]
     void *out;            // [T,d]
 };
@@ -48,7 +49,9 @@ struct BwdBufs {
     const void *wg, *wu, *wd, *ag, *bg, *au, *bu, *ad, *bd;
     const void *G, *U, *H, *Y;   // saved (Y may be null)
     const float *Zgu, *Zd;       // saved
+    const void *ZguT, *wZdT;     // saved (bf16 only)
     float *Pd, *Pgu;             // workspace [S,r], [S,2r]
+    void *wPdT, *PguT;           // workspace (bf16 only): [r,S] (w Pd)^T, [2r,S] Pgu^T
     void *dGU, *dXp;             // workspace [S,2F], [S,d]
     float *partial;              // workspace for LoRA-gradient partial sums
     void *dx;
@@ -66,5 +69,7 @@ template <typename T> hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStr
 
 // bytes of LoRA-gradient partial sums the backward may need
 size_t lora_grad_partial_bytes(const Dims &D);
+// leading dimension of the transposed bf16 LoRA-gradient operands [nr, ldT]
+inline int lgrad_ldT(const Dims &D) { return (D.S() + 7) & ~7; }
 
 }  // namespace moe

@@ -627,6 +627,12 @@ struct ProjP {
     const int32_t *sorted_slot, *offsets;
     float *out;
     int E, k, d, F, r;
+    // optional bf16 transposed copy [nr, ldT] of the output (ldT = S rounded
+    // up to a multiple of 8), each row p scaled by wt[sorted_slot[p]] when wt
+    // is set: the small operand of the LoRA-gradient kernel
+    bf16_t *outT;
+    const float *wt;
+    int ldT, S;
 };
 
 template <class Cfg, int KIND>
@@ -690,6 +696,21 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_proj(ProjP p) {
     for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
         if (m < tl.rows && n_base + n < nr) p.out[(size_t)(tl.row0 + m) * nr + n_base + n] = v;
     });
+    if (p.outT) {
+        // the padding columns [S, ldT) are read as operands (times zero rows):
+        // they must hold finite values
+        const int pad = p.ldT - p.S;
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < nr * pad; i += Cfg::NTHREADS)
+                p.outT[(size_t)(i / pad) * p.ldT + p.S + i % pad] = Elem<bf16_t>::from_f32(0.0f);
+        for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+            if (m < tl.rows && n_base + n < nr) {
+                const int pr = tl.row0 + m;
+                const float sc = p.wt ? p.wt[p.sorted_slot[pr]] : 1.0f;
+                p.outT[(size_t)(n_base + n) * p.ldT + pr] = Elem<bf16_t>::from_f32(v * sc);
+            }
+        });
+    }
 }
 
 // ===========================================================================
@@ -790,6 +811,8 @@ struct LGradP {
     float *out0, *out1;
     int E, k, d, F, r, D, nr, ldbig, ldsmall;
     float s;
+    const bf16_t *smallT;            // bf16 path: [nr, ldT] transposed small operand
+    int ldT, mode;                   // ldT = S rounded up to a multiple of 8
 };
 
 __device__ __forceinline__ void lgrad_store(int mode, const LGradP &p, int e, int m, int n, float v) {
@@ -907,164 +930,207 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_lora_grad(LGradP p) {
     });
 }
 
-// bf16 LoRA weight gradients on the LDS ring. Per block: expert e, a chunk
-// of up to kLgRC of its rows, 256 columns of the big operand. The product is
-// formed transposed, out^T[j][c] = sum_p Small[p][j] * Big[p][c]:
-//  - Small (fp32 [S, nr], times w for modes 2, 3) is staged once per block
-//    into LDS as bf16 Small^T in K-contiguous 32-row steps;
-//  - Big rows (gathered by token for modes 0, 3) stream through a 4-stage
-//    ring of direct loads, 32 rows x 256 columns per step (N-contiguous),
-//    read back with transposing LDS reads.
-constexpr int kLgRC = 512;            // rows per chunk
-constexpr int kLgSteps = kLgRC / 32;  // K steps per chunk
-constexpr int kLgBN = 256, kLgStage = 32 * kLgBN * 2, kLgNStage = 4;
+// bf16 LoRA weight gradients, all modes in one launch. A block takes
+// (mode, expert, chunk of up to kLgRC of its rows, 256 columns of the big
+// operand) and forms out^T[j][c] = sum_p SmallT[j][p] Big[p][c]. Both
+// operands stream through a ring of direct loads, one 32-row step per stage:
+//  - the big rows (gathered by token for modes 0 and 3), 32 x 256 bf16,
+//    N-contiguous, read back with transposing LDS reads;
+//  - the matching 32 columns of SmallT, the bf16 [nr, S] transposed copy of
+//    the small operand that the projection kernels write (with the combine
+//    weight already applied for modes 2 and 3), K-contiguous.
+// Rows past the chunk load as zeros on the big side, which zeroes their
+// products whatever the SmallT columns hold.
+constexpr int kLgRC = 512;          // rows per chunk
+constexpr int kLgRows = kLgRC + 8;   // chunk rows plus the alignment lead-in
+constexpr int kLgBN = 256;           // big-operand columns per block
 
-template <int NR>
-struct LgSmem {
-    __align__(16) char ring[kLgNStage * kLgStage];  // 64 KB
-    __align__(16) char small[kLgSteps * NR * 64];   // Small^T, 32 or 64 KB
-    uint32_t rowoff[kLgRC];                         // byte offset of each chunk row in Big
+template <int NR> struct LgRing {
+    static constexpr int NSTAGE = NR <= 32 ? 4 : 3;
+    static constexpr int BIG = 32 * kLgBN * 2;           // 16 KB
+    static constexpr int SMALL = NR * 64;                // NR rows j x 32 p
+    static constexpr int STAGE = BIG + SMALL;
+    static constexpr int SMALL_INSTR = SMALL / 1024;     // 4-byte direct loads (256 B) per wave
+    static constexpr int LOADS = 4 + SMALL_INSTR;        // direct loads per wave per step
+};
+
+template <int NR> struct LgSmem {
+    __align__(16) char ring[LgRing<NR>::NSTAGE * LgRing<NR>::STAGE];
+    uint32_t rowoff[kLgRows];  // byte offset of each step row in Big (kInvalid outside the chunk)
     int start[kMaxE + 1];
 };
 
-template <int NR, int MODE>
-__global__ __launch_bounds__(256) void k_lgrad_lds(LGradP p) {
+struct LGradSet {
+    LGradP m[4];
+    int base[4];  // first block of each mode (multiples of 8: the tile scheduler's XCD map)
+    int n;
+};
+
+template <int NR>
+__device__ __forceinline__ void lg_issue(const LGradP &p, int p0, const uint32_t *__restrict__ rowoff, rsrc_t rs,
+                                         rsrc_t rsm, int c_base, int ncol, int nsteps, int t,
+                                         char *__restrict__ st, int wave, int lane) {
+    using R = LgRing<NR>;
+    const bool live = t < nsteps;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // big: 2 rows of 512 B per 1 KB load
+        const int q = wave * 4 + j;
+        const int kr = q * 2 + (lane >> 5);
+        const int lch = (lane & 31) ^ lds::swz_n(kr);
+        const uint32_t ro = rowoff[min(t * 32 + kr, kLgRows - 1)];
+        const uint32_t vo =
+            (live && ro != kInvalid && lch * 8 + 8 <= ncol) ? ro + (uint32_t)(c_base + lch * 8) * 2u : kInvalid;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDS_PTR(st + q * 1024), 16, vo, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < R::SMALL_INSTR; ++i) {  // SmallT: 4 rows j of 64 B per 256 B load
+        const int q = wave * R::SMALL_INSTR + i;
+        const int jr = q * 4 + (lane >> 4);
+        const int lc = ((lane & 15) >> 2) ^ lds::swz_k(jr);
+        const uint32_t pr = (uint32_t)(p0 + t * 32 + lc * 8);  // 8-aligned: 16-byte aligned chunks
+        const uint32_t vo = (live && jr < p.nr) ? ((uint32_t)jr * (uint32_t)p.ldT + pr) * 2u + (uint32_t)(lane & 3) * 4u
+                                                : kInvalid;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsm, MOE_LDS_PTR(st + R::BIG + q * 256), 4, vo, 0, 0, 0);
+    }
+}
+
+// One steady step: the loads of step t + NSTAGE - 1 into `dst` (a different
+// ring slot from `st`, as the restrict qualifiers state, so the compiler
+// inserts no vmcnt drain before the LDS reads) and the MFMA work of step t.
+template <int NR>
+__device__ __forceinline__ void lg_iter(const LGradP &p, int p0, const uint32_t *__restrict__ rowoff, rsrc_t rs,
+                                        rsrc_t rsm, int c_base, int ncol, int nsteps, int t,
+                                        char *__restrict__ dst, const char *__restrict__ st, int wave, int lane,
+                                        f32x16_t (&acc)[NR / 32][2]) {
+    using R = LgRing<NR>;
+    constexpr int TM = NR / 32;
+    lg_issue<NR>(p, p0, rowoff, rs, rsm, c_base, ncol, nsteps, t + R::NSTAGE - 1, dst, wave, lane);
+    const char *sa = st + R::BIG;
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+        chunk_t af[TM], bfr[2];
+#pragma unroll
+        for (int mi2 = 0; mi2 < TM; ++mi2) {
+            const int row = mi2 * 32 + (lane & 31);
+            const int c = kg * 2 + (lane >> 5);
+            af[mi2] = *reinterpret_cast<const chunk_t *>(sa + row * 64 + ((c ^ lds::swz_k(row)) * 16));
+        }
+        const int kbase = kg * 16 + (g >> 1) * 8 + (sl >> 2);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            const int n = wave * 64 + ni * 32 + (g & 1) * 16 + 4 * (sl & 3);
+            lds::s16x4_t h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int k = kbase + 4 * half;
+                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) lds::s16x4_t *)(st + k * kLgBN * 2 +
+                                                                       (((n >> 3) ^ lds::swz_n(k)) * 16) + (n & 7) * 2));
+            }
+            bfr[ni] = chunk_t{(uint32_t)(uint16_t)h[0].x | ((uint32_t)(uint16_t)h[0].y << 16),
+                              (uint32_t)(uint16_t)h[0].z | ((uint32_t)(uint16_t)h[0].w << 16),
+                              (uint32_t)(uint16_t)h[1].x | ((uint32_t)(uint16_t)h[1].y << 16),
+                              (uint32_t)(uint16_t)h[1].z | ((uint32_t)(uint16_t)h[1].w << 16)};
+        }
+#pragma unroll
+        for (int mi2 = 0; mi2 < TM; ++mi2)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) Elem<bf16_t>::mma(acc[mi2][ni], af[mi2], bfr[ni]);
+    }
+}
+
+template <int NR>
+__global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
+    using R = LgRing<NR>;
     __shared__ LgSmem<NR> sm;
-    constexpr bool GATHER = MODE == 0 || MODE == 3;
-    constexpr bool WSCALE = MODE == 2 || MODE == 3;
+    const int b = blockIdx.x;
+    const int mi = (set.n > 1 && b >= set.base[1]) + (set.n > 2 && b >= set.base[2]) + (set.n > 3 && b >= set.base[3]);
+    const LGradP p = mi == 0 ? set.m[0] : mi == 1 ? set.m[1] : mi == 2 ? set.m[2] : set.m[3];
     const int ntn = cdiv(p.D, kLgBN);
     Tile tl;
-    if (!schedule_tile<kLgRC, 256>(p.offsets, p.E, ntn, blockIdx.x, sm.start, tl)) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (!schedule_tile<kLgRC, 256>(p.offsets, p.E, ntn, b - set.base[mi], sm.start, tl)) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool gather = p.mode == 0 || p.mode == 3;
     const int c_base = tl.nt * kLgBN;
     const int ncol = min(kLgBN, p.D - c_base);
-    // row offsets of Big for this chunk
-    for (int i = tid; i < kLgRC; i += 256) {
+    // steps start at p0, the chunk's first row rounded down to a multiple of
+    // 8, so SmallT columns load as aligned 16-byte chunks; the lead-in rows
+    // (previous expert) load as zeros on the big side
+    const int p0 = tl.row0 & ~7, lead = tl.row0 - p0;
+    for (int i = tid; i < kLgRows; i += 256) {
         uint32_t o = kInvalid;
-        if (i < tl.rows) {
-            const int pr = tl.row0 + i;
-            o = (GATHER ? (uint32_t)(p.sorted_slot[pr] / p.k) : (uint32_t)pr) * (uint32_t)p.ldbig * 2u;
+        if (i >= lead && i < lead + tl.rows) {
+            const int pr = p0 + i;
+            o = (gather ? (uint32_t)(p.sorted_slot[pr] / p.k) : (uint32_t)pr) * (uint32_t)p.ldbig * 2u;
         }
         sm.rowoff[i] = o;
     }
-    // Small^T: thread takes an 8-row x 8-column block, transposes it to 8 chunks of 8 rows
-    for (int b = tid; b < kLgRC / 8 * (NR / 8); b += 256) {
-        const int rb = b / (NR / 8), jb = b % (NR / 8);
-        const int p0 = rb * 8;
-        chunk_t in[8];
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-            const int pl = p0 + ii;
-            float v[8];
-            if (pl < tl.rows && jb * 8 < p.nr) {
-                const int pr = tl.row0 + pl;
-                const float sc = WSCALE ? p.topk_w[p.sorted_slot[pr]] : 1.0f;
-                const float4 *src = reinterpret_cast<const float4 *>(p.small + (size_t)pr * p.ldsmall + jb * 8);
-                const float4 a = src[0], c = src[1];
-                v[0] = a.x * sc; v[1] = a.y * sc; v[2] = a.z * sc; v[3] = a.w * sc;
-                v[4] = c.x * sc; v[5] = c.y * sc; v[6] = c.z * sc; v[7] = c.w * sc;
-            } else {
-#pragma unroll
-                for (int h = 0; h < 8; ++h) v[h] = 0.0f;
-            }
-            in[ii] = Elem<bf16_t>::pack(v);
-        }
-        chunk_t out[8];
-        NLoader<GemmCfg<bf16_t, 32, 32, 32, 1, 1>, 32>::transpose(in, out);
-        // out[jj] = rows p0..p0+7 of column j = jb*8 + jj: step p0/32, chunk (p0%32)/8
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            lds::st_kcontig(sm.small + (p0 / 32) * NR * 64, jb * 8 + jj, (p0 % 32) / 8, out[jj]);
-    }
     __syncthreads();
-
-    const rsrc_t rs = make_rsrc(p.big, 0x7fffffff);  // offsets are row-checked below
-    const int nsteps = cdiv(tl.rows, 32);
-    auto issue = [&](int t) {
-        char *st = sm.ring + (t % kLgNStage) * kLgStage;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int q = wave * 4 + j;
-            const int kr = q * 2 + (lane >> 5);       // row of the step (2 rows per 1 KB)
-            const int lch = (lane & 31) ^ lds::swz_n(kr);
-            const int col = c_base + lch * 8;
-            const uint32_t ro = sm.rowoff[t * 32 + kr];
-            const uint32_t vo = (ro != kInvalid && lch * 8 + 8 <= ncol) ? ro + (uint32_t)col * 2 : kInvalid;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDS_PTR(st + q * 1024), 16, vo, 0, 0, 0);
-        }
-    };
+    const rsrc_t rs = make_rsrc(p.big, 0x7fffffff);  // rows are range-checked through rowoff
+    const rsrc_t rsm = make_rsrc(p.smallT, (uint32_t)p.nr * (uint32_t)p.ldT * 2u);
+    const int nsteps = cdiv(lead + tl.rows, 32);
+    auto stage = [&](int t) { return sm.ring + (t % R::NSTAGE) * R::STAGE; };
     constexpr int TM = NR / 32;
     f32x16_t acc[TM][2];
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi)
+    for (int mi2 = 0; mi2 < TM; ++mi2)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+            for (int i = 0; i < 16; ++i) acc[mi2][ni][i] = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kLgNStage - 1; ++t)
-        if (t < nsteps) issue(t);
-    const int g = lane >> 4, sl = lane & 15;
+    for (int t = 0; t < R::NSTAGE - 1; ++t)
+        lg_issue<NR>(p, p0, sm.rowoff, rs, rsm, c_base, ncol, nsteps, t, stage(t), wave, lane);
     for (int t = 0; t < nsteps; ++t) {
-        const int ahead = nsteps - 1 - t;
-        if (ahead >= 2) lds::wait_vm<8>();
-        else if (ahead == 1) lds::wait_vm<4>();
-        else lds::wait_vm<0>();
-        asm volatile("" ::: "memory");
+        // every step issues the same loads (zeros past the end): a fixed wait count
+        lds::wait_vm<(R::NSTAGE - 2) * R::LOADS>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (t + kLgNStage - 1 < nsteps) issue(t + kLgNStage - 1);
-        const char *st = sm.ring + (t % kLgNStage) * kLgStage;
-        const char *sa = sm.small + t * NR * 64;
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-            chunk_t af[TM], bfr[2];
-#pragma unroll
-            for (int mi = 0; mi < TM; ++mi) {
-                const int row = mi * 32 + (lane & 31);
-                const int c = kg * 2 + (lane >> 5);
-                af[mi] = *reinterpret_cast<const chunk_t *>(sa + row * 64 + ((c ^ lds::swz_k(row)) * 16));
-            }
-            const int kbase = kg * 16 + (g >> 1) * 8 + (sl >> 2);
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int n = wave * 64 + ni * 32 + (g & 1) * 16 + 4 * (sl & 3);
-                lds::s16x4_t h[2];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int k = kbase + 4 * half;
-                    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) lds::s16x4_t *)(st + k * kLgBN * 2 +
-                                                                           (((n >> 3) ^ lds::swz_n(k)) * 16) +
-                                                                           (n & 7) * 2));
-                }
-                bfr[ni] = chunk_t{(uint32_t)(uint16_t)h[0].x | ((uint32_t)(uint16_t)h[0].y << 16),
-                                  (uint32_t)(uint16_t)h[0].z | ((uint32_t)(uint16_t)h[0].w << 16),
-                                  (uint32_t)(uint16_t)h[1].x | ((uint32_t)(uint16_t)h[1].y << 16),
-                                  (uint32_t)(uint16_t)h[1].z | ((uint32_t)(uint16_t)h[1].w << 16)};
-            }
-#pragma unroll
-            for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni) Elem<bf16_t>::mma(acc[mi][ni], af[mi], bfr[ni]);
-        }
+        lg_iter<NR>(p, p0, sm.rowoff, rs, rsm, c_base, ncol, nsteps, t, stage(t + R::NSTAGE - 1), stage(t), wave,
+                    lane, acc);
     }
-    // acc[mi][ni] holds out^T rows j = mi*32 + .., columns c = wave*64 + ni*32 + ..
+    lds::wait_vm<0>();  // the zero loads of the last steps
+    // acc[mi2][ni] holds out^T rows j = mi2*32 + .., columns c = wave*64 + ni*32 + ..
     const bool single = (p.offsets[tl.e + 1] - p.offsets[tl.e]) <= kLgRC;
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi)
+    for (int mi2 = 0; mi2 < TM; ++mi2)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int j = mi * 32 + acc_row(i, lane);
+                const int j = mi2 * 32 + acc_row(i, lane);
                 const int cl = wave * 64 + ni * 32 + acc_col(lane);
                 if (j < p.nr && cl < ncol) {
                     const int m = c_base + cl;
-                    if (single) lgrad_store(MODE, p, tl.e, m, j, p.s * acc[mi][ni][i]);
-                    else p.partial[((size_t)tl.gmt * p.D + m) * p.nr + j] = acc[mi][ni][i];
+                    if (single) lgrad_store(p.mode, p, tl.e, m, j, p.s * acc[mi2][ni][i]);
+                    else p.partial[((size_t)tl.gmt * p.D + m) * p.nr + j] = acc[mi2][ni][i];
                 }
             }
+}
+
+// Finalize of the bf16 path, every mode of a set in one launch (blockIdx.z):
+// exact zeros for empty experts, chunk-ordered sums for multi-chunk experts.
+__global__ __launch_bounds__(256) void k_lgrad_finalize(LGradSet set) {
+    __shared__ int s_start[kMaxE + 1];
+    const int mi = blockIdx.z;
+    const LGradP p = mi == 0 ? set.m[0] : mi == 1 ? set.m[1] : mi == 2 ? set.m[2] : set.m[3];
+    const int e = blockIdx.y;
+    const int ne = p.offsets[e + 1] - p.offsets[e];
+    if (ne > 0 && ne <= kLgRC) return;  // written by the gradient kernel directly
+    for (int x = threadIdx.x; x < p.E; x += 256) s_start[x] = (p.offsets[x + 1] - p.offsets[x] + kLgRC - 1) / kLgRC;
+    __syncthreads();
+    int c0 = 0;
+    for (int x = 0; x < e; ++x) c0 += s_start[x];
+    const int nch = s_start[e];
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= p.D * p.nr) return;
+    const int m = idx / p.nr, n = idx % p.nr;
+    float v = 0.0f;
+    for (int c = 0; c < nch; ++c) v += p.partial[((size_t)(c0 + c) * p.D + m) * p.nr + n];
+    lgrad_store(p.mode, p, e, m, n, p.s * v);
 }
 
 // Finalize: zeros for empty experts, chunk-ordered sums for multi-chunk experts.
@@ -1089,10 +1155,19 @@ __global__ __launch_bounds__(256) void k_lora_grad_finalize(LGradP p) {
     lgrad_store(MODE, p, e, m, n, p.s * v);
 }
 
-size_t lora_grad_partial_bytes(const Dims &D) {
+// Partial-sum regions of the four gradient modes (byte offsets; the bf16
+// kernel runs the modes concurrently, the fp32 path reuses region 0).
+static void lgrad_partial_layout(const Dims &D, size_t off[5]) {
     const size_t tiles = (size_t)max_row_tiles(D.S(), D.E, std::min(kLoraRC, kLgRC));
-    const size_t w = std::max<size_t>((size_t)D.d * 2 * D.r, (size_t)2 * D.F * 2 * D.r);
-    return tiles * w * sizeof(float);
+    const size_t w[4] = {(size_t)D.d * 2 * D.r, (size_t)2 * D.F * 2 * D.r, (size_t)D.F * D.r, (size_t)D.d * D.r};
+    off[0] = 0;
+    for (int m = 0; m < 4; ++m) off[m + 1] = off[m] + ((tiles * w[m] * sizeof(float) + 255) & ~(size_t)255);
+}
+
+size_t lora_grad_partial_bytes(const Dims &D) {
+    size_t off[5];
+    lgrad_partial_layout(D, off);
+    return off[4];
 }
 
 // ===========================================================================
@@ -1147,7 +1222,8 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
     if (D.T == 0) return hipSuccess;
     {
         TraceScope ts(tr, K_PROJ_GU, st);
-        ProjP pp{b.x, b.ag, b.au, b.sorted_slot, b.offsets, b.Zgu, D.E, D.k, D.d, D.F, D.r};
+        ProjP pp{b.x, b.ag, b.au, b.sorted_slot, b.offsets, b.Zgu, D.E, D.k, D.d, D.F, D.r,
+                 static_cast<bf16_t *>(b.ZguT), nullptr, lgrad_ldT(D), D.S()};
         hipError_t e = launch_proj<T, PROJ_GU>(D, pp, st);
         if (e != hipSuccess) return e;
     }
@@ -1162,7 +1238,8 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
     }
     {
         TraceScope ts(tr, K_PROJ_D, st);
-        ProjP pp{b.H, b.ad, nullptr, b.sorted_slot, b.offsets, b.Zd, D.E, D.k, D.d, D.F, D.r};
+        ProjP pp{b.H, b.ad, nullptr, b.sorted_slot, b.offsets, b.Zd, D.E, D.k, D.d, D.F, D.r,
+                 static_cast<bf16_t *>(b.wZdT), b.topk_w, lgrad_ldT(D), D.S()};
         hipError_t e = launch_proj<T, PROJ_D>(D, pp, st);
         if (e != hipSuccess) return e;
     }
@@ -1182,29 +1259,41 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
     return hipSuccess;
 }
 
-template <typename T, int MODE>
-static hipError_t launch_lgrad(const Dims &D, const LGradP &lp, hipStream_t st) {
-    if constexpr (std::is_same<T, bf16_t>::value) {
-        const int grid = max_row_tiles(D.S(), D.E, kLgRC) * cdiv(lp.D, kLgBN);
-        if (lp.nr <= 32) MOE_LAUNCH((k_lgrad_lds<32, MODE>), grid, 256, lp);
-        else if (lp.nr <= 64) MOE_LAUNCH((k_lgrad_lds<64, MODE>), grid, 256, lp);
-        else return hipErrorInvalidValue;
-        k_lora_grad_finalize<MODE, kLgRC><<<dim3(cdiv(lp.D * lp.nr, 256), D.E), dim3(256), 0, st>>>(lp);
-        return hipGetLastError();
+template <int MODE>
+static hipError_t launch_lgrad_f32(const Dims &D, const LGradP &lp, hipStream_t st) {
+    using T = float;
+    const int ntm = cdiv(lp.D, 128);
+    if (lp.nr <= 32) {
+        using Cfg = typename SkinnyCfg<T, 32>::type;
+        MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
+                   Cfg::NTHREADS, lp);
     } else {
-        const int ntm = cdiv(lp.D, 128);
-        if (lp.nr <= 32) {
-            using Cfg = typename SkinnyCfg<T, 32>::type;
-            MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
-                       Cfg::NTHREADS, lp);
-        } else {
-            using Cfg = typename SkinnyCfg<T, 64>::type;
-            MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
-                       Cfg::NTHREADS, lp);
-        }
-        k_lora_grad_finalize<MODE, kLoraRC><<<dim3(cdiv(lp.D * lp.nr, 256), D.E), dim3(256), 0, st>>>(lp);
-        return hipGetLastError();
+        using Cfg = typename SkinnyCfg<T, 64>::type;
+        MOE_LAUNCH((k_lora_grad<Cfg, MODE>), max_row_tiles(D.S(), D.E, kLoraRC) * ntm * cdiv(lp.nr, Cfg::BN),
+                   Cfg::NTHREADS, lp);
     }
+    k_lora_grad_finalize<MODE, kLoraRC><<<dim3(cdiv(lp.D * lp.nr, 256), D.E), dim3(256), 0, st>>>(lp);
+    return hipGetLastError();
+}
+
+// the bf16 modes whose small operand has at most NR columns, in one launch
+template <int NR>
+static hipError_t launch_lgrad_set(const Dims &D, const LGradP (&lp)[4], hipStream_t st) {
+    LGradSet set{};
+    int grid = 0, maxdn = 0;
+    for (int m = 0; m < 4; ++m) {
+        const bool mine = NR == 32 ? lp[m].nr <= 32 : lp[m].nr > 32;
+        if (!mine) continue;
+        set.m[set.n] = lp[m];
+        set.base[set.n] = grid;
+        ++set.n;
+        grid += (max_row_tiles(D.S(), D.E, kLgRC) * cdiv(lp[m].D, kLgBN) + 7) & ~7;
+        maxdn = std::max(maxdn, lp[m].D * lp[m].nr);
+    }
+    if (set.n == 0) return hipSuccess;
+    MOE_LAUNCH(k_lgrad<NR>, grid, 256, set);
+    k_lgrad_finalize<<<dim3(cdiv(maxdn, 256), D.E, set.n), dim3(256), 0, st>>>(set);
+    return hipGetLastError();
 }
 
 template <typename T>
@@ -1220,7 +1309,8 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
     if (D.T > 0) {
         {
             TraceScope ts(tr, K_PROJ_DOUT, st);
-            ProjP pp{b.dout, b.bd, nullptr, b.sorted_slot, b.offsets, b.Pd, D.E, D.k, D.d, D.F, D.r};
+            ProjP pp{b.dout, b.bd, nullptr, b.sorted_slot, b.offsets, b.Pd, D.E, D.k, D.d, D.F, D.r,
+                     static_cast<bf16_t *>(b.wPdT), b.topk_w, lgrad_ldT(D), D.S()};
             hipError_t e = launch_proj<T, PROJ_DOUT>(D, pp, st);
             if (e != hipSuccess) return e;
         }
@@ -1235,7 +1325,8 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         }
         {
             TraceScope ts(tr, K_PROJ_DGU, st);
-            ProjP pp{b.dGU, b.bg, b.bu, b.sorted_slot, b.offsets, b.Pgu, D.E, D.k, D.d, D.F, D.r};
+            ProjP pp{b.dGU, b.bg, b.bu, b.sorted_slot, b.offsets, b.Pgu, D.E, D.k, D.d, D.F, D.r,
+                     static_cast<bf16_t *>(b.PguT), nullptr, lgrad_ldT(D), D.S()};
             hipError_t e = launch_proj<T, PROJ_DGU>(D, pp, st);
             if (e != hipSuccess) return e;
         }
@@ -1255,22 +1346,29 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
     }
     {
         TraceScope ts(tr, K_LORA_GRAD, st);
-        (void)S;
-        LGradP l0{b.x, b.Pgu, b.sorted_slot, b.offsets, b.topk_w, b.partial, b.da_g, b.da_u,
-                  D.E, D.k, D.d, D.F, D.r, D.d, 2 * D.r, D.d, 2 * D.r, D.s};
-        hipError_t e = launch_lgrad<T, 0>(D, l0, st);
-        if (e != hipSuccess) return e;
-        LGradP l1{b.dGU, b.Zgu, b.sorted_slot, b.offsets, b.topk_w, b.partial, b.db_g, b.db_u,
-                  D.E, D.k, D.d, D.F, D.r, 2 * D.F, 2 * D.r, 2 * D.F, 2 * D.r, D.s};
-        e = launch_lgrad<T, 1>(D, l1, st);
-        if (e != hipSuccess) return e;
-        LGradP l2{b.H, b.Pd, b.sorted_slot, b.offsets, b.topk_w, b.partial, b.da_d, nullptr,
-                  D.E, D.k, D.d, D.F, D.r, D.F, D.r, D.F, D.r, D.s};
-        e = launch_lgrad<T, 2>(D, l2, st);
-        if (e != hipSuccess) return e;
-        LGradP l3{b.dout, b.Zd, b.sorted_slot, b.offsets, b.topk_w, b.partial, b.db_d, nullptr,
-                  D.E, D.k, D.d, D.F, D.r, D.d, D.r, D.d, D.r, D.s};
-        e = launch_lgrad<T, 3>(D, l3, st);
+        size_t po[5];
+        lgrad_partial_layout(D, po);
+        const bool bf = std::is_same<T, bf16_t>::value;
+        auto part = [&](int m) { return reinterpret_cast<float *>(reinterpret_cast<char *>(b.partial) + (bf ? po[m] : 0)); };
+        const LGradP lp[4] = {
+            {b.x, b.Pgu, b.sorted_slot, b.offsets, b.topk_w, part(0), b.da_g, b.da_u, D.E, D.k, D.d, D.F, D.r, D.d,
+             2 * D.r, D.d, 2 * D.r, D.s, static_cast<const bf16_t *>(b.PguT), lgrad_ldT(D), 0},
+            {b.dGU, b.Zgu, b.sorted_slot, b.offsets, b.topk_w, part(1), b.db_g, b.db_u, D.E, D.k, D.d, D.F, D.r,
+             2 * D.F, 2 * D.r, 2 * D.F, 2 * D.r, D.s, static_cast<const bf16_t *>(b.ZguT), lgrad_ldT(D), 1},
+            {b.H, b.Pd, b.sorted_slot, b.offsets, b.topk_w, part(2), b.da_d, nullptr, D.E, D.k, D.d, D.F, D.r, D.F,
+             D.r, D.F, D.r, D.s, static_cast<const bf16_t *>(b.wPdT), lgrad_ldT(D), 2},
+            {b.dout, b.Zd, b.sorted_slot, b.offsets, b.topk_w, part(3), b.db_d, nullptr, D.E, D.k, D.d, D.F, D.r, D.d,
+             D.r, D.d, D.r, D.s, static_cast<const bf16_t *>(b.wZdT), lgrad_ldT(D), 3}};
+        hipError_t e = hipSuccess;
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            e = launch_lgrad_set<32>(D, lp, st);
+            if (e == hipSuccess) e = launch_lgrad_set<64>(D, lp, st);
+        } else {
+            e = launch_lgrad_f32<0>(D, lp[0], st);
+            if (e == hipSuccess) e = launch_lgrad_f32<1>(D, lp[1], st);
+            if (e == hipSuccess) e = launch_lgrad_f32<2>(D, lp[2], st);
+            if (e == hipSuccess) e = launch_lgrad_f32<3>(D, lp[3], st);
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -60,7 +60,9 @@ def al(x):
 def test_saved_and_workspace_sizes():
     p = pb()
     S, es = p.T * p.k, 2
-    want = 3 * al(S * p.F * es) + al(S * 2 * p.r * 4) + al(S * p.r * 4)
+    ldT = (S + 7) // 8 * 8
+    want = (3 * al(S * p.F * es) + al(S * 2 * p.r * 4) + al(S * p.r * 4)
+            + al(2 * p.r * ldT * 2) + al(p.r * ldT * 2))  # bf16: transposed copies for the LoRA gradients
     assert moe.saved_bytes(p, False) == want
     assert moe.saved_bytes(p, True) == want + al(S * p.d * es)
     assert moe.fwd_workspace(p, True, True) == 0

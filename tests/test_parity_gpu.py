@@ -83,6 +83,12 @@ def test_small_layer_full_parity(name):
     check("H", r["H"], f["H"], tol, name)
     check("Zgu", r["Zgu"], np.concatenate([f["Zg"], f["Zu"]], 1), tol, name)
     check("Zd", r["Zd"], f["Zd"], tol, name)
+    if cfg.dtype == "bf16":
+        # transposed bf16 copies kept for the LoRA-gradient kernels; the down
+        # one carries each row's combine weight
+        w_row = rt["topk_w"].reshape(-1)[rt["sorted_slot"]][:, None]
+        check("ZguT", r["ZguT"], np.concatenate([f["Zg"], f["Zu"]], 1).T, tol, name)
+        check("wZdT", r["wZdT"], (w_row * f["Zd"]).T, tol, name)
     check("Y", r["Y"], f["Y"], tol, name)
     check("out", r["out"], f["out"], tol, name)
     check("dx", r["dx"], b["dx"], tol, name)
