@@ -291,6 +291,36 @@ __device__ __forceinline__ void ring_iter(const Operands<C> &op, int t_issue, ch
     __builtin_amdgcn_sched_group_barrier(0x008, NMMA / 2, 1);
 }
 
+// Ring prologue: steps 0 .. NSTAGE-2 go to slots 1 .. NSTAGE-1 (`rest`)
+// while the rank-r LoRA tiles are staged through registers into slot 0
+// (`s0`) and multiplied. The restrict qualifiers state that the two regions
+// are disjoint, so the LoRA stores and reads need no wait on the ring loads.
+template <class C, class Lora>
+__device__ __forceinline__ void ring_prologue(const Operands<C> &op, int nlora, const Lora &lora, char *__restrict__ s0,
+                                              char *__restrict__ rest, int wave, f32x16_t (&acc)[C::TM][C::TN]) {
+    typename Lora::Regs lr;
+    if (nlora > 0) lora.load(0, lr);
+    // keep the LoRA loads ahead of the ring loads: loads complete in order,
+    // so waiting for the LoRA data must not also wait for the ring
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < C::NSTAGE - 1; ++t) op.issue(t, rest + t * C::STAGE_BYTES, wave);  // zeros past nt
+    for (int lt = 0; lt < nlora; ++lt) {
+        if (lt > 0) lora.load(lt, lr);
+        lora.store(lr, s0);
+        // LDS writes done, then a bare barrier: the ring loads stay in flight
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        mma_step<C>(s0, s0 + C::A_BYTES, acc);
+        if (lt + 1 < nlora) {  // slot 0 is refilled by the next LoRA tile
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+    }
+}
+
 // Ring driver: LoRA tiles first (stage 0, staged through registers by
 // lora.load / lora.store), then nt steady steps through stages 1.. in a
 // ring. The first LoRA tile's global loads are issued before the ring's, so
@@ -306,30 +336,7 @@ __device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     auto stage_of = [&](int t) { return smem + ((t + 1) % C::NSTAGE) * C::STAGE_BYTES; };
-    typename Lora::Regs lr;
-    if (nlora > 0) lora.load(0, lr);
-    // keep the LoRA loads ahead of the ring loads: loads complete in order,
-    // so waiting for the LoRA data must not also wait for the ring
-    __builtin_amdgcn_sched_barrier(0);
-    // ring prologue: steps 0 .. NSTAGE-2 in flight
-#pragma unroll
-    for (int t = 0; t < C::NSTAGE - 1; ++t)
-        if (t < op.nt) op.issue(t, stage_of(t), wave);
-    // rank-r LoRA expansion tiles through stage 0 while the ring fills
-    for (int lt = 0; lt < nlora; ++lt) {
-        if (lt > 0) lora.load(lt, lr);
-        lora.store(lr, smem);
-        // LDS writes done, then a bare barrier: the ring loads stay in flight
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        mma_step<C>(smem, smem + C::A_BYTES, acc);
-        if (lt + 1 < nlora) {  // stage 0 is refilled by the next LoRA tile
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-        }
-    }
+    ring_prologue<C>(op, nlora, lora, smem, smem + C::STAGE_BYTES, wave, acc);
     // Steady loop, skewed by half a step: after the barrier of step t the
     // wave issues the loads of step t + NSTAGE - 1 and the LDS reads of step
     // t's first k group interleaved with the MFMAs of step t-1's second k
