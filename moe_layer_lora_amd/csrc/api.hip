@@ -82,7 +82,7 @@ FwdWs fwd_ws(const moe_problem_t *pb, int training, int keep) {
     return w;
 }
 
-struct BwdWs { size_t Pd, Pgu, wPdT, PguT, dGU, dXp, partial, total; };
+struct BwdWs { size_t Pd, Pgu, wPdT, PguT, w_row, dGU, dXp, partial, total; };
 BwdWs bwd_ws(const moe_problem_t *pb) {
     const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
     const bool bf = pb->dtype == MOE_BF16;
@@ -93,6 +93,7 @@ BwdWs bwd_ws(const moe_problem_t *pb) {
     const size_t ldT = (S + 7) & ~(size_t)7;
     w.wPdT = o; if (bf) o += al(ldT * pb->r * 2);
     w.PguT = o; if (bf) o += al(ldT * 2 * pb->r * 2);
+    w.w_row = o; o += al(S * sizeof(float));
     w.dGU = o; o += al(S * 2 * pb->F * es);
     w.dXp = o; o += al(S * pb->d * es);
     w.partial = o; o += al(moe::lora_grad_partial_bytes(dims_of(pb)));
@@ -288,6 +289,7 @@ moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout, c
         b.ZguT = at(saved, sl.ZguT); b.wZdT = at(saved, sl.wZdT);
         b.wPdT = at(ws, bw.wPdT); b.PguT = at(ws, bw.PguT);
     }
+    b.w_row = reinterpret_cast<float *>(at(ws, bw.w_row));
     b.dGU = at(ws, bw.dGU); b.dXp = at(ws, bw.dXp);
     b.partial = reinterpret_cast<float *>(at(ws, bw.partial));
     b.dx = dx;

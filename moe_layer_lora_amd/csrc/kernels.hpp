@@ -52,6 +52,7 @@ struct BwdBufs {
     const void *ZguT, *wZdT;     // saved (bf16 only)
     float *Pd, *Pgu;             // workspace [S,r], [S,2r]
     void *wPdT, *PguT;           // workspace (bf16 only): [r,S] (w Pd)^T, [2r,S] Pgu^T
+    float *w_row;                // workspace [S]: combine weight of each row p
     void *dGU, *dXp;             // workspace [S,2F], [S,d]
     float *partial;              // workspace for LoRA-gradient partial sums
     void *dx;

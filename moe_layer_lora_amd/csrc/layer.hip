@@ -207,6 +207,7 @@ struct DownBwdP {
     void *dGU;
     int T, E, k, d, F, r;
     float s;
+    const float *w_row;  // bf16 path: combine weight of each row p (topk_w[sorted_slot[p]])
 };
 
 template <class Cfg>
@@ -529,28 +530,68 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
     lora.pb = {ad, ad, p.r, p.r, p.F, ncol};
     f32x16_t acc[C::TM][C::TN];
     lds::run<C>(op, cdiv(p.r, C::BK), lora, ring, acc);
+    // SwiGLU backward epilogue. Per 32-row slab of each wave: the fp32 tile
+    // goes through LDS to 16-byte row chunks; G, U and the row weight of the
+    // next slab are loaded while this slab is computed and stored.
     const bf16_t *G = static_cast<const bf16_t *>(p.G), *U = static_cast<const bf16_t *>(p.U);
     bf16_t *dGU = static_cast<bf16_t *>(p.dGU);
-    lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
-        const int f = n_base + n;
-        if (m < tl.rows && f < p.F) {
-            const int pr = tl.row0 + m;
-            const float w = p.topk_w[p.sorted_slot[pr]];
-            const size_t o = (size_t)pr * p.F + f;
-            float g[8], u[8], dg[8], du[8];
-            unpack<bf16_t>(*reinterpret_cast<const chunk_t *>(G + o), g);
-            unpack<bf16_t>(*reinterpret_cast<const chunk_t *>(U + o), u);
+    constexpr int LPR = C::WTN / 8, RPP = 64 / LPR, NPASS = 32 / RPP;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int c8 = (lane % LPR) * 8, f = n_base + wn * C::WTN + c8;
+    struct Pre {
+        chunk_t g[NPASS], u[NPASS];
+        float w[NPASS];
+    };
+    auto prefetch = [&](int mi, Pre &q) {
 #pragma unroll
-            for (int h = 0; h < 8; ++h) {
-                const float dh = w * v[h];
-                const float sg = 1.0f / (1.0f + __expf(-g[h]));
-                dg[h] = dh * u[h] * sg * (1.0f + g[h] * (1.0f - sg));
-                du[h] = dh * g[h] * sg;
-            }
-            *reinterpret_cast<chunk_t *>(dGU + (size_t)pr * 2 * p.F + f) = Elem<bf16_t>::pack(dg);
-            *reinterpret_cast<chunk_t *>(dGU + (size_t)pr * 2 * p.F + p.F + f) = Elem<bf16_t>::pack(du);
+        for (int pass = 0; pass < NPASS; ++pass) {
+            const int m = wm * C::WTM + mi * 32 + pass * RPP + lane / LPR;
+            const bool ok = m < tl.rows && f < p.F;
+            const size_t o = (size_t)(tl.row0 + (ok ? m : 0)) * p.F + (ok ? f : 0);
+            q.g[pass] = *reinterpret_cast<const chunk_t *>(G + o);
+            q.u[pass] = *reinterpret_cast<const chunk_t *>(U + o);
+            q.w[pass] = p.w_row[tl.row0 + (ok ? m : 0)];
         }
-    });
+    };
+    float *buf = reinterpret_cast<float *>(ring) + wave * 32 * C::WTN;
+    __syncthreads();  // every wave is done with the ring
+    Pre q[2];
+    prefetch(0, q[0]);
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi) {
+        if (mi + 1 < C::TM) prefetch(mi + 1, q[(mi + 1) & 1]);
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) buf[acc_row(i, lane) * C::WTN + ni * 32 + acc_col(lane)] = acc[mi][ni][i];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) {
+            const int r = pass * RPP + lane / LPR;
+            const int m = wm * C::WTM + mi * 32 + r;
+            const float4 a = *reinterpret_cast<const float4 *>(buf + r * C::WTN + c8);
+            const float4 b4 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + c8 + 4);
+            const float v[8] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
+            if (m < tl.rows && f < p.F) {
+                const Pre &cq = q[mi & 1];
+                float g[8], u[8], dg[8], du[8];
+                unpack<bf16_t>(cq.g[pass], g);
+                unpack<bf16_t>(cq.u[pass], u);
+                const float w = cq.w[pass];
+#pragma unroll
+                for (int h = 0; h < 8; ++h) {
+                    const float dh = w * v[h];
+                    const float sg = 1.0f / (1.0f + __expf(-g[h]));
+                    dg[h] = dh * u[h] * sg * (1.0f + g[h] * (1.0f - sg));
+                    du[h] = dh * g[h] * sg;
+                }
+                const size_t pr = (size_t)(tl.row0 + m);
+                *reinterpret_cast<chunk_t *>(dGU + pr * 2 * p.F + f) = Elem<bf16_t>::pack(dg);
+                *reinterpret_cast<chunk_t *>(dGU + pr * 2 * p.F + p.F + f) = Elem<bf16_t>::pack(du);
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next slab overwrites
+    }
 }
 
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
@@ -633,6 +674,7 @@ struct ProjP {
     bf16_t *outT;
     const float *wt;
     int ldT, S;
+    float *w_row_out;  // optional: wt[sorted_slot[p]] for every row p (written by the first column tile)
 };
 
 template <class Cfg, int KIND>
@@ -696,6 +738,9 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_proj(ProjP p) {
     for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
         if (m < tl.rows && n_base + n < nr) p.out[(size_t)(tl.row0 + m) * nr + n_base + n] = v;
     });
+    if (p.w_row_out && tl.nt == 0)
+        for (int m = threadIdx.x; m < tl.rows; m += Cfg::NTHREADS)
+            p.w_row_out[tl.row0 + m] = p.wt[p.sorted_slot[tl.row0 + m]];
     if (p.outT) {
         // the padding columns [S, ldT) are read as operands (times zero rows):
         // they must hold finite values
@@ -1310,14 +1355,14 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         {
             TraceScope ts(tr, K_PROJ_DOUT, st);
             ProjP pp{b.dout, b.bd, nullptr, b.sorted_slot, b.offsets, b.Pd, D.E, D.k, D.d, D.F, D.r,
-                     static_cast<bf16_t *>(b.wPdT), b.topk_w, lgrad_ldT(D), D.S()};
+                     static_cast<bf16_t *>(b.wPdT), b.topk_w, lgrad_ldT(D), D.S(), b.w_row};
             hipError_t e = launch_proj<T, PROJ_DOUT>(D, pp, st);
             if (e != hipSuccess) return e;
         }
         {
             TraceScope ts(tr, K_DOWN_BWD, st);
             DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
-                        D.T, D.E, D.k, D.d, D.F, D.r, D.s};
+                        D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row};
             if constexpr (std::is_same<T, bf16_t>::value)
                 MOE_LAUNCH((k_down_bwd_lds<LdsNN, LdsNNh>), grid_for<Cfg>(D, LdsNN::BM, cdiv(D.F, LdsNN::BN)), 256, dp);
             else
