@@ -51,7 +51,12 @@ struct Cfg {
 };
 
 __device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ int swz_n(int krow) { return 4 * (krow & 3); }
+// N-contiguous k-rows: XOR the 16-byte chunk index by 4 (k & 3) (rows of at
+// least 16 chunks) or by 4 (k & 1) (8-chunk rows of 64-column tiles)
+template <int BN> __device__ __forceinline__ int swz_n(int krow) {
+    static_assert(BN >= 64, "at least 8 chunks per k-row");
+    return BN >= 128 ? 4 * (krow & 3) : 4 * (krow & 1);
+}
 
 // ---------------------------------------------------------------------------
 // Direct loads of one K-contiguous operand tile (ROWS x BK) into LDS.
@@ -99,16 +104,17 @@ struct NDirect {
     int ncol_off[INSTR];   // element offset n of this lane's chunk
     bool nok[INSTR];
 
-    __device__ void init(int wave, int lane, int ncol) {
+    // tile columns [c_lo, c_hi) are loaded (8-aligned bounds), the rest read as zero
+    __device__ void init(int wave, int lane, int ncol, int c_lo = 0) {
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
             const int q = wave * INSTR + j;
             const int byte = lane * 16;               // within the 1 KB block
             krow[j] = q * KR + byte / (BN * 2);
             const int pch = (byte % (BN * 2)) / 16;   // physical chunk in the k-row
-            const int lch = pch ^ swz_n(krow[j]);
+            const int lch = pch ^ swz_n<BN>(krow[j]);
             ncol_off[j] = lch * 8;
-            nok[j] = ncol_off[j] + 8 <= ncol;
+            nok[j] = ncol_off[j] >= c_lo && ncol_off[j] + 8 <= ncol;
         }
     }
     __device__ __forceinline__ void issue(rsrc_t rs, uint32_t ldb, int k0, int K, char *lds, int wave) const {
@@ -131,7 +137,7 @@ __device__ __forceinline__ void st_kcontig(char *lds, int row, int c, const chun
 // N-contiguous: 8 consecutive n at (k, n0) -> physical chunk (n0 / 8) ^ swz_n(k).
 template <int BN>
 __device__ __forceinline__ void st_ncontig(char *lds, int k, int n0, const chunk_t &v) {
-    *reinterpret_cast<chunk_t *>(lds + k * BN * 2 + (((n0 >> 3) ^ swz_n(k)) * 16)) = v;
+    *reinterpret_cast<chunk_t *>(lds + k * BN * 2 + (((n0 >> 3) ^ swz_n<BN>(k)) * 16)) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -173,7 +179,7 @@ __device__ __forceinline__ void read_frags(const char *sa, const char *sb, int k
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int k = kbase + 4 * half;
-                const char *p = sb + k * C::BN * 2 + (((n >> 3) ^ swz_n(k)) * 16) + (n & 7) * 2;
+                const char *p = sb + k * C::BN * 2 + (((n >> 3) ^ swz_n<C::BN>(k)) * 16) + (n & 7) * 2;
                 h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(p));
             }
             f.b[ni] = chunk_t{(uint32_t)(uint16_t)h[0].x | ((uint32_t)(uint16_t)h[0].y << 16),
@@ -228,8 +234,9 @@ struct Operands {
     // choice (bit j of bsel_mask for this wave)
     KDirect<C::BN, C::B_INSTR> bk;
     uint32_t bsel_mask = 0;
-    // B, N-contiguous
-    NDirect<C::BN, C::B_INSTR> bn;
+    // B, N-contiguous (bn1: segment 1, when its columns differ from segment 0's)
+    NDirect<C::BN, C::B_INSTR> bn, bn1;
+    bool bn_split = false;
     uint32_t ldb[2] = {0, 0};
     rsrc_t rb[2][2];
 
@@ -239,15 +246,21 @@ struct Operands {
         const bool s1 = t >= nt0;
         const int k0 = (s1 ? t - nt0 : t) * C::BK;
         const int Ks = t < nt ? (s1 ? K[1] : K[0]) : 0;
-        a.issue(s1 ? ra[1] : ra[0], s1 ? acol[1] : acol[0], k0, Ks, stage, wave);
+        // operands as values (no runtime index into the arrays: that would
+        // put the descriptors in scratch)
+        const rsrc_t ra0 = ra[0], ra1 = ra[1];
+        const rsrc_t r00 = rb[0][0], r01 = rb[0][1], r10 = rb[1][0], r11 = rb[1][1];
+        const uint32_t ac0 = acol[0], ac1 = acol[1], lb0 = ldb[0], lb1 = ldb[1];
+        a.issue(s1 ? ra1 : ra0, s1 ? ac1 : ac0, k0, Ks, stage, wave);
         char *sb = stage + C::A_BYTES;
         if constexpr (C::B_NCONTIG) {
-            bn.issue(s1 ? rb[1][0] : rb[0][0], s1 ? ldb[1] : ldb[0], k0, Ks, sb, wave);
+            if (s1 && bn_split) bn1.issue(r10, lb1, k0, Ks, sb, wave);
+            else bn.issue(s1 ? r10 : r00, s1 ? lb1 : lb0, k0, Ks, sb, wave);
         } else {
 #pragma unroll
             for (int j = 0; j < C::B_INSTR; ++j) {
                 const bool sel = (bsel_mask >> j) & 1u;
-                const rsrc_t d = s1 ? (sel ? rb[1][1] : rb[1][0]) : (sel ? rb[0][1] : rb[0][0]);
+                const rsrc_t d = s1 ? (sel ? r11 : r10) : (sel ? r01 : r00);
                 const int k = k0 + bk.lchunk[j] * 8;
                 const uint32_t vo = (bk.off[j] != kInvalid && k < Ks) ? bk.off[j] + (uint32_t)k * 2 : kInvalid;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(d, MOE_LDS_PTR(sb + (wave * C::B_INSTR + j) * 1024), 16, vo,
@@ -474,6 +487,13 @@ struct LoraTile {
     struct Regs { typename PA::Regs a; typename PB::Regs b; };
     __device__ __forceinline__ void load(int lt, Regs &r) const { pa.load(lt, r.a); pb.load(lt, r.b); }
     __device__ __forceinline__ void store(const Regs &r, char *st) const { pa.store(r.a, st); pb.store(r.b, st); }
+};
+
+// No rank-r tile (plain grouped GEMMs such as the LoRA projections).
+struct NoLora {
+    struct Regs {};
+    __device__ __forceinline__ void load(int, Regs &) const {}
+    __device__ __forceinline__ void store(const Regs &, char *) const {}
 };
 
 // ---------------------------------------------------------------------------

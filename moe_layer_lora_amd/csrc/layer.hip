@@ -758,6 +758,121 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_proj(ProjP p) {
     }
 }
 
+// bf16 projections on the direct-load ring: 128-row tiles, 64 output
+// columns (nr <= 64 per tile), A rows gathered by token for PROJ_GU and
+// PROJ_DOUT, B K-contiguous (A_g | A_u, A_d) or N-contiguous (B_d; B_g and B_u
+// as two K segments over the dG and dU columns of dGU, block-diagonal).
+using ProjNT = lds::Cfg<128, 64, 4, false>;
+using ProjNN = lds::Cfg<128, 64, 4, true>;
+
+template <class C, int KIND>
+__global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
+    __shared__ LdsSmem<C> sm;
+    constexpr bool GATHER = KIND == PROJ_GU || KIND == PROJ_DOUT;
+    const int nr = (KIND == PROJ_GU || KIND == PROJ_DGU) ? 2 * p.r : p.r;
+    Tile tl;
+    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(nr, C::BN), blockIdx.x, sm.start, tl)) return;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int n_base = tl.nt * C::BN;
+    // A: rows of length lda (elements); K per segment
+    const int lda = (KIND == PROJ_GU || KIND == PROJ_DOUT) ? p.d : (KIND == PROJ_D ? p.F : 2 * p.F);
+    const int K = (KIND == PROJ_GU || KIND == PROJ_DOUT) ? p.d : p.F;
+    const int arows = GATHER ? p.S / p.k : p.S;
+    lds::Operands<C> op;
+    uint32_t aro[C::A_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::A_INSTR; ++j) {
+        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        const uint32_t row = m < tl.rows ? (GATHER ? (uint32_t)token_of(p.sorted_slot, tl.row0 + m, p.k)
+                                                   : (uint32_t)(tl.row0 + m))
+                                         : 0u;
+        aro[j] = m < tl.rows ? row * (uint32_t)lda * 2u : kInvalid;
+    }
+    op.a.init_rows(wave, lane, aro);
+    op.ra[0] = op.ra[1] = make_rsrc(p.a, (uint32_t)arows * (uint32_t)lda * 2u);
+    op.K[0] = op.K[1] = K;
+    op.nt0 = op.nt = cdiv(K, C::BK);
+    if constexpr (!C::B_NCONTIG) {
+        // B rows n: n < r from b0 (A_gate / A_down), r <= n < 2r from b1 (A_up);
+        // one load covers 16 rows of one matrix (r is a multiple of 16 here)
+        uint32_t bro[C::B_INSTR];
+#pragma unroll
+        for (int j = 0; j < C::B_INSTR; ++j) {
+            const int n = n_base + lds_row(wave, lane, j, C::B_INSTR);
+            bro[j] = n < nr ? (uint32_t)(n % p.r) * (uint32_t)K * 2u : kInvalid;
+            const int n0 = n_base + (wave * C::B_INSTR + j) * 16;
+            op.bsel_mask |= (uint32_t)(KIND == PROJ_GU && n0 >= p.r) << j;
+        }
+        op.bk.init_rows(wave, lane, bro);
+        const size_t bofs = (size_t)tl.e * p.r * K;
+        op.rb[0][0] = op.rb[1][0] = make_rsrc(static_cast<const bf16_t *>(p.b0) + bofs, (uint32_t)p.r * K * 2u);
+        op.rb[0][1] = op.rb[1][1] =
+            make_rsrc(static_cast<const bf16_t *>(KIND == PROJ_GU ? p.b1 : p.b0) + bofs, (uint32_t)p.r * K * 2u);
+    } else {
+        const size_t bofs = (size_t)tl.e * K * p.r;
+        op.ldb[0] = op.ldb[1] = (uint32_t)p.r * 2u;
+        if (KIND == PROJ_DOUT) {
+            // B_d[e] is [d, r]: k = model dim, columns j < r
+            op.bn.init(wave, lane, min(C::BN, p.r - n_base));
+            op.rb[0][0] = op.rb[1][0] =
+                make_rsrc(static_cast<const bf16_t *>(p.b0) + bofs + n_base, (uint32_t)(K * p.r - n_base) * 2u);
+        } else {
+            // segment 0: dG (columns [0, F) of dGU) x B_g -> output columns [0, r)
+            // segment 1: dU (columns [F, 2F)) x B_u -> output columns [r, 2r)
+            op.acol[0] = 0;
+            op.acol[1] = (uint32_t)p.F * 2u;
+            op.bn.init(wave, lane, max(0, min(C::BN, p.r - n_base)));
+            op.bn1.init(wave, lane, min(C::BN, 2 * p.r - n_base), max(0, p.r - n_base));
+            op.bn_split = true;
+            const bf16_t *bg = static_cast<const bf16_t *>(p.b0) + bofs;
+            const bf16_t *bu = static_cast<const bf16_t *>(p.b1) + bofs;
+            op.rb[0][0] = make_rsrc(bg + n_base, (uint32_t)(K * p.r - min(n_base, K * p.r)) * 2u);
+            // column n of the tile is column n_base + n - r of B_u (n >= r - n_base only)
+            op.rb[1][0] = make_rsrc(bu + (n_base - p.r), (uint32_t)(K * p.r + p.r - n_base) * 2u);
+            const int nk = cdiv(K, C::BK);
+            const bool has0 = n_base < p.r, has1 = n_base + C::BN > p.r;
+            op.nt0 = has0 ? nk : 0;
+            op.nt = op.nt0 + (has1 ? nk : 0);
+        }
+    }
+    f32x16_t acc[C::TM][C::TN];
+    lds::NoLora nolora;
+    lds::run<C>(op, 0, nolora, sm.ring, acc);
+    if (p.w_row_out && tl.nt == 0)
+        for (int m = threadIdx.x; m < tl.rows; m += 256) p.w_row_out[tl.row0 + m] = p.wt[p.sorted_slot[tl.row0 + m]];
+    const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = wm * C::WTM + mi * 32 + acc_row(i, lane);
+                const int n = n_base + wn * C::WTN + ni * 32 + acc_col(lane);
+                if (m < tl.rows && n < nr) p.out[(size_t)(tl.row0 + m) * nr + n] = acc[mi][ni][i];
+            }
+    if (p.outT) {
+        const int pad = p.ldT - p.S;
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < nr * pad; i += 256)
+                p.outT[(size_t)(i / pad) * p.ldT + p.S + i % pad] = Elem<bf16_t>::from_f32(0.0f);
+#pragma unroll
+        for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int m = wm * C::WTM + mi * 32 + acc_row(i, lane);
+                    const int n = n_base + wn * C::WTN + ni * 32 + acc_col(lane);
+                    if (m < tl.rows && n < nr) {
+                        const int pr = tl.row0 + m;
+                        const float sc = p.wt ? p.wt[p.sorted_slot[pr]] : 1.0f;
+                        p.outT[(size_t)n * p.ldT + pr] = Elem<bf16_t>::from_f32(acc[mi][ni][i] * sc);
+                    }
+                }
+    }
+}
+
 // ===========================================================================
 // Weighted combine / dX gather-sum: out[t] = sum_j w[t,j] Y[slot_row[t*k+j]]
 // (w = 1 for dX), fp32 accumulation in ascending j.
@@ -1021,7 +1136,7 @@ __device__ __forceinline__ void lg_issue(const LGradP &p, int p0, const uint32_t
     for (int j = 0; j < 4; ++j) {  // big: 2 rows of 512 B per 1 KB load
         const int q = wave * 4 + j;
         const int kr = q * 2 + (lane >> 5);
-        const int lch = (lane & 31) ^ lds::swz_n(kr);
+        const int lch = (lane & 31) ^ lds::swz_n<kLgBN>(kr);
         const uint32_t ro = rowoff[min(t * 32 + kr, kLgRows - 1)];
         const uint32_t vo =
             (live && ro != kInvalid && lch * 8 + 8 <= ncol) ? ro + (uint32_t)(c_base + lch * 8) * 2u : kInvalid;
@@ -1071,7 +1186,7 @@ __device__ __forceinline__ void lg_iter(const LGradP &p, int p0, const uint32_t 
                 const int k = kbase + 4 * half;
                 h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) lds::s16x4_t *)(st + k * kLgBN * 2 +
-                                                                       (((n >> 3) ^ lds::swz_n(k)) * 16) + (n & 7) * 2));
+                                                                       (((n >> 3) ^ lds::swz_n<kLgBN>(k)) * 16) + (n & 7) * 2));
             }
             bfr[ni] = chunk_t{(uint32_t)(uint16_t)h[0].x | ((uint32_t)(uint16_t)h[0].y << 16),
                               (uint32_t)(uint16_t)h[0].z | ((uint32_t)(uint16_t)h[0].w << 16),
@@ -1251,6 +1366,13 @@ template <class Cfg> static int grid_for(const Dims &D, int BM, int NT) { return
 template <typename T, int KIND>
 static hipError_t launch_proj(const Dims &D, const ProjP &pp, hipStream_t st) {
     const int nr = (KIND == PROJ_GU || KIND == PROJ_DGU) ? 2 * D.r : D.r;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        if (KIND != PROJ_GU || D.r % 16 == 0) {
+            using C = typename std::conditional<KIND == PROJ_DOUT || KIND == PROJ_DGU, ProjNN, ProjNT>::type;
+            MOE_LAUNCH((k_proj_lds<C, KIND>), max_row_tiles(D.S(), D.E, C::BM) * cdiv(nr, C::BN), 256, pp);
+            return hipSuccess;
+        }
+    }
     if (nr <= 32) {
         using Cfg = typename SkinnyCfg<T, 32>::type;
         MOE_LAUNCH((k_proj<Cfg, KIND>), grid_for<Cfg>(D, Cfg::BM, cdiv(nr, Cfg::BN)), Cfg::NTHREADS, pp);
