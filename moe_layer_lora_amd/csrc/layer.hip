@@ -1101,7 +1101,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_lora_grad(LGradP p) {
 //    weight already applied for modes 2 and 3), K-contiguous.
 // Rows past the chunk load as zeros on the big side, which zeroes their
 // products whatever the SmallT columns hold.
-constexpr int kLgRC = 512;          // rows per chunk
+constexpr int kLgRC = 1024;         // rows per chunk
 constexpr int kLgRows = kLgRC + 8;   // chunk rows plus the alignment lead-in
 constexpr int kLgBN = 256;           // big-operand columns per block
 
@@ -1115,9 +1115,11 @@ template <int NR> struct LgRing {
 };
 
 template <int NR> struct LgSmem {
-    __align__(16) char ring[LgRing<NR>::NSTAGE * LgRing<NR>::STAGE];
+    union {  // the tile scheduler's table is dead once the ring starts
+        __align__(16) char ring[LgRing<NR>::NSTAGE * LgRing<NR>::STAGE];
+        int start[kMaxE + 1];
+    };
     uint32_t rowoff[kLgRows];  // byte offset of each step row in Big (kInvalid outside the chunk)
-    int start[kMaxE + 1];
 };
 
 struct LGradSet {
@@ -1210,6 +1212,7 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
     const int ntn = cdiv(p.D, kLgBN);
     Tile tl;
     if (!schedule_tile<kLgRC, 256>(p.offsets, p.E, ntn, b - set.base[mi], sm.start, tl)) return;
+    __syncthreads();  // every thread has read the scheduler table before the ring overwrites it
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool gather = p.mode == 0 || p.mode == 3;
@@ -1271,26 +1274,29 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
             }
 }
 
-// Finalize of the bf16 path, every mode of a set in one launch (blockIdx.z):
-// exact zeros for empty experts, chunk-ordered sums for multi-chunk experts.
+// Finalize of the bf16 path: kLgFinSplit blocks per (expert, mode). Experts
+// with one chunk were written by the gradient kernel and exit at once; empty
+// experts get exact zeros, multi-chunk experts the chunk-ordered sums.
+constexpr int kLgFinSplit = 16;  // finalize blocks per (expert, mode)
+
 __global__ __launch_bounds__(256) void k_lgrad_finalize(LGradSet set) {
     __shared__ int s_start[kMaxE + 1];
-    const int mi = blockIdx.z;
+    const int mi = blockIdx.y;
     const LGradP p = mi == 0 ? set.m[0] : mi == 1 ? set.m[1] : mi == 2 ? set.m[2] : set.m[3];
-    const int e = blockIdx.y;
+    const int e = blockIdx.x / kLgFinSplit, part = blockIdx.x % kLgFinSplit;
     const int ne = p.offsets[e + 1] - p.offsets[e];
-    if (ne > 0 && ne <= kLgRC) return;  // written by the gradient kernel directly
+    if (ne > 0 && ne <= kLgRC) return;
     for (int x = threadIdx.x; x < p.E; x += 256) s_start[x] = (p.offsets[x + 1] - p.offsets[x] + kLgRC - 1) / kLgRC;
     __syncthreads();
     int c0 = 0;
     for (int x = 0; x < e; ++x) c0 += s_start[x];
     const int nch = s_start[e];
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= p.D * p.nr) return;
-    const int m = idx / p.nr, n = idx % p.nr;
-    float v = 0.0f;
-    for (int c = 0; c < nch; ++c) v += p.partial[((size_t)(c0 + c) * p.D + m) * p.nr + n];
-    lgrad_store(p.mode, p, e, m, n, p.s * v);
+    for (int idx = part * 256 + threadIdx.x; idx < p.D * p.nr; idx += 256 * kLgFinSplit) {
+        const int m = idx / p.nr, n = idx % p.nr;
+        float v = 0.0f;
+        for (int c = 0; c < nch; ++c) v += p.partial[((size_t)(c0 + c) * p.D + m) * p.nr + n];
+        lgrad_store(p.mode, p, e, m, n, p.s * v);
+    }
 }
 
 // Finalize: zeros for empty experts, chunk-ordered sums for multi-chunk experts.
@@ -1447,7 +1453,7 @@ static hipError_t launch_lgrad_f32(const Dims &D, const LGradP &lp, hipStream_t 
 template <int NR>
 static hipError_t launch_lgrad_set(const Dims &D, const LGradP (&lp)[4], hipStream_t st) {
     LGradSet set{};
-    int grid = 0, maxdn = 0;
+    int grid = 0;
     for (int m = 0; m < 4; ++m) {
         const bool mine = NR == 32 ? lp[m].nr <= 32 : lp[m].nr > 32;
         if (!mine) continue;
@@ -1455,11 +1461,10 @@ static hipError_t launch_lgrad_set(const Dims &D, const LGradP (&lp)[4], hipStre
         set.base[set.n] = grid;
         ++set.n;
         grid += (max_row_tiles(D.S(), D.E, kLgRC) * cdiv(lp[m].D, kLgBN) + 7) & ~7;
-        maxdn = std::max(maxdn, lp[m].D * lp[m].nr);
     }
     if (set.n == 0) return hipSuccess;
     MOE_LAUNCH(k_lgrad<NR>, grid, 256, set);
-    k_lgrad_finalize<<<dim3(cdiv(maxdn, 256), D.E, set.n), dim3(256), 0, st>>>(set);
+    k_lgrad_finalize<<<dim3(D.E * kLgFinSplit, set.n), dim3(256), 0, st>>>(set);
     return hipGetLastError();
 }
 
