@@ -878,22 +878,34 @@ __global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
 // (w = 1 for dX), fp32 accumulation in ascending j.
 // ===========================================================================
 template <typename T>
-__global__ __launch_bounds__(128) void k_combine(const T *__restrict__ Y, const int32_t *__restrict__ slot_row,
+__global__ __launch_bounds__(256) void k_combine(const T *__restrict__ Y, const int32_t *__restrict__ slot_row,
                                                  const float *__restrict__ w, int k, int d, T *__restrict__ out) {
     constexpr int VEC = Elem<T>::VEC;
+    constexpr int KU = 8;  // choices loaded together (independent loads in flight)
     const int t = blockIdx.x;
     for (int c = threadIdx.x; c < d / VEC; c += blockDim.x) {
         float acc[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int q = t * k + j;
-            const float wj = w ? w[q] : 1.0f;
-            const chunk_t ch = *reinterpret_cast<const chunk_t *>(Y + (size_t)slot_row[q] * d + c * VEC);
-            float y[VEC];
-            unpack<T>(ch, y);
+        for (int j0 = 0; j0 < k; j0 += KU) {
+            chunk_t ch[KU];
+            float wj[KU];
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] += wj * y[v];
+            for (int u = 0; u < KU; ++u) {
+                const int j = j0 + u;
+                const int q = t * k + min(j, k - 1);
+                ch[u] = *reinterpret_cast<const chunk_t *>(Y + (size_t)slot_row[q] * d + c * VEC);
+                wj[u] = j < k ? (w ? w[q] : 1.0f) : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {  // j ascending
+                float y[VEC];
+                unpack<T>(ch[u], y);
+                if (j0 + u < k) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[v] += wj[u] * y[v];
+                }
+            }
         }
         *reinterpret_cast<chunk_t *>(out + (size_t)t * d + c * VEC) = Elem<T>::pack(acc);
     }
@@ -1426,7 +1438,7 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
     }
     {
         TraceScope ts(tr, K_COMBINE, st);
-        MOE_LAUNCH(k_combine<T>, D.T, 128, static_cast<const T *>(b.Y), b.slot_row, b.topk_w, D.k, D.d,
+        MOE_LAUNCH(k_combine<T>, D.T, 256, static_cast<const T *>(b.Y), b.slot_row, b.topk_w, D.k, D.d,
                    static_cast<T *>(b.out));
     }
     return hipSuccess;
@@ -1512,7 +1524,7 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         }
         {
             TraceScope ts(tr, K_DX_COMBINE, st);
-            MOE_LAUNCH(k_combine<T>, D.T, 128, static_cast<const T *>(b.dXp), b.slot_row,
+            MOE_LAUNCH(k_combine<T>, D.T, 256, static_cast<const T *>(b.dXp), b.slot_row,
                        static_cast<const float *>(nullptr), D.k, D.d, static_cast<T *>(b.dx));
         }
     }

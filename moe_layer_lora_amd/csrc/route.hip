@@ -38,6 +38,8 @@ __device__ __forceinline__ bool route_better(float ov, int oid, float bv, int bi
     return oid != INT_MAX && (bid == INT_MAX || ov > bv || (ov == bv && oid < bid));
 }
 
+// NPL: logits per lane (E <= 64 NPL); KS: result slots per lane (k <= 64 KS)
+template <int NPL, int KS>
 __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float *__restrict__ logits, int T, int E,
                                                               int k, int tpb, int nblk,
                                                               int32_t *__restrict__ topk_idx,
@@ -51,22 +53,22 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float *__res
     const int t0 = b * tpb, t1 = min(T, t0 + tpb);
     for (int t = t0 + wave; t < t1; t += kRouteWaves) {
         const float *row = logits + (size_t)t * E;
-        float v[kMaxPerLane];
+        float v[NPL];
         uint32_t avail = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
+        for (int i = 0; i < NPL; ++i) {
             const int e = lane + kWave * i;
             v[i] = e < E ? row[e] : 0.0f;
             if (e < E) avail |= 1u << i;
         }
-        int my_idx[kMaxPerLane];
-        float my_val[kMaxPerLane];
+        int my_idx[KS];
+        float my_val[KS];
         float v0 = 0.0f;
         for (int j = 0; j < k; ++j) {
             float bv = 0.0f;
             int bid = INT_MAX;
 #pragma unroll
-            for (int i = 0; i < kMaxPerLane; ++i)  // ids rise with i: a tie keeps the lower id
+            for (int i = 0; i < NPL; ++i)  // ids rise with i: a tie keeps the lower id
                 if (((avail >> i) & 1u) && (bid == INT_MAX || v[i] > bv)) {
                     bv = v[i];
                     bid = lane + kWave * i;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float *__res
             if ((bid & (kWave - 1)) == lane) avail &= ~(1u << (bid / kWave));
             if (j == 0) v0 = bv;
 #pragma unroll
-            for (int s = 0; s < kMaxPerLane; ++s)
+            for (int s = 0; s < KS; ++s)
                 if (s == (j / kWave) && lane == (j & (kWave - 1))) {
                     my_idx[s] = bid;
                     my_val[s] = bv;
@@ -94,12 +96,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float *__res
         // softmax over the k selected logits, shifted by the largest
         float sum = 0.0f;
 #pragma unroll
-        for (int s = 0; s < kMaxPerLane; ++s)
+        for (int s = 0; s < KS; ++s)
             if (s * kWave + lane < k) sum += expf(my_val[s] - v0);
 #pragma unroll
         for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
 #pragma unroll
-        for (int s = 0; s < kMaxPerLane; ++s) {
+        for (int s = 0; s < KS; ++s) {
             const int j = s * kWave + lane;
             if (j < k) {
                 topk_idx[(size_t)t * k + j] = my_idx[s];
@@ -153,8 +155,10 @@ __global__ __launch_bounds__(1024) void k_route_scan(const int32_t *__restrict__
     const int per = (nblk + G - 1) / G;
     const int b0 = min(nblk, g * per), b1 = min(nblk, b0 + per);
     int part = 0;
-    if (act)
-        for (int b = b0; b < b1; ++b) part += hist[(size_t)b * E + e];
+    if (act) {
+#pragma unroll 16
+        for (int b = b0; b < b1; ++b) part += hist[(size_t)b * E + e];  // unrolled: many loads in flight
+    }
     s_part[tid] = act ? part : 0;
     __syncthreads();
     int c = 0;
@@ -173,6 +177,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(const int32_t *__restrict__
     if (act) {
         int run = s_off[e];
         for (int q = 0; q < g; ++q) run += s_part[q * E + e];
+#pragma unroll 16
         for (int b = b0; b < b1; ++b) {
             const int h = hist[(size_t)b * E + e];
             base[(size_t)b * E + e] = run;
@@ -238,8 +243,15 @@ hipError_t launch_route_topk(const float *logits, int T, int E, int k, int32_t *
     const int nblk = route_nblk(T, E);
     if (nblk == 0) return hipSuccess;
     const int tpb = route_tokens_per_block(T, E);
-    hipLaunchKernelGGL(k_route_topk, dim3(nblk), dim3(kRouteThreads), 0, st, logits, T, E, k, tpb, nblk, topk_idx,
-                       topk_w, hist);
+#define MOE_TOPK(NPL, KS)                                                                                  \
+    hipLaunchKernelGGL((k_route_topk<NPL, KS>), dim3(nblk), dim3(kRouteThreads), 0, st, logits, T, E, k, tpb,    \
+                       nblk, topk_idx, topk_w, hist)
+    if (E <= 64) MOE_TOPK(1, 1);
+    else if (E <= 128) { if (k <= 64) MOE_TOPK(2, 1); else MOE_TOPK(2, 2); }
+    else if (E <= 256) { if (k <= 64) MOE_TOPK(4, 1); else MOE_TOPK(4, 4); }
+    else if (E <= 512) { if (k <= 64) MOE_TOPK(8, 1); else MOE_TOPK(8, 8); }
+    else { if (k <= 64) MOE_TOPK(16, 1); else MOE_TOPK(16, 16); }
+#undef MOE_TOPK
     return hipGetLastError();
 }
 
