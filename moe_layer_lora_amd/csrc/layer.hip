@@ -985,6 +985,7 @@ struct LGradP {
     float s;
     const bf16_t *smallT;            // bf16 path: [nr, ldT] transposed small operand
     int ldT, mode;                   // ldT = S rounded up to a multiple of 8
+    int j0;                          // bf16 path: first small-operand column of this slice
 };
 
 __device__ __forceinline__ void lgrad_store(int mode, const LGradP &p, int e, int m, int n, float v) {
@@ -1001,6 +1002,37 @@ __device__ __forceinline__ void lgrad_store(int mode, const LGradP &p, int e, in
     default: p.out0[((size_t)e * p.d + m) * p.r + n] = v; break;
     }
 }
+
+// The same mapping as strides, set up once per block: element (m, n) of
+// expert e goes to (n < split ? o0 : o1) + (n mod split) * sn + (m - mo_h) * sm,
+// where half 1 (n >= split) shifts m by mo; mode 1 keeps only the diagonal
+// blocks (m < F with n < r, m >= F with n >= r).
+struct LgOut {
+    float *o0, *o1;
+    int split, sn, sm, mo;
+    bool diag;
+    __device__ LgOut(const LGradP &p, int e) {
+        switch (p.mode) {
+        case 0:
+            o0 = p.out0 + (size_t)e * p.r * p.d; o1 = p.out1 + (size_t)e * p.r * p.d;
+            split = p.r; sn = p.d; sm = 1; mo = 0; diag = false; break;
+        case 1:
+            o0 = p.out0 + (size_t)e * p.F * p.r; o1 = p.out1 + (size_t)e * p.F * p.r;
+            split = p.r; sn = 1; sm = p.r; mo = p.F; diag = true; break;
+        case 2:
+            o0 = o1 = p.out0 + (size_t)e * p.r * p.F;
+            split = p.nr; sn = p.F; sm = 1; mo = 0; diag = false; break;
+        default:
+            o0 = o1 = p.out0 + (size_t)e * p.d * p.r;
+            split = p.nr; sn = 1; sm = p.r; mo = 0; diag = false; break;
+        }
+    }
+    __device__ __forceinline__ void store(int m, int n, float v) const {
+        const bool h = n >= split;
+        if (diag && h != (m >= mo)) return;
+        (h ? o1 : o0)[(size_t)(h ? n - split : n) * sn + (size_t)(h ? m - mo : m) * sm] = v;
+    }
+};
 
 // Transposing loader whose k index is a row p of the current chunk:
 // element (k = row, col) is src_row(p)[col], for ROWS tile columns.
@@ -1134,9 +1166,13 @@ template <int NR> struct LgSmem {
     uint32_t rowoff[kLgRows];  // byte offset of each step row in Big (kInvalid outside the chunk)
 };
 
+// Slices of the four modes in one launch: a slice covers NR columns j of a
+// mode's small operand (nr up to 2r = 512 takes several slices).
+constexpr int kLgMaxSlices = 24;
+constexpr int kLgSliceMax = 64;  // columns per slice of the NR = 64 kernel (NR = 32 slices take nr <= 32)
 struct LGradSet {
-    LGradP m[4];
-    int base[4];  // first block of each mode (multiples of 8: the tile scheduler's XCD map)
+    LGradP m[kLgMaxSlices];
+    int base[kLgMaxSlices];  // first block of each slice (multiples of 8: the tile scheduler's XCD map)
     int n;
 };
 
@@ -1162,8 +1198,9 @@ __device__ __forceinline__ void lg_issue(const LGradP &p, int p0, const uint32_t
         const int jr = q * 4 + (lane >> 4);
         const int lc = ((lane & 15) >> 2) ^ lds::swz_k(jr);
         const uint32_t pr = (uint32_t)(p0 + t * 32 + lc * 8);  // 8-aligned: 16-byte aligned chunks
-        const uint32_t vo = (live && jr < p.nr) ? ((uint32_t)jr * (uint32_t)p.ldT + pr) * 2u + (uint32_t)(lane & 3) * 4u
-                                                : kInvalid;
+        const uint32_t vo = (live && p.j0 + jr < p.nr)
+                                ? ((uint32_t)(p.j0 + jr) * (uint32_t)p.ldT + pr) * 2u + (uint32_t)(lane & 3) * 4u
+                                : kInvalid;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsm, MOE_LDS_PTR(st + R::BIG + q * 256), 4, vo, 0, 0, 0);
     }
 }
@@ -1219,8 +1256,9 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
     using R = LgRing<NR>;
     __shared__ LgSmem<NR> sm;
     const int b = blockIdx.x;
-    const int mi = (set.n > 1 && b >= set.base[1]) + (set.n > 2 && b >= set.base[2]) + (set.n > 3 && b >= set.base[3]);
-    const LGradP p = mi == 0 ? set.m[0] : mi == 1 ? set.m[1] : mi == 2 ? set.m[2] : set.m[3];
+    int mi = 0;
+    while (mi + 1 < set.n && b >= set.base[mi + 1]) ++mi;  // uniform
+    const LGradP &p = set.m[mi];
     const int ntn = cdiv(p.D, kLgBN);
     Tile tl;
     if (!schedule_tile<kLgRC, 256>(p.offsets, p.E, ntn, b - set.base[mi], sm.start, tl)) return;
@@ -1270,17 +1308,18 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
     lds::wait_vm<0>();  // the zero loads of the last steps
     // acc[mi2][ni] holds out^T rows j = mi2*32 + .., columns c = wave*64 + ni*32 + ..
     const bool single = (p.offsets[tl.e + 1] - p.offsets[tl.e]) <= kLgRC;
+    const LgOut dst(p, tl.e);
 #pragma unroll
     for (int mi2 = 0; mi2 < TM; ++mi2)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int j = mi2 * 32 + acc_row(i, lane);
+                const int j = p.j0 + mi2 * 32 + acc_row(i, lane);
                 const int cl = wave * 64 + ni * 32 + acc_col(lane);
-                if (j < p.nr && cl < ncol) {
+                if (j < p.nr && j < p.j0 + NR && cl < ncol) {
                     const int m = c_base + cl;
-                    if (single) lgrad_store(p.mode, p, tl.e, m, j, p.s * acc[mi2][ni][i]);
+                    if (single) dst.store(m, j, p.s * acc[mi2][ni][i]);
                     else p.partial[((size_t)tl.gmt * p.D + m) * p.nr + j] = acc[mi2][ni][i];
                 }
             }
@@ -1294,7 +1333,7 @@ constexpr int kLgFinSplit = 16;  // finalize blocks per (expert, mode)
 __global__ __launch_bounds__(256) void k_lgrad_finalize(LGradSet set) {
     __shared__ int s_start[kMaxE + 1];
     const int mi = blockIdx.y;
-    const LGradP p = mi == 0 ? set.m[0] : mi == 1 ? set.m[1] : mi == 2 ? set.m[2] : set.m[3];
+    const LGradP &p = set.m[mi];
     const int e = blockIdx.x / kLgFinSplit, part = blockIdx.x % kLgFinSplit;
     const int ne = p.offsets[e + 1] - p.offsets[e];
     if (ne > 0 && ne <= kLgRC) return;
@@ -1303,11 +1342,13 @@ __global__ __launch_bounds__(256) void k_lgrad_finalize(LGradSet set) {
     int c0 = 0;
     for (int x = 0; x < e; ++x) c0 += s_start[x];
     const int nch = s_start[e];
-    for (int idx = part * 256 + threadIdx.x; idx < p.D * p.nr; idx += 256 * kLgFinSplit) {
-        const int m = idx / p.nr, n = idx % p.nr;
+    const int ns = min(p.nr - p.j0, kLgSliceMax);
+    const LgOut dst(p, e);
+    for (int idx = part * 256 + threadIdx.x; idx < p.D * ns; idx += 256 * kLgFinSplit) {
+        const int m = idx / ns, n = p.j0 + idx % ns;
         float v = 0.0f;
         for (int c = 0; c < nch; ++c) v += p.partial[((size_t)(c0 + c) * p.D + m) * p.nr + n];
-        lgrad_store(p.mode, p, e, m, n, p.s * v);
+        dst.store(m, n, p.s * v);
     }
 }
 
@@ -1462,6 +1503,8 @@ static hipError_t launch_lgrad_f32(const Dims &D, const LGradP &lp, hipStream_t 
 }
 
 // the bf16 modes whose small operand has at most NR columns, in one launch
+// The bf16 modes with nr <= 32 (NR = 32) or nr > 32 (NR = 64, in 64-column
+// slices), in one launch plus one finalize launch.
 template <int NR>
 static hipError_t launch_lgrad_set(const Dims &D, const LGradP (&lp)[4], hipStream_t st) {
     LGradSet set{};
@@ -1469,10 +1512,14 @@ static hipError_t launch_lgrad_set(const Dims &D, const LGradP (&lp)[4], hipStre
     for (int m = 0; m < 4; ++m) {
         const bool mine = NR == 32 ? lp[m].nr <= 32 : lp[m].nr > 32;
         if (!mine) continue;
-        set.m[set.n] = lp[m];
-        set.base[set.n] = grid;
-        ++set.n;
-        grid += (max_row_tiles(D.S(), D.E, kLgRC) * cdiv(lp[m].D, kLgBN) + 7) & ~7;
+        for (int j0 = 0; j0 < lp[m].nr; j0 += NR) {
+            if (set.n == kLgMaxSlices) return hipErrorInvalidValue;
+            set.m[set.n] = lp[m];
+            set.m[set.n].j0 = j0;
+            set.base[set.n] = grid;
+            ++set.n;
+            grid += (max_row_tiles(D.S(), D.E, kLgRC) * cdiv(lp[m].D, kLgBN) + 7) & ~7;
+        }
     }
     if (set.n == 0) return hipSuccess;
     MOE_LAUNCH(k_lgrad<NR>, grid, 256, set);

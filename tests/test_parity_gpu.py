@@ -50,6 +50,12 @@ SMALL = {
                                alpha=64.0, router_grad=True),
     "wide_bf16": LayerConfig("wide_bf16", T=520, d=264, E=4, k=2, F=328, r=8, dtype="bf16",
                              alpha=16.0, router_grad=True),
+    # 2r = 128: the LoRA gradients of gate/up take two 64-column slices
+    "rank64_bf16": LayerConfig("rank64_bf16", T=160, d=128, E=5, k=2, F=96, r=64, dtype="bf16",
+                               alpha=128.0, router_grad=True),
+    # E = 300: 5 logits per lane in the top-k kernel
+    "many_experts_bf16": LayerConfig("many_experts_bf16", T=256, d=64, E=300, k=6, F=64, r=16,
+                                     dtype="bf16", alpha=32.0, router_grad=True),
 }
 
 
@@ -119,6 +125,8 @@ def edge_case(name):
     if name == "multi_chunk_expert":  # > 1024 rows on one expert: chunked LoRA gradients
         cfg = LayerConfig(name, T=2100, E=3, k=1, **base)
         return cfg, lambda l: l.__setitem__((slice(0, 2050), 0), 50.0)
+    if name == "many_choices":  # k > 64: two result slots per lane in the top-k kernel
+        return LayerConfig(name, T=12, E=96, k=72, **base), None
     if name == "fp32_ties":
         cfg = LayerConfig(name, T=64, E=6, k=2, d=32, F=40, r=8, dtype="f32", alpha=16.0,
                           router_grad=True)
@@ -127,7 +135,7 @@ def edge_case(name):
 
 
 EDGE = ["one_token", "k_equals_E", "single_expert", "all_to_one_expert", "integer_ties",
-        "multi_chunk_expert", "fp32_ties"]
+        "multi_chunk_expert", "many_choices", "fp32_ties"]
 
 
 @pytest.mark.parametrize("name", EDGE)
