@@ -30,27 +30,41 @@ namespace lds {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
-template <int BM_, int BN_, int NSTAGE_, bool BN_CONTIG_>
+template <int BM_, int BN_, int NSTAGE_, bool BN_CONTIG_, int BK_ = 32>
 struct Cfg {
     using T = bf16_t;
-    static constexpr int BM = BM_, BN = BN_, BK = 32, NSTAGE = NSTAGE_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, NSTAGE = NSTAGE_;
     static constexpr bool B_NCONTIG = BN_CONTIG_;
     static constexpr int WM = 2, WN = 2, NTHREADS = 256, NWAVES = 4;
     static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+    static constexpr int NKG = BK / 16;                      // 16-deep MFMA k groups per step
     static constexpr int CPR = BK / 8;                       // 16-byte chunks per K-contig row
+    static constexpr int RPI = 64 / CPR;                     // K-contig rows per 1 KB load
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;  // direct loads per wave per step
     static constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;
     static constexpr int LOADS_PER_STEP = A_INSTR + B_INSTR;
-    static constexpr int ROWS_PER_INSTR = 1024 / (BK * 2);   // K-contig rows per 1 KB
     static constexpr int KROWS_PER_INSTR = 1024 / (BN * 2);  // N-contig k-rows per 1 KB
+    // The rank-r LoRA tiles always use 32-deep steps (LoraCfg). With 32-deep
+    // ring steps they go through ring slot 0; with 64-deep steps through a
+    // region of their own after the ring.
+    using LoraCfg = Cfg<BM_, BN_, NSTAGE_, BN_CONTIG_, 32>;
+    static constexpr bool LORA_SEPARATE = BK != 32;
+    static constexpr int RING_BYTES = NSTAGE * STAGE_BYTES;
+    static constexpr int SMEM_BYTES = RING_BYTES + (LORA_SEPARATE ? (BM + BN) * 32 * 2 : 0);
     static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "whole loads per wave");
-    static_assert(CPR == 4, "the K-contig swizzle assumes 64-byte rows");
+    static_assert(CPR == 4 || CPR == 8, "64- or 128-byte K-contig rows");
     static_assert(!B_NCONTIG || (BN * 2) % 1024 == 0 || 1024 % (BN * 2) == 0, "k-rows tile 1 KB loads");
 };
 
-__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+// K-contiguous rows: XOR the 16-byte chunk index by (row >> 2) & 3 (64-byte
+// rows) or (row >> 1) & 7 (128-byte rows): 16 consecutive rows of one
+// logical chunk then hit 16 distinct 16-byte bank groups
+template <int CPR> __device__ __forceinline__ int swz_kc(int row) {
+    return CPR == 4 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
+__device__ __forceinline__ int swz_k(int row) { return swz_kc<4>(row); }
 // N-contiguous k-rows: XOR the 16-byte chunk index by 4 (k & 3) (rows of at
 // least 16 chunks) or by 4 (k & 1) (8-chunk rows of 64-column tiles)
 template <int BN> __device__ __forceinline__ int swz_n(int krow) {
@@ -63,26 +77,25 @@ template <int BN> __device__ __forceinline__ int swz_n(int krow) {
 // Each thread owns INSTR rows (one per wave instruction); their byte offsets
 // (row start + segment column base handled by the caller) are fixed for the
 // whole K loop.
-template <int ROWS, int INSTR>
+template <int ROWS, int INSTR, int CPR = 4>
 struct KDirect {
+    static constexpr int RPI = 64 / CPR;  // rows per 1 KB load
     uint32_t off[INSTR];   // byte offset of the thread's row, kInvalid if outside
     int pchunk;            // this lane's physical chunk within its row
     // chunk of the row this lane fetches: logical = physical ^ swizzle(row)
     int lchunk[INSTR];
 
     __device__ void init_rows(int wave, int lane, const uint32_t (&rowoff)[INSTR]) {
-        pchunk = lane & 3;
+        pchunk = lane % CPR;
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
-            const int row = (wave * INSTR + j) * 16 + (lane >> 2);
-            lchunk[j] = pchunk ^ swz_k(row);
+            const int row = (wave * INSTR + j) * RPI + lane / CPR;
+            lchunk[j] = pchunk ^ swz_kc<CPR>(row);
             off[j] = rowoff[j];
         }
     }
-    // row (within the tile) that instruction j of this lane covers
-    __device__ static int row_of(int wave, int lane, int j, int instr) { return (wave * instr + j) * 16 + (lane >> 2); }
 
-    // issue the INSTR loads of K-step kstep (k elements [k0, k0 + 32) of the
+    // issue the INSTR loads of one step (k elements [k0, k0 + 8 CPR) of the
     // segment, valid for k < K) into the stage region at `lds`
     __device__ __forceinline__ void issue(rsrc_t rs, uint32_t colbytes, int k0, int K, char *lds, int wave) const {
 #pragma unroll
@@ -131,8 +144,9 @@ struct NDirect {
 // Register-staged stores into the same layouts (used for the rank-r LoRA
 // tile, whose A side is fp32 scaled by s and so cannot be loaded directly).
 // K-contiguous: chunk (row, logical c) -> physical c ^ swz_k(row).
+template <int CPR = 4>
 __device__ __forceinline__ void st_kcontig(char *lds, int row, int c, const chunk_t &v) {
-    *reinterpret_cast<chunk_t *>(lds + row * 64 + ((c ^ swz_k(row)) * 16)) = v;
+    *reinterpret_cast<chunk_t *>(lds + row * CPR * 16 + ((c ^ swz_kc<CPR>(row)) * 16)) = v;
 }
 // N-contiguous: 8 consecutive n at (k, n0) -> physical chunk (n0 / 8) ^ swz_n(k).
 template <int BN>
@@ -158,7 +172,7 @@ __device__ __forceinline__ void read_frags(const char *sa, const char *sb, int k
     for (int mi = 0; mi < C::TM; ++mi) {
         const int row = arow0 + mi * 32;
         const int c = kg * 2 + (lane >> 5);
-        f.a[mi] = *reinterpret_cast<const chunk_t *>(sa + row * 64 + ((c ^ swz_k(row)) * 16));
+        f.a[mi] = *reinterpret_cast<const chunk_t *>(sa + row * C::CPR * 16 + ((c ^ swz_kc<C::CPR>(row)) * 16));
     }
     if constexpr (!C::B_NCONTIG) {
         const int brow0 = wn * C::WTN + (lane & 31);
@@ -166,7 +180,7 @@ __device__ __forceinline__ void read_frags(const char *sa, const char *sb, int k
         for (int ni = 0; ni < C::TN; ++ni) {
             const int row = brow0 + ni * 32;
             const int c = kg * 2 + (lane >> 5);
-            f.b[ni] = *reinterpret_cast<const chunk_t *>(sb + row * 64 + ((c ^ swz_k(row)) * 16));
+            f.b[ni] = *reinterpret_cast<const chunk_t *>(sb + row * C::CPR * 16 + ((c ^ swz_kc<C::CPR>(row)) * 16));
         }
     } else {
         // transposing reads: 16-lane group g gets 4 k of 16 columns per read
@@ -202,7 +216,7 @@ __device__ __forceinline__ void mma_frags(const Frags<C> &f, f32x16_t (&acc)[C::
 template <class C>
 __device__ __forceinline__ void mma_step(const char *sa, const char *sb, f32x16_t (&acc)[C::TM][C::TN]) {
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
+    for (int kg = 0; kg < C::NKG; ++kg) {
         Frags<C> f;
         read_frags<C>(sa, sb, kg, f);
         mma_frags<C>(f, acc);
@@ -223,20 +237,19 @@ namespace lds {
 
 // Operands of one grouped-GEMM tile for the ring driver below. Up to two K
 // segments; step t < nt0 is segment 0 at k = 32 t, else segment 1.
-template <class C>
+template <class C, bool NSPLIT = false>
 struct Operands {
-    KDirect<C::BM, C::A_INSTR> a;
+    KDirect<C::BM, C::A_INSTR, C::CPR> a;
     rsrc_t ra[2];
     uint32_t acol[2] = {0, 0};     // byte column base of the A rows per segment
     int K[2] = {0, 0};
     int nt0 = 0, nt = 0;
     // B, K-contiguous: rows through rb[seg][sel] with sel a per-instruction
     // choice (bit j of bsel_mask for this wave)
-    KDirect<C::BN, C::B_INSTR> bk;
+    KDirect<C::BN, C::B_INSTR, C::CPR> bk;
     uint32_t bsel_mask = 0;
-    // B, N-contiguous (bn1: segment 1, when its columns differ from segment 0's)
+    // B, N-contiguous (bn1: segment 1's columns, used when NSPLIT)
     NDirect<C::BN, C::B_INSTR> bn, bn1;
-    bool bn_split = false;
     uint32_t ldb[2] = {0, 0};
     rsrc_t rb[2][2];
 
@@ -254,7 +267,7 @@ struct Operands {
         a.issue(s1 ? ra1 : ra0, s1 ? ac1 : ac0, k0, Ks, stage, wave);
         char *sb = stage + C::A_BYTES;
         if constexpr (C::B_NCONTIG) {
-            if (s1 && bn_split) bn1.issue(r10, lb1, k0, Ks, sb, wave);
+            if (NSPLIT && s1) bn1.issue(r10, lb1, k0, Ks, sb, wave);
             else bn.issue(s1 ? r10 : r00, s1 ? lb1 : lb0, k0, Ks, sb, wave);
         } else {
 #pragma unroll
@@ -275,41 +288,46 @@ struct Operands {
 // the restrict qualifiers state: the compiler then knows the LDS reads of
 // `src` cannot see the direct loads into `dst` and inserts no vmcnt drain
 // before them (the loop's own vmcnt waits order the stages).
-template <class C>
-__device__ __forceinline__ void ring_iter(const Operands<C> &op, int t_issue, char *__restrict__ dst,
-                                          const char *__restrict__ src, int wave, Frags<C> &f0, Frags<C> &f1,
+template <class C, class Op>
+__device__ __forceinline__ void ring_iter(const Op &op, int t_issue, char *__restrict__ dst,
+                                          const char *__restrict__ src, int wave, Frags<C> (&f)[2],
                                           f32x16_t (&acc)[C::TM][C::TN]) {
+    static_assert(C::NKG % 2 == 0, "k groups alternate between two fragment sets");
     op.issue(t_issue, dst, wave);
     constexpr int NMMA = C::TM * C::TN, NRD = C::TM + (C::B_NCONTIG ? 2 : 1) * C::TN;
     constexpr int L = C::LOADS_PER_STEP;
-    // phase 1: loads of the later step and reads of f0 under the MFMAs of f1
-    read_frags<C>(src, src + C::A_BYTES, 0, f0);
-    mma_frags<C>(f1, acc);  // zeros in the first iteration
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                // direct load
-        __builtin_amdgcn_sched_group_barrier(0x100, (NRD + L - 1) / L, 0);  // LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMMA - L, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // phase 2: reads of f1 under the MFMAs of f0
-    read_frags<C>(src, src + C::A_BYTES, 1, f1);
-    mma_frags<C>(f0, acc);
+    for (int kg = 0; kg < C::NKG; ++kg) {
+        // reads of group kg under the MFMAs of the group before it (the
+        // previous step's last group when kg = 0; zeros in the first step)
+        read_frags<C>(src, src + C::A_BYTES, kg, f[kg & 1]);
+        mma_frags<C>(f[(kg + 1) & 1], acc);
+        if (kg == 0) {
 #pragma unroll
-    for (int i = 0; i < NMMA / 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, (NRD + NMMA / 2 - 1) / (NMMA / 2), 1);
+            for (int i = 0; i < L; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      // direct load
+                __builtin_amdgcn_sched_group_barrier(0x100, (NRD + L - 1) / L, 0);      // LDS read
+            }
+            if (NMMA > L) __builtin_amdgcn_sched_group_barrier(0x008, NMMA - L, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NMMA / 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, (NRD + NMMA / 2 - 1) / (NMMA / 2), 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NMMA / 2, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMMA / 2, 1);
 }
 
 // Ring prologue: steps 0 .. NSTAGE-2 go to slots 1 .. NSTAGE-1 (`rest`)
 // while the rank-r LoRA tiles are staged through registers into slot 0
 // (`s0`) and multiplied. The restrict qualifiers state that the two regions
 // are disjoint, so the LoRA stores and reads need no wait on the ring loads.
-template <class C, class Lora>
-__device__ __forceinline__ void ring_prologue(const Operands<C> &op, int nlora, const Lora &lora, char *__restrict__ s0,
+template <class C, class Op, class Lora>
+__device__ __forceinline__ void ring_prologue(const Op &op, int nlora, const Lora &lora, char *__restrict__ s0,
                                               char *__restrict__ rest, int wave, f32x16_t (&acc)[C::TM][C::TN]) {
     typename Lora::Regs lr;
     if (nlora > 0) lora.load(0, lr);
@@ -325,7 +343,7 @@ __device__ __forceinline__ void ring_prologue(const Operands<C> &op, int nlora, 
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        mma_step<C>(s0, s0 + C::A_BYTES, acc);
+        mma_step<typename C::LoraCfg>(s0, s0 + C::LoraCfg::A_BYTES, acc);
         if (lt + 1 < nlora) {  // slot 0 is refilled by the next LoRA tile
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
@@ -338,8 +356,8 @@ __device__ __forceinline__ void ring_prologue(const Operands<C> &op, int nlora, 
 // lora.load / lora.store), then nt steady steps through stages 1.. in a
 // ring. The first LoRA tile's global loads are issued before the ring's, so
 // waiting for them leaves the ring loads in flight.
-template <class C, class Lora>
-__device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora &lora, char *smem,
+template <class C, class Op, class Lora>
+__device__ __forceinline__ void run(const Op &op, int nlora, const Lora &lora, char *smem,
                                     f32x16_t (&acc)[C::TM][C::TN]) {
 #pragma unroll
     for (int mi = 0; mi < C::TM; ++mi)
@@ -348,20 +366,24 @@ __device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    auto stage_of = [&](int t) { return smem + ((t + 1) % C::NSTAGE) * C::STAGE_BYTES; };
-    ring_prologue<C>(op, nlora, lora, smem, smem + C::STAGE_BYTES, wave, acc);
-    // Steady loop, skewed by half a step: after the barrier of step t the
+    // 32-deep steps: LoRA in slot 0, step t in slot (t + 1) % NSTAGE;
+    // 64-deep steps: step t in slot t % NSTAGE, LoRA in its own region
+    constexpr int SHIFT = C::LORA_SEPARATE ? 0 : 1;
+    auto stage_of = [&](int t) { return smem + ((t + SHIFT) % C::NSTAGE) * C::STAGE_BYTES; };
+    char *lora_slot = C::LORA_SEPARATE ? smem + C::RING_BYTES : smem;
+    ring_prologue<C>(op, nlora, lora, lora_slot, stage_of(0), wave, acc);
+    // Steady loop, skewed by one k group: after the barrier of step t the
     // wave issues the loads of step t + NSTAGE - 1 and the LDS reads of step
-    // t's first k group interleaved with the MFMAs of step t-1's second k
-    // group (already in registers), then step t's second-group reads with
-    // its first-group MFMAs. Every iteration issues one step of loads (zeros
-    // past the end), so the wait count is the same in every iteration and
-    // the loop body is a single block the scheduler can interleave.
-    Frags<C> f0, f1;
+    // t's k groups, each interleaved with the MFMAs of the group before it
+    // (the previous step's last group first, already in registers), so the
+    // MFMA pipe has work while the barrier resolves and the reads are in
+    // flight. Every iteration issues one step of loads (zeros past the end),
+    // so the wait count is the same in every iteration.
+    Frags<C> f[2];
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) f1.a[i] = chunk_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < C::TM; ++i) f[1].a[i] = chunk_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < C::TN; ++i) f1.b[i] = chunk_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < C::TN; ++i) f[1].b[i] = chunk_t{0u, 0u, 0u, 0u};
     for (int t = 0; t < op.nt; ++t) {
         wait_vm<(C::NSTAGE - 2) * C::LOADS_PER_STEP>();
         // Every LDS read of step t-1 has completed (lgkmcnt) before the bare
@@ -371,9 +393,9 @@ __device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        ring_iter<C>(op, t + C::NSTAGE - 1, stage_of(t + C::NSTAGE - 1), stage_of(t), wave, f0, f1, acc);
+        ring_iter<C>(op, t + C::NSTAGE - 1, stage_of(t + C::NSTAGE - 1), stage_of(t), wave, f, acc);
     }
-    if (op.nt > 0) mma_frags<C>(f1, acc);
+    if (op.nt > 0) mma_frags<C>(f[1], acc);
     // the zero loads of the last iterations land in the ring: drain them
     // before the epilogue reuses its memory
     wait_vm<0>();
@@ -385,6 +407,7 @@ __device__ __forceinline__ void run(const Operands<C> &op, int nlora, const Lora
 // matrix times s, k = 32 lt + ..., into the K-contiguous A tile.
 template <class C>
 struct LoraA {
+    static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
     static constexpr int PER = C::BM * 4 / 256;
     const float *z;
     int nz, row0, rows;
@@ -422,6 +445,7 @@ struct LoraA {
 // The row map comes from the kernel as per-chunk pointers and offsets.
 template <class C>
 struct LoraBK {
+    static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
     static constexpr int PER = C::BN * 4 / 256;
     const bf16_t *rowp[PER];  // row start (element k = klo), nullptr outside
     int klo[PER];
@@ -452,6 +476,7 @@ struct LoraBK {
 // < split from a, the rest from b, K rows in all), tile columns [0, ncol).
 template <class C>
 struct LoraBN {
+    static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
     static constexpr int PER = 32 * C::BN / 8 / 256;
     const bf16_t *a, *b;
     int split, K, ld, ncol;

@@ -338,17 +338,24 @@ __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup_
 // bf16 versions of the four grouped GEMMs on the direct-to-LDS ring engine
 // (gemm_lds.hpp). Same math and epilogues as the kernels above.
 // ===========================================================================
-using LdsNT = lds::Cfg<256, 256, 4, false>;   // both operands K-contiguous
-using LdsNN = lds::Cfg<256, 256, 4, true>;    // B N-contiguous (transposing reads)
-using LdsNTh = lds::Cfg<128, 256, 4, false>;  // 128-row tail tiles
-using LdsNNh = lds::Cfg<128, 256, 4, true>;
+// Forward (both operands K-contiguous): 64-deep steps, so every row segment
+// a load touches is a whole 128-byte line (about twice the L2-to-LDS rate of
+// 64-byte segments), in two 64 KB stages. Backward (B N-contiguous, read with
+// transposing LDS reads): 32-deep steps in four 32 KB stages measured faster.
+using LdsNT = lds::Cfg<256, 256, 2, false, 64>;
+using LdsNN = lds::Cfg<256, 256, 4, true, 32>;
+using LdsNTh = lds::Cfg<128, 256, 2, false, 64>;  // 128-row tail tiles
+using LdsNNh = lds::Cfg<128, 256, 4, true, 32>;
 
-template <class C> struct LdsSmem {
-    __align__(16) char ring[C::NSTAGE * C::STAGE_BYTES];
+template <class C> union LdsSmem {  // the tile scheduler's table is dead once the ring starts
+    __align__(16) char ring[C::SMEM_BYTES];
     int start[kMaxE + 1];
 };
 
-__device__ __forceinline__ int lds_row(int wave, int lane, int j, int instr) { return (wave * instr + j) * 16 + (lane >> 2); }
+// K-contiguous tile row that load j (of instr per wave) of this lane covers
+template <class C> __device__ __forceinline__ int lds_row(int wave, int lane, int j, int instr) {
+    return (wave * instr + j) * C::RPI + lane / C::CPR;
+}
 
 template <class C>
 __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, char *ring) {
@@ -358,7 +365,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
     uint32_t aro[C::A_INSTR], bro[C::B_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
-        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        const int m = lds_row<C>(wave, lane, j, C::A_INSTR);
         aro[j] = m < tl.rows ? (uint32_t)token_of(p.sorted_slot, tl.row0 + m, p.k) * p.d * 2 : kInvalid;
     }
     op.a.init_rows(wave, lane, aro);
@@ -368,11 +375,11 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
     // B rows interleave gate / up in 32-row blocks; one load covers 16 rows of one block
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
-        const int n = lds_row(wave, lane, j, C::B_INSTR);
+        const int n = lds_row<C>(wave, lane, j, C::B_INSTR);
         const int wn = n / C::WTN, ni = (n % C::WTN) / 32;
         const int f = f_base + wn * (C::WTN / 2) + (ni / 2) * 32 + (n % 32);
         bro[j] = f < p.F ? (uint32_t)f * p.d * 2 : kInvalid;
-        const int n0 = (wave * C::B_INSTR + j) * 16;  // first row of the load (same block for every lane)
+        const int n0 = (wave * C::B_INSTR + j) * C::RPI;  // first row of the load (same block for every lane)
         op.bsel_mask |= (uint32_t)(((n0 % C::WTN) / 32) & 1) << j;
     }
     op.bk.init_rows(wave, lane, bro);
@@ -382,12 +389,12 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
     const bf16_t *bg = static_cast<const bf16_t *>(p.bg) + (size_t)tl.e * p.F * p.r;
     const bf16_t *bu = static_cast<const bf16_t *>(p.bu) + (size_t)tl.e * p.F * p.r;
     // LoRA tile: [s Zg | s Zu] rows against [B_g | 0] (gate rows) and [0 | B_u] (up rows)
-    lds::LoraTile<lds::LoraA<C>, lds::LoraBK<C>> lora;
+    lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBK<typename C::LoraCfg>> lora;
     lora.pa = {p.zgu, 2 * p.r, tl.row0, tl.rows, p.s};
     lora.pb.r = p.r;
     lora.pb.safe = bg;
 #pragma unroll
-    for (int i = 0; i < lds::LoraBK<C>::PER; ++i) {
+    for (int i = 0; i < lds::LoraBK<typename C::LoraCfg>::PER; ++i) {
         const int n = ((int)threadIdx.x + 256 * i) >> 2;
         const int wn = n / C::WTN, ni = (n % C::WTN) / 32;
         const int f = f_base + wn * (C::WTN / 2) + (ni / 2) * 32 + (n % 32);
@@ -396,7 +403,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
         lora.pb.klo[i] = up ? p.r : 0;
     }
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, ring, acc);
+    lds::run<C>(op, cdiv(2 * p.r, C::LoraCfg::BK), lora, ring, acc);
 
     // wave columns: [gate 32 | up 32 | gate 32 | up 32] for f = f_base + wn*64 + (0..63)
     bf16_t *G = static_cast<bf16_t *>(p.G), *U = static_cast<bf16_t *>(p.U), *H = static_cast<bf16_t *>(p.H);
@@ -446,6 +453,7 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUp
     __shared__ LdsSmem<C> sm;
     Tile tl;
     if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, C::BN / 2), blockIdx.x, sm.start, tl)) return;
+    __syncthreads();  // every thread has read the scheduler table
     if (tl.rows > CH::BM) gateup_tile<C>(p, tl, sm.ring);
     else gateup_tile<CH>(p, tl, sm.ring);
 }
@@ -458,7 +466,7 @@ __device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *
     uint32_t aro[C::A_INSTR], bro[C::B_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
-        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        const int m = lds_row<C>(wave, lane, j, C::A_INSTR);
         aro[j] = m < tl.rows ? (uint32_t)(tl.row0 + m) * p.F * 2 : kInvalid;
     }
     op.a.init_rows(wave, lane, aro);
@@ -467,25 +475,25 @@ __device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *
     op.nt0 = op.nt = cdiv(p.F, C::BK);
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
-        const int n = n_base + lds_row(wave, lane, j, C::B_INSTR);
+        const int n = n_base + lds_row<C>(wave, lane, j, C::B_INSTR);
         bro[j] = n < p.d ? (uint32_t)n * p.F * 2 : kInvalid;
     }
     op.bk.init_rows(wave, lane, bro);
     op.rb[0][0] = op.rb[0][1] = op.rb[1][0] = op.rb[1][1] =
         make_rsrc(static_cast<const bf16_t *>(p.wd) + (size_t)tl.e * p.d * p.F, (uint32_t)p.d * p.F * 2);
     const bf16_t *bd = static_cast<const bf16_t *>(p.bd) + (size_t)tl.e * p.d * p.r;
-    lds::LoraTile<lds::LoraA<C>, lds::LoraBK<C>> lora;
+    lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBK<typename C::LoraCfg>> lora;
     lora.pa = {p.zd, p.r, tl.row0, tl.rows, p.s};
     lora.pb.r = p.r;
     lora.pb.safe = bd;
 #pragma unroll
-    for (int i = 0; i < lds::LoraBK<C>::PER; ++i) {
+    for (int i = 0; i < lds::LoraBK<typename C::LoraCfg>::PER; ++i) {
         const int n = n_base + (((int)threadIdx.x + 256 * i) >> 2);
         lora.pb.rowp[i] = n < p.d ? bd + (size_t)n * p.r : nullptr;
         lora.pb.klo[i] = 0;
     }
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(p.r, C::BK), lora, ring, acc);
+    lds::run<C>(op, cdiv(p.r, C::LoraCfg::BK), lora, ring, acc);
     bf16_t *Y = static_cast<bf16_t *>(p.Y);
     lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
         if (m < tl.rows && n_base + n < p.d)
@@ -499,6 +507,7 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_lds(DownP p)
     __shared__ LdsSmem<C> sm;
     Tile tl;
     if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
+    __syncthreads();  // every thread has read the scheduler table
     if (tl.rows > CH::BM) down_tile<C>(p, tl, sm.ring);
     else down_tile<CH>(p, tl, sm.ring);
 }
@@ -512,7 +521,7 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
     uint32_t aro[C::A_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
-        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        const int m = lds_row<C>(wave, lane, j, C::A_INSTR);
         aro[j] = m < tl.rows ? (uint32_t)token_of(p.sorted_slot, tl.row0 + m, p.k) * p.d * 2 : kInvalid;
     }
     op.a.init_rows(wave, lane, aro);
@@ -525,11 +534,11 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
                                           (uint32_t)((size_t)p.d * p.F - n_base) * 2);
     op.ldb[0] = op.ldb[1] = (uint32_t)p.F * 2;
     const bf16_t *ad = static_cast<const bf16_t *>(p.ad) + (size_t)tl.e * p.r * p.F + n_base;
-    lds::LoraTile<lds::LoraA<C>, lds::LoraBN<C>> lora;
+    lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBN<typename C::LoraCfg>> lora;
     lora.pa = {p.pd, p.r, tl.row0, tl.rows, p.s};
     lora.pb = {ad, ad, p.r, p.r, p.F, ncol};
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(p.r, C::BK), lora, ring, acc);
+    lds::run<C>(op, cdiv(p.r, C::LoraCfg::BK), lora, ring, acc);
     // SwiGLU backward epilogue. Per 32-row slab of each wave: the fp32 tile
     // goes through LDS to 16-byte row chunks; G, U and the row weight of the
     // next slab are loaded while this slab is computed and stored.
@@ -600,6 +609,7 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(Down
     __shared__ LdsSmem<C> sm;
     Tile tl;
     if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, C::BN), blockIdx.x, sm.start, tl)) return;
+    __syncthreads();  // every thread has read the scheduler table
     if (tl.rows > CH::BM) down_bwd_tile<C>(p, tl, sm.ring);
     else down_bwd_tile<CH>(p, tl, sm.ring);
 }
@@ -613,7 +623,7 @@ __device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile 
     uint32_t aro[C::A_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
-        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        const int m = lds_row<C>(wave, lane, j, C::A_INSTR);
         aro[j] = m < tl.rows ? (uint32_t)(tl.row0 + m) * 2 * p.F * 2 : kInvalid;
     }
     op.a.init_rows(wave, lane, aro);
@@ -631,11 +641,11 @@ __device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile 
     op.ldb[0] = op.ldb[1] = (uint32_t)p.d * 2;
     const size_t aofs = (size_t)tl.e * p.r * p.d + n_base;
     const bf16_t *ag = static_cast<const bf16_t *>(p.ag) + aofs, *au = static_cast<const bf16_t *>(p.au) + aofs;
-    lds::LoraTile<lds::LoraA<C>, lds::LoraBN<C>> lora;
+    lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBN<typename C::LoraCfg>> lora;
     lora.pa = {p.pgu, 2 * p.r, tl.row0, tl.rows, p.s};
     lora.pb = {ag, au, p.r, 2 * p.r, p.d, ncol};
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(2 * p.r, C::BK), lora, ring, acc);
+    lds::run<C>(op, cdiv(2 * p.r, C::LoraCfg::BK), lora, ring, acc);
     bf16_t *dXp = static_cast<bf16_t *>(p.dXp);
     lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
         if (m < tl.rows && n_base + n < p.d)
@@ -649,6 +659,7 @@ __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd_lds(Ga
     __shared__ LdsSmem<C> sm;
     Tile tl;
     if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
+    __syncthreads();  // every thread has read the scheduler table
     if (tl.rows > CH::BM) gateup_bwd_tile<C>(p, tl, sm.ring);
     else gateup_bwd_tile<CH>(p, tl, sm.ring);
 }
@@ -772,17 +783,18 @@ __global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
     const int nr = (KIND == PROJ_GU || KIND == PROJ_DGU) ? 2 * p.r : p.r;
     Tile tl;
     if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(nr, C::BN), blockIdx.x, sm.start, tl)) return;
+    __syncthreads();  // every thread has read the scheduler table
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int n_base = tl.nt * C::BN;
     // A: rows of length lda (elements); K per segment
     const int lda = (KIND == PROJ_GU || KIND == PROJ_DOUT) ? p.d : (KIND == PROJ_D ? p.F : 2 * p.F);
     const int K = (KIND == PROJ_GU || KIND == PROJ_DOUT) ? p.d : p.F;
     const int arows = GATHER ? p.S / p.k : p.S;
-    lds::Operands<C> op;
+    lds::Operands<C, KIND == PROJ_DGU> op;
     uint32_t aro[C::A_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
-        const int m = lds_row(wave, lane, j, C::A_INSTR);
+        const int m = lds_row<C>(wave, lane, j, C::A_INSTR);
         const uint32_t row = m < tl.rows ? (GATHER ? (uint32_t)token_of(p.sorted_slot, tl.row0 + m, p.k)
                                                    : (uint32_t)(tl.row0 + m))
                                          : 0u;
@@ -798,9 +810,9 @@ __global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
         uint32_t bro[C::B_INSTR];
 #pragma unroll
         for (int j = 0; j < C::B_INSTR; ++j) {
-            const int n = n_base + lds_row(wave, lane, j, C::B_INSTR);
+            const int n = n_base + lds_row<C>(wave, lane, j, C::B_INSTR);
             bro[j] = n < nr ? (uint32_t)(n % p.r) * (uint32_t)K * 2u : kInvalid;
-            const int n0 = n_base + (wave * C::B_INSTR + j) * 16;
+            const int n0 = n_base + (wave * C::B_INSTR + j) * C::RPI;
             op.bsel_mask |= (uint32_t)(KIND == PROJ_GU && n0 >= p.r) << j;
         }
         op.bk.init_rows(wave, lane, bro);
@@ -823,7 +835,6 @@ __global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
             op.acol[1] = (uint32_t)p.F * 2u;
             op.bn.init(wave, lane, max(0, min(C::BN, p.r - n_base)));
             op.bn1.init(wave, lane, min(C::BN, 2 * p.r - n_base), max(0, p.r - n_base));
-            op.bn_split = true;
             const bf16_t *bg = static_cast<const bf16_t *>(p.b0) + bofs;
             const bf16_t *bu = static_cast<const bf16_t *>(p.b1) + bofs;
             op.rb[0][0] = make_rsrc(bg + n_base, (uint32_t)(K * p.r - min(n_base, K * p.r)) * 2u);
