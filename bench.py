@@ -193,7 +193,8 @@ def main():
         grads = moe.alloc_grads(pb, dev)
         dtw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev) if keep else None
         dlg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev) if keep else None
-    host_counts = np.zeros(cfg.E, np.int32)
+    # pinned: the count readback is a stream-ordered copy that needs no host wait
+    host_counts = torch.zeros(cfg.E, dtype=torch.int32, pin_memory=True)
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration, dev)

@@ -37,9 +37,8 @@
  *    *_workspace queries) and `saved`. The library allocates no device
  *    memory, frees nothing and keeps no pointer after a call returns.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null
- *    stream). Only moe_route with a non-NULL host_counts blocks the host
- *    (one device->host copy and a stream synchronisation). moe_fwd and
- *    moe_bwd never synchronise.
+ *    stream). No call synchronises the stream. The only device->host
+ *    transfer is moe_route's optional copy of the expert counts (see there).
  *  - Errors: arguments are checked on the host before anything is enqueued;
  *    on any error nothing is launched and outputs are untouched. MOE_E_HIP
  *    means a HIP call failed after checks passed (outputs then undefined).
@@ -143,9 +142,14 @@ size_t moe_bwd_workspace(const moe_problem_t *pb);
 size_t moe_saved_bytes(const moe_problem_t *pb, int keep_expert_out);
 
 /* Routing. logits [T,E] float32 -> rt (all six arrays written).
- * host_counts: (host) int32[E] that receives counts, or NULL; when non-NULL
- * the call copies counts to it and synchronises `stream` before returning:
- * the one device->host crossing of the layer. */
+ * host_counts: (host) int32[E] that receives counts, or NULL: the one
+ * device->host crossing of the layer, a copy enqueued on `stream` after the
+ * routing kernels. With pinned (page-locked) host memory the call returns
+ * at once and host_counts is valid once the stream has passed this point
+ * (synchronise the stream or an event recorded after the call); with
+ * pageable memory the runtime finishes the copy, and so waits for the
+ * routing, before the call returns. The GPU path itself never needs the
+ * counts on the host: tiles are scheduled on the device from offsets. */
 moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt,
                        int32_t *host_counts, void *ws, size_t ws_bytes, void *stream,
                        const moe_trace_t *trace);

@@ -210,12 +210,12 @@ moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_r
         e = moe::launch_route_scatter(rt->topk_idx, base, pb->T, pb->E, pb->k, rt->sorted_slot, rt->slot_row, s);
     }
     if (e != hipSuccess) return MOE_E_HIP;
-    if (host_counts) {
-        if (hipMemcpyAsync(host_counts, rt->counts, (size_t)pb->E * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
-                hipSuccess ||
-            hipStreamSynchronize(s) != hipSuccess)
-            return MOE_E_HIP;
-    }
+    // the one device->host copy, in stream order (asynchronous for pinned
+    // host memory; the runtime completes a copy to pageable memory before
+    // returning)
+    if (host_counts && hipMemcpyAsync(host_counts, rt->counts, (size_t)pb->E * sizeof(int32_t),
+                                      hipMemcpyDeviceToHost, s) != hipSuccess)
+        return MOE_E_HIP;
     return MOE_OK;
 }
 

@@ -191,6 +191,11 @@ def test_host_counts_readback_and_determinism():
     L.bwd(router_grad=True)
     r1 = L.results(router_grad=True, intermediates=True)
     assert np.array_equal(hc, oracle.route(inputs["logits"], cfg.k)["counts"])
+    # pinned host memory: the copy is asynchronous, valid after a stream sync
+    hp = torch.zeros(cfg.E, dtype=torch.int32, pin_memory=True)
+    L.route(host_counts=hp)
+    torch.cuda.synchronize()
+    assert np.array_equal(hp.numpy(), hc)
     L.step(backward=True, router_grad=True)
     r2 = L.results(router_grad=True, intermediates=True)
     for n in r1:
