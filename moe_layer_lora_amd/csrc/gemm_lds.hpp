@@ -22,6 +22,8 @@
 // so each lane loads the global chunk that belongs at its LDS slot.
 #pragma once
 
+#include <utility>
+
 #include "gemm.hpp"
 
 namespace moe {
@@ -29,6 +31,8 @@ namespace lds {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int BM_, int BN_, int NSTAGE_, bool BN_CONTIG_, int BK_ = 32>
 struct Cfg {
@@ -46,13 +50,17 @@ struct Cfg {
     static constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;
     static constexpr int LOADS_PER_STEP = A_INSTR + B_INSTR;
     static constexpr int KROWS_PER_INSTR = 1024 / (BN * 2);  // N-contig k-rows per 1 KB
-    // The rank-r LoRA tiles always use 32-deep steps (LoraCfg). With 32-deep
-    // ring steps they go through ring slot 0; with 64-deep steps through a
-    // region of their own after the ring.
+    // The rank-r LoRA tiles always use 32-deep steps (LoraCfg) and go
+    // through one ring slot before the K loop.
     using LoraCfg = Cfg<BM_, BN_, NSTAGE_, BN_CONTIG_, 32>;
-    static constexpr bool LORA_SEPARATE = BK != 32;
-    static constexpr int RING_BYTES = NSTAGE * STAGE_BYTES;
-    static constexpr int SMEM_BYTES = RING_BYTES + (LORA_SEPARATE ? (BM + BN) * 32 * 2 : 0);
+    // 32-deep steps: a ring of NSTAGE whole stages (A and B of one step).
+    // 64-deep steps (SPLIT): a ring of NSTAGE operand slots, each holding the
+    // A tile or the B tile of one step (or the LoRA tile), so the B tiles can
+    // be loaded two steps ahead and the A tiles one step ahead.
+    static constexpr bool SPLIT = BK == 64;
+    static constexpr int SLOT_BYTES = SPLIT ? cmax(cmax(A_BYTES, B_BYTES), (BM + BN) * 32 * 2) : STAGE_BYTES;
+    static constexpr int SMEM_BYTES = NSTAGE * SLOT_BYTES;
+    static_assert(!SPLIT || NSTAGE == 5, "the split ring holds five operand slots");
     static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "whole loads per wave");
     static_assert(CPR == 4 || CPR == 8, "64- or 128-byte K-contig rows");
     static_assert(!B_NCONTIG || (BN * 2) % 1024 == 0 || 1024 % (BN * 2) == 0, "k-rows tile 1 KB loads");
@@ -95,11 +103,12 @@ struct KDirect {
         }
     }
 
-    // issue the INSTR loads of one step (k elements [k0, k0 + 8 CPR) of the
-    // segment, valid for k < K) into the stage region at `lds`
+    // issue loads [J0, J1) of the INSTR of one step (k elements [k0, k0 + 8 CPR)
+    // of the segment, valid for k < K) into the stage region at `lds`
+    template <int J0 = 0, int J1 = INSTR>
     __device__ __forceinline__ void issue(rsrc_t rs, uint32_t colbytes, int k0, int K, char *lds, int wave) const {
 #pragma unroll
-        for (int j = 0; j < INSTR; ++j) {
+        for (int j = J0; j < J1; ++j) {
             const int k = k0 + lchunk[j] * 8;
             const uint32_t vo = (off[j] != kInvalid && k < K) ? off[j] + colbytes + (uint32_t)k * 2 : kInvalid;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDS_PTR(lds + (wave * INSTR + j) * 1024), 16, vo, 0, 0, 0);
@@ -130,9 +139,10 @@ struct NDirect {
             nok[j] = ncol_off[j] >= c_lo && ncol_off[j] + 8 <= ncol;
         }
     }
+    template <int J0 = 0, int J1 = INSTR>
     __device__ __forceinline__ void issue(rsrc_t rs, uint32_t ldb, int k0, int K, char *lds, int wave) const {
 #pragma unroll
-        for (int j = 0; j < INSTR; ++j) {
+        for (int j = J0; j < J1; ++j) {
             const int k = k0 + krow[j];
             const uint32_t vo = (nok[j] && k < K) ? (uint32_t)k * ldb + (uint32_t)ncol_off[j] * 2 : kInvalid;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDS_PTR(lds + (wave * INSTR + j) * 1024), 16, vo, 0, 0, 0);
@@ -236,7 +246,7 @@ namespace moe {
 namespace lds {
 
 // Operands of one grouped-GEMM tile for the ring driver below. Up to two K
-// segments; step t < nt0 is segment 0 at k = 32 t, else segment 1.
+// segments; step t < nt0 is segment 0 at k = BK t, else segment 1.
 template <class C, bool NSPLIT = false>
 struct Operands {
     KDirect<C::BM, C::A_INSTR, C::CPR> a;
@@ -253,25 +263,32 @@ struct Operands {
     uint32_t ldb[2] = {0, 0};
     rsrc_t rb[2][2];
 
-    // Loads of step t into `stage`. Steps at or beyond nt load zeros (every
-    // offset out of range), so the steady loop can issue unconditionally.
-    __device__ __forceinline__ void issue(int t, char *stage, int wave) const {
+    // Loads of step t (A tile into `sa`, B tile into `sb`). Steps at or
+    // beyond nt load zeros (every offset out of range), so the steady loop can
+    // issue unconditionally. Operands are used as values (no runtime index
+    // into the arrays: that would put the descriptors in scratch).
+    template <int J0 = 0, int J1 = C::A_INSTR>
+    __device__ __forceinline__ void issue_a(int t, char *sa, int wave) const {
         const bool s1 = t >= nt0;
         const int k0 = (s1 ? t - nt0 : t) * C::BK;
         const int Ks = t < nt ? (s1 ? K[1] : K[0]) : 0;
-        // operands as values (no runtime index into the arrays: that would
-        // put the descriptors in scratch)
         const rsrc_t ra0 = ra[0], ra1 = ra[1];
+        const uint32_t ac0 = acol[0], ac1 = acol[1];
+        a.template issue<J0, J1>(s1 ? ra1 : ra0, s1 ? ac1 : ac0, k0, Ks, sa, wave);
+    }
+    template <int J0 = 0, int J1 = C::B_INSTR>
+    __device__ __forceinline__ void issue_b(int t, char *sb, int wave) const {
+        const bool s1 = t >= nt0;
+        const int k0 = (s1 ? t - nt0 : t) * C::BK;
+        const int Ks = t < nt ? (s1 ? K[1] : K[0]) : 0;
         const rsrc_t r00 = rb[0][0], r01 = rb[0][1], r10 = rb[1][0], r11 = rb[1][1];
-        const uint32_t ac0 = acol[0], ac1 = acol[1], lb0 = ldb[0], lb1 = ldb[1];
-        a.issue(s1 ? ra1 : ra0, s1 ? ac1 : ac0, k0, Ks, stage, wave);
-        char *sb = stage + C::A_BYTES;
+        const uint32_t lb0 = ldb[0], lb1 = ldb[1];
         if constexpr (C::B_NCONTIG) {
-            if (NSPLIT && s1) bn1.issue(r10, lb1, k0, Ks, sb, wave);
-            else bn.issue(s1 ? r10 : r00, s1 ? lb1 : lb0, k0, Ks, sb, wave);
+            if (NSPLIT && s1) bn1.template issue<J0, J1>(r10, lb1, k0, Ks, sb, wave);
+            else bn.template issue<J0, J1>(s1 ? r10 : r00, s1 ? lb1 : lb0, k0, Ks, sb, wave);
         } else {
 #pragma unroll
-            for (int j = 0; j < C::B_INSTR; ++j) {
+            for (int j = J0; j < J1; ++j) {
                 const bool sel = (bsel_mask >> j) & 1u;
                 const rsrc_t d = s1 ? (sel ? r11 : r10) : (sel ? r01 : r00);
                 const int k = k0 + bk.lchunk[j] * 8;
@@ -281,70 +298,114 @@ struct Operands {
             }
         }
     }
+    // both tiles of step t into one stage (A first, then B)
+    __device__ __forceinline__ void issue(int t, char *stage, int wave) const {
+        issue_a(t, stage, wave);
+        issue_b(t, stage + C::A_BYTES, wave);
+    }
 };
 
-// One steady iteration: the loads of step t_issue into `dst` and the MFMA
-// work of the step in `src`. The two stages are distinct ring slots, which
-// the restrict qualifiers state: the compiler then knows the LDS reads of
-// `src` cannot see the direct loads into `dst` and inserts no vmcnt drain
-// before them (the loop's own vmcnt waits order the stages).
+template <int N> struct KGroup { static constexpr int value = N; };
+
+// One 16-deep k group of a step out of its A tile `sa` and B tile `sb`,
+// skewed by one group: the LDS reads of group KG go under the MFMAs of the
+// group before it (the previous step's last group when KG = 0; zeros in the
+// first step). issue(KGroup<KG>) issues NL direct loads of a later step,
+// spread evenly over the group's MFMAs: a wave issues in order, so a burst
+// of loads the address and L1 path cannot take at once would hold back the
+// MFMAs behind it.
+template <class C, int KG, int NL, class Issue>
+__device__ __forceinline__ void kg_group(const Issue &issue, const char *sa, const char *sb, Frags<C> (&f)[2],
+                                         f32x16_t (&acc)[C::TM][C::TN]) {
+    constexpr int NMMA = C::TM * C::TN, NRD = C::TM + (C::B_NCONTIG ? 2 : 1) * C::TN;
+    static_assert(NL <= NMMA, "at most one load per MFMA");
+    constexpr int LSTEP = NL > 0 ? NMMA / NL : NMMA;
+    constexpr int HALF = NMMA > 1 ? NMMA / 2 : 1;
+    constexpr int RPM = (NRD + HALF - 1) / HALF;  // LDS reads per MFMA over the first half
+    issue(KGroup<KG>{});
+    read_frags<C>(sa, sb, KG, f[KG & 1]);
+    mma_frags<C>(f[(KG + 1) & 1], acc);
+#pragma unroll
+    for (int i = 0; i < NMMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, KG);                           // MFMA
+        if (NL > 0 && i % LSTEP == 0 && i / LSTEP < NL)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, KG);                       // direct load
+        if (i < HALF) __builtin_amdgcn_sched_group_barrier(0x100, RPM, KG);           // LDS reads
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The NKG k groups of a step; NLA loads per group in the first half of the
+// groups, NLB in the second.
+template <class C, int NLA, int NLB, class Issue, int... G>
+__device__ __forceinline__ void kg_groups(const Issue &issue, const char *sa, const char *sb, Frags<C> (&f)[2],
+                                          f32x16_t (&acc)[C::TM][C::TN], std::integer_sequence<int, G...>) {
+    static_assert(C::NKG % 2 == 0, "k groups alternate between two fragment sets");
+    (kg_group<C, G, (G < C::NKG / 2 ? NLA : NLB)>(issue, sa, sb, f, acc), ...);
+}
+
+// MFMA work of one step with the loads of later steps: the A tile's loads
+// in the first half of the k groups, the B tile's in the second.
+template <class C, class IssueA, class IssueB>
+__device__ __forceinline__ void kg_loop(const IssueA &issue_a, const IssueB &issue_b, const char *sa, const char *sb,
+                                        Frags<C> (&f)[2], f32x16_t (&acc)[C::TM][C::TN]) {
+    constexpr int H = C::NKG / 2;
+    static_assert(C::A_INSTR % H == 0 && C::B_INSTR % H == 0, "loads split evenly over the k groups");
+    auto issue = [&](auto g) {
+        constexpr int G = decltype(g)::value;
+        if constexpr (G < H) issue_a(KGroup<G * C::A_INSTR / H>{}, KGroup<(G + 1) * C::A_INSTR / H>{});
+        else issue_b(KGroup<(G - H) * C::B_INSTR / H>{}, KGroup<(G - H + 1) * C::B_INSTR / H>{});
+    };
+    kg_groups<C, C::A_INSTR / H, C::B_INSTR / H>(issue, sa, sb, f, acc, std::make_integer_sequence<int, C::NKG>{});
+}
+
+// One steady iteration of the whole-stage ring: the loads of step t_issue
+// into `dst` and the MFMA work of the step in `src`. The two stages are
+// distinct ring slots, which the restrict qualifiers state: the compiler
+// then knows the LDS reads of `src` cannot see the direct loads into `dst`
+// and inserts no vmcnt drain before them (the loop's own vmcnt waits order
+// the stages).
 template <class C, class Op>
 __device__ __forceinline__ void ring_iter(const Op &op, int t_issue, char *__restrict__ dst,
                                           const char *__restrict__ src, int wave, Frags<C> (&f)[2],
                                           f32x16_t (&acc)[C::TM][C::TN]) {
-    static_assert(C::NKG % 2 == 0, "k groups alternate between two fragment sets");
-    op.issue(t_issue, dst, wave);
-    constexpr int NMMA = C::TM * C::TN, NRD = C::TM + (C::B_NCONTIG ? 2 : 1) * C::TN;
-    constexpr int L = C::LOADS_PER_STEP;
-#pragma unroll
-    for (int kg = 0; kg < C::NKG; ++kg) {
-        // reads of group kg under the MFMAs of the group before it (the
-        // previous step's last group when kg = 0; zeros in the first step)
-        read_frags<C>(src, src + C::A_BYTES, kg, f[kg & 1]);
-        mma_frags<C>(f[(kg + 1) & 1], acc);
-        if (kg == 0) {
-#pragma unroll
-            for (int i = 0; i < L; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      // direct load
-                __builtin_amdgcn_sched_group_barrier(0x100, (NRD + L - 1) / L, 0);      // LDS read
-            }
-            if (NMMA > L) __builtin_amdgcn_sched_group_barrier(0x008, NMMA - L, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NMMA / 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x100, (NRD + NMMA / 2 - 1) / (NMMA / 2), 1);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, NMMA / 2, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    kg_loop<C>(
+        [&](auto j0, auto j1) { op.template issue_a<decltype(j0)::value, decltype(j1)::value>(t_issue, dst, wave); },
+        [&](auto j0, auto j1) {
+            op.template issue_b<decltype(j0)::value, decltype(j1)::value>(t_issue, dst + C::A_BYTES, wave);
+        },
+        src, src + C::A_BYTES, f, acc);
 }
 
-// Ring prologue: steps 0 .. NSTAGE-2 go to slots 1 .. NSTAGE-1 (`rest`)
-// while the rank-r LoRA tiles are staged through registers into slot 0
-// (`s0`) and multiplied. The restrict qualifiers state that the two regions
-// are disjoint, so the LoRA stores and reads need no wait on the ring loads.
-template <class C, class Op, class Lora>
-__device__ __forceinline__ void ring_prologue(const Op &op, int nlora, const Lora &lora, char *__restrict__ s0,
-                                              char *__restrict__ rest, int wave, f32x16_t (&acc)[C::TM][C::TN]) {
-    typename Lora::Regs lr;
-    if (nlora > 0) lora.load(0, lr);
-    // keep the LoRA loads ahead of the ring loads: loads complete in order,
-    // so waiting for the LoRA data must not also wait for the ring
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < C::NSTAGE - 1; ++t) op.issue(t, rest + t * C::STAGE_BYTES, wave);  // zeros past nt
+// One steady iteration of the operand-slot ring, at step t: the A tile of
+// step t + 1 into `da`, the B tile of step t + 2 into `db`, and the MFMA work
+// of step t out of `sa` / `sb`. Four distinct slots (restrict, as above).
+template <class C, class Op>
+__device__ __forceinline__ void split_iter(const Op &op, int t, char *__restrict__ da, char *__restrict__ db,
+                                           const char *__restrict__ sa, const char *__restrict__ sb, int wave,
+                                           Frags<C> (&f)[2], f32x16_t (&acc)[C::TM][C::TN]) {
+    kg_loop<C>([&](auto j0, auto j1) { op.template issue_a<decltype(j0)::value, decltype(j1)::value>(t + 1, da, wave); },
+               [&](auto j0, auto j1) { op.template issue_b<decltype(j0)::value, decltype(j1)::value>(t + 2, db, wave); },
+               sa, sb, f, acc);
+}
+
+// The rank-r LoRA tiles, staged through registers into `slot` and
+// multiplied, while the ring loads the prologue issued stay in flight. The
+// caller issued the first LoRA tile's global loads before the ring's: loads
+// complete in order, so waiting for the LoRA data does not wait for the ring.
+// `slot` is not a slot those ring loads write (restrict in the callers).
+template <class C, class Lora>
+__device__ __forceinline__ void lora_tiles(int nlora, const Lora &lora, typename Lora::Regs &lr, char *slot,
+                                           f32x16_t (&acc)[C::TM][C::TN]) {
     for (int lt = 0; lt < nlora; ++lt) {
         if (lt > 0) lora.load(lt, lr);
-        lora.store(lr, s0);
+        lora.store(lr, slot);
         // LDS writes done, then a bare barrier: the ring loads stay in flight
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        mma_step<typename C::LoraCfg>(s0, s0 + C::LoraCfg::A_BYTES, acc);
-        if (lt + 1 < nlora) {  // slot 0 is refilled by the next LoRA tile
+        mma_step<typename C::LoraCfg>(slot, slot + C::LoraCfg::A_BYTES, acc);
+        if (lt + 1 < nlora) {  // the slot is refilled by the next LoRA tile
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
@@ -352,10 +413,48 @@ __device__ __forceinline__ void ring_prologue(const Op &op, int nlora, const Lor
     }
 }
 
-// Ring driver: LoRA tiles first (stage 0, staged through registers by
-// lora.load / lora.store), then nt steady steps through stages 1.. in a
-// ring. The first LoRA tile's global loads are issued before the ring's, so
-// waiting for them leaves the ring loads in flight.
+// Whole-stage ring prologue: steps 0 .. NSTAGE-2 go to stages 1 .. NSTAGE-1
+// (`rest`) while the LoRA tiles go through stage 0 (`s0`).
+template <class C, class Op, class Lora>
+__device__ __forceinline__ void ring_prologue(const Op &op, int nlora, const Lora &lora, char *__restrict__ s0,
+                                              char *__restrict__ rest, int wave, f32x16_t (&acc)[C::TM][C::TN]) {
+    typename Lora::Regs lr;
+    if (nlora > 0) lora.load(0, lr);
+    __builtin_amdgcn_sched_barrier(0);  // LoRA loads ahead of the ring loads
+#pragma unroll
+    for (int t = 0; t < C::NSTAGE - 1; ++t) op.issue(t, rest + t * C::STAGE_BYTES, wave);  // zeros past nt
+    lora_tiles<C>(nlora, lora, lr, s0, acc);
+}
+
+// Operand-slot ring prologue: B of step 0, A of step 0 and B of step 1 into
+// slots 0, 1, 2 while the LoRA tiles go through slot 4.
+template <class C, class Op, class Lora>
+__device__ __forceinline__ void split_prologue(const Op &op, int nlora, const Lora &lora, char *__restrict__ s0,
+                                               char *__restrict__ s1, char *__restrict__ s2,
+                                               char *__restrict__ s4, int wave, f32x16_t (&acc)[C::TM][C::TN]) {
+    typename Lora::Regs lr;
+    if (nlora > 0) lora.load(0, lr);
+    __builtin_amdgcn_sched_barrier(0);  // LoRA loads ahead of the ring loads
+    op.issue_b(0, s0, wave);
+    op.issue_a(0, s1, wave);
+    op.issue_b(1, s2, wave);
+    lora_tiles<C>(nlora, lora, lr, s4, acc);
+}
+
+// Ring driver: the LoRA tiles first, then nt steady steps. Every iteration
+// issues one step of loads (zeros past the end), so the wait count is the
+// same in every iteration. After the barrier of step t the wave issues its
+// loads and the LDS reads of step t's k groups, each interleaved with the
+// MFMAs of the group before it (the previous step's last group first,
+// already in registers), so the MFMA pipe has work while the barrier
+// resolves and the reads are in flight.
+//  - Whole-stage ring (32-deep steps): step t in stage (t + 1) % NSTAGE, the
+//    LoRA tiles in stage 0; NSTAGE - 1 steps in flight.
+//  - Operand-slot ring (64-deep steps, five slots): half-tile h in slot
+//    h % 5, with h = 2 t the B tile and h = 2 t + 1 the A tile of step t; the
+//    LoRA tiles in slot 4 before its first ring use. Iteration t issues
+//    halves 2 t + 3 (A of t + 1) and 2 t + 4 (B of t + 2) into the slots of
+//    step t - 1, so B tiles have two steps to land and A tiles one.
 template <class C, class Op, class Lora>
 __device__ __forceinline__ void run(const Op &op, int nlora, const Lora &lora, char *smem,
                                     f32x16_t (&acc)[C::TM][C::TN]) {
@@ -366,34 +465,41 @@ __device__ __forceinline__ void run(const Op &op, int nlora, const Lora &lora, c
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    // 32-deep steps: LoRA in slot 0, step t in slot (t + 1) % NSTAGE;
-    // 64-deep steps: step t in slot t % NSTAGE, LoRA in its own region
-    constexpr int SHIFT = C::LORA_SEPARATE ? 0 : 1;
-    auto stage_of = [&](int t) { return smem + ((t + SHIFT) % C::NSTAGE) * C::STAGE_BYTES; };
-    char *lora_slot = C::LORA_SEPARATE ? smem + C::RING_BYTES : smem;
-    ring_prologue<C>(op, nlora, lora, lora_slot, stage_of(0), wave, acc);
-    // Steady loop, skewed by one k group: after the barrier of step t the
-    // wave issues the loads of step t + NSTAGE - 1 and the LDS reads of step
-    // t's k groups, each interleaved with the MFMAs of the group before it
-    // (the previous step's last group first, already in registers), so the
-    // MFMA pipe has work while the barrier resolves and the reads are in
-    // flight. Every iteration issues one step of loads (zeros past the end),
-    // so the wait count is the same in every iteration.
     Frags<C> f[2];
+    if constexpr (C::SPLIT) {
+        auto slot = [&](int h) { return smem + (h % C::NSTAGE) * C::SLOT_BYTES; };
+        split_prologue<C>(op, nlora, lora, slot(0), slot(1), slot(2), slot(4), wave, acc);
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) f[1].a[i] = chunk_t{0u, 0u, 0u, 0u};
+        for (int i = 0; i < C::TM; ++i) f[1].a[i] = chunk_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < C::TN; ++i) f[1].b[i] = chunk_t{0u, 0u, 0u, 0u};
-    for (int t = 0; t < op.nt; ++t) {
-        wait_vm<(C::NSTAGE - 2) * C::LOADS_PER_STEP>();
-        // Every LDS read of step t-1 has completed (lgkmcnt) before the bare
-        // barrier, so after it step t-1's stage can be refilled. A full
-        // __syncthreads() would add a release fence, i.e. a vmcnt(0) drain of
-        // the steps still in flight. The asm keeps LDS accesses in place.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        ring_iter<C>(op, t + C::NSTAGE - 1, stage_of(t + C::NSTAGE - 1), stage_of(t), wave, f, acc);
+        for (int i = 0; i < C::TN; ++i) f[1].b[i] = chunk_t{0u, 0u, 0u, 0u};
+        for (int t = 0; t < op.nt; ++t) {
+            // halves up to 2 t + 1 have landed; half 2 t + 2 (a B tile) may be in flight
+            wait_vm<C::B_INSTR>();
+            // Every LDS read of step t-1 has completed (lgkmcnt) before the
+            // bare barrier, so after it that step's slots can be refilled. A
+            // full __syncthreads() would add a release fence, i.e. a vmcnt(0)
+            // drain of the loads still in flight. The asm keeps LDS accesses
+            // in place.
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            split_iter<C>(op, t, slot(2 * t + 3), slot(2 * t + 4), slot(2 * t + 1), slot(2 * t), wave, f, acc);
+        }
+    } else {
+        auto stage_of = [&](int t) { return smem + ((t + 1) % C::NSTAGE) * C::STAGE_BYTES; };
+        ring_prologue<C>(op, nlora, lora, smem, stage_of(0), wave, acc);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) f[1].a[i] = chunk_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < C::TN; ++i) f[1].b[i] = chunk_t{0u, 0u, 0u, 0u};
+        for (int t = 0; t < op.nt; ++t) {
+            wait_vm<(C::NSTAGE - 2) * C::LOADS_PER_STEP>();
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // as above
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            ring_iter<C>(op, t + C::NSTAGE - 1, stage_of(t + C::NSTAGE - 1), stage_of(t), wave, f, acc);
+        }
     }
     if (op.nt > 0) mma_frags<C>(f[1], acc);
     // the zero loads of the last iterations land in the ring: drain them

@@ -340,11 +340,12 @@ __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup_
 // ===========================================================================
 // Forward (both operands K-contiguous): 64-deep steps, so every row segment
 // a load touches is a whole 128-byte line (about twice the L2-to-LDS rate of
-// 64-byte segments), in two 64 KB stages. Backward (B N-contiguous, read with
-// transposing LDS reads): 32-deep steps in four 32 KB stages measured faster.
-using LdsNT = lds::Cfg<256, 256, 2, false, 64>;
+// 64-byte segments), through five 32 KB operand slots (B tiles two steps
+// ahead, A tiles one). Backward (B N-contiguous, read with transposing LDS
+// reads): 32-deep steps in four 32 KB stages measured faster.
+using LdsNT = lds::Cfg<256, 256, 5, false, 64>;
 using LdsNN = lds::Cfg<256, 256, 4, true, 32>;
-using LdsNTh = lds::Cfg<128, 256, 2, false, 64>;  // 128-row tail tiles
+using LdsNTh = lds::Cfg<128, 256, 5, false, 64>;  // 128-row tail tiles
 using LdsNNh = lds::Cfg<128, 256, 4, true, 32>;
 
 template <class C> union LdsSmem {  // the tile scheduler's table is dead once the ring starts
