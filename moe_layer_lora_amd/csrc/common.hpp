@@ -81,8 +81,11 @@ template <> __device__ __forceinline__ void unpack<bf16_t>(const chunk_t &c, flo
 __device__ __forceinline__ int acc_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// Logistic function from the hardware exp and reciprocal (about 1 ulp each)
+// instead of an IEEE-exact division: for epilogues whose results are stored
+// as bf16 (8 mantissa bits), where the exact division's ~10 VALU
+// instructions per element would dominate the tile's epilogue.
+__device__ __forceinline__ float sigmoid_fast(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // ---------------------------------------------------------------------------
 // Grouped-tile scheduler. Expert e owns rows offsets[e] .. offsets[e+1]-1,

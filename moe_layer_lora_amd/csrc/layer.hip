@@ -436,7 +436,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
                 if (m < tl.rows && f < p.F) {
                     float h[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) h[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
+                    for (int e = 0; e < 8; ++e) h[e] = g[e] * sigmoid_fast(g[e]) * u[e];
                     const size_t o = (size_t)(tl.row0 + m) * p.F + f;
                     if (G) *reinterpret_cast<chunk_t *>(G + o) = Elem<bf16_t>::pack(g);
                     if (U) *reinterpret_cast<chunk_t *>(U + o) = Elem<bf16_t>::pack(u);
@@ -591,7 +591,7 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
 #pragma unroll
                 for (int h = 0; h < 8; ++h) {
                     const float dh = w * v[h];
-                    const float sg = 1.0f / (1.0f + __expf(-g[h]));
+                    const float sg = sigmoid_fast(g[h]);
                     dg[h] = dh * u[h] * sg * (1.0f + g[h] * (1.0f - sg));
                     du[h] = dh * g[h] * sg;
                 }
