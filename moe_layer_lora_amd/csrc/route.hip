@@ -32,10 +32,29 @@ int route_tokens_per_block(int T, int E) {
     return tpb;
 }
 
-// (v, id) ordering of the router: larger logit first, ties to the lower id.
-// Float comparison makes -0.0 equal to +0.0.
-__device__ __forceinline__ bool route_better(float ov, int oid, float bv, int bid) {
-    return oid != INT_MAX && (bid == INT_MAX || ov > bv || (ov == bv && oid < bid));
+// The router's order: larger logit first, ties to the lower id. Logits are
+// compared through an order-preserving 32-bit key: larger logit, larger key.
+// -0.0 is first made +0.0 (the two compare equal, so the lower id must win);
+// 0 is below every finite logit's key and marks taken or absent entries.
+__device__ __forceinline__ uint32_t route_key(float v) {
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float route_key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Maximum over the wave by DPP: row_shr 1, 2, 4, 8 leave each row's maximum
+// in its lane 15, row_bcast 15 and 31 carry it to lane 63. Out-of-range
+// sources read 0, the smallest key.
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));  // row_shr:1
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));  // row_shr:2
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));  // row_shr:4
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));  // row_shr:8
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false)); // row_bcast:15
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false)); // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // NPL: logits per lane (E <= 64 NPL); KS: result slots per lane (k <= 64 KS)
@@ -53,37 +72,32 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float *__res
     const int t0 = b * tpb, t1 = min(T, t0 + tpb);
     for (int t = t0 + wave; t < t1; t += kRouteWaves) {
         const float *row = logits + (size_t)t * E;
-        float v[NPL];
-        uint32_t avail = 0;
+        // entry i of this lane is expert lane + 64 i: ids rise with i
+        uint32_t key[NPL];
 #pragma unroll
         for (int i = 0; i < NPL; ++i) {
             const int e = lane + kWave * i;
-            v[i] = e < E ? row[e] : 0.0f;
-            if (e < E) avail |= 1u << i;
+            key[i] = e < E ? route_key(row[e]) : 0u;
         }
         int my_idx[KS];
         float my_val[KS];
         float v0 = 0.0f;
         for (int j = 0; j < k; ++j) {
-            float bv = 0.0f;
-            int bid = INT_MAX;
+            // the best key left, then the lowest id holding it (ballots in id order)
+            uint32_t m = key[0];
 #pragma unroll
-            for (int i = 0; i < NPL; ++i)  // ids rise with i: a tie keeps the lower id
-                if (((avail >> i) & 1u) && (bid == INT_MAX || v[i] > bv)) {
-                    bv = v[i];
-                    bid = lane + kWave * i;
-                }
+            for (int i = 1; i < NPL; ++i) m = max(m, key[i]);
+            m = wave_max_key(m);
+            int bid = -1;
 #pragma unroll
-            for (int off = kWave / 2; off > 0; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, kWave);
-                const int oid = __shfl_xor(bid, off, kWave);
-                if (route_better(ov, oid, bv, bid)) {
-                    bv = ov;
-                    bid = oid;
-                }
+            for (int i = 0; i < NPL; ++i) {
+                const uint64_t hit = __ballot(key[i] == m);
+                if (bid < 0 && hit != 0) bid = __builtin_ctzll(hit) + kWave * i;
             }
-            // every lane now holds the winner
-            if ((bid & (kWave - 1)) == lane) avail &= ~(1u << (bid / kWave));
+            const float bv = route_key_value(m);
+#pragma unroll
+            for (int i = 0; i < NPL; ++i)
+                if (bid == lane + kWave * i) key[i] = 0u;  // taken
             if (j == 0) v0 = bv;
 #pragma unroll
             for (int s = 0; s < KS; ++s)

@@ -127,6 +127,14 @@ def edge_case(name):
         return cfg, lambda l: l.__setitem__((slice(0, 2050), 0), 50.0)
     if name == "many_choices":  # k > 64: two result slots per lane in the top-k kernel
         return LayerConfig(name, T=12, E=96, k=72, **base), None
+    if name == "signed_zero_ties":  # -0.0 and +0.0 compare equal: the lower id wins
+        cfg = LayerConfig(name, T=64, E=8, k=3, **base)
+
+        def mutate(l):
+            rng = np.random.default_rng(5)
+            l[:] = np.where(rng.random(l.shape) < 0.5, np.float32(-0.0), np.float32(0.0))
+            l[rng.random(l.shape) < 0.15] = 1.0
+        return cfg, mutate
     if name == "fp32_ties":
         cfg = LayerConfig(name, T=64, E=6, k=2, d=32, F=40, r=8, dtype="f32", alpha=16.0,
                           router_grad=True)
@@ -135,7 +143,7 @@ def edge_case(name):
 
 
 EDGE = ["one_token", "k_equals_E", "single_expert", "all_to_one_expert", "integer_ties",
-        "multi_chunk_expert", "many_choices", "fp32_ties"]
+        "signed_zero_ties", "multi_chunk_expert", "many_choices", "fp32_ties"]
 
 
 @pytest.mark.parametrize("name", EDGE)
