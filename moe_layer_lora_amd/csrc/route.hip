@@ -21,13 +21,13 @@
 
 namespace moe {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 1024;  // 16 waves: 4 tokens per wave, a 4x smaller block histogram to scan
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / kWave;  // 16 logits per lane
 
 int route_tokens_per_block(int T, int E) {
-    int tpb = 16;  // 4 tokens per wave: enough waves to fill the chip at a few thousand tokens
+    int tpb = 64;  // 4 tokens per wave: enough waves to fill the chip at a few thousand tokens
     while ((long long)E * ((T + tpb - 1) / tpb) > 65536) tpb *= 2;
     return tpb;
 }
