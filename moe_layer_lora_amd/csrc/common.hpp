@@ -157,6 +157,15 @@ __device__ bool schedule_tile(const int *__restrict__ offsets, int E, int NT, in
     tile.row0 = offsets[e] + tile.mt * BM;
     tile.rows = min(BM, offsets[e + 1] - tile.row0);
     tile.gmt = s_start[e] + tile.mt;
+    // the same in every lane; say so, so that buffer descriptors built from
+    // them stay in scalar registers (else the compiler wraps every load
+    // using them in a loop over lanes)
+    tile.e = __builtin_amdgcn_readfirstlane(tile.e);
+    tile.nt = __builtin_amdgcn_readfirstlane(tile.nt);
+    tile.mt = __builtin_amdgcn_readfirstlane(tile.mt);
+    tile.row0 = __builtin_amdgcn_readfirstlane(tile.row0);
+    tile.rows = __builtin_amdgcn_readfirstlane(tile.rows);
+    tile.gmt = __builtin_amdgcn_readfirstlane(tile.gmt);
     return true;
 }
 

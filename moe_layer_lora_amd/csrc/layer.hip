@@ -338,15 +338,18 @@ __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup_
 // bf16 versions of the four grouped GEMMs on the direct-to-LDS ring engine
 // (gemm_lds.hpp). Same math and epilogues as the kernels above.
 // ===========================================================================
-// Forward (both operands K-contiguous): 64-deep steps, so every row segment
-// a load touches is a whole 128-byte line (about twice the L2-to-LDS rate of
-// 64-byte segments), through five 32 KB operand slots (B tiles two steps
-// ahead, A tiles one). Backward (B N-contiguous, read with transposing LDS
-// reads): 32-deep steps in four 32 KB stages measured faster.
+// Forward (both operands K-contiguous) and gate/up backward: 64-deep steps,
+// so every K-contiguous row segment a load touches is a whole 128-byte line
+// (about twice the L2-to-LDS rate of 64-byte segments), through five 32 KB
+// operand slots (B tiles two steps ahead, A tiles one). Down backward (B
+// N-contiguous, read with transposing LDS reads, as in gate/up backward):
+// 32-deep steps in four 32 KB stages measured faster there.
 using LdsNT = lds::Cfg<256, 256, 5, false, 64>;
 using LdsNN = lds::Cfg<256, 256, 4, true, 32>;
+using LdsNN64 = lds::Cfg<256, 256, 5, true, 64>;
 using LdsNTh = lds::Cfg<128, 256, 5, false, 64>;  // 128-row tail tiles
 using LdsNNh = lds::Cfg<128, 256, 4, true, 32>;
+using LdsNN64h = lds::Cfg<128, 256, 5, true, 64>;
 
 template <class C> union LdsSmem {  // the tile scheduler's table is dead once the ring starts
     __align__(16) char ring[C::SMEM_BYTES];
@@ -1577,7 +1580,7 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
             TraceScope ts(tr, K_GATEUP_BWD, st);
             GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.S(), D.E, D.d, D.F, D.r, D.s};
             if constexpr (std::is_same<T, bf16_t>::value)
-                MOE_LAUNCH((k_gateup_bwd_lds<LdsNN, LdsNNh>), grid_for<Cfg>(D, LdsNN::BM, cdiv(D.d, LdsNN::BN)), 256, gp);
+                MOE_LAUNCH((k_gateup_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.d, LdsNN64::BN)), 256, gp);
             else
                 MOE_LAUNCH(k_gateup_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, gp);
         }
