@@ -67,10 +67,17 @@ SavedLayout saved_layout(const moe_problem_t *pb, int keep) {
 }
 
 // forward workspace: what the forward needs that is not kept in `saved`
-struct FwdWs { size_t H, Zgu, Zd, Y, total; };
+struct FwdWs { size_t H, Zgu, Zd, Y, tiles, total; };
+
+// bf16: the grouped GEMMs' row-tile table
+size_t tile_table_bytes(const moe_problem_t *pb) {
+    if (pb->dtype != MOE_BF16) return 0;
+    return al((1 + (size_t)moe::max_row_tiles(pb->T * pb->k, pb->E, moe::kRowTile)) * 16);
+}
+
 FwdWs fwd_ws(const moe_problem_t *pb, int training, int keep) {
     const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
-    FwdWs w{0, 0, 0, 0, 0};
+    FwdWs w{0, 0, 0, 0, 0, 0};
     size_t o = 0;
     if (!training) {
         w.H = o; o += al(S * pb->F * es);
@@ -78,11 +85,12 @@ FwdWs fwd_ws(const moe_problem_t *pb, int training, int keep) {
         w.Zd = o; o += al(S * pb->r * sizeof(float));
     }
     if (!training || !keep) { w.Y = o; o += al(S * pb->d * es); }
+    w.tiles = o; o += tile_table_bytes(pb);
     w.total = o;
     return w;
 }
 
-struct BwdWs { size_t Pd, Pgu, wPdT, PguT, w_row, dGU, dXp, partial, total; };
+struct BwdWs { size_t Pd, Pgu, wPdT, PguT, w_row, dGU, dXp, partial, tiles, total; };
 BwdWs bwd_ws(const moe_problem_t *pb) {
     const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
     const bool bf = pb->dtype == MOE_BF16;
@@ -97,6 +105,7 @@ BwdWs bwd_ws(const moe_problem_t *pb) {
     w.dGU = o; o += al(S * 2 * pb->F * es);
     w.dXp = o; o += al(S * pb->d * es);
     w.partial = o; o += al(moe::lora_grad_partial_bytes(dims_of(pb)));
+    w.tiles = o; o += tile_table_bytes(pb);
     w.total = o;
     return w;
 }
@@ -250,6 +259,7 @@ moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t
         b.Y = at(ws, fw.Y);
     }
     b.out = out;
+    b.tiles = pb->dtype == MOE_BF16 ? reinterpret_cast<int32_t *>(at(ws, fw.tiles)) : nullptr;
     const moe::Trace tr = to_trace(trace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Dims D = dims_of(pb);
@@ -296,6 +306,7 @@ moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout, c
     b.da_g = grads->da_gate; b.db_g = grads->db_gate; b.da_u = grads->da_up; b.db_u = grads->db_up;
     b.da_d = grads->da_down; b.db_d = grads->db_down;
     b.d_topk_w = d_topk_w; b.d_logits = d_logits;
+    b.tiles = pb->dtype == MOE_BF16 ? reinterpret_cast<int32_t *>(at(ws, bw.tiles)) : nullptr;
     const moe::Trace tr = to_trace(trace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Dims D = dims_of(pb);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace moe {
 
 typedef uint16_t bf16_t;  // bf16 bit pattern in memory
@@ -105,12 +107,11 @@ struct Tile {
     int gmt;    // row tile index over all experts (expert-major)
 };
 
-// s_start: __shared__ int[E+1] scratch. Returns false if block b has no work.
+// Per-expert row-tile counts ceil(n_e / BM) and their inclusive scan into
+// s_start[0..E] (__shared__ int[E+1], E <= 1024); ends with a barrier.
 template <int BM, int NTHREADS>
-__device__ bool schedule_tile(const int *__restrict__ offsets, int E, int NT, int b, int *s_start,
-                              Tile &tile) {
+__device__ void scan_row_tiles(const int *__restrict__ offsets, int E, int *s_start) {
     const int tid = threadIdx.x;
-    // per-expert row-tile counts, then an inclusive scan (E <= 1024)
     for (int e = tid; e < E; e += NTHREADS) {
         const int n = offsets[e + 1] - offsets[e];
         s_start[e + 1] = (n + BM - 1) / BM;
@@ -136,12 +137,23 @@ __device__ bool schedule_tile(const int *__restrict__ offsets, int E, int NT, in
         }
     }
     __syncthreads();
-    const int total = s_start[E] * NT;
-    if (b >= total) return false;
-    // XCD-contiguous remap of block ids (a bijection on [0, total))
+}
+
+// XCD-contiguous remap of block ids (a bijection on [0, total))
+__device__ __forceinline__ int xcd_item(int b, int total) {
     const int xcd = b & 7, local = b >> 3;
     const int q = total >> 3, rem = total & 7;
-    const int lam = xcd * q + min(xcd, rem) + local;
+    return xcd * q + min(xcd, rem) + local;
+}
+
+// s_start: __shared__ int[E+1] scratch. Returns false if block b has no work.
+template <int BM, int NTHREADS>
+__device__ bool schedule_tile(const int *__restrict__ offsets, int E, int NT, int b, int *s_start,
+                              Tile &tile) {
+    scan_row_tiles<BM, NTHREADS>(offsets, E, s_start);
+    const int total = s_start[E] * NT;
+    if (b >= total) return false;
+    const int lam = xcd_item(b, total);
     // find expert: largest e with s_start[e] * NT <= lam
     int lo = 0, hi = E;  // invariant: s_start[lo]*NT <= lam < s_start[hi]*NT
     while (hi - lo > 1) {
@@ -169,8 +181,47 @@ __device__ bool schedule_tile(const int *__restrict__ offsets, int E, int NT, in
     return true;
 }
 
-// Upper bound on the number of row tiles over all experts (a launch size
-// chosen before the counts are known on the host).
-__host__ __device__ inline int max_row_tiles(int S, int E, int BM) { return (S + BM - 1) / BM + E; }
+// ---------------------------------------------------------------------------
+// Row-tile table of the grouped GEMMs (kRowTile-row tiles), int4 entries:
+// entry 0 = {number of row tiles, 0, 0, 0}; entry 1 + g, g a row tile over
+// all experts in expert order, = {its expert e, e's first row tile, e's
+// first row, e's row count}; capacity 1 + max_row_tiles(S, E, kRowTile).
+// Built once per pass by block 0 of the pass's first kernel, so that each
+// GEMM block finds its work item with two table loads instead of rescanning
+// the counts.
+template <int NTHREADS>
+__device__ void build_row_tiles(const int *__restrict__ offsets, int E, int *s_start, int32_t *table) {
+    scan_row_tiles<kRowTile, NTHREADS>(offsets, E, s_start);
+    int4 *t4 = reinterpret_cast<int4 *>(table);
+    for (int e = threadIdx.x; e < E; e += NTHREADS) {
+        const int o = offsets[e], n = offsets[e + 1] - o;
+        for (int g = s_start[e]; g < s_start[e + 1]; ++g) t4[1 + g] = make_int4(e, s_start[e], o, n);
+    }
+    if (threadIdx.x == 0) t4[0] = make_int4(s_start[E], 0, 0, 0);
+    __syncthreads();  // s_start is reused by the caller
+}
+
+// The work item of block b, ordered as schedule_tile<kRowTile> orders them,
+// from the table. Expert e owns items [s*NT, (s+mte)*NT), s its first row
+// tile, so the item lam belongs to the expert of row tile lam / NT.
+__device__ __forceinline__ bool table_tile(const int32_t *__restrict__ table, int NT, int b, Tile &tile) {
+    const int total = __builtin_amdgcn_readfirstlane(table[0]) * NT;
+    if (b >= total) return false;
+    const int lam = xcd_item(b, total);
+    const int4 te = reinterpret_cast<const int4 *>(table)[1 + lam / NT];
+    const int e = __builtin_amdgcn_readfirstlane(te.x);
+    const int s = __builtin_amdgcn_readfirstlane(te.y);
+    const int off = __builtin_amdgcn_readfirstlane(te.z);
+    const int n = __builtin_amdgcn_readfirstlane(te.w);
+    const int mte = (n + kRowTile - 1) / kRowTile;
+    const int rem2 = lam - s * NT;
+    tile.e = e;
+    tile.nt = rem2 / mte;
+    tile.mt = rem2 - tile.nt * mte;
+    tile.row0 = off + tile.mt * kRowTile;
+    tile.rows = min(kRowTile, n - tile.mt * kRowTile);
+    tile.gmt = s + tile.mt;
+    return true;
+}
 
 }  // namespace moe

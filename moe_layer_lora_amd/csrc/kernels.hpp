@@ -7,6 +7,14 @@
 
 namespace moe {
 
+// Rows per tile of the bf16 grouped GEMMs; their row-tile table lives in the
+// forward and backward workspaces.
+constexpr int kRowTile = 256;
+
+// Upper bound on the number of row tiles over all experts (a launch size
+// chosen before the counts are known on the host).
+__host__ __device__ inline int max_row_tiles(int S, int E, int BM) { return (S + BM - 1) / BM + E; }
+
 typedef uint16_t bf16_t;  // bf16 bit pattern in memory
 
 struct Dims {
@@ -40,6 +48,7 @@ struct FwdBufs {
     void *ZguT, *wZdT;    // bf16 training only: [2r,S] Zgu^T, [r,S] (w Zd)^T; else null
     void *Y;              // [S,d]
     void *out;            // [T,d]
+    int32_t *tiles;       // workspace: row-tile table of the grouped GEMMs
 };
 
 struct BwdBufs {
@@ -58,6 +67,7 @@ struct BwdBufs {
     void *dx;
     float *da_g, *db_g, *da_u, *db_u, *da_d, *db_d;
     float *d_topk_w, *d_logits;  // optional
+    int32_t *tiles;              // workspace: row-tile table of the grouped GEMMs
 };
 
 // per-kernel timing events (hipEvent_t or null), indexed like MOE_K_*

@@ -56,6 +56,7 @@ struct GateUpP {
     void *G, *U, *H;
     int T, E, k, d, F, r;
     float s;
+    const int32_t *tiles;  // bf16 path: row-tile table (build_row_tiles)
 };
 
 template <class Cfg>
@@ -145,6 +146,7 @@ struct DownP {
     void *Y;
     int S, E, d, F, r;
     float s;
+    const int32_t *tiles;  // bf16 path: row-tile table (build_row_tiles)
 };
 
 template <class Cfg>
@@ -208,6 +210,7 @@ struct DownBwdP {
     int T, E, k, d, F, r;
     float s;
     const float *w_row;  // bf16 path: combine weight of each row p (topk_w[sorted_slot[p]])
+    const int32_t *tiles;  // bf16 path: row-tile table (build_row_tiles)
 };
 
 template <class Cfg>
@@ -284,6 +287,7 @@ struct GateUpBwdP {
     void *dXp;
     int S, E, d, F, r;
     float s;
+    const int32_t *tiles;  // bf16 path: row-tile table (build_row_tiles)
 };
 
 template <class Cfg>
@@ -455,9 +459,9 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
 template <class C, class CH>
 __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUpP p) {
     __shared__ LdsSmem<C> sm;
+    static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
-    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, C::BN / 2), blockIdx.x, sm.start, tl)) return;
-    __syncthreads();  // every thread has read the scheduler table
+    if (!table_tile(p.tiles, cdiv(p.F, C::BN / 2), blockIdx.x, tl)) return;
     if (tl.rows > CH::BM) gateup_tile<C>(p, tl, sm.ring);
     else gateup_tile<CH>(p, tl, sm.ring);
 }
@@ -509,9 +513,9 @@ __device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *
 template <class C, class CH>
 __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_lds(DownP p) {
     __shared__ LdsSmem<C> sm;
+    static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
-    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
-    __syncthreads();  // every thread has read the scheduler table
+    if (!table_tile(p.tiles, cdiv(p.d, C::BN), blockIdx.x, tl)) return;
     if (tl.rows > CH::BM) down_tile<C>(p, tl, sm.ring);
     else down_tile<CH>(p, tl, sm.ring);
 }
@@ -611,9 +615,9 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
 template <class C, class CH>
 __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(DownBwdP p) {
     __shared__ LdsSmem<C> sm;
+    static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
-    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.F, C::BN), blockIdx.x, sm.start, tl)) return;
-    __syncthreads();  // every thread has read the scheduler table
+    if (!table_tile(p.tiles, cdiv(p.F, C::BN), blockIdx.x, tl)) return;
     if (tl.rows > CH::BM) down_bwd_tile<C>(p, tl, sm.ring);
     else down_bwd_tile<CH>(p, tl, sm.ring);
 }
@@ -661,9 +665,9 @@ __device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile 
 template <class C, class CH>
 __global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd_lds(GateUpBwdP p) {
     __shared__ LdsSmem<C> sm;
+    static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
-    if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(p.d, C::BN), blockIdx.x, sm.start, tl)) return;
-    __syncthreads();  // every thread has read the scheduler table
+    if (!table_tile(p.tiles, cdiv(p.d, C::BN), blockIdx.x, tl)) return;
     if (tl.rows > CH::BM) gateup_bwd_tile<C>(p, tl, sm.ring);
     else gateup_bwd_tile<CH>(p, tl, sm.ring);
 }
@@ -690,6 +694,7 @@ struct ProjP {
     const float *wt;
     int ldT, S;
     float *w_row_out;  // optional: wt[sorted_slot[p]] for every row p (written by the first column tile)
+    int32_t *tiles_out;  // optional: block 0 builds the grouped GEMMs' row-tile table here
 };
 
 template <class Cfg, int KIND>
@@ -701,6 +706,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_proj(ProjP p) {
     const int nr = (KIND == PROJ_GU || KIND == PROJ_DGU) ? 2 * p.r : p.r;
     const int K = (KIND == PROJ_GU || KIND == PROJ_DOUT) ? p.d : (KIND == PROJ_D ? p.F : 2 * p.F);
     Tile tl;
+    if (p.tiles_out && blockIdx.x == 0) build_row_tiles<Cfg::NTHREADS>(p.offsets, p.E, sm.start, p.tiles_out);
     if (!schedule_tile<Cfg::BM, Cfg::NTHREADS>(p.offsets, p.E, cdiv(nr, Cfg::BN), blockIdx.x, sm.start, tl)) return;
     const int n_base = tl.nt * Cfg::BN;
     const int nk = cdiv(K, Cfg::BK);
@@ -786,6 +792,7 @@ __global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
     constexpr bool GATHER = KIND == PROJ_GU || KIND == PROJ_DOUT;
     const int nr = (KIND == PROJ_GU || KIND == PROJ_DGU) ? 2 * p.r : p.r;
     Tile tl;
+    if (p.tiles_out && blockIdx.x == 0) build_row_tiles<256>(p.offsets, p.E, sm.start, p.tiles_out);
     if (!schedule_tile<C::BM, 256>(p.offsets, p.E, cdiv(nr, C::BN), blockIdx.x, sm.start, tl)) return;
     __syncthreads();  // every thread has read the scheduler table
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1465,13 +1472,14 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
         TraceScope ts(tr, K_PROJ_GU, st);
         ProjP pp{b.x, b.ag, b.au, b.sorted_slot, b.offsets, b.Zgu, D.E, D.k, D.d, D.F, D.r,
                  static_cast<bf16_t *>(b.ZguT), nullptr, lgrad_ldT(D), D.S()};
+        pp.tiles_out = b.tiles;
         hipError_t e = launch_proj<T, PROJ_GU>(D, pp, st);
         if (e != hipSuccess) return e;
     }
     {
         TraceScope ts(tr, K_GATEUP, st);
         GateUpP gp{b.x, b.wg, b.wu, b.bg, b.bu, b.Zgu, b.sorted_slot, b.offsets, b.G, b.U, b.H,
-                   D.T, D.E, D.k, D.d, D.F, D.r, D.s};
+                   D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.tiles};
         if constexpr (std::is_same<T, bf16_t>::value)
             MOE_LAUNCH((k_gateup_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.F, LdsNT::BN / 2)), 256, gp);
         else
@@ -1486,7 +1494,7 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
     }
     {
         TraceScope ts(tr, K_DOWN, st);
-        DownP dp{b.H, b.wd, b.bd, b.Zd, b.offsets, b.Y, D.S(), D.E, D.d, D.F, D.r, D.s};
+        DownP dp{b.H, b.wd, b.bd, b.Zd, b.offsets, b.Y, D.S(), D.E, D.d, D.F, D.r, D.s, b.tiles};
         if constexpr (std::is_same<T, bf16_t>::value)
             MOE_LAUNCH((k_down_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)), 256, dp);
         else
@@ -1556,14 +1564,14 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         {
             TraceScope ts(tr, K_PROJ_DOUT, st);
             ProjP pp{b.dout, b.bd, nullptr, b.sorted_slot, b.offsets, b.Pd, D.E, D.k, D.d, D.F, D.r,
-                     static_cast<bf16_t *>(b.wPdT), b.topk_w, lgrad_ldT(D), D.S(), b.w_row};
+                     static_cast<bf16_t *>(b.wPdT), b.topk_w, lgrad_ldT(D), D.S(), b.w_row, b.tiles};
             hipError_t e = launch_proj<T, PROJ_DOUT>(D, pp, st);
             if (e != hipSuccess) return e;
         }
         {
             TraceScope ts(tr, K_DOWN_BWD, st);
             DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
-                        D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row};
+                        D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row, b.tiles};
             if constexpr (std::is_same<T, bf16_t>::value)
                 MOE_LAUNCH((k_down_bwd_lds<LdsNN, LdsNNh>), grid_for<Cfg>(D, LdsNN::BM, cdiv(D.F, LdsNN::BN)), 256, dp);
             else
@@ -1578,7 +1586,8 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         }
         {
             TraceScope ts(tr, K_GATEUP_BWD, st);
-            GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.S(), D.E, D.d, D.F, D.r, D.s};
+            GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.S(), D.E, D.d, D.F, D.r, D.s,
+                          b.tiles};
             if constexpr (std::is_same<T, bf16_t>::value)
                 MOE_LAUNCH((k_gateup_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.d, LdsNN64::BN)), 256, gp);
             else

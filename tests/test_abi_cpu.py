@@ -65,12 +65,14 @@ def test_saved_and_workspace_sizes():
             + al(2 * p.r * ldT * 2) + al(p.r * ldT * 2))  # bf16: transposed copies for the LoRA gradients
     assert moe.saved_bytes(p, False) == want
     assert moe.saved_bytes(p, True) == want + al(S * p.d * es)
-    assert moe.fwd_workspace(p, True, True) == 0
-    assert moe.fwd_workspace(p, True, False) == al(S * p.d * es)
+    tiles = al((1 + (S + 255) // 256 + p.E) * 16)  # bf16: row-tile table of the grouped GEMMs
+    assert moe.fwd_workspace(p, True, True) == tiles
+    assert moe.fwd_workspace(p, True, False) == al(S * p.d * es) + tiles
     assert moe.fwd_workspace(p, False, False) == (al(S * p.F * es) + al(S * 2 * p.r * 4)
-                                                  + al(S * p.r * 4) + al(S * p.d * es))
+                                                  + al(S * p.r * 4) + al(S * p.d * es) + tiles)
     assert moe.route_workspace(p) > 0 and moe.bwd_workspace(p) > 0
     p32 = pb(dtype=moe.MOE_F32)
+    assert moe.fwd_workspace(p32, True, True) == 0
     assert moe.saved_bytes(p32, False) == 3 * al(S * p.F * 4) + al(S * 2 * p.r * 4) + al(S * p.r * 4)
 
 
