@@ -77,7 +77,7 @@ class Trace(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (or "
-                      "python -m moe_layer_lora_amd._build) first")
+                      "python __graft_entry__.py) first")
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.POINTER
