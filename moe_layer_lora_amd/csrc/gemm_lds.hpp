@@ -34,12 +34,12 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <int BM_, int BN_, int NSTAGE_, bool BN_CONTIG_, int BK_ = 32>
+template <int BM_, int BN_, int NSTAGE_, bool BN_CONTIG_, int BK_ = 32, int WM_ = 2, int WN_ = 2>
 struct Cfg {
     using T = bf16_t;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, NSTAGE = NSTAGE_;
     static constexpr bool B_NCONTIG = BN_CONTIG_;
-    static constexpr int WM = 2, WN = 2, NTHREADS = 256, NWAVES = 4;
+    static constexpr int WM = WM_, WN = WN_, NWAVES = WM_ * WN_, NTHREADS = 64 * NWAVES;
     static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     static constexpr int NKG = BK / 16;                      // 16-deep MFMA k groups per step
     static constexpr int CPR = BK / 8;                       // 16-byte chunks per K-contig row
@@ -52,7 +52,7 @@ struct Cfg {
     static constexpr int KROWS_PER_INSTR = 1024 / (BN * 2);  // N-contig k-rows per 1 KB
     // The rank-r LoRA tiles always use 32-deep steps (LoraCfg) and go
     // through one ring slot before the K loop.
-    using LoraCfg = Cfg<BM_, BN_, NSTAGE_, BN_CONTIG_, 32>;
+    using LoraCfg = Cfg<BM_, BN_, NSTAGE_, BN_CONTIG_, 32, WM_, WN_>;
     // 32-deep steps: a ring of NSTAGE whole stages (A and B of one step).
     // 64-deep steps (SPLIT): a ring of NSTAGE operand slots, each holding the
     // A tile or the B tile of one step (or the LoRA tile), so the B tiles can
@@ -514,7 +514,7 @@ __device__ __forceinline__ void run(const Op &op, int nlora, const Lora &lora, c
 template <class C>
 struct LoraA {
     static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
-    static constexpr int PER = C::BM * 4 / 256;
+    static constexpr int PER = C::BM * 4 / C::NTHREADS;
     const float *z;
     int nz, row0, rows;
     float s;
@@ -525,7 +525,7 @@ struct LoraA {
         r.ok = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int c = (int)threadIdx.x + 256 * i;
+            const int c = (int)threadIdx.x + C::NTHREADS * i;
             const int row = c >> 2, k = lt * 32 + (c & 3) * 8;
             const bool ok = row < rows && k < nz;
             const float4 *src = reinterpret_cast<const float4 *>(ok ? z + (size_t)(row0 + row) * nz + k : z);
@@ -537,7 +537,7 @@ struct LoraA {
     __device__ __forceinline__ void store(const Regs &r, char *st) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int c = (int)threadIdx.x + 256 * i;
+            const int c = (int)threadIdx.x + C::NTHREADS * i;
             const float m = ((r.ok >> i) & 1u) ? s : 0.0f;
             const float4 a = r.v[i][0], b = r.v[i][1];
             const float v[8] = {a.x * m, a.y * m, a.z * m, a.w * m, b.x * m, b.y * m, b.z * m, b.w * m};
@@ -552,7 +552,7 @@ struct LoraA {
 template <class C>
 struct LoraBK {
     static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
-    static constexpr int PER = C::BN * 4 / 256;
+    static constexpr int PER = C::BN * 4 / C::NTHREADS;
     const bf16_t *rowp[PER];  // row start (element k = klo), nullptr outside
     int klo[PER];
     int r;
@@ -562,7 +562,7 @@ struct LoraBK {
         rg.ok = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int c = (int)threadIdx.x + 256 * i;
+            const int c = (int)threadIdx.x + C::NTHREADS * i;
             const int k = lt * 32 + (c & 3) * 8 - klo[i];
             const bool ok = rowp[i] && k >= 0 && k < r;
             rg.v[i] = *reinterpret_cast<const chunk_t *>(ok ? rowp[i] + k : safe);
@@ -572,7 +572,7 @@ struct LoraBK {
     __device__ __forceinline__ void store(const Regs &rg, char *st) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int c = (int)threadIdx.x + 256 * i;
+            const int c = (int)threadIdx.x + C::NTHREADS * i;
             st_kcontig(st + C::A_BYTES, c >> 2, c & 3, ((rg.ok >> i) & 1u) ? rg.v[i] : zero4());
         }
     }
@@ -583,7 +583,7 @@ struct LoraBK {
 template <class C>
 struct LoraBN {
     static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
-    static constexpr int PER = 32 * C::BN / 8 / 256;
+    static constexpr int PER = 32 * C::BN / 8 / C::NTHREADS;
     const bf16_t *a, *b;
     int split, K, ld, ncol;
     struct Regs { chunk_t v[PER]; uint32_t ok; };
@@ -591,7 +591,7 @@ struct LoraBN {
         rg.ok = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int c = (int)threadIdx.x + 256 * i;
+            const int c = (int)threadIdx.x + C::NTHREADS * i;
             const int kr = c / (C::BN / 8), n = (c % (C::BN / 8)) * 8;
             const int j = lt * 32 + kr;
             const bool ok = j < K && n + 8 <= ncol;
@@ -603,7 +603,7 @@ struct LoraBN {
     __device__ __forceinline__ void store(const Regs &rg, char *st) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int c = (int)threadIdx.x + 256 * i;
+            const int c = (int)threadIdx.x + C::NTHREADS * i;
             st_ncontig<C::BN>(st + C::A_BYTES, c / (C::BN / 8), (c % (C::BN / 8)) * 8,
                               ((rg.ok >> i) & 1u) ? rg.v[i] : zero4());
         }

@@ -26,6 +26,9 @@ __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 // one wave per SIMD, so the full 512-entry register file (256 VGPR + 256
 // AGPR) is available to it.
 #define MOE_ONE_WAVE_PER_SIMD __attribute__((amdgpu_waves_per_eu(1, 1)))
+// ring-engine kernels: C::NWAVES waves per block, one block per CU (the ring
+// fills the LDS), so C::NWAVES / 4 waves on each SIMD
+#define MOE_LDS_BLOCK(C) __launch_bounds__(C::NTHREADS) __attribute__((amdgpu_waves_per_eu(C::NWAVES / 4, C::NWAVES / 4)))
 
 // Main grouped-GEMM tile shapes.
 template <typename T> struct MainCfg;
@@ -348,12 +351,18 @@ __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup_
 // operand slots (B tiles two steps ahead, A tiles one). Down backward (B
 // N-contiguous, read with transposing LDS reads, as in gate/up backward):
 // 32-deep steps in four 32 KB stages measured faster there.
-using LdsNT = lds::Cfg<256, 256, 5, false, 64>;
-using LdsNN = lds::Cfg<256, 256, 4, true, 32>;
-using LdsNN64 = lds::Cfg<256, 256, 5, true, 64>;
-using LdsNTh = lds::Cfg<128, 256, 5, false, 64>;  // 128-row tail tiles
-using LdsNNh = lds::Cfg<128, 256, 4, true, 32>;
-using LdsNN64h = lds::Cfg<128, 256, 5, true, 64>;
+// Waves: 2 x 4 per block (each wave 128 x 64 of the tile, two waves per SIMD,
+// so one wave's waits are covered by the other's MFMAs) for down, down
+// backward and gate/up backward; gate/up forward keeps 2 x 2 waves of
+// 128 x 128 (fewer LDS fragment reads per MFMA; measured faster there).
+using LdsGU = lds::Cfg<256, 256, 5, false, 64>;
+using LdsGUh = lds::Cfg<128, 256, 5, false, 64>;  // 128-row tail tiles
+using LdsNT = lds::Cfg<256, 256, 5, false, 64, 2, 4>;
+using LdsNN = lds::Cfg<256, 256, 4, true, 32, 2, 4>;
+using LdsNN64 = lds::Cfg<256, 256, 5, true, 64, 2, 4>;
+using LdsNTh = lds::Cfg<128, 256, 5, false, 64, 2, 4>;
+using LdsNNh = lds::Cfg<128, 256, 4, true, 32, 2, 4>;
+using LdsNN64h = lds::Cfg<128, 256, 5, true, 64, 2, 4>;
 
 template <class C> union LdsSmem {  // the tile scheduler's table is dead once the ring starts
     __align__(16) char ring[C::SMEM_BYTES];
@@ -403,7 +412,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
     lora.pb.safe = bg;
 #pragma unroll
     for (int i = 0; i < lds::LoraBK<typename C::LoraCfg>::PER; ++i) {
-        const int n = ((int)threadIdx.x + 256 * i) >> 2;
+        const int n = ((int)threadIdx.x + C::NTHREADS * i) >> 2;
         const int wn = n / C::WTN, ni = (n % C::WTN) / 32;
         const int f = f_base + wn * (C::WTN / 2) + (ni / 2) * 32 + (n % 32);
         const bool up = ni & 1;
@@ -413,7 +422,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
     f32x16_t acc[C::TM][C::TN];
     lds::run<C>(op, cdiv(2 * p.r, C::LoraCfg::BK), lora, ring, acc);
 
-    // wave columns: [gate 32 | up 32 | gate 32 | up 32] for f = f_base + wn*64 + (0..63)
+    // wave columns: pairs [gate 32 | up 32] for f = f_base + wn * WTN / 2 + (0 .. WTN / 2 - 1)
     bf16_t *G = static_cast<bf16_t *>(p.G), *U = static_cast<bf16_t *>(p.U), *H = static_cast<bf16_t *>(p.H);
     {
         const int wn = wave % C::WN, wm = wave / C::WN;
@@ -427,11 +436,12 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
                 for (int i = 0; i < 16; ++i)
                     buf[acc_row(i, lane) * C::WTN + ni * 32 + acc_col(lane)] = acc[mi][ni][i];
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // 64 f per row = 8 lanes x 8 f; 8 rows per pass
+            // WTN / 2 f per row = LPR lanes x 8 f; RPP rows per pass
+            constexpr int LPR = C::WTN / 16, RPP = 64 / LPR;
 #pragma unroll
-            for (int pass = 0; pass < 4; ++pass) {
-                const int r = pass * 8 + lane / 8, q = lane % 8;  // q: 8-f group
-                const int gc = (q / 4) * 64 + (q % 4) * 8;       // gate column in the wave tile
+            for (int pass = 0; pass < 32 / RPP; ++pass) {
+                const int r = pass * RPP + lane / LPR, q = lane % LPR;  // q: 8-f group
+                const int gc = (q / 4) * 64 + (q % 4) * 8;             // gate column in the wave tile
                 const float4 g0 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc);
                 const float4 g1 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 4);
                 const float4 u0 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 32);
@@ -457,7 +467,8 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
 
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
 template <class C, class CH>
-__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_lds(GateUpP p) {
+__global__ MOE_LDS_BLOCK(C) void k_gateup_lds(GateUpP p) {
+    static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
     __shared__ LdsSmem<C> sm;
     static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
@@ -496,7 +507,7 @@ __device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *
     lora.pb.safe = bd;
 #pragma unroll
     for (int i = 0; i < lds::LoraBK<typename C::LoraCfg>::PER; ++i) {
-        const int n = n_base + (((int)threadIdx.x + 256 * i) >> 2);
+        const int n = n_base + (((int)threadIdx.x + C::NTHREADS * i) >> 2);
         lora.pb.rowp[i] = n < p.d ? bd + (size_t)n * p.r : nullptr;
         lora.pb.klo[i] = 0;
     }
@@ -511,7 +522,8 @@ __device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *
 
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
 template <class C, class CH>
-__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_lds(DownP p) {
+__global__ MOE_LDS_BLOCK(C) void k_down_lds(DownP p) {
+    static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
     __shared__ LdsSmem<C> sm;
     static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
@@ -613,7 +625,8 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
 
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
 template <class C, class CH>
-__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_down_bwd_lds(DownBwdP p) {
+__global__ MOE_LDS_BLOCK(C) void k_down_bwd_lds(DownBwdP p) {
+    static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
     __shared__ LdsSmem<C> sm;
     static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
@@ -663,7 +676,8 @@ __device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile 
 
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
 template <class C, class CH>
-__global__ __launch_bounds__(256) MOE_ONE_WAVE_PER_SIMD void k_gateup_bwd_lds(GateUpBwdP p) {
+__global__ MOE_LDS_BLOCK(C) void k_gateup_bwd_lds(GateUpBwdP p) {
+    static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
     __shared__ LdsSmem<C> sm;
     static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
@@ -1481,7 +1495,7 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
         GateUpP gp{b.x, b.wg, b.wu, b.bg, b.bu, b.Zgu, b.sorted_slot, b.offsets, b.G, b.U, b.H,
                    D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.tiles};
         if constexpr (std::is_same<T, bf16_t>::value)
-            MOE_LAUNCH((k_gateup_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.F, LdsNT::BN / 2)), 256, gp);
+            MOE_LAUNCH((k_gateup_lds<LdsGU, LdsGUh>), grid_for<Cfg>(D, LdsGU::BM, cdiv(D.F, LdsGU::BN / 2)), LdsGU::NTHREADS, gp);
         else
             MOE_LAUNCH(k_gateup<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN / 2)), Cfg::NTHREADS, gp);
     }
@@ -1496,7 +1510,7 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
         TraceScope ts(tr, K_DOWN, st);
         DownP dp{b.H, b.wd, b.bd, b.Zd, b.offsets, b.Y, D.S(), D.E, D.d, D.F, D.r, D.s, b.tiles};
         if constexpr (std::is_same<T, bf16_t>::value)
-            MOE_LAUNCH((k_down_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)), 256, dp);
+            MOE_LAUNCH((k_down_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)), LdsNT::NTHREADS, dp);
         else
             MOE_LAUNCH(k_down<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, dp);
     }
@@ -1573,7 +1587,7 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
             DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
                         D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row, b.tiles};
             if constexpr (std::is_same<T, bf16_t>::value)
-                MOE_LAUNCH((k_down_bwd_lds<LdsNN, LdsNNh>), grid_for<Cfg>(D, LdsNN::BM, cdiv(D.F, LdsNN::BN)), 256, dp);
+                MOE_LAUNCH((k_down_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.F, LdsNN64::BN)), LdsNN64::NTHREADS, dp);
             else
                 MOE_LAUNCH(k_down_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN)), Cfg::NTHREADS, dp);
         }
@@ -1589,7 +1603,7 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
             GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.S(), D.E, D.d, D.F, D.r, D.s,
                           b.tiles};
             if constexpr (std::is_same<T, bf16_t>::value)
-                MOE_LAUNCH((k_gateup_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.d, LdsNN64::BN)), 256, gp);
+                MOE_LAUNCH((k_gateup_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.d, LdsNN64::BN)), LdsNN64::NTHREADS, gp);
             else
                 MOE_LAUNCH(k_gateup_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, gp);
         }
