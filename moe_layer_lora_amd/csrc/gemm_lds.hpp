@@ -1,11 +1,12 @@
 // gemm_lds.hpp - bf16 grouped-GEMM engine for gfx950 built on direct
 // global->LDS loads and transposing LDS reads.
 //
-// Tile: BM x BN per workgroup of 4 waves (2 x 2), each wave 128 x 128 for the
-// 256 x 256 shape: 16 v_mfma_f32_32x32x16_bf16 accumulators (256 registers).
-// K advances BK = 32 per step through a ring of NSTAGE LDS stages filled by
-// buffer_load_dwordx4 ... lds (no staging registers): NSTAGE-1 steps are in
-// flight while one is multiplied.
+// Tile: BM x BN per workgroup of WM x WN waves: 2 x 2 waves of 128 x 128 for
+// the 256 x 256 shape (16 v_mfma_f32_32x32x16_bf16 accumulators, 256
+// registers, one wave per SIMD) or 2 x 4 waves of 128 x 64 (8 accumulators,
+// two waves per SIMD). K advances BK (32 or 64) per step through a ring of LDS
+// stages or operand slots filled by buffer_load_dwordx4 ... lds (no staging
+// registers), with later steps in flight while one is multiplied.
 //
 // LDS layouts (byte offsets inside a stage):
 //  K-contiguous operand [rows][BK]: 64-byte rows of 4 16-byte chunks; chunk c

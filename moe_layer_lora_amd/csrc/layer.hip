@@ -345,12 +345,11 @@ __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup_
 // bf16 versions of the four grouped GEMMs on the direct-to-LDS ring engine
 // (gemm_lds.hpp). Same math and epilogues as the kernels above.
 // ===========================================================================
-// Forward (both operands K-contiguous) and gate/up backward: 64-deep steps,
-// so every K-contiguous row segment a load touches is a whole 128-byte line
-// (about twice the L2-to-LDS rate of 64-byte segments), through five 32 KB
-// operand slots (B tiles two steps ahead, A tiles one). Down backward (B
-// N-contiguous, read with transposing LDS reads, as in gate/up backward):
-// 32-deep steps in four 32 KB stages measured faster there.
+// All four run 64-deep steps, so every K-contiguous row segment a load
+// touches is a whole 128-byte line (about twice the L2-to-LDS rate of 64-byte
+// segments), through five 32 KB operand slots (B tiles two steps ahead, A
+// tiles one). The backward GEMMs read their N-contiguous weights with
+// transposing LDS reads.
 // Waves: 2 x 4 per block (each wave 128 x 64 of the tile, two waves per SIMD,
 // so one wave's waits are covered by the other's MFMAs) for down, down
 // backward and gate/up backward; gate/up forward keeps 2 x 2 waves of
@@ -358,10 +357,8 @@ __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup_
 using LdsGU = lds::Cfg<256, 256, 5, false, 64>;
 using LdsGUh = lds::Cfg<128, 256, 5, false, 64>;  // 128-row tail tiles
 using LdsNT = lds::Cfg<256, 256, 5, false, 64, 2, 4>;
-using LdsNN = lds::Cfg<256, 256, 4, true, 32, 2, 4>;
-using LdsNN64 = lds::Cfg<256, 256, 5, true, 64, 2, 4>;
 using LdsNTh = lds::Cfg<128, 256, 5, false, 64, 2, 4>;
-using LdsNNh = lds::Cfg<128, 256, 4, true, 32, 2, 4>;
+using LdsNN64 = lds::Cfg<256, 256, 5, true, 64, 2, 4>;
 using LdsNN64h = lds::Cfg<128, 256, 5, true, 64, 2, 4>;
 
 template <class C> union LdsSmem {  // the tile scheduler's table is dead once the ring starts
