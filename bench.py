@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--whereloop-steps", type=int, default=3,
+                    help="steps of the per-expert where() loop baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before warm-up, run a plain device copy (y = -x, fp32) of MIB MiB "
                          "three times: the known-size kernel that scales rocprofv3's "
@@ -145,6 +147,60 @@ def cpu_baseline(cfg, tokens):
             "sample": f"first {tokens} of the {cfg.T} tokens of the same layer (same weights and "
                       f"generator), route+fwd" + ("+bwd" if cfg.backward else "") +
                       ", fp64 plain loops, OpenMP over experts"}
+
+
+def whereloop_baseline(torch, cfg, x, logits, w, dout, steps, warmup=1):
+    """The per-expert loop that sorted routing and the grouped GEMM replace, in
+    plain PyTorch on the same GPU and inputs: top-k + softmax over the selected
+    logits, then for every expert a where() over the routing table (one host
+    sync each, to size the gather), a gathered copy of its tokens, its SwiGLU
+    MLP with the LoRA terms added after the base product, and a weighted
+    index_add into the output; the backward is autograd over x and the LoRA
+    factors (base weights frozen). Library GEMMs (hipBLASLt) do the products.
+    Returns ms per step (forward, backward) and the output it computed."""
+    E, k, s = cfg.E, cfg.k, cfg.s
+    # frozen base weights transposed once, outside the timed region
+    wt = {n: w[n].transpose(1, 2).contiguous() for n in ("w_gate", "w_up", "w_down")}
+    lora = {n: w[n].detach().clone().requires_grad_(True)
+            for n in ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")}
+    xr = x.detach().clone().requires_grad_(cfg.backward)
+
+    def lin(h, e, base, a, b):  # h W^T + s (h A^T) B^T, never forming W + s B A
+        return h @ wt[base][e] + s * ((h @ lora[a][e].t()) @ lora[b][e].t())
+
+    def forward():
+        top = torch.topk(logits, k, dim=1)
+        wts = torch.softmax(top.values, dim=1)
+        out = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device=x.device)
+        for e in range(E):
+            tok, j = torch.where(top.indices == e)
+            if tok.numel() == 0:
+                continue
+            h = xr[tok]
+            g = lin(h, e, "w_gate", "a_gate", "b_gate")
+            u = lin(h, e, "w_up", "a_up", "b_up")
+            y = lin(torch.nn.functional.silu(g) * u, e, "w_down", "a_down", "b_down")
+            out = out.index_add(0, tok, wts[tok, j, None] * y.float())
+        return out
+
+    fwd_ms, bwd_ms, out = [], [], None
+    for it in range(warmup + steps):
+        for t in list(lora.values()) + [xr]:
+            t.grad = None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.set_grad_enabled(cfg.backward):
+            out = forward()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if cfg.backward:
+            out.backward(dout.float())
+            torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        if it >= warmup:
+            fwd_ms.append((t1 - t0) * 1e3)
+            bwd_ms.append((t2 - t1) * 1e3)
+    return sum(fwd_ms) / steps, sum(bwd_ms) / steps, out.detach()
 
 
 def main():
@@ -312,6 +368,32 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
         "input_setup_s": round(t_gen, 2),
     }
+    if args.whereloop_steps > 0 and cfg.dtype == "bf16":
+        # the library's forward and backward alone (routing excluded), to set
+        # against the loop's
+        fb = make_trace(["proj_gu", "combine"] + (["proj_dout", "lora_grad"] if cfg.backward else []))
+        step(fb)
+        torch.cuda.synchronize()
+        i = moe.KERNELS.index
+        lib_fwd = hip.elapsed_ms(fb.start[i("proj_gu")], fb.stop[i("combine")])
+        lib_bwd = (hip.elapsed_ms(fb.start[i("proj_dout")], fb.stop[i("lora_grad")])
+                   if cfg.backward else 0.0)
+        for n in range(moe.MOE_K_COUNT):
+            if fb.start[n]:
+                hip.destroy(fb.start[n])
+                hip.destroy(fb.stop[n])
+        wl_fwd, wl_bwd, wl_out = whereloop_baseline(torch, cfg, x, logits, w, dout,
+                                                    args.whereloop_steps)
+        diff = (wl_out - out.float()).norm() / wl_out.norm()
+        rec["whereloop_baseline"] = {
+            "what": "per-expert where() loop in PyTorch on the same GPU and inputs "
+                    "(one host sync per expert, gathered copies, hipBLASLt products, "
+                    "index_add combine; autograd backward)",
+            "steps": args.whereloop_steps, "fwd_ms": round(wl_fwd, 3), "bwd_ms": round(wl_bwd, 3),
+            "library_fwd_ms": round(lib_fwd, 4), "library_bwd_ms": round(lib_bwd, 4),
+            "fwd_speedup": round(wl_fwd / lib_fwd, 2),
+            "bwd_speedup": round(wl_bwd / lib_bwd, 2) if cfg.backward else None,
+            "out_rel_l2_vs_library": float(diff)}
     if not args.skip_cpu:
         rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T))
     print(json.dumps(rec), flush=True)
