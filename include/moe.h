@@ -120,6 +120,9 @@ enum {
     MOE_K_GATEUP_BWD,       /* grouped GEMM dXp + LoRA                      */
     MOE_K_DX_COMBINE,       /* dX gather-sum                                */
     MOE_K_LORA_GRAD,        /* all LoRA weight-gradient kernels             */
+    MOE_K_ROUTER_LOGITS,    /* router projection x W_r^T                    */
+    MOE_K_ROUTER_DX,        /* router share of dX: d_logits W_r             */
+    MOE_K_ROUTER_DW,        /* router weight gradient d_logits^T x          */
     MOE_K_COUNT
 };
 typedef struct {
@@ -170,6 +173,34 @@ moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout,
                      int keep_expert_out, void *dx, const moe_lora_grads_t *grads,
                      float *d_topk_w, float *d_logits, void *ws, size_t ws_bytes,
                      void *stream, const moe_trace_t *trace);
+
+/* Router projection: the linear gate in front of moe_route. The pages start
+ * the layer from a per-token routing decision over router logits (Unsloth x
+ * NVIDIA blog, MoE routing paragraph; Unsloth 2026 wiki chapter,
+ * "Optimisation 3", opening paragraph) without writing the gate out; this
+ * is the plain bias-free one, logits = x W_r^T.
+ *   w_router [E,d] in dtype (nn.Linear orientation); logits [T,E] float32.
+ *   Requires E to be a multiple of 8 (else MOE_E_UNSUPPORTED).
+ * moe_router_fwd: x [T,d] -> logits (fp32 accumulation over d). */
+moe_status_t moe_router_fwd(const moe_problem_t *pb, const void *x, const void *w_router, float *logits,
+                            void *stream, const moe_trace_t *trace);
+
+/* Workspace bytes of moe_router_bwd (0 for an invalid problem). */
+size_t moe_router_workspace(const moe_problem_t *pb);
+
+/* Backward of the router projection for d_logits [T,E] float32 (the layer's
+ * logit gradient, as moe_bwd writes it):
+ *   dx [T,d] dtype     = dx_in + d_logits W_r   (dx_in is typically moe_bwd's
+ *                        dx; dx may be the same buffer as dx_in; d_logits is
+ *                        rounded to dtype as the product reads it)
+ *   dw_router [E,d] fp32 = d_logits^T x        (overwritten; zeros if T = 0)
+ * Either output may be NULL to skip it (dx_in is then unused); a frozen
+ * router passes dw_router = NULL. ws: moe_router_workspace(pb) bytes (only
+ * used for dw_router). The result does not depend on launch timing: dW_r is
+ * summed over token chunks in a fixed order. */
+moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *w_router, const float *d_logits,
+                            const void *dx_in, void *dx, float *dw_router, void *ws, size_t ws_bytes,
+                            void *stream, const moe_trace_t *trace);
 
 /* Static string naming a status code. */
 const char *moe_status_str(moe_status_t st);

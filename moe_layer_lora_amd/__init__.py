@@ -33,11 +33,12 @@ MOE_F32, MOE_BF16 = 0, 1
 
 KERNELS = ["route_topk", "route_scan", "route_scatter", "proj_gu", "gateup", "proj_d", "down",
            "combine", "router_grad", "proj_dout", "down_bwd", "proj_dgu", "gateup_bwd",
-           "dx_combine", "lora_grad"]
+           "dx_combine", "lora_grad", "router_logits", "router_dx", "router_dw"]
 MOE_K_COUNT = len(KERNELS)
 
 EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe_saved_bytes",
-           "moe_route", "moe_fwd", "moe_bwd", "moe_status_str"]
+           "moe_route", "moe_fwd", "moe_bwd", "moe_status_str", "moe_router_workspace",
+           "moe_router_fwd", "moe_router_bwd"]
 
 
 class Problem(ctypes.Structure):
@@ -94,7 +95,11 @@ _lib.moe_fwd.argtypes = [_P(Problem), _vp, _P(Routing), _P(Weights), _vp, _vp, _
                          _vp, _P(Trace)]
 _lib.moe_bwd.argtypes = [_P(Problem), _vp, _vp, _P(Routing), _P(Weights), _vp, _i32, _vp,
                          _P(LoraGrads), _vp, _vp, _vp, _sz, _vp, _P(Trace)]
-for _f in (_lib.moe_route, _lib.moe_fwd, _lib.moe_bwd):
+_lib.moe_router_workspace.argtypes = [_P(Problem)]
+_lib.moe_router_workspace.restype = _sz
+_lib.moe_router_fwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _P(Trace)]
+_lib.moe_router_bwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _P(Trace)]
+for _f in (_lib.moe_route, _lib.moe_fwd, _lib.moe_bwd, _lib.moe_router_fwd, _lib.moe_router_bwd):
     _f.restype = _i32
 _lib.moe_status_str.argtypes = [_i32]
 _lib.moe_status_str.restype = ctypes.c_char_p
@@ -191,6 +196,26 @@ def moe_bwd(pb, x, dout, rt: dict, w: dict, saved, keep_expert_out, dx, grads: d
                       _ptr(d_logits), _ptr(ws), _nbytes(ws), _stream(stream),
                       ctypes.byref(trace) if trace is not None else None)
     _check(st, "moe_bwd")
+
+
+def router_workspace(pb: Problem) -> int:
+    return _lib.moe_router_workspace(ctypes.byref(pb))
+
+
+def moe_router_fwd(pb, x, w_router, logits, stream=None, trace=None):
+    """logits [T,E] fp32 = x [T,d] W_r^T (w_router [E,d] in the layer dtype)."""
+    st = _lib.moe_router_fwd(ctypes.byref(pb), _ptr(x), _ptr(w_router), _ptr(logits), _stream(stream),
+                             ctypes.byref(trace) if trace is not None else None)
+    _check(st, "moe_router_fwd")
+
+
+def moe_router_bwd(pb, x, w_router, d_logits, dx_in=None, dx=None, dw_router=None, ws=None,
+                   stream=None, trace=None):
+    """dx = dx_in + d_logits W_r (dx may be dx_in); dw_router = d_logits^T x."""
+    st = _lib.moe_router_bwd(ctypes.byref(pb), _ptr(x), _ptr(w_router), _ptr(d_logits), _ptr(dx_in),
+                             _ptr(dx), _ptr(dw_router), _ptr(ws), _nbytes(ws), _stream(stream),
+                             ctypes.byref(trace) if trace is not None else None)
+    _check(st, "moe_router_bwd")
 
 
 # ---------------------------------------------------------------- allocation helpers

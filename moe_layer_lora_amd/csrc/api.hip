@@ -315,4 +315,60 @@ moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout, c
     return e == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
+size_t moe_router_workspace(const moe_problem_t *pb) {
+    if (check_problem(pb) != MOE_OK || pb->E % 8) return 0;
+    const moe::RouterWs w = moe::router_ws(dims_of(pb));
+    return al(w.dlT_bytes) + al(w.partial_bytes);
+}
+
+moe_status_t moe_router_fwd(const moe_problem_t *pb, const void *x, const void *w_router, float *logits,
+                            void *stream, const moe_trace_t *trace) {
+    moe_status_t st = check_problem(pb);
+    if (st != MOE_OK) return st;
+    if (pb->E % 8) return MOE_E_UNSUPPORTED;
+    if (!buf_ok(w_router)) return MOE_E_ARG;
+    if (pb->T > 0 && (!buf_ok(x) || !buf_ok(logits))) return MOE_E_ARG;
+    if ((long long)pb->T * pb->d >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+    const moe::Trace tr = to_trace(trace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Dims D = dims_of(pb);
+    const hipError_t e = pb->dtype == MOE_BF16
+                             ? moe::run_router_fwd<moe::bf16_t>(D, x, w_router, logits, s, trace ? &tr : nullptr)
+                             : moe::run_router_fwd<float>(D, x, w_router, logits, s, trace ? &tr : nullptr);
+    return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *w_router, const float *d_logits,
+                            const void *dx_in, void *dx, float *dw_router, void *ws, size_t ws_bytes,
+                            void *stream, const moe_trace_t *trace) {
+    moe_status_t st = check_problem(pb);
+    if (st != MOE_OK) return st;
+    if (pb->E % 8) return MOE_E_UNSUPPORTED;
+    if (!buf_ok(w_router)) return MOE_E_ARG;
+    if ((long long)pb->T * pb->d >= (1LL << 31) || (long long)pb->E * ((pb->T + 7) & ~7) >= (1LL << 31))
+        return MOE_E_UNSUPPORTED;
+    if (pb->T > 0 && (dx || dw_router) && (!buf_ok(x) || !buf_ok(d_logits))) return MOE_E_ARG;
+    if (dx && pb->T > 0 && (!buf_ok(dx) || !buf_ok(dx_in))) return MOE_E_ARG;
+    if (dw_router && !buf_ok(dw_router)) return MOE_E_ARG;
+    const Dims D = dims_of(pb);
+    const moe::RouterWs w = moe::router_ws(D);
+    void *dlT = nullptr, *partial = nullptr;
+    if (dw_router) {
+        const size_t need = al(w.dlT_bytes) + al(w.partial_bytes);
+        if (ws_bytes < need) return MOE_E_WORKSPACE;
+        if (need > 0 && !buf_ok(ws)) return MOE_E_ARG;
+        dlT = ws;
+        partial = w.partial_bytes ? at(ws, al(w.dlT_bytes)) : nullptr;
+    }
+    const moe::Trace tr = to_trace(trace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e =
+        pb->dtype == MOE_BF16
+            ? moe::run_router_bwd<moe::bf16_t>(D, x, w_router, d_logits, dx_in, dx, dw_router, dlT, partial, s,
+                                               trace ? &tr : nullptr)
+            : moe::run_router_bwd<float>(D, x, w_router, d_logits, dx_in, dx, dw_router, dlT, partial, s,
+                                         trace ? &tr : nullptr);
+    return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
 }  // extern "C"

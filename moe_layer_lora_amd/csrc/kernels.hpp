@@ -17,6 +17,8 @@ __host__ __device__ inline int max_row_tiles(int S, int E, int BM) { return (S +
 
 typedef uint16_t bf16_t;  // bf16 bit pattern in memory
 
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
 struct Dims {
     int T, d, E, k, F, r;
     float s;  // LoRA scale
@@ -77,6 +79,22 @@ struct Trace {
 
 template <typename T> hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace *tr);
 template <typename T> hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace *tr);
+
+// ---- router projection (logits = x W_r^T) and its backward ---------------------
+// Workspace of the backward: d_logits transposed [E, Tp] (Tp = T rounded up
+// to 8) and, when the token range is split into nch > 1 chunks, the fp32
+// partial dW_r of each chunk [nch, E, d].
+struct RouterWs {
+    int Tp, chunk, nch;
+    size_t dlT_bytes, partial_bytes;
+};
+RouterWs router_ws(const Dims &D);
+template <typename T>
+hipError_t run_router_fwd(const Dims &D, const void *x, const void *wr, float *logits, hipStream_t st,
+                          const Trace *tr);
+template <typename T>
+hipError_t run_router_bwd(const Dims &D, const void *x, const void *wr, const float *d_logits, const void *dx_in,
+                          void *dx, float *dw, void *dlT, void *partial, hipStream_t st, const Trace *tr);
 
 // bytes of LoRA-gradient partial sums the backward may need
 size_t lora_grad_partial_bytes(const Dims &D);

@@ -20,7 +20,6 @@
 namespace moe {
 
 constexpr int kMaxE = 1024;
-__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // The large tiles hold a 128x128 fp32 accumulator per wave (256 registers):
 // one wave per SIMD, so the full 512-entry register file (256 VGPR + 256

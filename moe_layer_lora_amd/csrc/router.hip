@@ -1,0 +1,247 @@
+// router.hip - the router projection in front of the routing (the linear gate
+// logits = x W_r^T, no bias) and its backward: the router's share of dX and
+// the gradient of W_r. The pages start the MoE layer from a per-token routing
+// decision over router logits (Unsloth x NVIDIA blog, MoE routing paragraph;
+// Unsloth 2026 wiki chapter, "Optimisation 3: grouped_mm and Split-LoRA in
+// MoE training", opening paragraph); this is the plain linear gate.
+//
+// All three products run on the register-staged MFMA tile engine
+// (gemm.hpp), 128 x 128 tiles of 4 waves, fp32 accumulation:
+//   logits [T,E]   = x [T,d] . W_r[E,d]^T          (both K-contiguous)
+//   dx     [T,d]   = dx_in + d_logits [T,E] . W_r  (d_logits fp32, rounded
+//                    to the storage type as it is staged; W_r N-contiguous)
+//   dW_r   [E,d]   = d_logits^T . x                (K = tokens: d_logits is
+//                    transposed once into the workspace; the token range is
+//                    split into chunks whose fp32 partial products are summed
+//                    in chunk order, so the result is deterministic)
+#include "gemm.hpp"
+#include "kernels.hpp"
+#include "moe.h"
+
+namespace moe {
+namespace {
+
+template <typename T> struct RouterCfg { using type = GemmCfg<T, 128, 128, 32, 2, 2>; };
+
+template <class Cfg> struct RSmem {
+    __align__(16) typename Cfg::T a[2 * Cfg::A_ELEMS];
+    __align__(16) typename Cfg::T b[2 * Cfg::B_ELEMS];
+};
+
+struct RouterP {
+    const void *x, *wr;
+    const float *dl;      // d_logits [T,E]
+    float *dlT;           // workspace [E,Tp]: d_logits transposed, zero for T <= t < Tp
+    const void *dx_in;
+    void *dx;
+    float *logits, *dw, *partial;
+    int T, d, E, Tp, chunk, nch;
+};
+
+// logits = x W_r^T: tile (m0, n0) of [T, E]
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_router_logits(RouterP p) {
+    using T = typename Cfg::T;
+    __shared__ RSmem<Cfg> sm;
+    const int ntn = cdiv(p.E, Cfg::BN);
+    const int m0 = (int)(blockIdx.x / ntn) * Cfg::BM, n0 = (int)(blockIdx.x % ntn) * Cfg::BN;
+    const int nk = cdiv(p.d, Cfg::BK);
+    KLoader<Cfg, Cfg::BM, false> la;
+    la.K0 = p.d; la.K1 = 0; la.nk0 = nk; la.scale1 = 0.0f;
+    la.b0[0] = la.b0[1] = static_cast<const T *>(p.x);
+    la.b1[0] = la.b1[1] = nullptr;
+#pragma unroll
+    for (int i = 0; i < la.PER; ++i) {
+        const int m = la.row_of(i);
+        if (la.active(i) && m0 + m < p.T) la.set0(i, (uint32_t)(m0 + m) * (uint32_t)p.d, 0);
+    }
+    KLoader<Cfg, Cfg::BN, false> lb;
+    lb.K0 = p.d; lb.K1 = 0; lb.nk0 = nk; lb.scale1 = 0.0f;
+    lb.b0[0] = lb.b0[1] = static_cast<const T *>(p.wr);
+    lb.b1[0] = lb.b1[1] = nullptr;
+#pragma unroll
+    for (int i = 0; i < lb.PER; ++i) {
+        const int n = lb.row_of(i);
+        if (lb.active(i) && n0 + n < p.E) lb.set0(i, (uint32_t)(n0 + n) * (uint32_t)p.d, 0);
+    }
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    gemm_mainloop<Cfg>(la, lb, nk, sm.a, sm.b, acc);
+    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+        if (m0 + m < p.T && n0 + n < p.E) p.logits[(size_t)(m0 + m) * p.E + n0 + n] = v;
+    });
+}
+
+// dx = dx_in + d_logits W_r: tile (m0, n0) of [T, d], K = E
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_router_dx(RouterP p) {
+    using T = typename Cfg::T;
+    __shared__ RSmem<Cfg> sm;
+    const int ntn = cdiv(p.d, Cfg::BN);
+    const int m0 = (int)(blockIdx.x / ntn) * Cfg::BM, n0 = (int)(blockIdx.x % ntn) * Cfg::BN;
+    const int ncol = min(Cfg::BN, p.d - n0);
+    // A: only the fp32 segment (rows of d_logits, scale 1)
+    KLoader<Cfg, Cfg::BM, true> la;
+    la.K0 = 0; la.nk0 = 0; la.K1 = p.E; la.scale1 = 1.0f;
+    la.b0[0] = la.b0[1] = static_cast<const T *>(p.wr);  // never read (no segment 0)
+    la.b1[0] = la.b1[1] = p.dl;
+#pragma unroll
+    for (int i = 0; i < la.PER; ++i) {
+        const int m = la.row_of(i);
+        if (la.active(i) && m0 + m < p.T) la.set1(i, (uint32_t)(m0 + m) * (uint32_t)p.E, 0);
+    }
+    // B: W_r [E, d], element (k = e, n) at row e, column n0 + n
+    NLoader<Cfg, Cfg::BN> lb;
+    lb.nk0 = 1 << 30;
+    lb.s0 = NSeg{static_cast<const T *>(p.wr) + n0, nullptr, p.E, p.E, p.d, 0, ncol, 0, 0};
+    lb.s1 = lb.s0;
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    gemm_mainloop<Cfg>(la, lb, cdiv(p.E, Cfg::BK), sm.a, sm.b, acc);
+    const T *dxi = static_cast<const T *>(p.dx_in);
+    T *dxo = static_cast<T *>(p.dx);
+    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+        if (m0 + m < p.T && n0 + n < p.d) {
+            const size_t o = (size_t)(m0 + m) * p.d + n0 + n;
+            dxo[o] = Elem<T>::from_f32(Elem<T>::to_f32(dxi[o]) + v);
+        }
+    });
+}
+
+// dlT[e][t] = d_logits[t][e] for t < T, 0 for T <= t < Tp; 32 x 32 tiles
+__global__ __launch_bounds__(256) void k_router_dlT(RouterP p) {
+    __shared__ float tile[32][33];
+    const int t0 = (int)blockIdx.x * 32, e0 = (int)blockIdx.y * 32;
+    const int tx = (int)threadIdx.x & 31, ty = (int)threadIdx.x >> 5;
+#pragma unroll
+    for (int i = ty; i < 32; i += 8) {
+        const int t = t0 + i, e = e0 + tx;
+        tile[i][tx] = (t < p.T && e < p.E) ? p.dl[(size_t)t * p.E + e] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = ty; i < 32; i += 8) {
+        const int e = e0 + i, t = t0 + tx;
+        if (e < p.E && t < p.Tp) p.dlT[(size_t)e * p.Tp + t] = tile[tx][i];
+    }
+}
+
+// dW_r (one chunk of tokens): tile (m0 = expert, n0 = model dim) of [E, d],
+// K = the chunk's tokens; written to dw directly when there is one chunk,
+// else to partial[c]
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void k_router_dw(RouterP p) {
+    using T = typename Cfg::T;
+    __shared__ RSmem<Cfg> sm;
+    const int ntn = cdiv(p.d, Cfg::BN), ntm = cdiv(p.E, Cfg::BM);
+    const int c = (int)blockIdx.x / (ntm * ntn), rem = (int)blockIdx.x % (ntm * ntn);
+    const int m0 = (rem / ntn) * Cfg::BM, n0 = (rem % ntn) * Cfg::BN;
+    const int t0 = c * p.chunk, kc = min(p.chunk, p.T - t0);
+    const int ncol = min(Cfg::BN, p.d - n0);
+    // A: rows e of dlT from token t0 (zero-padded past T, so a chunk's last
+    // partial vector reads zeros, never the next chunk)
+    KLoader<Cfg, Cfg::BM, true> la;
+    la.K0 = 0; la.nk0 = 0; la.K1 = kc; la.scale1 = 1.0f;
+    la.b0[0] = la.b0[1] = static_cast<const T *>(p.x);  // never read (no segment 0)
+    la.b1[0] = la.b1[1] = p.dlT + t0;
+#pragma unroll
+    for (int i = 0; i < la.PER; ++i) {
+        const int m = la.row_of(i);
+        if (la.active(i) && m0 + m < p.E) la.set1(i, (uint32_t)(m0 + m) * (uint32_t)p.Tp, 0);
+    }
+    // B: x rows t0 .. t0 + kc - 1, element (k = token, n) at column n0 + n
+    NLoader<Cfg, Cfg::BN> lb;
+    lb.nk0 = 1 << 30;
+    lb.s0 = NSeg{static_cast<const T *>(p.x) + (size_t)t0 * p.d + n0, nullptr, kc, kc, p.d, 0, ncol, 0, 0};
+    lb.s1 = lb.s0;
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    gemm_mainloop<Cfg>(la, lb, cdiv(kc, Cfg::BK), sm.a, sm.b, acc);
+    float *dst = p.nch == 1 ? p.dw : p.partial + (size_t)c * p.E * p.d;
+    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
+        if (m0 + m < p.E && n0 + n < p.d) dst[(size_t)(m0 + m) * p.d + n0 + n] = v;
+    });
+}
+
+// dw = sum of the chunk partials in chunk order (zeros when there are no tokens)
+__global__ __launch_bounds__(256) void k_router_dw_sum(RouterP p) {
+    const size_t n = (size_t)p.E * p.d;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+        float acc = 0.0f;
+        for (int c = 0; c < p.nch; ++c) acc += p.partial[(size_t)c * n + i];
+        p.dw[i] = acc;
+    }
+}
+
+struct Scope {  // event pair around one launch, if asked for
+    const Trace *tr; int id; hipStream_t st;
+    Scope(const Trace *t, int i, hipStream_t s) : tr(t), id(i), st(s) {
+        if (tr && tr->start[id] && tr->stop[id]) (void)hipEventRecord(tr->start[id], st);
+    }
+    ~Scope() { if (tr && tr->start[id] && tr->stop[id]) (void)hipEventRecord(tr->stop[id], st); }
+};
+
+#define MOE_RLAUNCH(kern, grid, block, ...)                                 \
+    do {                                                                    \
+        kern<<<(grid), dim3(block), 0, st>>>(__VA_ARGS__);                  \
+        const hipError_t _e = hipGetLastError();                            \
+        if (_e != hipSuccess) return _e;                                    \
+    } while (0)
+
+}  // namespace
+
+RouterWs router_ws(const Dims &D) {
+    RouterWs w{};
+    w.Tp = (D.T + 7) & ~7;
+    const int nch0 = D.T > 0 ? min(16, max(1, (D.T + 255) / 256)) : 1;
+    w.chunk = D.T > 0 ? ((D.T + nch0 - 1) / nch0 + 31) & ~31 : 32;
+    w.nch = D.T > 0 ? (D.T + w.chunk - 1) / w.chunk : 1;
+    w.dlT_bytes = (size_t)D.E * w.Tp * sizeof(float);
+    w.partial_bytes = w.nch > 1 ? (size_t)w.nch * D.E * D.d * sizeof(float) : 0;
+    return w;
+}
+
+template <typename T>
+hipError_t run_router_fwd(const Dims &D, const void *x, const void *wr, float *logits, hipStream_t st,
+                          const Trace *tr) {
+    using Cfg = typename RouterCfg<T>::type;
+    if (D.T == 0) return hipSuccess;
+    RouterP p{};
+    p.x = x; p.wr = wr; p.logits = logits; p.T = D.T; p.d = D.d; p.E = D.E;
+    Scope sc(tr, MOE_K_ROUTER_LOGITS, st);
+    MOE_RLAUNCH(k_router_logits<Cfg>, dim3(cdiv(D.T, Cfg::BM) * cdiv(D.E, Cfg::BN)), Cfg::NTHREADS, p);
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t run_router_bwd(const Dims &D, const void *x, const void *wr, const float *d_logits, const void *dx_in,
+                          void *dx, float *dw, void *dlT, void *partial, hipStream_t st, const Trace *tr) {
+    using Cfg = typename RouterCfg<T>::type;
+    const RouterWs w = router_ws(D);
+    RouterP p{};
+    p.x = x; p.wr = wr; p.dl = d_logits; p.dlT = static_cast<float *>(dlT); p.dx_in = dx_in; p.dx = dx;
+    p.dw = dw; p.partial = static_cast<float *>(partial);
+    p.T = D.T; p.d = D.d; p.E = D.E; p.Tp = w.Tp; p.chunk = w.chunk; p.nch = w.nch;
+    if (dx && D.T > 0) {
+        Scope sc(tr, MOE_K_ROUTER_DX, st);
+        MOE_RLAUNCH(k_router_dx<Cfg>, dim3(cdiv(D.T, Cfg::BM) * cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, p);
+    }
+    if (dw) {
+        Scope sc(tr, MOE_K_ROUTER_DW, st);
+        if (D.T == 0) {  // an empty sum: zeros
+            p.nch = 0;
+            MOE_RLAUNCH(k_router_dw_sum, dim3(min(1024, cdiv(D.E * D.d, 256))), 256, p);
+            return hipSuccess;
+        }
+        MOE_RLAUNCH(k_router_dlT, dim3(cdiv(w.Tp, 32), cdiv(D.E, 32)), 256, p);
+        MOE_RLAUNCH(k_router_dw<Cfg>, dim3(w.nch * cdiv(D.E, Cfg::BM) * cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, p);
+        if (w.nch > 1) MOE_RLAUNCH(k_router_dw_sum, dim3(min(1024, cdiv(D.E * D.d, 256))), 256, p);
+    }
+    return hipSuccess;
+}
+
+template hipError_t run_router_fwd<float>(const Dims &, const void *, const void *, float *, hipStream_t, const Trace *);
+template hipError_t run_router_fwd<bf16_t>(const Dims &, const void *, const void *, float *, hipStream_t, const Trace *);
+template hipError_t run_router_bwd<float>(const Dims &, const void *, const void *, const float *, const void *, void *,
+                                          float *, void *, void *, hipStream_t, const Trace *);
+template hipError_t run_router_bwd<bf16_t>(const Dims &, const void *, const void *, const float *, const void *, void *,
+                                           float *, void *, void *, hipStream_t, const Trace *);
+
+}  // namespace moe

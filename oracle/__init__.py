@@ -55,8 +55,10 @@ def _load():
         lib.orc_fwd_tokens.argtypes = [lp, vp, vp, i32, vp, vp, vp]
         lib.orc_bwd_tokens.argtypes = [lp, vp, vp, vp, i32, vp, vp, vp, vp]
         lib.orc_lora_grads.argtypes = [lp, vp, vp, vp, vp, vp, i32, vp] + [vp] * 6
+        lib.orc_router_fwd.argtypes = [i32, i32, i32, i32, vp, vp, vp]
+        lib.orc_router_bwd.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
         for f in (lib.orc_route, lib.orc_fwd, lib.orc_bwd, lib.orc_fwd_tokens,
-                  lib.orc_bwd_tokens, lib.orc_lora_grads):
+                  lib.orc_bwd_tokens, lib.orc_lora_grads, lib.orc_router_fwd, lib.orc_router_bwd):
             f.restype = ctypes.c_int
         lib.orc_threads.argtypes = []
         lib.orc_threads.restype = ctypes.c_int
@@ -209,4 +211,37 @@ def lora_grads(L: Layer, rt: dict, dout: np.ndarray, experts) -> dict:
                                   *[o[k].ctypes.data for k in ("da_gate", "db_gate", "da_up",
                                                                "db_up", "da_down", "db_down")]),
            "lora_grads")
+    return o
+
+
+_DTYPE_CODE = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.float64): 2}
+
+
+def router_fwd(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
+    """Router logits x W_r^T in fp64. x [T,d] and w_r [E,d] in one storage
+    dtype (float32, bf16 bits as uint16, or float64)."""
+    x, w_r = np.ascontiguousarray(x), np.ascontiguousarray(w_r)
+    if x.dtype != w_r.dtype or x.ndim != 2 or w_r.ndim != 2 or x.shape[1] != w_r.shape[1]:
+        raise ValueError(f"router_fwd: x {x.dtype}{x.shape}, w_r {w_r.dtype}{w_r.shape}")
+    T, d = x.shape
+    E = w_r.shape[0]
+    out = np.empty((T, E))
+    _check(_load().orc_router_fwd(T, d, E, _DTYPE_CODE[x.dtype], x.ctypes.data, w_r.ctypes.data,
+                                  out.ctypes.data), "router_fwd")
+    return out
+
+
+def router_bwd(x: np.ndarray, w_r: np.ndarray, d_logits: np.ndarray) -> dict:
+    """The router projection's backward for a gradient d_logits [T,E] of its
+    output: {"dx": d_logits W_r [T,d], "dw_r": d_logits^T x [E,d]}, fp64."""
+    x, w_r = np.ascontiguousarray(x), np.ascontiguousarray(w_r)
+    d_logits = np.ascontiguousarray(d_logits, dtype=np.float64)
+    T, d = x.shape
+    E = w_r.shape[0]
+    if x.dtype != w_r.dtype or w_r.shape[1] != d or d_logits.shape != (T, E):
+        raise ValueError("router_bwd: shape or dtype mismatch")
+    o = {"dx": np.empty((T, d)), "dw_r": np.empty((E, d))}
+    _check(_load().orc_router_bwd(T, d, E, _DTYPE_CODE[x.dtype], x.ctypes.data, w_r.ctypes.data,
+                                  d_logits.ctypes.data, o["dx"].ctypes.data,
+                                  o["dw_r"].ctypes.data), "router_bwd")
     return o

@@ -29,6 +29,9 @@
  *            "bottleneck of the existing implementation" subsection, with the
  *            combine weight applied to the expert OUTPUT and summed over the
  *            k choices.
+ *  router  - the linear gate before the routing: logits = x W_r^T (no bias),
+ *            and its backward (the router's share of dX and dW_r) for a
+ *            given gradient of the logits.
  *  backward- hand-derived closed form (GPU MODE lecture 32 notes, "Unsloth -
  *            Faster, Lower-Memory LLM Fine-Tuning", section on deriving each
  *            layer's gradient by hand): dX, dA and dB for gate/up/down with
@@ -608,4 +611,61 @@ int orc_lora_grads(const orc_layer_t *L, const int32_t *topk_idx, const double *
         free(rb);
     }
     return err;
+}
+
+/* ------------------------------------------------------------------------
+ * Router projection: the gate that turns each token into its expert logits,
+ * logits[t][e] = sum_i x[t][i] * W_r[e][i] (W_r [E,d], nn.Linear orientation,
+ * no bias). The pages start the MoE layer from a per-token routing decision
+ * over router logits (blog, MoE routing paragraph; wiki chapter,
+ * "Optimisation 3", opening paragraph) without writing the gate out; this is
+ * the plain linear gate. Inputs in the storage dtype, output fp64.
+ * ------------------------------------------------------------------------ */
+int orc_router_fwd(int32_t T, int32_t d, int32_t E, int32_t dtype, const void *x, const void *w_r,
+                   double *logits)
+{
+    if (T < 0 || d < 1 || E < 1)
+        return 1;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i)
+                acc += ld(x, dtype, (size_t)t * d + i) * ld(w_r, dtype, (size_t)e * d + i);
+            logits[(size_t)t * E + e] = acc;
+        }
+    return 0;
+}
+
+/* Backward of the router projection for an upstream gradient d_logits [T,E]
+ * (the layer's gradient with respect to its logits):
+ *   dx_r[t][i] = sum_e d_logits[t][e] * W_r[e][i]   (the router's share of dX)
+ *   dw_r[e][i] = sum_t d_logits[t][e] * x[t][i]
+ * Either output may be NULL. Sums run in ascending e and t. */
+int orc_router_bwd(int32_t T, int32_t d, int32_t E, int32_t dtype, const void *x, const void *w_r,
+                   const double *d_logits, double *dx_r, double *dw_r)
+{
+    if (T < 0 || d < 1 || E < 1)
+        return 1;
+    if (dx_r) {
+#pragma omp parallel for schedule(static)
+        for (int t = 0; t < T; ++t)
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int e = 0; e < E; ++e)
+                    acc += d_logits[(size_t)t * E + e] * ld(w_r, dtype, (size_t)e * d + i);
+                dx_r[(size_t)t * d + i] = acc;
+            }
+    }
+    if (dw_r) {
+#pragma omp parallel for schedule(static)
+        for (int e = 0; e < E; ++e)
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int t = 0; t < T; ++t)
+                    acc += d_logits[(size_t)t * E + e] * ld(x, dtype, (size_t)t * d + i);
+                dw_r[(size_t)e * d + i] = acc;
+            }
+    }
+    return 0;
 }

@@ -26,7 +26,7 @@ _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 TENSOR_IDS = {
     "x": 0, "logits": 1, "w_gate": 2, "w_up": 3, "w_down": 4,
     "a_gate": 5, "b_gate": 6, "a_up": 7, "b_up": 8, "a_down": 9, "b_down": 10,
-    "dout": 11,
+    "dout": 11, "w_router": 12, "d_logits": 13,
 }
 
 
@@ -126,6 +126,17 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, tokens: int | None = None,
     if with_dout:
         out["dout"] = normal(seed, TENSOR_IDS["dout"], 1.0, (T, d), dt)
     return out
+
+
+def make_router(cfg: LayerConfig, seed: int = 0, tokens: int | None = None) -> dict:
+    """Inputs of the router projection in front of the layer: w_router [E,d]
+    in the layer's dtype, with sigma 1 / (sigma_w sqrt(d)) so that x W_r^T has
+    unit variance like the workloads' N(0,1) logits; and a logit gradient
+    d_logits [T,E] float32 ~ N(0,1) for the backward on its own."""
+    T = cfg.T if tokens is None else int(tokens)
+    sr = 1.0 / (cfg.sigma_w * float(np.sqrt(cfg.d)))
+    return {"w_router": normal(seed, TENSOR_IDS["w_router"], sr, (cfg.E, cfg.d), cfg.dtype),
+            "d_logits": normal(seed, TENSOR_IDS["d_logits"], 1.0, (T, cfg.E), "f32")}
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:

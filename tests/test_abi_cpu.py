@@ -149,3 +149,26 @@ def test_binding_raises_on_error():
                                                          "sorted_slot", "slot_row")},
                       stream=0)
     assert ei.value.status == moe.MOE_E_ARG
+
+
+def test_router_workspace_and_argument_errors():
+    p = pb()  # T=512, d=256, E=16
+    Tp = (p.T + 7) // 8 * 8
+    nch0 = min(16, max(1, (p.T + 255) // 256))
+    chunk = ((p.T + nch0 - 1) // nch0 + 31) // 32 * 32
+    nch = (p.T + chunk - 1) // chunk
+    want = al(p.E * Tp * 4) + (al(nch * p.E * p.d * 4) if nch > 1 else 0)
+    assert nch == 2 and moe.router_workspace(p) == want
+    p12 = pb(E=12, k=2)
+    assert moe.router_workspace(p12) == 0
+    L, A = moe.lib(), 1 << 20
+    assert L.moe_router_fwd(ctypes.byref(p12), A, A, A, None, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_router_fwd(ctypes.byref(p), A, None, A, None, None) == moe.MOE_E_ARG
+    assert L.moe_router_fwd(ctypes.byref(p), A + 4, A, A, None, None) == moe.MOE_E_ARG
+    # dx without dx_in; misaligned dw; short workspace for dw
+    assert L.moe_router_bwd(ctypes.byref(p), A, A, A, None, A, None, None, 0, None,
+                            None) == moe.MOE_E_ARG
+    assert L.moe_router_bwd(ctypes.byref(p), A, A, A, None, None, A + 8, A, want, None,
+                            None) == moe.MOE_E_ARG
+    assert L.moe_router_bwd(ctypes.byref(p), A, A, A, None, None, A, A, want - 1, None,
+                            None) == moe.MOE_E_WORKSPACE

@@ -382,3 +382,92 @@ def test_sampled_entry_points_agree_with_full_layer():
     lg = oracle.lora_grads(L, rt, inp["dout"], ex)
     for n in lg:
         assert np.allclose(lg[n], b[n][ex], rtol=1e-12, atol=1e-18)
+
+
+# ---------------------------------------------------------------- router projection
+
+def _route_f64(logits64, k):
+    """Routing of fp64 logits: selection, order and grouping from their fp32
+    rounding (no near-ties in these cases), weights from the fp64 values."""
+    rt = oracle.route(logits64.astype(np.float32), k)
+    sel = np.take_along_axis(logits64, rt["topk_idx"].astype(np.int64), axis=1)
+    w = np.exp(sel - sel[:, :1])
+    rt["topk_w"] = w / w.sum(1, keepdims=True)
+    return rt
+
+
+def test_router_identity_gate_passes_x_through():
+    rng = np.random.default_rng(3)
+    x = rng.normal(0.0, 1.0, (5, 8))
+    assert np.array_equal(oracle.router_fwd(x, np.eye(8)), x)
+    # one-hot rows pick columns: logits[:, e] = x[:, perm[e]]
+    perm = rng.permutation(8)
+    assert np.array_equal(oracle.router_fwd(x, np.eye(8)[perm]), x[:, perm])
+
+
+def test_router_storage_formats_agree():
+    rng = np.random.default_rng(4)
+    xb = synth.f32_to_bf16(rng.normal(0.0, 1.0, (6, 16)).astype(np.float32))
+    wb = synth.f32_to_bf16(rng.normal(0.0, 1.0, (8, 16)).astype(np.float32))
+    x64, w64 = synth.to_f64(xb, "bf16"), synth.to_f64(wb, "bf16")
+    assert np.array_equal(oracle.router_fwd(xb, wb), oracle.router_fwd(x64, w64))
+    dl = rng.normal(0.0, 1.0, (6, 8))
+    a, b = oracle.router_bwd(xb, wb, dl), oracle.router_bwd(x64, w64, dl)
+    assert np.array_equal(a["dx"], b["dx"]) and np.array_equal(a["dw_r"], b["dw_r"])
+
+
+@pytest.fixture(scope="module")
+def router_fd_case():
+    T, d, E, k, F, r = FD_SHAPE
+    L, t, _, dout = make(T, d, E, k, F, r, s=1.3, seed=11)
+    rng = np.random.default_rng(12)
+    w_r = rng.normal(0.0, 0.7, (E, d))
+    rt = _route_f64(oracle.router_fwd(t["x"], w_r), k)
+    g = oracle.bwd(L, rt, dout)
+    rg = oracle.router_bwd(t["x"], w_r, g["d_logits"])
+    return T, d, E, k, F, r, t, w_r, dout, rt, g, rg
+
+
+def _chain_loss(shape, t, w_r, dout, idx):
+    """Loss of the layer with its router: logits = x W_r^T feed the routing."""
+    T, d, E, k, F, r = shape
+    rt = _route_f64(oracle.router_fwd(t["x"], w_r), k)
+    assert np.array_equal(rt["topk_idx"], idx)  # a small step keeps the selection
+    return _loss(oracle.Layer(T, d, E, k, F, r, 1.3, "f64", t), rt, dout)
+
+
+def test_router_chain_dx_matches_central_differences(router_fd_case):
+    """dX of the whole layer = the expert path's dX + the router's share."""
+    T, d, E, k, F, r, t, w_r, dout, rt, g, rg = router_fd_case
+    h = 1e-6
+    fd = np.empty(T * d)
+    for i in range(T * d):
+        vals = []
+        for sign in (+1, -1):
+            tt = dict(t)
+            p = t["x"].copy().reshape(-1)
+            p[i] += sign * h
+            tt["x"] = p.reshape(T, d)
+            vals.append(_chain_loss(FD_SHAPE, tt, w_r, dout, rt["topk_idx"]))
+        fd[i] = (vals[0] - vals[1]) / (2 * h)
+    ana = (g["dx"] + rg["dx"]).reshape(-1)
+    assert np.max(np.abs(fd - ana)) <= 1e-7 * max(1.0, np.max(np.abs(ana)))
+    # the router's share is not negligible here, so a dropped term would fail
+    assert np.max(np.abs(rg["dx"])) > 1e-3 * np.max(np.abs(ana))
+
+
+def test_router_weight_gradient_chain_matches_central_differences(router_fd_case):
+    T, d, E, k, F, r, t, w_r, dout, rt, g, rg = router_fd_case
+    h = 1e-6
+    fd = np.empty(E * d)
+    for i in range(E * d):
+        vals = []
+        for sign in (+1, -1):
+            p = w_r.copy().reshape(-1)
+            p[i] += sign * h
+            vals.append(_chain_loss(FD_SHAPE, t, p.reshape(E, d), dout, rt["topk_idx"]))
+        fd[i] = (vals[0] - vals[1]) / (2 * h)
+    ana = rg["dw_r"].reshape(-1)
+    assert np.max(np.abs(fd - ana)) <= 1e-7 * max(1.0, np.max(np.abs(ana)))
+    # logit gradients sum to zero per token, so the columns of dW_r sum to zero
+    assert np.allclose(rg["dw_r"].sum(0), 0.0, atol=1e-12)
