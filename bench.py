@@ -203,6 +203,51 @@ def whereloop_baseline(torch, cfg, x, logits, w, dout, steps, warmup=1):
     return sum(fwd_ms) / steps, sum(bwd_ms) / steps, out.detach()
 
 
+def router_bench(torch, moe, synth, cfg, pb, x, hip, dev, iters=20):
+    """The router projection in front of the layer (logits = x W_r^T) and its
+    backward (dx += d_logits W_r; dW_r = d_logits^T x), timed with events on
+    its own: ms per call and TF/s (2 T d E flops per product)."""
+    import numpy as np
+    ri = synth.make_router(cfg, seed=0)
+    w_r = torch.from_numpy(ri["w_router"].view(np.int16)).to(dev).view(torch.bfloat16)
+    dl = torch.from_numpy(ri["d_logits"]).to(dev)
+    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    dxr = torch.zeros((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((cfg.E, cfg.d), dtype=torch.float32, device=dev)
+    ws = moe.alloc_bytes(moe.router_workspace(pb), dev)
+    names = ("router_logits", "router_dx", "router_dw")
+    traces = []
+    for _ in range(iters):
+        tr = moe.Trace()
+        for n in names:
+            k = moe.KERNELS.index(n)
+            tr.start[k], tr.stop[k] = hip.event(), hip.event()
+        traces.append(tr)
+    stream = torch.cuda.current_stream()
+    for it in range(3 + iters):
+        tr = traces[it - 3] if it >= 3 else None
+        moe.moe_router_fwd(pb, x, w_r, logits, stream=stream, trace=tr)
+        moe.moe_router_bwd(pb, x, w_r, dl, dx_in=dxr, dx=dxr, dw_router=dw, ws=ws, stream=stream,
+                           trace=tr)
+    torch.cuda.synchronize()
+    ms = {}
+    for n in names:
+        k = moe.KERNELS.index(n)
+        ms[n] = sum(hip.elapsed_ms(tr.start[k], tr.stop[k]) for tr in traces) / iters
+    for tr in traces:
+        for n in names:
+            k = moe.KERNELS.index(n)
+            hip.destroy(tr.start[k])
+            hip.destroy(tr.stop[k])
+    f_ms, b_ms = ms["router_logits"], ms["router_dx"] + ms["router_dw"]
+    fl = 2.0 * cfg.T * cfg.d * cfg.E
+    return {"fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "kernels_ms": {n: round(v, 4) for n, v in ms.items()},
+            "fwd_tflops": round(fl / (f_ms * 1e-3) / 1e12, 1),
+            "bwd_tflops": round(2 * fl / (b_ms * 1e-3) / 1e12, 1),
+            "note": "not part of the step: the workloads take logits as an input"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,7 +338,8 @@ def main():
     timed_traces = [make_trace(gemm_kernels) for _ in range(args.steps)]
     all_names = [n for n in moe.KERNELS
                  if (cfg.backward or moe.KERNELS.index(n) < moe.KERNELS.index("router_grad"))
-                 and (n != "router_grad" or keep)]
+                 and (n != "router_grad" or keep)
+                 and n not in ("router_logits", "router_dx", "router_dw")]  # not in the step
     n_breakdown = min(args.steps, 10)
     full_traces = [make_trace(all_names) for _ in range(n_breakdown)]
 
@@ -368,6 +414,8 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
         "input_setup_s": round(t_gen, 2),
     }
+    if cfg.dtype == "bf16":
+        rec["router_projection"] = router_bench(torch, moe, synth, cfg, pb, x, hip, dev)
     if args.whereloop_steps > 0 and cfg.dtype == "bf16":
         # the library's forward and backward alone (routing excluded), to set
         # against the loop's

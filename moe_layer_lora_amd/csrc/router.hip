@@ -6,7 +6,8 @@
 // MoE training", opening paragraph); this is the plain linear gate.
 //
 // All three products run on the register-staged MFMA tile engine
-// (gemm.hpp), 128 x 128 tiles of 4 waves, fp32 accumulation:
+// (gemm.hpp), tiles of 4 waves (64 x 64 for the logits, else 128 x 128),
+// fp32 accumulation:
 //   logits [T,E]   = x [T,d] . W_r[E,d]^T          (both K-contiguous)
 //   dx     [T,d]   = dx_in + d_logits [T,E] . W_r  (d_logits fp32, rounded
 //                    to the storage type as it is staged; W_r N-contiguous)
@@ -22,6 +23,8 @@ namespace moe {
 namespace {
 
 template <typename T> struct RouterCfg { using type = GemmCfg<T, 128, 128, 32, 2, 2>; };
+// the logits have only E columns: 64 x 64 tiles give 4x the blocks of 128 x 128
+template <typename T> struct LogitsCfg { using type = GemmCfg<T, 64, 64, 32, 2, 2>; };
 
 template <class Cfg> struct RSmem {
     __align__(16) typename Cfg::T a[2 * Cfg::A_ELEMS];
@@ -201,7 +204,7 @@ RouterWs router_ws(const Dims &D) {
 template <typename T>
 hipError_t run_router_fwd(const Dims &D, const void *x, const void *wr, float *logits, hipStream_t st,
                           const Trace *tr) {
-    using Cfg = typename RouterCfg<T>::type;
+    using Cfg = typename LogitsCfg<T>::type;
     if (D.T == 0) return hipSuccess;
     RouterP p{};
     p.x = x; p.wr = wr; p.logits = logits; p.T = D.T; p.d = D.d; p.E = D.E;
