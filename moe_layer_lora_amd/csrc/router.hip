@@ -99,14 +99,38 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_router_dx(RouterP p) {
     lb.s1 = lb.s0;
     f32x16_t acc[Cfg::TM][Cfg::TN];
     gemm_mainloop<Cfg>(la, lb, cdiv(p.E, Cfg::BK), sm.a, sm.b, acc);
+    // Epilogue through LDS (the tiles are dead after the loop's last barrier):
+    // each wave parks 32 rows x WTN fp32 of its sub-tile, then every lane adds
+    // VEC consecutive columns of one row to dx_in with 16-byte accesses.
+    constexpr int VEC = Cfg::VEC, WTN = Cfg::WTN, LPR = WTN / VEC, RPP = 64 / LPR;
+    static_assert(32 * WTN * 4 * Cfg::WM * Cfg::WN <= (int)sizeof(RSmem<Cfg>), "staging fits the tiles");
+    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    float *buf = reinterpret_cast<float *>(&sm) + wave * 32 * WTN;
     const T *dxi = static_cast<const T *>(p.dx_in);
     T *dxo = static_cast<T *>(p.dx);
-    for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
-        if (m0 + m < p.T && n0 + n < p.d) {
-            const size_t o = (size_t)(m0 + m) * p.d + n0 + n;
-            dxo[o] = Elem<T>::from_f32(Elem<T>::to_f32(dxi[o]) + v);
+#pragma unroll
+    for (int mi = 0; mi < Cfg::TM; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < Cfg::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) buf[acc_row(i, lane) * WTN + ni * 32 + acc_col(lane)] = acc[mi][ni][i];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int pass = 0; pass < 32 / RPP; ++pass) {
+            const int r = pass * RPP + lane / LPR, c = (lane % LPR) * VEC;
+            const int m = m0 + wm * Cfg::WTM + mi * 32 + r, n = n0 + wn * WTN + c;
+            if (m < p.T && n < p.d) {  // d is a multiple of 8: the whole chunk is inside
+                const size_t o = (size_t)m * p.d + n;
+                float a[VEC];
+                unpack<T>(*reinterpret_cast<const chunk_t *>(dxi + o), a);
+#pragma unroll
+                for (int h = 0; h < VEC; ++h) a[h] += buf[r * WTN + c + h];
+                *reinterpret_cast<chunk_t *>(dxo + o) = Elem<T>::pack(a);
+            }
         }
-    });
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next slab
+    }
 }
 
 // dlT[e][t] = d_logits[t][e] for t < T, 0 for T <= t < Tp; 32 x 32 tiles
