@@ -217,7 +217,7 @@ struct Scope {  // event pair around one launch, if asked for
 RouterWs router_ws(const Dims &D) {
     RouterWs w{};
     w.Tp = (D.T + 7) & ~7;
-    const int nch0 = D.T > 0 ? min(16, max(1, (D.T + 255) / 256)) : 1;
+    const int nch0 = D.T > 0 ? min(32, max(1, (D.T + 255) / 256)) : 1;
     w.chunk = D.T > 0 ? ((D.T + nch0 - 1) / nch0 + 31) & ~31 : 32;
     w.nch = D.T > 0 ? (D.T + w.chunk - 1) / w.chunk : 1;
     w.dlT_bytes = (size_t)D.E * w.Tp * sizeof(float);

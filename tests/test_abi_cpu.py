@@ -154,7 +154,7 @@ def test_binding_raises_on_error():
 def test_router_workspace_and_argument_errors():
     p = pb()  # T=512, d=256, E=16
     Tp = (p.T + 7) // 8 * 8
-    nch0 = min(16, max(1, (p.T + 255) // 256))
+    nch0 = min(32, max(1, (p.T + 255) // 256))
     chunk = ((p.T + nch0 - 1) // nch0 + 31) // 32 * 32
     nch = (p.T + chunk - 1) // chunk
     want = al(p.E * Tp * 4) + (al(nch * p.E * p.d * 4) if nch > 1 else 0)
