@@ -516,6 +516,7 @@ template <class C>
 struct LoraA {
     static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
     static constexpr int PER = C::BM * 4 / C::NTHREADS;
+    static_assert(C::BM * 4 % C::NTHREADS == 0, "whole 16-byte chunks per thread");
     const float *z;
     int nz, row0, rows;
     float s;
@@ -554,6 +555,7 @@ template <class C>
 struct LoraBK {
     static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
     static constexpr int PER = C::BN * 4 / C::NTHREADS;
+    static_assert(C::BN * 4 % C::NTHREADS == 0, "whole 16-byte chunks per thread");
     const bf16_t *rowp[PER];  // row start (element k = klo), nullptr outside
     int klo[PER];
     int r;
@@ -585,6 +587,7 @@ template <class C>
 struct LoraBN {
     static_assert(C::BK == 32, "LoRA tiles use 32-deep steps");
     static constexpr int PER = 32 * C::BN / 8 / C::NTHREADS;
+    static_assert(32 * C::BN / 8 % C::NTHREADS == 0, "whole 16-byte chunks per thread");
     const bf16_t *a, *b;
     int split, K, ld, ncol;
     struct Regs { chunk_t v[PER]; uint32_t ok; };
