@@ -132,3 +132,17 @@ def test_router_full_size_sampled(name):
                            np.ascontiguousarray(dl[:, ex]).astype(np.float64))
     assert lr.rel_l2(g["dw"][ex], re["dw_r"]) <= tol
     assert np.all(np.isfinite(g["dw"]))
+
+
+def test_router_empty_batch_writes_zero_weight_gradient():
+    import moe_layer_lora_amd as moe
+    cfg = LayerConfig("router_empty", T=0, d=64, E=16, k=2, F=64, r=8, dtype="bf16", alpha=16.0)
+    pb = moe.Problem.from_config(cfg)
+    dev = torch.device("cuda")
+    w_r = torch.zeros((cfg.E, cfg.d), dtype=torch.bfloat16, device=dev)
+    dw = torch.full((cfg.E, cfg.d), float("nan"), dtype=torch.float32, device=dev)
+    ws = moe.alloc_bytes(moe.router_workspace(pb), dev)
+    moe.moe_router_fwd(pb, None, w_r, None)
+    moe.moe_router_bwd(pb, None, w_r, None, dw_router=dw, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0.0)
