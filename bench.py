@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--offload-reps", type=int, default=3,
+                    help="repetitions of the saved-activation offload measurement (0 = skip)")
     ap.add_argument("--whereloop-steps", type=int, default=3,
                     help="steps of the per-expert where() loop baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -248,6 +250,45 @@ def router_bench(torch, moe, synth, cfg, pb, x, hip, dev, iters=20):
             "note": "not part of the step: the workloads take logits as an input"}
 
 
+def offload_bench(torch, moe, pb, saved, keep, fwd, reps=3):
+    """moe_saved_copy of this layer's `saved` buffer to pinned host memory and
+    back on a copy stream: bandwidth of each direction, and the forward's time
+    alone and while an offload runs beside it (the double-buffered checkpoint
+    reload overlaps these copies with compute)."""
+    n = moe.saved_bytes(pb, keep)
+    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    copy = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        best = float("inf")
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            best = min(best, time.perf_counter() - t0)
+        return best
+
+    d2h = timed(lambda: moe.moe_saved_copy(pb, keep, False, saved, host, copy_stream=copy))
+    h2d = timed(lambda: moe.moe_saved_copy(pb, keep, True, saved, host, copy_stream=copy))
+    f_alone = timed(fwd)
+    ev_start, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f_during = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        moe.moe_saved_copy(pb, keep, False, saved, host, copy_stream=copy)
+        ev_start.record()
+        fwd()
+        ev_end.record()
+        torch.cuda.synchronize()
+        f_during.append(ev_start.elapsed_time(ev_end))
+    return {"bytes": n, "d2h_GBs": round(n / d2h / 1e9, 1), "h2d_GBs": round(n / h2d / 1e9, 1),
+            "fwd_ms": round(f_alone * 1e3, 3), "fwd_ms_during_offload": round(min(f_during), 3),
+            "offload_ms": round(d2h * 1e3, 3),
+            "note": "pinned host buffer, one copy stream; not part of the step"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -416,6 +457,11 @@ def main():
     }
     if cfg.dtype == "bf16":
         rec["router_projection"] = router_bench(torch, moe, synth, cfg, pb, x, hip, dev)
+    if cfg.backward and args.offload_reps > 0:
+        rec["saved_offload"] = offload_bench(
+            torch, moe, pb, saved, keep,
+            lambda: moe.moe_fwd(pb, x, rt, w, out, saved=saved, keep_expert_out=keep, ws=ws_f,
+                                stream=stream), args.offload_reps)
     if args.whereloop_steps > 0 and cfg.dtype == "bf16":
         # the library's forward and backward alone (routing excluded), to set
         # against the loop's

@@ -202,6 +202,24 @@ moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *
                             const void *dx_in, void *dx, float *dw_router, void *ws, size_t ws_bytes,
                             void *stream, const moe_trace_t *trace);
 
+/* Offload and reload of `saved` between moe_fwd and moe_bwd: the
+ * double-buffered checkpoint reload of the Unsloth x NVIDIA blog (section
+ * "core idea / structure / how it works", checkpoint paragraph) keeps
+ * activations in pinned host memory and brings them back for the backward on
+ * a copy stream, two device buffers taking turns so that the backward of one
+ * layer reads buffer A while the next layer's activations arrive in B.
+ * moe_saved_copy copies the moe_saved_bytes(pb, keep_expert_out) bytes of one
+ * `saved` buffer to (to_device = 0) or from (to_device = 1) `host`, on
+ * `copy_stream`, after `wait_event` (a hipEvent_t the caller recorded on its
+ * compute stream, e.g. after moe_fwd, or before the backward that last read
+ * the device buffer; NULL: no wait), and records `done_event` on copy_stream
+ * after the copy (NULL: none); the compute stream waits on that event before
+ * moe_bwd reads the buffer. `host` must be pinned (page-locked, e.g.
+ * hipHostMalloc): pageable memory would make the copy synchronous, so it is
+ * rejected (MOE_E_ARG). The bytes are copied unchanged. */
+moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to_device, void *saved,
+                            void *host, void *wait_event, void *copy_stream, void *done_event);
+
 /* Static string naming a status code. */
 const char *moe_status_str(moe_status_t st);
 

@@ -38,7 +38,7 @@ MOE_K_COUNT = len(KERNELS)
 
 EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe_saved_bytes",
            "moe_route", "moe_fwd", "moe_bwd", "moe_status_str", "moe_router_workspace",
-           "moe_router_fwd", "moe_router_bwd"]
+           "moe_router_fwd", "moe_router_bwd", "moe_saved_copy"]
 
 
 class Problem(ctypes.Structure):
@@ -99,7 +99,9 @@ _lib.moe_router_workspace.argtypes = [_P(Problem)]
 _lib.moe_router_workspace.restype = _sz
 _lib.moe_router_fwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _P(Trace)]
 _lib.moe_router_bwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _P(Trace)]
-for _f in (_lib.moe_route, _lib.moe_fwd, _lib.moe_bwd, _lib.moe_router_fwd, _lib.moe_router_bwd):
+_lib.moe_saved_copy.argtypes = [_P(Problem), _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+for _f in (_lib.moe_route, _lib.moe_fwd, _lib.moe_bwd, _lib.moe_router_fwd, _lib.moe_router_bwd,
+           _lib.moe_saved_copy):
     _f.restype = _i32
 _lib.moe_status_str.argtypes = [_i32]
 _lib.moe_status_str.restype = ctypes.c_char_p
@@ -216,6 +218,21 @@ def moe_router_bwd(pb, x, w_router, d_logits, dx_in=None, dx=None, dw_router=Non
                              _ptr(dx), _ptr(dw_router), _ptr(ws), _nbytes(ws), _stream(stream),
                              ctypes.byref(trace) if trace is not None else None)
     _check(st, "moe_router_bwd")
+
+
+def moe_saved_copy(pb, keep_expert_out, to_device, saved, host, wait_event=None, copy_stream=None,
+                   done_event=None):
+    """Copy a `saved` buffer to (to_device=False) or from a pinned host tensor
+    on copy_stream, after wait_event (a torch.cuda.Event or raw hipEvent_t);
+    records done_event on copy_stream."""
+    def ev(e):
+        if e is None or isinstance(e, int):
+            return e
+        return e.cuda_event
+    hp = host.data_ptr() if hasattr(host, "data_ptr") else host
+    st = _lib.moe_saved_copy(ctypes.byref(pb), int(keep_expert_out), int(to_device), _ptr(saved), hp,
+                             ev(wait_event), _stream(copy_stream), ev(done_event))
+    _check(st, "moe_saved_copy")
 
 
 # ---------------------------------------------------------------- allocation helpers

@@ -371,4 +371,26 @@ moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *
     return e == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
+moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to_device, void *saved, void *host,
+                            void *wait_event, void *copy_stream, void *done_event) {
+    moe_status_t st = check_problem(pb);
+    if (st != MOE_OK) return st;
+    if (!buf_ok(saved) || !host) return MOE_E_ARG;
+    hipPointerAttribute_t pa{};
+    if (hipPointerGetAttributes(&pa, host) != hipSuccess) {
+        (void)hipGetLastError();  // pageable memory: not an error to leave for the next call
+        return MOE_E_ARG;
+    }
+    if (pa.type != hipMemoryTypeHost) return MOE_E_ARG;
+    const size_t n = saved_layout(pb, keep_expert_out != 0).total;
+    hipStream_t cs = static_cast<hipStream_t>(copy_stream);
+    if (wait_event && hipStreamWaitEvent(cs, static_cast<hipEvent_t>(wait_event), 0) != hipSuccess)
+        return MOE_E_HIP;
+    const hipError_t e = to_device ? hipMemcpyAsync(saved, host, n, hipMemcpyHostToDevice, cs)
+                                   : hipMemcpyAsync(host, saved, n, hipMemcpyDeviceToHost, cs);
+    if (e != hipSuccess) return MOE_E_HIP;
+    if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), cs) != hipSuccess) return MOE_E_HIP;
+    return MOE_OK;
+}
+
 }  // extern "C"

@@ -172,3 +172,11 @@ def test_router_workspace_and_argument_errors():
                             None) == moe.MOE_E_ARG
     assert L.moe_router_bwd(ctypes.byref(p), A, A, A, None, None, A, A, want - 1, None,
                             None) == moe.MOE_E_WORKSPACE
+
+
+def test_saved_copy_argument_errors_before_any_call():
+    p, L, A = pb(), moe.lib(), 1 << 20
+    assert L.moe_saved_copy(ctypes.byref(p), 0, 0, A, None, None, None, None) == moe.MOE_E_ARG
+    assert L.moe_saved_copy(ctypes.byref(p), 0, 0, None, A, None, None, None) == moe.MOE_E_ARG
+    assert L.moe_saved_copy(ctypes.byref(p), 0, 0, A + 8, A, None, None, None) == moe.MOE_E_ARG
+    assert L.moe_saved_copy(ctypes.byref(pb(k=0)), 0, 0, A, A, None, None, None) == moe.MOE_E_ARG
