@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--no-nf4", dest="nf4", action="store_false",
+                    help="skip the 4-bit weight dequantisation measurement")
     ap.add_argument("--offload-reps", type=int, default=3,
                     help="repetitions of the saved-activation offload measurement (0 = skip)")
     ap.add_argument("--whereloop-steps", type=int, default=3,
@@ -289,6 +291,39 @@ def offload_bench(torch, moe, pb, saved, keep, fwd, reps=3):
             "note": "pinned host buffer, one copy stream; not part of the step"}
 
 
+def nf4_bench(torch, moe, synth, cfg, dev, reps=5):
+    """Dequantisation of 4-bit NormalFloat frozen weights (W_g, W_u, W_d of the
+    layer) to bf16: ms for all three and the HBM rate (code + scale bytes read,
+    bf16 bytes written)."""
+    import numpy as np
+    mats = [(cfg.E * cfg.F, cfg.d, 20), (cfg.E * cfg.F, cfg.d, 21), (cfg.E * cfg.d, cfg.F, 22)]
+    if any(c % 64 for _, c, _ in mats):
+        return None
+    bufs = []
+    for rows, cols, tau in mats:
+        q = synth.make_nf4(rows, cols, seed=0, tensor=tau)
+        bufs.append((torch.from_numpy(q["codes"]).to(dev), torch.from_numpy(q["scales"]).to(dev),
+                     torch.empty((rows, cols), dtype=torch.bfloat16, device=dev), rows, cols))
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for c, s, o, rows, cols in bufs:
+            moe.moe_nf4_dequant(c, s, rows, cols, o, stream=stream)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = sum(c.numel() + s.numel() * 4 + o.numel() * 2 for c, s, o, _, _ in bufs)
+    return {"ms": round(ms, 4), "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": int(nbytes),
+            "weights": int(sum(r * c for _, _, _, r, c in bufs)),
+            "note": "W_g, W_u, W_d from 4-bit NormalFloat to bf16; not part of the step"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -457,6 +492,8 @@ def main():
     }
     if cfg.dtype == "bf16":
         rec["router_projection"] = router_bench(torch, moe, synth, cfg, pb, x, hip, dev)
+    if cfg.dtype == "bf16" and args.nf4:
+        rec["nf4_dequant"] = nf4_bench(torch, moe, synth, cfg, dev)
     if cfg.backward and args.offload_reps > 0:
         rec["saved_offload"] = offload_bench(
             torch, moe, pb, saved, keep,

@@ -220,6 +220,25 @@ moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *
 moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to_device, void *saved,
                             void *host, void *wait_event, void *copy_stream, void *done_event);
 
+/* 4-bit NormalFloat (NF4) frozen base weights, the 4-bit QLoRA variant the
+ * pages name for MoE fine-tuning (Unsloth 2026 wiki chapter, model-support
+ * table; GPU MODE lecture 32 notes, QLoRA part), dequantised to bf16 so that
+ * moe_fwd / moe_bwd run on them unchanged (the frozen weights stay 4-bit in
+ * memory; one projection's bf16 copy lives in a scratch buffer for the pass).
+ * Format (the QLoRA paper's NormalFloat code): 16 levels, quantiles of
+ * N(0,1) with an exact zero, scaled into [-1, 1] (level 0 = -1, level 7 = 0,
+ * level 15 = +1); weight = level[code] * scale, one float32 scale per 64
+ * consecutive weights of a row.
+ *   codes  [rows, cols/2] uint8: element 2i of a row in the low nibble of
+ *          byte i, element 2i+1 in the high nibble (16-byte aligned)
+ *   scales [rows, cols/64] float32
+ *   out    [rows, cols] bf16 (16-byte aligned)
+ * Requires cols to be a positive multiple of 64 and rows >= 0 (else
+ * MOE_E_ARG / MOE_E_UNSUPPORTED). For a stacked weight [E, out, in], rows =
+ * E * out and cols = in. */
+moe_status_t moe_nf4_dequant(const uint8_t *codes, const float *scales, int64_t rows, int32_t cols, void *out,
+                             void *stream);
+
 /* Static string naming a status code. */
 const char *moe_status_str(moe_status_t st);
 

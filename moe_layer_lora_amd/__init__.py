@@ -38,7 +38,7 @@ MOE_K_COUNT = len(KERNELS)
 
 EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe_saved_bytes",
            "moe_route", "moe_fwd", "moe_bwd", "moe_status_str", "moe_router_workspace",
-           "moe_router_fwd", "moe_router_bwd", "moe_saved_copy"]
+           "moe_router_fwd", "moe_router_bwd", "moe_saved_copy", "moe_nf4_dequant"]
 
 
 class Problem(ctypes.Structure):
@@ -100,6 +100,8 @@ _lib.moe_router_workspace.restype = _sz
 _lib.moe_router_fwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _P(Trace)]
 _lib.moe_router_bwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _P(Trace)]
 _lib.moe_saved_copy.argtypes = [_P(Problem), _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_nf4_dequant.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]
+_lib.moe_nf4_dequant.restype = _i32
 for _f in (_lib.moe_route, _lib.moe_fwd, _lib.moe_bwd, _lib.moe_router_fwd, _lib.moe_router_bwd,
            _lib.moe_saved_copy):
     _f.restype = _i32
@@ -233,6 +235,14 @@ def moe_saved_copy(pb, keep_expert_out, to_device, saved, host, wait_event=None,
     st = _lib.moe_saved_copy(ctypes.byref(pb), int(keep_expert_out), int(to_device), _ptr(saved), hp,
                              ev(wait_event), _stream(copy_stream), ev(done_event))
     _check(st, "moe_saved_copy")
+
+
+def moe_nf4_dequant(codes, scales, rows, cols, out, stream=None):
+    """bf16 out [rows, cols] = NF4 level[code] * scale (codes [rows, cols/2]
+    uint8, low nibble first; scales [rows, cols/64] fp32)."""
+    st = _lib.moe_nf4_dequant(_ptr(codes), _ptr(scales), int(rows), int(cols), _ptr(out),
+                              _stream(stream))
+    _check(st, "moe_nf4_dequant")
 
 
 # ---------------------------------------------------------------- allocation helpers

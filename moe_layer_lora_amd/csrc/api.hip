@@ -393,4 +393,16 @@ moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to
     return MOE_OK;
 }
 
+moe_status_t moe_nf4_dequant(const uint8_t *codes, const float *scales, int64_t rows, int32_t cols, void *out,
+                             void *stream) {
+    if (rows < 0 || cols <= 0) return MOE_E_ARG;
+    if (cols % 64) return MOE_E_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!codes || ((uintptr_t)codes & 15u) || !scales || ((uintptr_t)scales & 3u) || !buf_ok(out)) return MOE_E_ARG;
+    if (rows > (int64_t(1) << 40) / cols) return MOE_E_UNSUPPORTED;
+    const hipError_t e = moe::run_nf4_dequant(codes, scales, rows, cols, static_cast<moe::bf16_t *>(out),
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
 }  // extern "C"

@@ -96,6 +96,10 @@ template <typename T>
 hipError_t run_router_bwd(const Dims &D, const void *x, const void *wr, const float *d_logits, const void *dx_in,
                           void *dx, float *dw, void *dlT, void *partial, hipStream_t st, const Trace *tr);
 
+// ---- 4-bit NormalFloat frozen weights -> bf16 ---------------------------------
+hipError_t run_nf4_dequant(const uint8_t *codes, const float *scales, int64_t rows, int cols, bf16_t *out,
+                           hipStream_t st);
+
 // bytes of LoRA-gradient partial sums the backward may need
 size_t lora_grad_partial_bytes(const Dims &D);
 // leading dimension of the transposed bf16 LoRA-gradient operands [nr, ldT]

@@ -139,6 +139,18 @@ def make_router(cfg: LayerConfig, seed: int = 0, tokens: int | None = None) -> d
             "d_logits": normal(seed, TENSOR_IDS["d_logits"], 1.0, (T, cfg.E), "f32")}
 
 
+def make_nf4(rows: int, cols: int, seed: int = 0, tensor: int = 20, sigma: float = 0.02) -> dict:
+    """A 4-bit NormalFloat weight [rows, cols] (cols a multiple of 64) as stored:
+    uniform random codes packed two per byte ({"codes": [rows, cols/2] uint8})
+    and one positive scale per 64 weights ({"scales": [rows, cols/64] float32})
+    drawn as sigma * 1.9 * (0.5 + u), u uniform in [0, 1), so the weights'
+    standard deviation is about sigma (uniform codes give level RMS ~ 0.53)."""
+    rng = np.random.default_rng([seed, tensor])
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = (sigma * 1.9 * (0.5 + rng.random((rows, cols // 64)))).astype(np.float32)
+    return {"codes": codes, "scales": scales}
+
+
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     """Exact upcast of a stored tensor (float32, or bf16 bits) to float64."""
     if dtype == "bf16" and a.dtype == np.uint16:

@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -180,3 +180,14 @@ def test_saved_copy_argument_errors_before_any_call():
     assert L.moe_saved_copy(ctypes.byref(p), 0, 0, None, A, None, None, None) == moe.MOE_E_ARG
     assert L.moe_saved_copy(ctypes.byref(p), 0, 0, A + 8, A, None, None, None) == moe.MOE_E_ARG
     assert L.moe_saved_copy(ctypes.byref(pb(k=0)), 0, 0, A, A, None, None, None) == moe.MOE_E_ARG
+
+
+def test_nf4_dequant_argument_errors_before_launch():
+    L, A = moe.lib(), 1 << 20
+    assert L.moe_nf4_dequant(A, A, -1, 64, A, None) == moe.MOE_E_ARG
+    assert L.moe_nf4_dequant(A, A, 4, 0, A, None) == moe.MOE_E_ARG
+    assert L.moe_nf4_dequant(A, A, 4, 100, A, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_nf4_dequant(A + 4, A, 4, 64, A, None) == moe.MOE_E_ARG     # codes 16-byte aligned
+    assert L.moe_nf4_dequant(A, A + 2, 4, 64, A, None) == moe.MOE_E_ARG     # scales 4-byte aligned
+    assert L.moe_nf4_dequant(A, A, 4, 64, A + 8, None) == moe.MOE_E_ARG     # out 16-byte aligned
+    assert L.moe_nf4_dequant(None, None, 0, 64, None, None) == moe.MOE_OK   # nothing to do

@@ -1,0 +1,98 @@
+"""4-bit NormalFloat frozen weights on the GPU (moe_nf4_dequant) against the
+oracle's fp64 dequantisation, and the whole layer run on dequantised weights
+against the oracle layer on the same weights. Dequantised weights are bf16:
+each element within one bf16 rounding of the oracle's value."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from oracle import nf4  # noqa: E402
+from synth.configs import LayerConfig  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _dequant_gpu(codes, scales, rows, cols):
+    import layer_runner as lr
+    import moe_layer_lora_amd as moe
+    out = torch.full((rows, cols), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_nf4_dequant(lr.to_dev(codes), lr.to_dev(scales), rows, cols, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def _within_one_bf16_rounding(got, want):
+    # |got - want| <= half a bf16 ulp of want (plus the fp32 product's rounding)
+    tol = np.abs(want) * 2.0 ** -8 * 1.0001 + 1e-30
+    return np.all(np.abs(got - want) <= tol)
+
+
+def test_nf4_codebook_on_gpu():
+    import layer_runner as lr
+    codes = np.array([[(2 * i) | ((2 * i + 1) << 4) for i in range(8)] * 4], dtype=np.uint8)  # 0..15, x4
+    scales = np.ones((1, 1), np.float32)
+    got = lr.to_f64(_dequant_gpu(codes, scales, 1, 64))[0]
+    want = np.tile(nf4.levels(), 4)
+    assert _within_one_bf16_rounding(got, want)
+    assert got[7] == 0.0 and got[0] == -1.0 and got[15] == 1.0
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (300, 192), (7, 2880)])
+def test_nf4_dequant_matches_oracle(rows, cols):
+    import layer_runner as lr
+    q = synth.make_nf4(rows, cols, seed=1)
+    got = lr.to_f64(_dequant_gpu(q["codes"], q["scales"], rows, cols))
+    want = nf4.dequant(q["codes"], q["scales"], cols)
+    assert _within_one_bf16_rounding(got, want)
+
+
+def test_layer_on_nf4_weights_matches_oracle():
+    """x, A, B in bf16, W_g / W_u / W_d in NF4: dequantise on the GPU, run the
+    layer; the oracle runs on its own dequantisation rounded to bf16."""
+    import layer_runner as lr
+    cfg = LayerConfig("nf4_bf16", T=300, d=128, E=6, k=3, F=192, r=16, dtype="bf16", alpha=32.0,
+                      router_grad=True)
+    inp = synth.make_inputs(cfg, seed=0)
+    q = {"w_gate": synth.make_nf4(cfg.E * cfg.F, cfg.d, seed=0, tensor=20),
+         "w_up": synth.make_nf4(cfg.E * cfg.F, cfg.d, seed=0, tensor=21),
+         "w_down": synth.make_nf4(cfg.E * cfg.d, cfg.F, seed=0, tensor=22)}
+    shapes = {"w_gate": (cfg.E, cfg.F, cfg.d), "w_up": (cfg.E, cfg.F, cfg.d),
+              "w_down": (cfg.E, cfg.d, cfg.F)}
+    L = lr.Layer(cfg, inp, keep_expert_out=True)
+    for n, qq in q.items():
+        rows, cols = shapes[n][0] * shapes[n][1], shapes[n][2]
+        L.w[n].copy_(_dequant_gpu(qq["codes"], qq["scales"], rows, cols).view(*shapes[n]))
+    L.step(backward=True, router_grad=True)
+    r = L.results(backward=True, router_grad=True)
+    # oracle: every tensor in fp64; W from its own dequantisation rounded to bf16
+    t = {n: synth.to_f64(inp[n], "bf16") for n in ("x", "a_gate", "b_gate", "a_up", "b_up", "a_down",
+                                                   "b_down")}
+    for n, qq in q.items():
+        t[n] = nf4.round_bf16(nf4.dequant(qq["codes"], qq["scales"], shapes[n][2])).reshape(shapes[n])
+    OL = oracle.Layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.r, cfg.s, "f64", t)
+    rt = oracle.route(inp["logits"], cfg.k)
+    f = oracle.fwd(OL, rt)
+    b = oracle.bwd(OL, rt, synth.to_f64(inp["dout"], "bf16"))
+    for n in ("topk_idx", "counts", "offsets", "sorted_slot", "slot_row"):
+        assert np.array_equal(r[n], rt[n]), n
+    assert lr.rel_l2(r["out"], f["out"]) <= 2e-2
+    for n in ("dx", "da_gate", "db_gate", "da_up", "db_up", "da_down", "db_down", "d_topk_w",
+              "d_logits"):
+        assert lr.rel_l2(r[n], b[n]) <= 2e-2, n
+
+
+@pytest.mark.slow
+def test_nf4_full_size_gate_weights_sampled_rows():
+    """The Qwen3-30B-A3B-shaped gate weight [128 x 768, 2048] dequantised in
+    one call; sampled rows against the oracle."""
+    import layer_runner as lr
+    rows, cols = 128 * 768, 2048
+    q = synth.make_nf4(rows, cols, seed=0, tensor=20)
+    got = _dequant_gpu(q["codes"], q["scales"], rows, cols)
+    sel = np.array([0, 1, 4095, 50000, rows - 1])
+    want = nf4.dequant(q["codes"][sel], q["scales"][sel], cols)
+    assert _within_one_bf16_rounding(lr.to_f64(got[torch.from_numpy(sel).cuda()]), want)
+    assert not torch.isnan(got.float()).any()

@@ -471,3 +471,60 @@ def test_router_weight_gradient_chain_matches_central_differences(router_fd_case
     assert np.max(np.abs(fd - ana)) <= 1e-7 * max(1.0, np.max(np.abs(ana)))
     # logit gradients sum to zero per token, so the columns of dW_r sum to zero
     assert np.allclose(rg["dw_r"].sum(0), 0.0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- 4-bit NormalFloat weights
+
+def test_nf4_levels_are_normal_quantiles():
+    import math
+    from oracle import nf4
+    lv = nf4.levels()
+    assert lv.shape == (16,) and np.all(np.diff(lv) > 0)
+    assert lv[0] == -1.0 and lv[7] == 0.0 and lv[15] == 1.0
+    assert np.sum(lv < 0) == 7 and np.sum(lv > 0) == 8
+    # inverse relation through the error function (not the quantile routine
+    # that built them): Phi(level * Q(p)) hits the stated probabilities
+    p = nf4.P_TOP
+    qmax = float(np.sqrt(2.0)) * _erfinv_newton(2 * p - 1)  # Q(p)
+
+    def phi(x):
+        return 0.5 * (1.0 + math.erf(x / math.sqrt(2.0)))
+
+    for j in range(1, 9):
+        assert phi(lv[7 + j] * qmax) == pytest.approx(0.5 + j / 8 * (p - 0.5), abs=1e-12)
+    for j in range(1, 8):
+        assert phi(-lv[7 - j] * qmax) == pytest.approx(0.5 + j / 7 * (p - 0.5), abs=1e-12)
+
+
+def _erfinv_newton(y):
+    import math
+    x = 0.0
+    for _ in range(100):
+        step = (math.erf(x) - y) / (2.0 / math.sqrt(math.pi) * math.exp(-x * x))
+        x -= step
+        if abs(step) < 1e-16:
+            break
+    return x
+
+
+def test_nf4_nibble_order_and_block_scales():
+    from oracle import nf4
+    codes = np.zeros((1, 64), np.uint8)
+    codes[0, 0] = 0x21        # element 0 -> code 1, element 1 -> code 2
+    codes[0, 32] = 0xF0       # element 64 -> code 0, element 65 -> code 15
+    q = nf4.unpack_codes(codes, 128)
+    assert q[0, 0] == 1 and q[0, 1] == 2 and q[0, 64] == 0 and q[0, 65] == 15 and q[0, 2] == 0
+    w = nf4.dequant(codes, np.array([[2.0, 0.5]], np.float32), 128)
+    lv = nf4.levels()
+    assert w[0, 0] == 2.0 * lv[1] and w[0, 1] == 2.0 * lv[2] and w[0, 2] == 2.0 * lv[0]
+    assert w[0, 64] == 0.5 * lv[0] and w[0, 65] == 0.5 * lv[15] and w[0, 127] == 0.5 * lv[0]
+
+
+def test_bf16_rounding_ties_to_even():
+    from oracle import nf4
+    one = 1.0
+    assert nf4.round_bf16(np.array([one]))[0] == 1.0
+    assert nf4.round_bf16(np.array([one + 2.0 ** -8]))[0] == 1.0            # tie -> even
+    assert nf4.round_bf16(np.array([one + 3 * 2.0 ** -8]))[0] == one + 2.0 ** -6  # tie -> even (up)
+    assert nf4.round_bf16(np.array([one + 3 * 2.0 ** -9]))[0] == one + 2.0 ** -7
+    assert nf4.round_bf16(np.array([-0.0]))[0] == 0.0
