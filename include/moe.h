@@ -222,7 +222,8 @@ moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to
 
 /* 4-bit NormalFloat (NF4) frozen base weights, the 4-bit QLoRA variant the
  * pages name for MoE fine-tuning (Unsloth 2026 wiki chapter, model-support
- * table; GPU MODE lecture 32 notes, QLoRA part), dequantised to bf16 so that
+ * table; QLoRA's NF4 in the GPU MODE lecture 32 notes, closing open
+ * questions), dequantised to bf16 so that
  * moe_fwd / moe_bwd run on them unchanged (the frozen weights stay 4-bit in
  * memory; one projection's bf16 copy lives in a scratch buffer for the pass).
  * Format (the QLoRA paper's NormalFloat code): 16 levels, quantiles of

@@ -1,9 +1,9 @@
 // nf4.hip - 4-bit NormalFloat frozen base weights: dequantisation to bf16.
 //
 // The pages name 4-bit QLoRA as the frozen-base variant of MoE fine-tuning
-// (Unsloth 2026 wiki chapter, model-support table; GPU MODE lecture 32
-// notes, QLoRA part) without giving the format. The code is the NormalFloat
-// one of the QLoRA paper (section 3): 16 levels that are quantiles of
+// (Unsloth 2026 wiki chapter, model-support table) and QLoRA's NF4 code
+// (GPU MODE lecture 32 notes, closing open questions) without giving the
+// format. The code is the NormalFloat one of the QLoRA paper (section 3): 16 levels that are quantiles of
 // N(0, 1), asymmetric so that zero is exact, scaled into [-1, 1]:
 //   q = 0 .. 6  : -Q(0.5 + j/7 (p - 0.5)) / Q(p), j = 7 .. 1
 //   q = 7       : 0

@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY (like the rest of this package): imported by the
 test suite and the benchmark, never by the library.
 
 The pages name 4-bit QLoRA as the frozen-base variant of MoE fine-tuning
-(Unsloth 2026 wiki chapter, model-support table; GPU MODE lecture 32 notes,
-QLoRA part) without giving the format. The reading taken is the NormalFloat
+(Unsloth 2026 wiki chapter, model-support table) and QLoRA's NF4 code (GPU
+MODE lecture 32 notes, closing open questions) without giving the format. The reading taken is the NormalFloat
 code of the QLoRA paper (Dettmers et al., 2023, section 3): 16 levels that
 are quantiles of N(0, 1), built asymmetrically so that zero is exact, and
 scaled into [-1, 1]; each block of 64 consecutive weights along a row has
