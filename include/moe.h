@@ -47,7 +47,8 @@
  *    T*k*max(d,2F,2r) < 2^31. Logits must be finite (NaN/Inf: undefined order).
  *  - Gradient outputs are overwritten, never accumulated into.
  *  - Calls on different streams may run concurrently if they share no
- *    buffers (workspaces included). The library has no global state.
+ *    buffers (workspaces included). The library keeps no state between calls
+ *    (its only static data is the table of 16 NF4 levels, computed once).
  */
 #ifndef MOE_H
 #define MOE_H
