@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the HIP-graph replay of the step")
     ap.add_argument("--no-nf4", dest="nf4", action="store_false",
                     help="skip the 4-bit weight dequantisation measurement")
     ap.add_argument("--offload-reps", type=int, default=3,
@@ -324,6 +326,40 @@ def nf4_bench(torch, moe, synth, cfg, dev, reps=5):
             "note": "W_g, W_u, W_d from 4-bit NormalFloat to bf16; not part of the step"}
 
 
+def graph_replay(torch, step, out, dx, steps):
+    """The same step captured once in a HIP graph and replayed: ms per step
+    (no per-kernel launch work on the host), and whether a replay's outputs
+    equal the eager step's bit for bit."""
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, dx) if t is not None]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step(st=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for t in (out, dx):
+        if t is not None:
+            t.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(ref, [t for t in (out, dx) if t is not None]))
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    del g
+    return {"ms_per_step": round(ms, 4), "replay_equals_eager": bool(same),
+            "note": "same step captured once and replayed; value above is the eager step"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -376,14 +412,15 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration, dev)
 
-    def step(trace=None):
+    def step(trace=None, st=None):
+        st = stream if st is None else st
         moe.moe_route(pb, logits, rt, host_counts=None if args.no_readback else host_counts,
-                      ws=ws_r, stream=stream, trace=trace)
-        moe.moe_fwd(pb, x, rt, w, out, saved=saved, keep_expert_out=keep, ws=ws_f, stream=stream,
+                      ws=ws_r, stream=st, trace=trace)
+        moe.moe_fwd(pb, x, rt, w, out, saved=saved, keep_expert_out=keep, ws=ws_f, stream=st,
                     trace=trace)
         if cfg.backward:
             moe.moe_bwd(pb, x, dout, rt, w, saved, keep, dx, grads, d_topk_w=dtw, d_logits=dlg,
-                        ws=ws_b, stream=stream, trace=trace)
+                        ws=ws_b, stream=st, trace=trace)
 
     hip = Hip()
     gemm_kernels = [n for n in ("gateup", "down", "down_bwd", "gateup_bwd") if cfg.backward or
@@ -438,6 +475,8 @@ def main():
     for ev in events:
         hip.destroy(ev)
 
+    graph = graph_replay(torch, step, out, dx if cfg.backward else None, args.steps) \
+        if args.graph else None
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = cfg.T * args.steps / elapsed
     fps = gemm_flops_per_slot(cfg)
@@ -487,6 +526,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                      "flops_per_launch": fps[dom] * S},
         "hbm_kernels": hbm,
+        "graph_replay": graph,
         "kernel_source_hash": kernel_source_hash(),
         "input_setup_s": round(t_gen, 2),
     }
