@@ -451,9 +451,9 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
 #pragma unroll
                     for (int e = 0; e < 8; ++e) h[e] = g[e] * sigmoid_fast(g[e]) * u[e];
                     const size_t o = (size_t)(tl.row0 + m) * p.F + f;
-                    if (G) *reinterpret_cast<chunk_t *>(G + o) = Elem<bf16_t>::pack(g);
-                    if (U) *reinterpret_cast<chunk_t *>(U + o) = Elem<bf16_t>::pack(u);
-                    *reinterpret_cast<chunk_t *>(H + o) = Elem<bf16_t>::pack(h);
+                    if (G) st_stream(G + o, Elem<bf16_t>::pack(g));
+                    if (U) st_stream(U + o, Elem<bf16_t>::pack(u));
+                    st_stream(H + o, Elem<bf16_t>::pack(h));
                 }
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -512,7 +512,7 @@ __device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *
     bf16_t *Y = static_cast<bf16_t *>(p.Y);
     lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
         if (m < tl.rows && n_base + n < p.d)
-            *reinterpret_cast<chunk_t *>(Y + (size_t)(tl.row0 + m) * p.d + n_base + n) = Elem<bf16_t>::pack(v);
+            st_stream(Y + (size_t)(tl.row0 + m) * p.d + n_base + n, Elem<bf16_t>::pack(v));
     });
 }
 
@@ -611,8 +611,8 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
                     du[h] = dh * g[h] * sg;
                 }
                 const size_t pr = (size_t)(tl.row0 + m);
-                *reinterpret_cast<chunk_t *>(dGU + pr * 2 * p.F + f) = Elem<bf16_t>::pack(dg);
-                *reinterpret_cast<chunk_t *>(dGU + pr * 2 * p.F + p.F + f) = Elem<bf16_t>::pack(du);
+                st_stream(dGU + pr * 2 * p.F + f, Elem<bf16_t>::pack(dg));
+                st_stream(dGU + pr * 2 * p.F + p.F + f, Elem<bf16_t>::pack(du));
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next slab overwrites
@@ -666,7 +666,7 @@ __device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile 
     bf16_t *dXp = static_cast<bf16_t *>(p.dXp);
     lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
         if (m < tl.rows && n_base + n < p.d)
-            *reinterpret_cast<chunk_t *>(dXp + (size_t)(tl.row0 + m) * p.d + n_base + n) = Elem<bf16_t>::pack(v);
+            st_stream(dXp + (size_t)(tl.row0 + m) * p.d + n_base + n, Elem<bf16_t>::pack(v));
     });
 }
 
