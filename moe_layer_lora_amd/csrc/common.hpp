@@ -19,6 +19,10 @@ typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // one 16-byte ch
 __device__ __forceinline__ void st_stream(void *p, const chunk_t &v) {
     __builtin_nontemporal_store(v, reinterpret_cast<chunk_t *>(p));
 }
+// 16-byte load marked non-temporal: for data a kernel reads exactly once
+__device__ __forceinline__ chunk_t ld_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const chunk_t *>(p));
+}
 
 constexpr int kWave = 64;
 

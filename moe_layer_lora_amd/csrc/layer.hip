@@ -573,8 +573,8 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
             const int m = wm * C::WTM + mi * 32 + pass * RPP + lane / LPR;
             const bool ok = m < tl.rows && f < p.F;
             const size_t o = (size_t)(tl.row0 + (ok ? m : 0)) * p.F + (ok ? f : 0);
-            q.g[pass] = *reinterpret_cast<const chunk_t *>(G + o);
-            q.u[pass] = *reinterpret_cast<const chunk_t *>(U + o);
+            q.g[pass] = ld_stream(G + o);
+            q.u[pass] = ld_stream(U + o);
             q.w[pass] = p.w_row[tl.row0 + (ok ? m : 0)];
         }
     };
@@ -926,7 +926,7 @@ __global__ __launch_bounds__(256) void k_combine(const T *__restrict__ Y, const 
             for (int u = 0; u < KU; ++u) {
                 const int j = j0 + u;
                 const int q = t * k + min(j, k - 1);
-                ch[u] = *reinterpret_cast<const chunk_t *>(Y + (size_t)slot_row[q] * d + c * VEC);
+                ch[u] = ld_stream(Y + (size_t)slot_row[q] * d + c * VEC);  // each row read once
                 wj[u] = j < k ? (w ? w[q] : 1.0f) : 0.0f;
             }
 #pragma unroll
@@ -939,7 +939,7 @@ __global__ __launch_bounds__(256) void k_combine(const T *__restrict__ Y, const 
                 }
             }
         }
-        *reinterpret_cast<chunk_t *>(out + (size_t)t * d + c * VEC) = Elem<T>::pack(acc);
+        st_stream(out + (size_t)t * d + c * VEC, Elem<T>::pack(acc));
     }
 }
 
