@@ -465,12 +465,17 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
 template <class C, class CH>
 __global__ MOE_LDS_BLOCK(C) void k_gateup_lds(GateUpP p) {
     static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
+    // an expert's last tile of at most 64 rows runs a 64-row shape: half the
+    // padded MFMA work of the 128-row one (the 8-wave kernels cannot split
+    // a 64-row tile's loads evenly, so only this 4-wave kernel has it)
+    using CQ = lds::Cfg<64, 256, 5, false, 64>;
     __shared__ LdsSmem<C> sm;
     static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
     Tile tl;
     if (!table_tile(p.tiles, cdiv(p.F, C::BN / 2), blockIdx.x, tl)) return;
     if (tl.rows > CH::BM) gateup_tile<C>(p, tl, sm.ring);
-    else gateup_tile<CH>(p, tl, sm.ring);
+    else if (tl.rows > CQ::BM) gateup_tile<CH>(p, tl, sm.ring);
+    else gateup_tile<CQ>(p, tl, sm.ring);
 }
 
 template <class C>
