@@ -146,3 +146,24 @@ def test_router_empty_batch_writes_zero_weight_gradient():
     moe.moe_router_bwd(pb, None, w_r, None, dw_router=dw, ws=ws)
     torch.cuda.synchronize()
     assert torch.all(dw == 0.0)
+
+
+def test_router_backward_outputs_are_independent():
+    """dx alone (frozen router: dw_router NULL) and dW_r alone (dx NULL) give
+    the same values as the call that writes both."""
+    import layer_runner as lr
+    import moe_layer_lora_amd as moe
+    cfg = SMALL["ragged_bf16"]
+    x, w_r, dl, dx_in = _inputs(cfg)
+    pb = moe.Problem.from_config(cfg)
+    dev = torch.device("cuda")
+    xt, wt, dlt = lr.to_dev(x), lr.to_dev(w_r), lr.to_dev(dl)
+    ws = moe.alloc_bytes(moe.router_workspace(pb), dev)
+    dx_both, dx_only = lr.to_dev(dx_in), lr.to_dev(dx_in)
+    dw_both = torch.empty((cfg.E, cfg.d), dtype=torch.float32, device=dev)
+    dw_only = torch.empty_like(dw_both)
+    moe.moe_router_bwd(pb, xt, wt, dlt, dx_in=dx_both, dx=dx_both, dw_router=dw_both, ws=ws)
+    moe.moe_router_bwd(pb, xt, wt, dlt, dx_in=dx_only, dx=dx_only)
+    moe.moe_router_bwd(pb, xt, wt, dlt, dw_router=dw_only, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_both, dx_only) and torch.equal(dw_both, dw_only)
