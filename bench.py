@@ -360,6 +360,65 @@ def graph_replay(torch, step, out, dx, steps):
             "note": "same step captured once and replayed; value above is the eager step"}
 
 
+def grouped_mm_baseline(torch, cfg, x, logits, w, dout, steps, warmup=1):
+    """The pages' own design in PyTorch on the same GPU and inputs: routing by
+    one flatten / stable sort by expert / bincount / offsets, the experts'
+    projections as torch._grouped_mm over all experts (the vendor library's
+    grouped GEMM), Split-LoRA as separate grouped products added after the
+    base one, SwiGLU in PyTorch ops, and a weighted index_add combine; the
+    backward is autograd over x and the LoRA factors (base weights frozen).
+    Returns ms per step (forward, backward) and the output, or None if the
+    grouped product is unavailable."""
+    if not hasattr(torch, "_grouped_mm"):
+        return None
+    E, k, s = cfg.E, cfg.k, cfg.s
+    # [E, in, out] layouts of every weight, made once outside the timed region
+    wt = {n: w[n].transpose(1, 2).contiguous() for n in
+          ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")}
+    lora = {n: wt[n].detach().clone().requires_grad_(True)
+            for n in ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")}
+    xr = x.detach().clone().requires_grad_(cfg.backward)
+
+    def gmm(a, b, offs):
+        return torch._grouped_mm(a, b, offs=offs)
+
+    def lin(h, base, a, b, offs):  # h W^T + s (h A^T) B^T, W + s B A never formed
+        return gmm(h, wt[base], offs) + s * gmm(gmm(h, lora[a], offs), lora[b], offs)
+
+    def forward():
+        top = torch.topk(logits, k, dim=1)
+        wts = torch.softmax(top.values, dim=1).reshape(-1)
+        flat = top.indices.reshape(-1)
+        order = torch.sort(flat, stable=True).indices
+        offs = torch.cumsum(torch.bincount(flat, minlength=E), 0).to(torch.int32)
+        tok = order // k
+        h = xr[tok]
+        g = lin(h, "w_gate", "a_gate", "b_gate", offs)
+        u = lin(h, "w_up", "a_up", "b_up", offs)
+        y = lin(torch.nn.functional.silu(g) * u, "w_down", "a_down", "b_down", offs)
+        out = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device=x.device)
+        return out.index_add(0, tok, wts[order, None] * y.float())
+
+    fwd_ms, bwd_ms, out = [], [], None
+    for it in range(warmup + steps):
+        for t in list(lora.values()) + [xr]:
+            t.grad = None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.set_grad_enabled(cfg.backward):
+            out = forward()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if cfg.backward:
+            out.backward(dout.float())
+            torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        if it >= warmup:
+            fwd_ms.append((t1 - t0) * 1e3)
+            bwd_ms.append((t2 - t1) * 1e3)
+    return sum(fwd_ms) / steps, sum(bwd_ms) / steps, out.detach()
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -565,6 +624,19 @@ def main():
             "fwd_speedup": round(wl_fwd / lib_fwd, 2),
             "bwd_speedup": round(wl_bwd / lib_bwd, 2) if cfg.backward else None,
             "out_rel_l2_vs_library": float(diff)}
+    if args.whereloop_steps > 0 and cfg.dtype == "bf16":
+        gm = grouped_mm_baseline(torch, cfg, x, logits, w, dout, args.whereloop_steps)
+        if gm is not None:
+            g_fwd, g_bwd, g_out = gm
+            rec["grouped_mm_baseline"] = {
+                "what": "sort-based routing + torch._grouped_mm over all experts (vendor grouped "
+                        "GEMM) with Split-LoRA as added grouped products, SwiGLU and combine in "
+                        "PyTorch, autograd backward; same GPU and inputs",
+                "steps": args.whereloop_steps, "fwd_ms": round(g_fwd, 3), "bwd_ms": round(g_bwd, 3),
+                "fwd_speedup": round(g_fwd / rec["whereloop_baseline"]["library_fwd_ms"], 2),
+                "bwd_speedup": (round(g_bwd / rec["whereloop_baseline"]["library_bwd_ms"], 2)
+                                if cfg.backward else None),
+                "out_rel_l2_vs_library": float((g_out - out.float()).norm() / g_out.norm())}
     if not args.skip_cpu:
         rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T))
     print(json.dumps(rec), flush=True)
