@@ -967,22 +967,42 @@ __global__ __launch_bounds__(256) void k_router_grad(const T *__restrict__ dout,
     const bool valid = t < Tn;
     float dot = 0.0f;
     if (valid) {
-        for (int j = 0; j < k; ++j) {
-            const int q = t * k + j;
-            const T *yr = Y + (size_t)slot_row[q] * d;
-            const T *gr = dout + (size_t)t * d;
-            float acc = 0.0f;
-            for (int c = lane; c < d / VEC; c += kWave) {
-                float a[VEC], b[VEC];
-                unpack<T>(*reinterpret_cast<const chunk_t *>(gr + c * VEC), a);
-                unpack<T>(*reinterpret_cast<const chunk_t *>(yr + c * VEC), b);
+        // four choices per pass: each dOut chunk is loaded once for the four,
+        // and their expert rows (each read once, so non-temporal) are in
+        // flight together; each choice sums in the same order as alone
+        constexpr int JU = 4;
+        const T *gr = dout + (size_t)t * d;
+        for (int j0 = 0; j0 < k; j0 += JU) {
+            const T *yr[JU];
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) acc += a[v] * b[v];
+            for (int u = 0; u < JU; ++u) yr[u] = Y + (size_t)slot_row[t * k + min(j0 + u, k - 1)] * d;
+            float acc[JU];
+#pragma unroll
+            for (int u = 0; u < JU; ++u) acc[u] = 0.0f;
+            for (int c = lane; c < d / VEC; c += kWave) {
+                float a[VEC];
+                unpack<T>(*reinterpret_cast<const chunk_t *>(gr + c * VEC), a);
+                chunk_t yc[JU];
+#pragma unroll
+                for (int u = 0; u < JU; ++u) yc[u] = ld_stream(yr[u] + c * VEC);
+#pragma unroll
+                for (int u = 0; u < JU; ++u) {
+                    float b[VEC];
+                    unpack<T>(yc[u], b);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[u] += a[v] * b[v];
+                }
             }
 #pragma unroll
-            for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-            if (lane == 0) s_dw[wave][j] = acc;
-            dot += topk_w[q] * acc;
+            for (int u = 0; u < JU; ++u) {
+                float a = acc[u];
+#pragma unroll
+                for (int off = kWave / 2; off > 0; off >>= 1) a += __shfl_xor(a, off, kWave);
+                if (j0 + u < k) {  // past k: a repeat of choice k-1, dropped
+                    if (lane == 0) s_dw[wave][j0 + u] = a;
+                    dot += topk_w[t * k + j0 + u] * a;
+                }
+            }
         }
     }
     __syncthreads();
