@@ -12,6 +12,7 @@ namespace moe {
 typedef uint16_t bf16_t;  // bf16 bit pattern in memory
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // one 16-byte chunk
 // 16-byte store marked non-temporal (no L2 allocation): for grouped-GEMM
 // outputs that only a later kernel reads, so they do not evict the operand

@@ -893,20 +893,35 @@ __global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
         if (blockIdx.x == 0)
             for (int i = threadIdx.x; i < nr * pad; i += 256)
                 p.outT[(size_t)(i / pad) * p.ldT + p.S + i % pad] = Elem<bf16_t>::from_f32(0.0f);
+        // Transposed store through LDS (the ring is drained): the tile goes
+        // in column-major as fp32, then each wave writes 64 adjacent rows of
+        // one column, a run of 128 contiguous bytes of outT, where stores
+        // straight from the accumulators put 2 bytes into each of 32 outT rows
+        constexpr int P = C::BM + 4;  // float pitch: 16-byte aligned, rotates the banks
+        static_assert(C::BN * P * 4 <= C::SMEM_BYTES, "the staged tile fits the ring");
+        float *stg = reinterpret_cast<float *>(sm.ring);
 #pragma unroll
         for (int mi = 0; mi < C::TM; ++mi)
 #pragma unroll
             for (int ni = 0; ni < C::TN; ++ni)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int m = wm * C::WTM + mi * 32 + acc_row(i, lane);
-                    const int n = n_base + wn * C::WTN + ni * 32 + acc_col(lane);
-                    if (m < tl.rows && n < nr) {
-                        const int pr = tl.row0 + m;
-                        const float sc = p.wt ? p.wt[p.sorted_slot[pr]] : 1.0f;
-                        p.outT[(size_t)n * p.ldT + pr] = Elem<bf16_t>::from_f32(acc[mi][ni][i] * sc);
-                    }
+                for (int q = 0; q < 4; ++q) {  // accumulator rows 4q .. 4q+3 are consecutive
+                    const int m = wm * C::WTM + mi * 32 + acc_row(4 * q, lane);
+                    const int n = wn * C::WTN + ni * 32 + acc_col(lane);
+                    *reinterpret_cast<f32x4_t *>(stg + n * P + m) =
+                        f32x4_t{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                                acc[mi][ni][4 * q + 3]};
                 }
+        __syncthreads();
+        // each thread keeps one row (and its weight) over the columns
+        static_assert(256 % C::BM == 0, "whole tile columns per pass");
+        const int ncols = min(C::BN, nr - n_base), m = threadIdx.x % C::BM;
+        if (m < tl.rows) {
+            const int pr = tl.row0 + m;
+            const float sc = p.wt ? p.wt[p.sorted_slot[pr]] : 1.0f;
+            for (int n = threadIdx.x / C::BM; n < ncols; n += 256 / C::BM)
+                p.outT[(size_t)(n_base + n) * p.ldT + pr] = Elem<bf16_t>::from_f32(stg[n * P + m] * sc);
+        }
     }
 }
 
@@ -1088,6 +1103,17 @@ struct LgOut {
         const bool h = n >= split;
         if (diag && h != (m >= mo)) return;
         (h ? o1 : o0)[(size_t)(h ? n - split : n) * sn + (size_t)(h ? m - mo : m) * sm] = v;
+    }
+    // columns n .. n+3 (n a multiple of 4, as split is): one 16-byte store
+    // where they are adjacent in memory ([m][n] outputs), four otherwise
+    __device__ __forceinline__ void store4(int m, int n, f32x4_t v) const {
+        if (sn != 1) {
+            for (int u = 0; u < 4; ++u) store(m, n + u, v[u]);
+            return;
+        }
+        const bool h = n >= split;
+        if (diag && h != (m >= mo)) return;
+        *reinterpret_cast<f32x4_t *>((h ? o1 : o0) + (size_t)(h ? n - split : n) + (size_t)(h ? m - mo : m) * sm) = v;
     }
 };
 
@@ -1366,18 +1392,22 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
     // acc[mi2][ni] holds out^T rows j = mi2*32 + .., columns c = wave*64 + ni*32 + ..
     const bool single = (p.offsets[tl.e + 1] - p.offsets[tl.e]) <= kLgRC;
     const LgOut dst(p, tl.e);
+    // a lane's accumulator rows 4q .. 4q+3 are four consecutive j of one
+    // column m; nr, NR and j0 are multiples of 8, so the four share a fate
 #pragma unroll
     for (int mi2 = 0; mi2 < TM; ++mi2)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int j = p.j0 + mi2 * 32 + acc_row(i, lane);
+            for (int q = 0; q < 4; ++q) {
+                const int j = p.j0 + mi2 * 32 + acc_row(4 * q, lane);
                 const int cl = wave * 64 + ni * 32 + acc_col(lane);
                 if (j < p.nr && j < p.j0 + NR && cl < ncol) {
                     const int m = c_base + cl;
-                    if (single) dst.store(m, j, p.s * acc[mi2][ni][i]);
-                    else p.partial[((size_t)tl.gmt * p.D + m) * p.nr + j] = acc[mi2][ni][i];
+                    const f32x4_t v{acc[mi2][ni][4 * q], acc[mi2][ni][4 * q + 1], acc[mi2][ni][4 * q + 2],
+                                    acc[mi2][ni][4 * q + 3]};
+                    if (single) dst.store4(m, j, p.s * v);
+                    else *reinterpret_cast<f32x4_t *>(p.partial + ((size_t)tl.gmt * p.D + m) * p.nr + j) = v;
                 }
             }
 }
