@@ -21,13 +21,16 @@
 
 namespace moe {
 
-constexpr int kRouteThreads = 1024;  // 16 waves: 4 tokens per wave, a 4x smaller block histogram to scan
+constexpr int kRouteThreads = 1024;  // 16 waves per block: few blocks, so a small block histogram to scan
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / kWave;  // 16 logits per lane
 
 int route_tokens_per_block(int T, int E) {
-    int tpb = 64;  // 4 tokens per wave: enough waves to fill the chip at a few thousand tokens
+    // 2 tokens per wave: 256 blocks at 8192 tokens fill every CU (64 tokens per
+    // block, half of them, made top-k 50% slower; 16 per block made the scan
+    // of the larger histogram cost more than top-k gained)
+    int tpb = 32;
     while ((long long)E * ((T + tpb - 1) / tpb) > 65536) tpb *= 2;
     return tpb;
 }
