@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void k_nf4_dequant(const uint8_t *__restrict__
         float v[8];
 #pragma unroll
         for (int h = 0; h < 8; ++h) v[h] = lvl[(q >> (4 * h)) & 15u] * s;
-        *reinterpret_cast<chunk_t *>(out + row * cols + c8) = Elem<bf16_t>::pack(v);
+        st_stream(out + row * cols + c8, Elem<bf16_t>::pack(v));  // written once, read by a later pass
     }
 }
 
