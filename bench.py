@@ -36,7 +36,9 @@ def parse():
     ap.add_argument("--no-readback", action="store_true",
                     help="route without copying the expert counts to the host")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
-                    help="tokens of the workload the CPU oracle baseline runs on")
+                    help="tokens of the workload the CPU oracle baseline runs on (all cores)")
+    ap.add_argument("--cpu-tokens-1t", type=int, default=128,
+                    help="tokens of the workload for the single-thread oracle run")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay of the step")
@@ -78,6 +80,11 @@ class Hip:
         if rc != 0:
             raise RuntimeError(f"hipEventCreate failed ({rc})")
         return ev.value
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -137,22 +144,107 @@ def copy_calibration(torch, mib, dev):
     del src, dst
 
 
-def cpu_baseline(cfg, tokens):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
+
+
+def cpu_baseline(cfg, tokens, tokens_1t):
+    """The fp64 row-loop oracle as it stands, on the first `tokens` tokens of
+    the same layer with all of its OpenMP threads, and on the first
+    `tokens_1t` with one thread: seconds per phase and GFLOP/s of the
+    algorithmic GEMM work."""
     import oracle
     import synth
-    inputs = synth.make_inputs(cfg, seed=0, tokens=tokens)
-    L = oracle.Layer.from_config(cfg, inputs, tokens=tokens)
-    t0 = time.perf_counter()
-    rt = oracle.route(inputs["logits"], cfg.k)
-    oracle.fwd(L, rt)
-    if cfg.backward:
-        oracle.bwd(L, rt, inputs["dout"])
-    dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"first {tokens} of the {cfg.T} tokens of the same layer (same weights and "
-                      f"generator), route+fwd" + ("+bwd" if cfg.backward else "") +
-                      ", fp64 plain loops, OpenMP over experts"}
+
+    def run(ntok, threads):
+        inputs = synth.make_inputs(cfg, seed=0, tokens=ntok, with_dout=cfg.backward)
+        L = oracle.Layer.from_config(cfg, inputs, tokens=ntok)
+        oracle.set_threads(threads)
+        t0 = time.perf_counter()
+        rt = oracle.route(inputs["logits"], cfg.k)
+        t1 = time.perf_counter()
+        oracle.fwd(L, rt)
+        t2 = time.perf_counter()
+        if cfg.backward:
+            oracle.bwd(L, rt, inputs["dout"])
+        t3 = time.perf_counter()
+        flops = cfg.with_(T=ntok).gemm_flops()["total"]
+        return {"tokens": ntok, "threads": threads, "route_s": round(t1 - t0, 4),
+                "fwd_s": round(t2 - t1, 3), "bwd_s": round(t3 - t2, 3), "seconds": round(t3 - t0, 3),
+                "tokens_per_s": round(ntok / (t3 - t0), 2), "gflops": round(flops / (t3 - t0) / 1e9, 3)}
+
+    nthreads = oracle.threads()
+    all_cores = run(tokens, nthreads)
+    single = run(tokens_1t, 1)
+    oracle.set_threads(nthreads)
+    return {"value": all_cores["tokens_per_s"], "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": cpu_model(), "all_cores": all_cores, "single_thread": single,
+            "sample": f"first {tokens} (all {nthreads} threads) and first {tokens_1t} (one thread) of "
+                      f"the {cfg.T} tokens of the same layer (same weights and generator), route+fwd" +
+                      ("+bwd" if cfg.backward else "") + "; fp64 row loops, OpenMP over experts; bwd "
+                      "recomputes each row's forward; gflops = algorithmic GEMM flops / seconds"}
+
+
+class ClockSampler:
+    """The GPU's current graphics clock from amdsmi, sampled from a host
+    thread about every millisecond while the GPU runs steps."""
+
+    def __init__(self):
+        self.err = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handles()[0]
+            self.read()
+        except Exception as e:  # no amdsmi, no permission: reported, not fatal
+            self.amdsmi, self.err = None, f"{type(e).__name__}: {e}"
+
+    def read(self):
+        info = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)
+        return float(info["clk"]), float(info.get("max_clk", 0) or 0)
+
+    def sample_during(self, fn):
+        import threading
+        if self.amdsmi is None:
+            fn()
+            return None
+        samples, done = [], threading.Event()
+
+        def loop():
+            while not done.is_set():
+                try:
+                    samples.append(self.read())
+                except Exception:
+                    pass
+                time.sleep(0.001)
+        th = threading.Thread(target=loop, daemon=True)
+        th.start()
+        try:
+            fn()
+        finally:
+            done.set()
+            th.join()
+        if not samples:
+            return None
+        clk = sorted(c for c, _ in samples)
+        rec = {"gfx_mhz_median": clk[len(clk) // 2], "gfx_mhz_min": clk[0], "gfx_mhz_max": clk[-1],
+               "max_clk_mhz": samples[-1][1], "samples": len(samples),
+               "source": "amdsmi current GFX clock, sampled about every 1 ms from a host thread "
+                         "while steps run"}
+        # a reading far below the engine's range while the GPU is busy is not
+        # the shader clock (some boards report an idle or another domain's
+        # value here): kept for the record, not used for a peak
+        rec["plausible"] = rec["gfx_mhz_median"] >= 0.5 * (rec["max_clk_mhz"] or 2400.0)
+        return rec
 
 
 def whereloop_baseline(torch, cfg, x, logits, w, dout, steps, warmup=1):
@@ -360,65 +452,6 @@ def graph_replay(torch, step, out, dx, steps):
             "note": "same step captured once and replayed; value above is the eager step"}
 
 
-def grouped_mm_baseline(torch, cfg, x, logits, w, dout, steps, warmup=1):
-    """The pages' own design in PyTorch on the same GPU and inputs: routing by
-    one flatten / stable sort by expert / bincount / offsets, the experts'
-    projections as torch._grouped_mm over all experts (the vendor library's
-    grouped GEMM), Split-LoRA as separate grouped products added after the
-    base one, SwiGLU in PyTorch ops, and a weighted index_add combine; the
-    backward is autograd over x and the LoRA factors (base weights frozen).
-    Returns ms per step (forward, backward) and the output, or None if the
-    grouped product is unavailable."""
-    if not hasattr(torch, "_grouped_mm"):
-        return None
-    E, k, s = cfg.E, cfg.k, cfg.s
-    # [E, in, out] layouts of every weight, made once outside the timed region
-    wt = {n: w[n].transpose(1, 2).contiguous() for n in
-          ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")}
-    lora = {n: wt[n].detach().clone().requires_grad_(True)
-            for n in ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")}
-    xr = x.detach().clone().requires_grad_(cfg.backward)
-
-    def gmm(a, b, offs):
-        return torch._grouped_mm(a, b, offs=offs)
-
-    def lin(h, base, a, b, offs):  # h W^T + s (h A^T) B^T, W + s B A never formed
-        return gmm(h, wt[base], offs) + s * gmm(gmm(h, lora[a], offs), lora[b], offs)
-
-    def forward():
-        top = torch.topk(logits, k, dim=1)
-        wts = torch.softmax(top.values, dim=1).reshape(-1)
-        flat = top.indices.reshape(-1)
-        order = torch.sort(flat, stable=True).indices
-        offs = torch.cumsum(torch.bincount(flat, minlength=E), 0).to(torch.int32)
-        tok = order // k
-        h = xr[tok]
-        g = lin(h, "w_gate", "a_gate", "b_gate", offs)
-        u = lin(h, "w_up", "a_up", "b_up", offs)
-        y = lin(torch.nn.functional.silu(g) * u, "w_down", "a_down", "b_down", offs)
-        out = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device=x.device)
-        return out.index_add(0, tok, wts[order, None] * y.float())
-
-    fwd_ms, bwd_ms, out = [], [], None
-    for it in range(warmup + steps):
-        for t in list(lora.values()) + [xr]:
-            t.grad = None
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        with torch.set_grad_enabled(cfg.backward):
-            out = forward()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        if cfg.backward:
-            out.backward(dout.float())
-            torch.cuda.synchronize()
-        t2 = time.perf_counter()
-        if it >= warmup:
-            fwd_ms.append((t1 - t0) * 1e3)
-            bwd_ms.append((t2 - t1) * 1e3)
-    return sum(fwd_ms) / steps, sum(bwd_ms) / steps, out.detach()
-
-
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -519,12 +552,19 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps
+    # timed region: K steps (an event pair per step on the launch stream
+    # gives each step's own duration: median and min next to the mean)
+    step_ev = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    events.extend(e for pair in step_ev for e in pair)
+    sh = stream.cuda_stream
     t0 = time.perf_counter()
     for s in range(args.steps):
+        hip.record(step_ev[s][0], sh)
         step(timed_traces[s])
+        hip.record(step_ev[s][1], sh)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(hip.elapsed_ms(a, b) for a, b in step_ev)
 
     gemm_ms_timed = kernel_ms(timed_traces, gemm_kernels)
     for s in range(n_breakdown):  # untimed: every kernel bracketed by events
@@ -533,6 +573,16 @@ def main():
     kern_ms = kernel_ms(full_traces, all_names)
     for ev in events:
         hip.destroy(ev)
+
+    # the graphics clock while the step runs (untimed steps after the timed region)
+    def clock_steps():
+        for _ in range(max(100, args.steps)):
+            step()
+        torch.cuda.synchronize()
+    clock = ClockSampler()
+    clk = clock.sample_during(clock_steps)
+    if clk is None and clock.err:
+        clk = {"error": clock.err}
 
     graph = graph_replay(torch, step, out, dx if cfg.backward else None, args.steps) \
         if args.graph else None
@@ -565,6 +615,9 @@ def main():
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
+                    "mean_of_events": round(sum(step_ms) / len(step_ms), 4),
+                    "note": "per-step HIP events on the launch stream inside the timed region"},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name} MoE layer", "T": cfg.T, "d": cfg.d, "E": cfg.E,
@@ -585,6 +638,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                      "flops_per_launch": fps[dom] * S},
         "hbm_kernels": hbm,
+        "clock": clk,
         "graph_replay": graph,
         "kernel_source_hash": kernel_source_hash(),
         "input_setup_s": round(t_gen, 2),
@@ -624,21 +678,15 @@ def main():
             "fwd_speedup": round(wl_fwd / lib_fwd, 2),
             "bwd_speedup": round(wl_bwd / lib_bwd, 2) if cfg.backward else None,
             "out_rel_l2_vs_library": float(diff)}
-    if args.whereloop_steps > 0 and cfg.dtype == "bf16":
-        gm = grouped_mm_baseline(torch, cfg, x, logits, w, dout, args.whereloop_steps)
-        if gm is not None:
-            g_fwd, g_bwd, g_out = gm
-            rec["grouped_mm_baseline"] = {
-                "what": "sort-based routing + torch._grouped_mm over all experts (vendor grouped "
-                        "GEMM) with Split-LoRA as added grouped products, SwiGLU and combine in "
-                        "PyTorch, autograd backward; same GPU and inputs",
-                "steps": args.whereloop_steps, "fwd_ms": round(g_fwd, 3), "bwd_ms": round(g_bwd, 3),
-                "fwd_speedup": round(g_fwd / rec["whereloop_baseline"]["library_fwd_ms"], 2),
-                "bwd_speedup": (round(g_bwd / rec["whereloop_baseline"]["library_bwd_ms"], 2)
-                                if cfg.backward else None),
-                "out_rel_l2_vs_library": float((g_out - out.float()).norm() / g_out.norm())}
+    if clk and clk.get("plausible"):
+        # the dense bf16 rate the chip can reach at the clock it held while the step ran
+        pk = peak * clk["gfx_mhz_median"] / 2400.0
+        rec["roofline"]["peak_at_measured_clock"] = round(pk, 1)
+        rec["roofline"]["frac_at_measured_clock"] = round(ach / pk, 4)
+        rec["grouped_gemm"]["frac_of_peak_at_measured_clock"] = round(gemm_tflops / pk, 4)
     if not args.skip_cpu:
-        rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T))
+        rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T),
+                                           min(args.cpu_tokens_1t, cfg.T))
     print(json.dumps(rec), flush=True)
 
 

@@ -17,9 +17,12 @@
  *              with Split-LoRA (same chapter, Split-LoRA subsection): the
  *              frozen W is applied and s * (x A^T) B^T is added, W + s B A is
  *              never formed; then the combine out[t] = sum_j w[t,j] y[t,j].
- *   moe_bwd    the backward with base W frozen: dX, dA and dB of gate, up and
- *              down, and optionally the gradient of the combine weights and
- *              its chain through the top-k softmax into the logits.
+ *   moe_bwd    the backward with base W frozen, derived by hand in closed form
+ *              (GPU MODE lecture 32 notes, "Unsloth - Faster, Lower-Memory LLM
+ *              Fine-Tuning", part on hand-derived backward passes): dX, dA and
+ *              dB of gate, up and down, and optionally the gradient of the
+ *              combine weights and its chain through the top-k softmax into
+ *              the logits.
  *
  * Conventions for every call
  *  - Pointers are DEVICE pointers unless marked (host). All tensors are
@@ -44,7 +47,10 @@
  *    means a HIP call failed after checks passed (outputs then undefined).
  *    Nothing is printed and no exception crosses the ABI.
  *  - Limits: 0 <= T; 1 <= k <= E <= 1024; d, F, r >= 8 and multiples of 8;
- *    T*k*max(d,2F,2r) < 2^31. Logits must be finite (NaN/Inf: undefined order).
+ *    r <= 256; no tensor above 2 GiB, i.e. with S = T*k and es the element
+ *    size of dtype: S*max(d,2F)*es, S*2r*4, F*d*es and T*E*4 bytes are each
+ *    at most 2^31 (else MOE_E_UNSUPPORTED; the kernels use 32-bit byte
+ *    offsets). Logits must be finite (NaN/Inf: undefined order).
  *  - Gradient outputs are overwritten, never accumulated into.
  *  - Calls on different streams may run concurrently if they share no
  *    buffers (workspaces included). The library keeps no state between calls
@@ -136,6 +142,22 @@ size_t moe_route_workspace(const moe_problem_t *pb);
 size_t moe_fwd_workspace(const moe_problem_t *pb, int training, int keep_expert_out);
 size_t moe_bwd_workspace(const moe_problem_t *pb);
 
+/* Where an intermediate sits inside a caller-owned workspace, for callers
+ * that inspect it after the call (tests, debugging; the next call using the
+ * workspace overwrites it). Returns its byte offset, or SIZE_MAX if that
+ * workspace does not hold it for these arguments or the problem is invalid.
+ *   MOE_PART_Y    moe_fwd workspace (sized with the same training and
+ *                 keep_expert_out): Y [S,d] dtype, the expert outputs by
+ *                 row p; held unless training with keep_expert_out = 1
+ *                 (then Y is in `saved`).
+ *   MOE_PART_DGU  moe_bwd workspace: [S,2F] dtype, row p = dG | dU (the
+ *                 gradients of the gate and up projections' outputs).
+ *   MOE_PART_DXP  moe_bwd workspace: dXp [S,d] dtype, row p's share of dX
+ *                 before the gather-sum over the k choices of its token.
+ * training and keep_expert_out are ignored for the moe_bwd parts. */
+enum { MOE_PART_Y = 0, MOE_PART_DGU = 1, MOE_PART_DXP = 2 };
+size_t moe_workspace_part(const moe_problem_t *pb, int part, int training, int keep_expert_out);
+
 /* Bytes of the `saved` buffer that moe_fwd fills for moe_bwd. Layout, each
  * part starting on a 256-byte boundary: G, U, H [S,F] dtype; Zgu [S,2r]
  * float32 (x A_gate^T | x A_up^T); Zd [S,r] float32 (h A_down^T); for bf16
@@ -165,10 +187,29 @@ moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t
                      const moe_weights_t *w, void *out, void *saved, int keep_expert_out,
                      void *ws, size_t ws_bytes, void *stream, const moe_trace_t *trace);
 
-/* Backward. x and dout [T,d]; saved as filled by moe_fwd for the same x,
- * routing and weights. Writes dx [T,d] and all six LoRA gradients. d_topk_w
- * [T,k] and d_logits [T,E] are optional (NULL to skip) and need saved to
- * hold Y (keep_expert_out = 1 in moe_fwd; pass the same flag here). */
+/* Backward: the gradients of the layer derived by hand in closed form and
+ * computed by dedicated kernels rather than by autograd (GPU MODE lecture 32
+ * notes, "Unsloth - Faster, Lower-Memory LLM Fine-Tuning", part on deriving
+ * every layer's backward by hand), with the frozen base W getting no
+ * gradient and the LoRA factors A, B getting theirs (Unsloth 2026 wiki
+ * chapter, "Optimisation 3", Split-LoRA subsection: only the low-rank
+ * factors train). For dout = dL/dout:
+ *   dy[t,j] = w[t,j] dout[t];  dh = dy W_d + s (dy B_d) A_d;
+ *   dg = dh u sigma(g) (1 + g (1 - sigma(g))),  du = dh silu(g);
+ *   dx[t] = sum_j (dg W_g + du W_u + s (dg B_g) A_g + s (du B_u) A_u)[t,j];
+ *   dB_d = s dy^T (h A_d^T), dA_d = s (dy B_d)^T h, and the same pattern for
+ *   gate and up with (dg, x) and (du, x), each summed over an expert's rows.
+ * x and dout [T,d]; saved as filled by moe_fwd for the same x, routing and
+ * weights. Writes dx [T,d] and all six LoRA gradients (experts with no rows
+ * get exact zeros). d_topk_w [T,k] (= <dout[t], y[t,j]>) and d_logits [T,E]
+ * (its chain through the softmax over the k selected logits, 0 for experts
+ * not selected) are optional (NULL to skip) and need saved to hold Y
+ * (keep_expert_out = 1 in moe_fwd; pass the same flag here).
+ * Errors as for every call: arguments are checked before anything is
+ * enqueued (MOE_E_ARG for NULL or misaligned buffers, or d_topk_w / d_logits
+ * without keep_expert_out; MOE_E_WORKSPACE if ws_bytes is below
+ * moe_bwd_workspace). The result does not depend on launch timing: every
+ * reduction runs in a fixed order. */
 moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout,
                      const moe_routing_t *rt, const moe_weights_t *w, const void *saved,
                      int keep_expert_out, void *dx, const moe_lora_grads_t *grads,
@@ -227,9 +268,10 @@ moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to
  * questions), dequantised to bf16 so that
  * moe_fwd / moe_bwd run on them unchanged (the frozen weights stay 4-bit in
  * memory; one projection's bf16 copy lives in a scratch buffer for the pass).
- * Format (the QLoRA paper's NormalFloat code): 16 levels, quantiles of
- * N(0,1) with an exact zero, scaled into [-1, 1] (level 0 = -1, level 7 = 0,
- * level 15 = +1); weight = level[code] * scale, one float32 scale per 64
+ * Format (the QLoRA paper's NormalFloat code, the 16 values its appendix
+ * lists): quantiles of N(0,1) with an exact zero, scaled into [-1, 1]
+ * (level 0 = -1, level 7 = 0, level 15 = +1), built with top probability
+ * 0.9677083; weight = level[code] * scale, one float32 scale per 64
  * consecutive weights of a row.
  *   codes  [rows, cols/2] uint8: element 2i of a row in the low nibble of
  *          byte i, element 2i+1 in the high nibble (16-byte aligned)

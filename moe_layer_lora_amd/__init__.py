@@ -38,7 +38,9 @@ MOE_K_COUNT = len(KERNELS)
 
 EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe_saved_bytes",
            "moe_route", "moe_fwd", "moe_bwd", "moe_status_str", "moe_router_workspace",
-           "moe_router_fwd", "moe_router_bwd", "moe_saved_copy", "moe_nf4_dequant"]
+           "moe_router_fwd", "moe_router_bwd", "moe_saved_copy", "moe_nf4_dequant",
+           "moe_workspace_part"]
+MOE_PART_Y, MOE_PART_DGU, MOE_PART_DXP = range(3)
 
 
 class Problem(ctypes.Structure):
@@ -95,6 +97,8 @@ _lib.moe_fwd.argtypes = [_P(Problem), _vp, _P(Routing), _P(Weights), _vp, _vp, _
                          _vp, _P(Trace)]
 _lib.moe_bwd.argtypes = [_P(Problem), _vp, _vp, _P(Routing), _P(Weights), _vp, _i32, _vp,
                          _P(LoraGrads), _vp, _vp, _vp, _sz, _vp, _P(Trace)]
+_lib.moe_workspace_part.argtypes = [_P(Problem), _i32, _i32, _i32]
+_lib.moe_workspace_part.restype = _sz
 _lib.moe_router_workspace.argtypes = [_P(Problem)]
 _lib.moe_router_workspace.restype = _sz
 _lib.moe_router_fwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _P(Trace)]
@@ -172,11 +176,25 @@ def _check(st, what):
         raise MoeError(st, what)
 
 
+def _host_buffer(a, what):
+    """(address, bytes, dtype name) of a host numpy array or CPU torch tensor."""
+    if hasattr(a, "ctypes"):  # numpy
+        return a.ctypes.data, a.nbytes, str(a.dtype)
+    if getattr(a, "is_cuda", False):
+        raise MoeError(MOE_E_ARG, f"{what}: a host buffer is needed, got a device tensor")
+    return a.data_ptr(), a.numel() * a.element_size(), str(a.dtype).replace("torch.", "")
+
+
 def moe_route(pb, logits, rt: dict, host_counts=None, ws=None, stream=None, trace=None):
-    """rt: dict of the six routing tensors; host_counts: CPU int32 tensor/array or None."""
+    """rt: dict of the six routing tensors; host_counts: CPU int32 tensor/array
+    of at least E elements, or None. The library writes E int32 counts there,
+    so a shorter or differently typed buffer is refused before the call."""
     hc = None
     if host_counts is not None:
-        hc = host_counts.ctypes.data if hasattr(host_counts, "ctypes") else host_counts.data_ptr()
+        hc, nbytes, dt = _host_buffer(host_counts, "moe_route host_counts")
+        if dt != "int32" or nbytes < 4 * pb.E:
+            raise MoeError(MOE_E_ARG, f"moe_route host_counts: need int32[{pb.E}], got {dt} "
+                                      f"of {nbytes} bytes")
     st = _lib.moe_route(ctypes.byref(pb), _ptr(logits), ctypes.byref(_struct(Routing, rt)), hc,
                         _ptr(ws), _nbytes(ws), _stream(stream),
                         ctypes.byref(trace) if trace is not None else None)
@@ -231,7 +249,14 @@ def moe_saved_copy(pb, keep_expert_out, to_device, saved, host, wait_event=None,
         if e is None or isinstance(e, int):
             return e
         return e.cuda_event
-    hp = host.data_ptr() if hasattr(host, "data_ptr") else host
+    if isinstance(host, int):
+        hp = host
+    else:
+        hp, nbytes, _ = _host_buffer(host, "moe_saved_copy host")
+        need = saved_bytes(pb, keep_expert_out)
+        if nbytes < need:
+            raise MoeError(MOE_E_ARG, f"moe_saved_copy host: {nbytes} bytes for a {need}-byte "
+                                      "saved buffer")
     st = _lib.moe_saved_copy(ctypes.byref(pb), int(keep_expert_out), int(to_device), _ptr(saved), hp,
                              ev(wait_event), _stream(copy_stream), ev(done_event))
     _check(st, "moe_saved_copy")
@@ -270,6 +295,30 @@ def alloc_grads(pb: Problem, device):
             "db_up": torch.empty((E, F, r), dtype=f, device=device),
             "da_down": torch.empty((E, r, F), dtype=f, device=device),
             "db_down": torch.empty((E, d, r), dtype=f, device=device)}
+
+
+def workspace_part(pb: Problem, part: int, training: bool = True, keep_expert_out: bool = False):
+    """Byte offset of an inspectable intermediate in a workspace (MOE_PART_*), or None."""
+    o = _lib.moe_workspace_part(ctypes.byref(pb), int(part), int(training), int(keep_expert_out))
+    return None if o == ctypes.c_size_t(-1).value else int(o)
+
+
+def workspace_views(pb: Problem, ws_fwd=None, ws_bwd=None, training=True,
+                    keep_expert_out=False) -> dict:
+    """Typed views of the intermediates the workspaces hold after moe_fwd /
+    moe_bwd: Y (fwd workspace, if held there), dGU [S,2F] and dXp [S,d]."""
+    S, F, d = pb.S, pb.F, pb.d
+    dt = torch.bfloat16 if pb.dtype == MOE_BF16 else torch.float32
+    es = 2 if pb.dtype == MOE_BF16 else 4
+    out = {}
+    for name, buf, part, cols in (("Y", ws_fwd, MOE_PART_Y, d), ("dGU", ws_bwd, MOE_PART_DGU, 2 * F),
+                                  ("dXp", ws_bwd, MOE_PART_DXP, d)):
+        if buf is None:
+            continue
+        o = workspace_part(pb, part, training, keep_expert_out)
+        if o is not None:
+            out[name] = buf[o:o + S * cols * es].view(dt).view(S, cols)
+    return out
 
 
 def saved_views(pb: Problem, saved, keep_expert_out: bool) -> dict:

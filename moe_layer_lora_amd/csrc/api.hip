@@ -2,8 +2,10 @@
 // and saved-buffer layouts, and the launch sequence on the caller's stream.
 #include "moe.h"
 #include "kernels.hpp"
+#include "api_internal.hpp"
 
 #include <cmath>
+#include <cstdint>
 
 namespace {
 
@@ -25,10 +27,14 @@ moe_status_t check_problem(const moe_problem_t *pb) {
     if (!std::isfinite(pb->lora_scale)) return MOE_E_ARG;
     if (pb->d % 8 || pb->F % 8 || pb->r % 8) return MOE_E_UNSUPPORTED;
     if (pb->E > 1024 || pb->r > 256) return MOE_E_UNSUPPORTED;
-    const long long S = (long long)pb->T * pb->k;
-    long long wide = pb->d > 2 * pb->F ? pb->d : 2LL * pb->F;
-    if (2LL * pb->r > wide) wide = 2LL * pb->r;
-    if (S * wide >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+    // The kernels address every tensor through 32-bit byte offsets (buffer
+    // descriptors, with 2^31 as the out-of-range sentinel), so no tensor may
+    // exceed 2 GiB: the [S, max(d, 2F)] activations, the fp32 [S, 2r]
+    // projections, one expert's [F, d] weight and the fp32 [T, E] logits.
+    const long long S = (long long)pb->T * pb->k, es = (long long)esize(pb->dtype), lim = 1LL << 31;
+    const long long wide = pb->d > 2LL * pb->F ? pb->d : 2LL * pb->F;
+    if (S * wide * es > lim || S * 2LL * pb->r * 4 > lim) return MOE_E_UNSUPPORTED;
+    if ((long long)pb->F * pb->d * es > lim || (long long)pb->T * pb->E * 4 > lim) return MOE_E_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -186,19 +192,43 @@ size_t moe_bwd_workspace(const moe_problem_t *pb) {
     return check_problem(pb) == MOE_OK ? bwd_ws(pb).total : 0;
 }
 
+size_t moe_workspace_part(const moe_problem_t *pb, int part, int training, int keep_expert_out) {
+    if (check_problem(pb) != MOE_OK) return SIZE_MAX;
+    switch (part) {
+    case MOE_PART_Y:
+        if (training && keep_expert_out) return SIZE_MAX;
+        return fwd_ws(pb, training != 0, keep_expert_out != 0).Y;
+    case MOE_PART_DGU: return bwd_ws(pb).dGU;
+    case MOE_PART_DXP: return bwd_ws(pb).dXp;
+    }
+    return SIZE_MAX;
+}
+
 size_t moe_saved_bytes(const moe_problem_t *pb, int keep_expert_out) {
     return check_problem(pb) == MOE_OK ? saved_layout(pb, keep_expert_out != 0).total : 0;
 }
 
-moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt,
-                       int32_t *host_counts, void *ws, size_t ws_bytes, void *stream, const moe_trace_t *trace) {
+}  // extern "C"
+
+namespace moe {
+namespace api {
+
+// Argument checks of a routing call, without its workspace: MOE_OK and the
+// workspace bytes it needs in *ws_bytes, or the error.
+moe_status_t route_check(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt, size_t *ws_bytes) {
     moe_status_t st = check_problem(pb);
     if (st != MOE_OK) return st;
     if (!routing_ok(rt, pb->T)) return MOE_E_ARG;
     if (pb->T > 0 && !buf_ok(logits)) return MOE_E_ARG;
+    *ws_bytes = route_ws(pb).total;
+    return MOE_OK;
+}
+
+// The routing launches and the optional count copy, on a checked problem,
+// with the workspace at `ws` (route_check's bytes).
+moe_status_t route_impl(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt,
+                        int32_t *host_counts, void *ws, void *stream, const moe_trace_t *trace) {
     const RouteWs w = route_ws(pb);
-    if (ws_bytes < w.total) return MOE_E_WORKSPACE;
-    if (w.total > 0 && !buf_ok(ws)) return MOE_E_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const moe::Trace tr = to_trace(trace);
     int32_t *hist = reinterpret_cast<int32_t *>(at(ws, w.hist));
@@ -226,6 +256,32 @@ moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_r
                                       hipMemcpyDeviceToHost, s) != hipSuccess)
         return MOE_E_HIP;
     return MOE_OK;
+}
+
+// true if p is page-locked host memory (pageable memory is not an error to
+// leave for the next call)
+bool pinned_host(const void *p) {
+    hipPointerAttribute_t pa{};
+    if (hipPointerGetAttributes(&pa, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return pa.type == hipMemoryTypeHost;
+}
+
+}  // namespace api
+}  // namespace moe
+
+extern "C" {
+
+moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt,
+                       int32_t *host_counts, void *ws, size_t ws_bytes, void *stream, const moe_trace_t *trace) {
+    size_t need = 0;
+    const moe_status_t st = moe::api::route_check(pb, logits, rt, &need);
+    if (st != MOE_OK) return st;
+    if (ws_bytes < need) return MOE_E_WORKSPACE;
+    if (need > 0 && !buf_ok(ws)) return MOE_E_ARG;
+    return moe::api::route_impl(pb, logits, rt, host_counts, ws, stream, trace);
 }
 
 moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t *rt, const moe_weights_t *w,
@@ -375,13 +431,7 @@ moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to
                             void *wait_event, void *copy_stream, void *done_event) {
     moe_status_t st = check_problem(pb);
     if (st != MOE_OK) return st;
-    if (!buf_ok(saved) || !host) return MOE_E_ARG;
-    hipPointerAttribute_t pa{};
-    if (hipPointerGetAttributes(&pa, host) != hipSuccess) {
-        (void)hipGetLastError();  // pageable memory: not an error to leave for the next call
-        return MOE_E_ARG;
-    }
-    if (pa.type != hipMemoryTypeHost) return MOE_E_ARG;
+    if (!buf_ok(saved) || !host || !moe::api::pinned_host(host)) return MOE_E_ARG;
     const size_t n = saved_layout(pb, keep_expert_out != 0).total;
     hipStream_t cs = static_cast<hipStream_t>(copy_stream);
     if (wait_event && hipStreamWaitEvent(cs, static_cast<hipEvent_t>(wait_event), 0) != hipSuccess)

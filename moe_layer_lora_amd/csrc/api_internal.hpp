@@ -1,0 +1,26 @@
+// api_internal.hpp - pieces of the C ABI implementation shared between its
+// source files (internal to the library).
+#pragma once
+
+#include <stddef.h>
+
+#include "moe.h"
+
+namespace moe {
+namespace api {
+
+// Argument checks of a routing call, without its workspace: MOE_OK and the
+// workspace bytes it needs in *ws_bytes, or the error.
+moe_status_t route_check(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt, size_t *ws_bytes);
+
+// The routing launches and the optional count copy on `stream`, for a problem
+// route_check accepted, with its workspace at `ws`.
+moe_status_t route_impl(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt,
+                        int32_t *host_counts, void *ws, void *stream, const moe_trace_t *trace);
+
+// true if p is page-locked host memory; pageable memory returns false and
+// leaves no HIP error behind
+bool pinned_host(const void *p);
+
+}  // namespace api
+}  // namespace moe

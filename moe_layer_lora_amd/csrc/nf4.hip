@@ -3,13 +3,16 @@
 // The pages name 4-bit QLoRA as the frozen-base variant of MoE fine-tuning
 // (Unsloth 2026 wiki chapter, model-support table) and QLoRA's NF4 code
 // (GPU MODE lecture 32 notes, closing open questions) without giving the
-// format. The code is the NormalFloat one of the QLoRA paper (section 3): 16 levels that are quantiles of
-// N(0, 1), asymmetric so that zero is exact, scaled into [-1, 1]:
+// format. The code is the NormalFloat one of the QLoRA paper (section 3,
+// values listed in its appendix): 16 levels that are quantiles of N(0, 1),
+// asymmetric so that zero is exact, scaled into [-1, 1]:
 //   q = 0 .. 6  : -Q(0.5 + j/7 (p - 0.5)) / Q(p), j = 7 .. 1
 //   q = 7       : 0
 //   q = 8 .. 15 : +Q(0.5 + j/8 (p - 0.5)) / Q(p), j = 1 .. 8
-// with Q the standard normal quantile and p = 1 - 1/32. A weight is
-// level[code] * scale, one fp32 scale per 64 consecutive weights of a row.
+// with Q the standard normal quantile and p = 0.9677083, the top probability
+// for which this construction gives the paper's published levels (to float32
+// rounding). A weight is level[code] * scale, one fp32 scale per 64
+// consecutive weights of a row.
 // Codes are packed two per byte, element 2i in the low nibble of byte i.
 //
 // The kernel is a stream: 4 code bytes in, 16 bytes of bf16 out per thread
@@ -27,7 +30,7 @@ struct Nf4Levels {
 };
 
 // standard normal quantile by Newton's method on the complementary error
-// function (p in (0, 1), here at most 1 - 1/32)
+// function (p in (0, 1), here at most 0.9677083)
 double normal_quantile(double p) {
     double x = 0.0;
     for (int it = 0; it < 60; ++it) {
@@ -43,7 +46,7 @@ double normal_quantile(double p) {
 Nf4Levels nf4_levels() {
     static const Nf4Levels lv = [] {
         Nf4Levels l{};
-        const double p = 1.0 - 1.0 / 32.0, qmax = normal_quantile(p);
+        const double p = 0.9677083, qmax = normal_quantile(p);
         for (int j = 7; j >= 1; --j) l.v[7 - j] = (float)(-normal_quantile(0.5 + j / 7.0 * (p - 0.5)) / qmax);
         l.v[7] = 0.0f;
         for (int j = 1; j <= 8; ++j) l.v[7 + j] = (float)(normal_quantile(0.5 + j / 8.0 * (p - 0.5)) / qmax);

@@ -62,6 +62,8 @@ def _load():
             f.restype = ctypes.c_int
         lib.orc_threads.argtypes = []
         lib.orc_threads.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -69,6 +71,11 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """Number of OpenMP threads for the oracle's parallel loops."""
+    _load().orc_set_threads(int(n))
 
 
 def _p(a):

@@ -17,8 +17,12 @@ Levels (ascending, code q indexes them):
   q = 0 .. 6   : -Q(0.5 + j/7 * (p - 0.5)) / Q(p) for j = 7 .. 1
   q = 7        : 0
   q = 8 .. 15  : +Q(0.5 + j/8 * (p - 0.5)) / Q(p) for j = 1 .. 8
-with Q the standard normal quantile and p = 1 - 1/32 (half of one of 16
-bins below 1), so level 0 is -1 and level 15 is +1.
+with Q the standard normal quantile, so level 0 is -1 and level 15 is +1.
+The paper's text leaves the top probability p open; its appendix prints the
+16 resulting values, and p = 0.9677083 (about 1 - (1/64 + 1/60), between the
+half-bin offsets of 16 and of 15 bins) reproduces them to float32 rounding.
+That p is used here, so weights quantised with the published code
+dequantise unchanged.
 
 Packing: codes [rows, cols/2] uint8, element 2i of a row in the low nibble of
 byte i and element 2i+1 in the high nibble; scales [rows, cols/64] float32.
@@ -28,7 +32,7 @@ from __future__ import annotations
 import numpy as np
 from scipy.stats import norm
 
-P_TOP = 1.0 - 1.0 / 32.0
+P_TOP = 0.9677083
 BLOCK = 64
 
 

@@ -63,6 +63,9 @@ typedef struct {
 /* threads the parallel loops below will use */
 int orc_threads(void) { return omp_get_max_threads(); }
 
+/* set that number (n >= 1) */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* ------------------------------------------------------------------ */
 /* stored value -> double (exact)                                      */
 

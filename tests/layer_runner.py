@@ -82,6 +82,12 @@ class Layer:
         if intermediates and self.training:
             for n, v in moe.saved_views(self.pb, self.saved, self.keep).items():
                 r[n] = to_f64(v)
+        if intermediates:
+            ws = moe.workspace_views(self.pb, ws_fwd=self.ws_fwd,
+                                     ws_bwd=self.ws_bwd if (backward and self.training) else None,
+                                     training=self.training, keep_expert_out=self.keep)
+            for n, v in ws.items():
+                r[n] = to_f64(v)
         if backward:
             r["dx"] = to_f64(self.dx)
             for n, v in self.grads.items():

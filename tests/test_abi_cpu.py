@@ -82,6 +82,12 @@ def test_saved_and_workspace_sizes():
     (dict(d=100), moe.MOE_E_UNSUPPORTED), (dict(F=36), moe.MOE_E_UNSUPPORTED),
     (dict(r=12), moe.MOE_E_UNSUPPORTED), (dict(E=1025, k=2), moe.MOE_E_UNSUPPORTED),
     (dict(T=1 << 20, d=4096, k=8), moe.MOE_E_UNSUPPORTED),
+    # GPT-OSS-120B shapes at 49152 tokens: the [S, 2F] bf16 dG|dU tensor is 2.26 GB
+    (dict(T=49152, d=2880, E=128, k=4, F=2880, r=32), moe.MOE_E_UNSUPPORTED),
+    # fp32 [S, d] activations of 4 GB
+    (dict(T=1 << 17, d=2048, E=16, k=4, F=128, dtype=moe.MOE_F32), moe.MOE_E_UNSUPPORTED),
+    # one expert's [F, d] weight above 2 GiB
+    (dict(T=8, d=32768, E=2, k=1, F=32768 + 8), moe.MOE_E_UNSUPPORTED),
 ])
 def test_bad_problems_rejected(kw, code):
     p = pb(**kw)
@@ -191,3 +197,28 @@ def test_nf4_dequant_argument_errors_before_launch():
     assert L.moe_nf4_dequant(A, A + 2, 4, 64, A, None) == moe.MOE_E_ARG     # scales 4-byte aligned
     assert L.moe_nf4_dequant(A, A, 4, 64, A + 8, None) == moe.MOE_E_ARG     # out 16-byte aligned
     assert L.moe_nf4_dequant(None, None, 0, 64, None, None) == moe.MOE_OK   # nothing to do
+
+
+def test_two_gib_limit_is_in_bytes():
+    """Every tensor must fit 2^31 bytes (32-bit byte offsets in the kernels):
+    the largest GPT-OSS-120B-shaped batch that fits is accepted, one more
+    token is refused."""
+    F2 = 2 * 2880
+    t_max = (1 << 31) // (F2 * 2) // 4   # S = 4 T slots of [2F] bf16
+    ok, over = pb(T=t_max, d=2880, E=128, k=4, F=2880, r=32), pb(T=t_max + 1, d=2880, E=128, k=4, F=2880, r=32)
+    assert moe.route_workspace(ok) > 0 and moe.saved_bytes(ok, True) > 0
+    assert moe.route_workspace(over) == 0 and moe.saved_bytes(over, True) == 0
+
+
+def test_binding_checks_host_buffers():
+    import numpy as np
+    p = pb()
+    rt = {n: 1 << 20 for n in ("topk_idx", "topk_w", "counts", "offsets", "sorted_slot", "slot_row")}
+    for bad in (np.zeros(p.E - 1, np.int32), np.zeros(p.E, np.int64), np.zeros(p.E, np.float32)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_route(p, 1 << 20, rt, host_counts=bad, stream=0)
+        assert ei.value.status == moe.MOE_E_ARG
+    short = np.zeros(moe.saved_bytes(p, False) - 1, np.uint8)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_saved_copy(p, False, False, 1 << 20, short, copy_stream=0)
+    assert ei.value.status == moe.MOE_E_ARG

@@ -17,6 +17,12 @@ import pytest
 
 import oracle
 import synth
+from oracle import grouped as oracle_grouped
+
+# The two forms of the oracle's expert layer (row-at-a-time C loops, and one
+# matrix product per expert and step): every layer pin below runs on both.
+IMPLS = {"loops": oracle, "grouped": oracle_grouped}
+impl_param = pytest.mark.parametrize("impl", list(IMPLS))
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -177,17 +183,19 @@ def test_grouping_invariants():
 
 # ---------------------------------------------------------------- forward
 
+@impl_param
 @pytest.mark.parametrize("shape", [(7, 8, 4, 2, 12, 3), (5, 16, 1, 1, 8, 4), (9, 8, 6, 6, 8, 2)])
-def test_split_lora_equals_materialised_dense(shape):
+def test_split_lora_equals_materialised_dense(shape, impl):
     T, d, E, k, F, r = shape
     L, t, logits, _ = make(T, d, E, k, F, r, s=1.7, seed=3)
     rt = oracle.route(logits, k)
-    out = oracle.fwd(L, rt)["out"]
+    out = IMPLS[impl].fwd(L, rt)["out"]
     ref = dense_materialised_out(t, rt, 1.7)
     assert rel_l2(out, ref) < 1e-13
 
 
-def test_swiglu_closed_form_tiny():
+@impl_param
+def test_swiglu_closed_form_tiny(impl):
     """T=d... one token, one expert: g = x0 + s*bg*(ag . x), u = 2 x1, h = silu(g) u,
     z_d = a_d h, y = (h, 3h + s*z_d)."""
     s = 2.0
@@ -199,7 +207,7 @@ def test_swiglu_closed_form_tiny():
          "a_down": np.array([[[2.0]]]), "b_down": np.array([[[0.0], [1.0]]])}
     L = oracle.Layer(1, 2, 1, 1, 1, 1, s, "f64", t)
     rt = oracle.route(np.zeros((1, 1), np.float32), 1)
-    f = oracle.fwd(L, rt, intermediates=True)
+    f = IMPLS[impl].fwd(L, rt, intermediates=True)
     g = 1.0 + s * 0.5 * 0.5                 # 1.5
     u = 1.0
     h = g / (1.0 + math.exp(-g)) * u
@@ -212,14 +220,15 @@ def test_swiglu_closed_form_tiny():
     assert f["H"][0, 0] != pytest.approx(u / (1 + math.exp(-u)) * g)
 
 
-def test_identical_experts_make_routing_irrelevant():
+@impl_param
+def test_identical_experts_make_routing_irrelevant(impl):
     T, d, E, k, F, r = 11, 8, 5, 3, 12, 2
     t, logits, _ = rand_tensors(T, d, E, F, r, seed=4)
     for n in t:
         if n != "x":
             t[n] = np.repeat(t[n][:1], E, axis=0)
     L = oracle.Layer(T, d, E, k, F, r, 0.9, "f64", t)
-    out = oracle.fwd(L, oracle.route(logits, k))["out"]
+    out = IMPLS[impl].fwd(L, oracle.route(logits, k))["out"]
     wg = t["w_gate"][0] + 0.9 * t["b_gate"][0] @ t["a_gate"][0]
     wu = t["w_up"][0] + 0.9 * t["b_up"][0] @ t["a_up"][0]
     wd = t["w_down"][0] + 0.9 * t["b_down"][0] @ t["a_down"][0]
@@ -227,19 +236,27 @@ def test_identical_experts_make_routing_irrelevant():
     assert rel_l2(out, single) < 1e-13
 
 
-def test_token_permutation_equivariance_bit_exact():
+@impl_param
+def test_token_permutation_equivariance_bit_exact(impl):
+    """Bit-exact for the row loops; the matrix form's library products may
+    round a row differently at another position inside an expert's block,
+    so there the bound is a few ulps."""
     T, d, E, k, F, r = 13, 8, 6, 2, 8, 2
     L, t, logits, _ = make(T, d, E, k, F, r, s=2.0, seed=5)
-    out = oracle.fwd(L, oracle.route(logits, k))["out"]
+    out = IMPLS[impl].fwd(L, oracle.route(logits, k))["out"]
     perm = np.random.default_rng(0).permutation(T)
     t2 = dict(t)
     t2["x"] = t["x"][perm]
     L2 = oracle.Layer(T, d, E, k, F, r, 2.0, "f64", t2)
-    out2 = oracle.fwd(L2, oracle.route(logits[perm], k))["out"]
-    assert np.array_equal(out2, out[perm])
+    out2 = IMPLS[impl].fwd(L2, oracle.route(logits[perm], k))["out"]
+    if impl == "loops":
+        assert np.array_equal(out2, out[perm])
+    else:
+        assert rel_l2(out2, out[perm]) < 1e-14
 
 
-def test_lora_b_zero_gives_base_only_bit_exact():
+@impl_param
+def test_lora_b_zero_gives_base_only_bit_exact(impl):
     T, d, E, k, F, r = 9, 8, 4, 2, 8, 3
     L, t, logits, dout = make(T, d, E, k, F, r, s=2.0, seed=6)
     rt = oracle.route(logits, k)
@@ -248,9 +265,10 @@ def test_lora_b_zero_gives_base_only_bit_exact():
         t0[n] = np.zeros_like(t[n])
     Lb0 = oracle.Layer(T, d, E, k, F, r, 2.0, "f64", t0)
     Ls0 = oracle.Layer(T, d, E, k, F, r, 0.0, "f64", t)
-    assert np.array_equal(oracle.fwd(Lb0, rt)["out"], oracle.fwd(Ls0, rt)["out"])
-    gb0 = oracle.bwd(Lb0, rt, dout)
-    gs0 = oracle.bwd(Ls0, rt, dout)
+    O = IMPLS[impl]
+    assert np.array_equal(O.fwd(Lb0, rt)["out"], O.fwd(Ls0, rt)["out"])
+    gb0 = O.bwd(Lb0, rt, dout)
+    gs0 = O.bwd(Ls0, rt, dout)
     assert np.array_equal(gb0["dx"], gs0["dx"])
     for n in ("da_gate", "da_up", "da_down"):
         assert np.all(gb0[n] == 0.0)
@@ -258,7 +276,8 @@ def test_lora_b_zero_gives_base_only_bit_exact():
         assert np.all(gs0[n] == 0.0)
 
 
-def test_storage_formats_agree():
+@impl_param
+def test_storage_formats_agree(impl):
     """bf16 bits, their exact float32 widening and float64 give identical results."""
     cfg = synth.get_config("tiny_fp32").with_(dtype="bf16", T=32)
     inp = synth.make_inputs(cfg)
@@ -269,10 +288,11 @@ def test_storage_formats_agree():
                       {n: synth.bf16_to_f32(inp[n]) for n in names})
     Ld = oracle.Layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.r, cfg.s, "f64",
                       {n: synth.bf16_to_f32(inp[n]).astype(np.float64) for n in names})
-    ob, of_, od = (oracle.fwd(L, rt)["out"] for L in (Lb, Lf, Ld))
+    O = IMPLS[impl]
+    ob, of_, od = (O.fwd(L, rt)["out"] for L in (Lb, Lf, Ld))
     assert np.array_equal(ob, of_) and np.array_equal(ob, od)
-    gb = oracle.bwd(Lb, rt, inp["dout"])
-    gd = oracle.bwd(Ld, rt, synth.bf16_to_f32(inp["dout"]).astype(np.float64))
+    gb = O.bwd(Lb, rt, inp["dout"])
+    gd = O.bwd(Ld, rt, synth.bf16_to_f32(inp["dout"]).astype(np.float64))
     for n in gb:
         assert np.array_equal(gb[n], gd[n]), n
 
@@ -280,18 +300,20 @@ def test_storage_formats_agree():
 # ---------------------------------------------------------------- backward
 
 def _loss(L, rt, dout):
+    # the loss is evaluated by the row-loop forward for both forms: its
+    # derivatives are then what each form's backward must reproduce
     return float(np.sum(dout * oracle.fwd(L, rt)["out"]))
 
 
 FD_SHAPE = (6, 8, 4, 2, 12, 3)
 
 
-@pytest.fixture(scope="module")
-def fd_case():
+@pytest.fixture(scope="module", params=list(IMPLS))
+def fd_case(request):
     T, d, E, k, F, r = FD_SHAPE
     L, t, logits, dout = make(T, d, E, k, F, r, s=1.3, seed=7)
     rt = oracle.route(logits, k)
-    g = oracle.bwd(L, rt, dout)
+    g = IMPLS[request.param].bwd(L, rt, dout)
     return T, d, E, k, F, r, t, logits, dout, rt, g
 
 
@@ -354,13 +376,14 @@ def test_logit_gradient_matches_central_differences(fd_case):
     assert np.allclose(g["d_logits"].sum(1), 0.0, atol=1e-14)
 
 
-def test_empty_expert_gradients_are_exact_zeros():
+@impl_param
+def test_empty_expert_gradients_are_exact_zeros(impl):
     T, d, E, k, F, r = 8, 8, 6, 2, 8, 2
     L, t, logits, dout = make(T, d, E, k, F, r, s=2.0, seed=8)
     logits[:, 4:] = -50.0  # experts 4 and 5 never chosen
     rt = oracle.route(logits, k)
     assert rt["counts"][4] == 0 and rt["counts"][5] == 0
-    g = oracle.bwd(L, rt, dout)
+    g = IMPLS[impl].bwd(L, rt, dout)
     for n in ("da_gate", "db_gate", "da_up", "db_up", "da_down", "db_down"):
         assert np.all(g[n][4:] == 0.0)
 
@@ -378,6 +401,7 @@ def test_sampled_entry_points_agree_with_full_layer():
     assert np.array_equal(ft["out"], f["out"][toks])
     assert np.array_equal(bt["dx"], b["dx"][toks])
     assert np.array_equal(bt["d_logits"], b["d_logits"][toks])
+    assert np.array_equal(bt["d_topk_w"], b["d_topk_w"][toks])
     ex = [2, 7]
     lg = oracle.lora_grads(L, rt, inp["dout"], ex)
     for n in lg:
@@ -496,6 +520,19 @@ def test_nf4_levels_are_normal_quantiles():
         assert phi(-lv[7 - j] * qmax) == pytest.approx(0.5 + j / 7 * (p - 0.5), abs=1e-12)
 
 
+def test_nf4_levels_match_the_published_table():
+    """The 16 levels against the values the QLoRA paper's appendix prints
+    (float32 there, so agreement is to float32 rounding)."""
+    from oracle import nf4
+    with open(os.path.join(GOLDEN, "nf4_levels_qlora.json")) as f:
+        pub = np.array(json.load(f)["levels"], dtype=np.float64)
+    lv = nf4.levels()
+    assert np.max(np.abs(lv - pub)) <= 2.5e-7
+    # the float32 values are the float32 roundings of the fp64 levels, up to
+    # the last bit of the published rounding
+    assert np.max(np.abs(lv.astype(np.float32).astype(np.float64) - pub)) <= 1.2e-7
+
+
 def _erfinv_newton(y):
     import math
     x = 0.0
@@ -528,3 +565,19 @@ def test_bf16_rounding_ties_to_even():
     assert nf4.round_bf16(np.array([one + 3 * 2.0 ** -8]))[0] == one + 2.0 ** -6  # tie -> even (up)
     assert nf4.round_bf16(np.array([one + 3 * 2.0 ** -9]))[0] == one + 2.0 ** -7
     assert nf4.round_bf16(np.array([-0.0]))[0] == 0.0
+
+
+@pytest.mark.parametrize("cfg_name,tokens", [("tiny_fp32", None), ("qwen3_30b_a3b", 96)])
+def test_the_two_forms_agree_on_the_workloads(cfg_name, tokens):
+    """Both forms on stored workload inputs (fp32; bf16 on the first tokens of
+    the Qwen3-30B-A3B shapes, 128 experts, many of them with few rows), every
+    output and intermediate: they differ only in the summation order of fp64
+    dot products."""
+    cfg = synth.get_config(cfg_name)
+    inp = synth.make_inputs(cfg, seed=0, tokens=tokens)
+    L = oracle.Layer.from_config(cfg, inp, tokens=tokens)
+    rt = oracle.route(inp["logits"], cfg.k)
+    a = {**oracle.fwd(L, rt, intermediates=True), **oracle.bwd(L, rt, inp["dout"], intermediates=True)}
+    b = oracle_grouped.layer(L, rt, inp["dout"], intermediates=True)
+    for n in a:
+        assert rel_l2(b[n], a[n]) < 1e-12, n
