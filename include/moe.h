@@ -180,6 +180,22 @@ moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_r
                        int32_t *host_counts, void *ws, size_t ws_bytes, void *stream,
                        const moe_trace_t *trace);
 
+/* moe_route for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, outputs and errors as moe_route except that there is no
+ * workspace argument: the routing workspace comes from a device array inside
+ * the library (512 KiB on each GPU the library runs on, held until the
+ * process ends), which covers every problem moe_route accepts
+ * (MOE_E_UNSUPPORTED otherwise). The call allocates nothing; host_counts must
+ * be NULL or pinned host memory (a copy to pageable memory would allocate
+ * staging memory), else MOE_E_ARG. Every call on one GPU uses that GPU's one
+ * array: calls that overlap on one GPU (different streams or host threads
+ * without ordering between them) race and give undefined routing; order them
+ * on one stream. The stream must belong to the current device; the array's
+ * device address is looked up on the first call on each device. */
+moe_status_t moe_route_noalloc(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt,
+                               int32_t *host_counts, void *stream, const moe_trace_t *trace);
+
 /* Forward. x [T,d] -> out [T,d]. saved: NULL for inference (no backward
  * possible), else moe_saved_bytes(pb, keep_expert_out) bytes that moe_bwd
  * reads. ws: moe_fwd_workspace(pb, saved != NULL, keep_expert_out) bytes. */

@@ -39,7 +39,7 @@ MOE_K_COUNT = len(KERNELS)
 EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe_saved_bytes",
            "moe_route", "moe_fwd", "moe_bwd", "moe_status_str", "moe_router_workspace",
            "moe_router_fwd", "moe_router_bwd", "moe_saved_copy", "moe_nf4_dequant",
-           "moe_workspace_part"]
+           "moe_workspace_part", "moe_route_noalloc"]
 MOE_PART_Y, MOE_PART_DGU, MOE_PART_DXP = range(3)
 
 
@@ -93,6 +93,7 @@ for _f in (_lib.moe_route_workspace, _lib.moe_fwd_workspace, _lib.moe_bwd_worksp
            _lib.moe_saved_bytes):
     _f.restype = _sz
 _lib.moe_route.argtypes = [_P(Problem), _vp, _P(Routing), _vp, _vp, _sz, _vp, _P(Trace)]
+_lib.moe_route_noalloc.argtypes = [_P(Problem), _vp, _P(Routing), _vp, _vp, _P(Trace)]
 _lib.moe_fwd.argtypes = [_P(Problem), _vp, _P(Routing), _P(Weights), _vp, _vp, _i32, _vp, _sz,
                          _vp, _P(Trace)]
 _lib.moe_bwd.argtypes = [_P(Problem), _vp, _vp, _P(Routing), _P(Weights), _vp, _i32, _vp,
@@ -106,7 +107,7 @@ _lib.moe_router_bwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _vp, _vp, _vp, 
 _lib.moe_saved_copy.argtypes = [_P(Problem), _i32, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_nf4_dequant.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]
 _lib.moe_nf4_dequant.restype = _i32
-for _f in (_lib.moe_route, _lib.moe_fwd, _lib.moe_bwd, _lib.moe_router_fwd, _lib.moe_router_bwd,
+for _f in (_lib.moe_route, _lib.moe_route_noalloc, _lib.moe_fwd, _lib.moe_bwd, _lib.moe_router_fwd, _lib.moe_router_bwd,
            _lib.moe_saved_copy):
     _f.restype = _i32
 _lib.moe_status_str.argtypes = [_i32]
@@ -199,6 +200,21 @@ def moe_route(pb, logits, rt: dict, host_counts=None, ws=None, stream=None, trac
                         _ptr(ws), _nbytes(ws), _stream(stream),
                         ctypes.byref(trace) if trace is not None else None)
     _check(st, "moe_route")
+
+
+def moe_route_noalloc(pb, logits, rt: dict, host_counts=None, stream=None, trace=None):
+    """moe_route without a workspace: the library's own device scratch array
+    (for callers that cannot allocate). host_counts: None or a pinned CPU int32
+    tensor of at least E elements."""
+    hc = None
+    if host_counts is not None:
+        hc, nbytes, dt = _host_buffer(host_counts, "moe_route_noalloc host_counts")
+        if dt != "int32" or nbytes < 4 * pb.E:
+            raise MoeError(MOE_E_ARG, f"moe_route_noalloc host_counts: need int32[{pb.E}], got {dt} "
+                                      f"of {nbytes} bytes")
+    st = _lib.moe_route_noalloc(ctypes.byref(pb), _ptr(logits), ctypes.byref(_struct(Routing, rt)), hc,
+                                _stream(stream), ctypes.byref(trace) if trace is not None else None)
+    _check(st, "moe_route_noalloc")
 
 
 def moe_fwd(pb, x, rt: dict, w: dict, out, saved=None, keep_expert_out=False, ws=None,
