@@ -45,7 +45,9 @@ def parse():
     ap.add_argument("--no-nf4", dest="nf4", action="store_false",
                     help="skip the 4-bit weight dequantisation measurement")
     ap.add_argument("--offload-reps", type=int, default=3,
-                    help="repetitions of the saved-activation offload measurement (0 = skip)")
+                    help="repetitions of the stacked-layer offload measurement (0 = skip)")
+    ap.add_argument("--offload-layers", type=int, default=4,
+                    help="layers in the stacked-layer offload measurement")
     ap.add_argument("--whereloop-steps", type=int, default=3,
                     help="steps of the per-expert where() loop baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -346,43 +348,78 @@ def router_bench(torch, moe, synth, cfg, pb, x, hip, dev, iters=20):
             "note": "not part of the step: the workloads take logits as an input"}
 
 
-def offload_bench(torch, moe, pb, saved, keep, fwd, reps=3):
-    """moe_saved_copy of this layer's `saved` buffer to pinned host memory and
-    back on a copy stream: bandwidth of each direction, and the forward's time
-    alone and while an offload runs beside it (the double-buffered checkpoint
-    reload overlaps these copies with compute)."""
-    n = moe.saved_bytes(pb, keep)
-    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
-    copy = torch.cuda.Stream()
-    torch.cuda.synchronize()
+def stack_offload_bench(torch, moe, cfg, pb, x, logits, w, dout, keep, n=4, reps=3):
+    """n stacked layers of the workload's shape (the step's weights in every
+    layer, each layer's logits rolled by its index so each routes differently;
+    layer i+1's input is layer i's output) forward + backward, timed (a) with
+    a device `saved` buffer per layer and (b) with moe_stack_fwd / bwd, which
+    offload layers 0 .. n-3 to pinned host memory and reload them
+    double-buffered. Also the time of one layer's copy each way alone, so the
+    share of the copies the schedule hides is measured, not assumed."""
+    dev = x.device
+    dt = x.dtype
+    nbytes = moe.saved_bytes(pb, keep)
+    layers = []
+    for i in range(n):
+        L = {"logits": torch.roll(logits, shifts=i, dims=1).contiguous(), "w": w,
+             "rt": moe.alloc_routing(pb, dev), "grads": moe.alloc_grads(pb, dev),
+             "out": torch.empty_like(x), "dx": torch.empty_like(x),
+             "host_saved": torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) if i <= n - 3 else None}
+        layers.append(L)
+    for i, L in enumerate(layers):
+        L["x"] = x if i == 0 else layers[i - 1]["out"]
+        L["dout"] = dout if i == n - 1 else layers[i + 1]["dx"]
+    per_layer = [moe.alloc_bytes(nbytes, dev) for _ in range(n)]
+    ws_r = moe.alloc_bytes(moe.route_workspace(pb), dev)
+    ws_f = moe.alloc_bytes(moe.fwd_workspace(pb, True, keep), dev)
+    ws_b = moe.alloc_bytes(moe.bwd_workspace(pb), dev)
+    dsaved = [moe.alloc_bytes(nbytes, dev) for _ in range(2)]
+    ws = moe.alloc_bytes(moe.stack_workspace(pb, keep), dev)
+    cs = torch.cuda.Stream()
+    events = [torch.cuda.Event() for _ in range(4)]
+    for e in events:  # torch creates the HIP event at its first record
+        e.record()
+
+    def resident():
+        for L, sv in zip(layers, per_layer):
+            moe.moe_route(pb, L["logits"], L["rt"], ws=ws_r)
+            moe.moe_fwd(pb, L["x"], L["rt"], L["w"], L["out"], saved=sv, keep_expert_out=keep, ws=ws_f)
+        for L, sv in reversed(list(zip(layers, per_layer))):
+            moe.moe_bwd(pb, L["x"], L["dout"], L["rt"], L["w"], sv, keep, L["dx"], L["grads"], ws=ws_b)
+
+    def offloaded():
+        moe.moe_stack_fwd(pb, layers, keep, dsaved, cs, events, ws)
+        moe.moe_stack_bwd(pb, layers, keep, dsaved, cs, events, ws)
 
     def timed(fn):
-        best = float("inf")
-        for _ in range(reps):
+        ts = []
+        for _ in range(reps + 1):  # the first run warms up
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             fn()
             torch.cuda.synchronize()
-            best = min(best, time.perf_counter() - t0)
-        return best
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts[1:])[len(ts[1:]) // 2] * 1e3
 
-    d2h = timed(lambda: moe.moe_saved_copy(pb, keep, False, saved, host, copy_stream=copy))
-    h2d = timed(lambda: moe.moe_saved_copy(pb, keep, True, saved, host, copy_stream=copy))
-    f_alone = timed(fwd)
-    ev_start, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f_during = []
-    for _ in range(reps):
-        torch.cuda.synchronize()
-        moe.moe_saved_copy(pb, keep, False, saved, host, copy_stream=copy)
-        ev_start.record()
-        fwd()
-        ev_end.record()
-        torch.cuda.synchronize()
-        f_during.append(ev_start.elapsed_time(ev_end))
-    return {"bytes": n, "d2h_GBs": round(n / d2h / 1e9, 1), "h2d_GBs": round(n / h2d / 1e9, 1),
-            "fwd_ms": round(f_alone * 1e3, 3), "fwd_ms_during_offload": round(min(f_during), 3),
-            "offload_ms": round(d2h * 1e3, 3),
-            "note": "pinned host buffer, one copy stream; not part of the step"}
+    t_res = timed(resident)
+    ref_dx = layers[0]["dx"].clone()
+    t_off = timed(offloaded)
+    same = bool(torch.equal(layers[0]["dx"], ref_dx))
+    host = layers[0]["host_saved"]
+    d2h = timed(lambda: moe.moe_saved_copy(pb, keep, False, dsaved[0], host, copy_stream=cs))
+    h2d = timed(lambda: moe.moe_saved_copy(pb, keep, True, dsaved[0], host, copy_stream=cs))
+    copies = (n - 2) * (d2h + h2d)
+    hidden = 1.0 - (t_off - t_res) / copies if copies > 0 else None
+    return {"layers": n, "saved_bytes_per_layer": nbytes,
+            "device_activation_bytes": {"per_layer_buffers": n * nbytes, "double_buffered": 2 * nbytes},
+            "fwd_bwd_ms_per_layer_buffers": round(t_res, 3), "fwd_bwd_ms_offloaded": round(t_off, 3),
+            "copy_ms_per_layer": {"d2h": round(d2h, 3), "h2d": round(h2d, 3)},
+            "copy_GBs": {"d2h": round(nbytes / d2h / 1e6, 1), "h2d": round(nbytes / h2d / 1e6, 1)},
+            "copies_ms_total": round(copies, 3),
+            "hidden_fraction": None if hidden is None else round(max(0.0, min(1.0, hidden)), 3),
+            "dx_equal_to_per_layer_buffers": same,
+            "note": "median of %d runs each; hidden_fraction = 1 - (offloaded - resident) / (time of the "
+                    "2(n-2) copies alone); layers n-2 and n-1 stay on the device" % reps}
 
 
 def nf4_bench(torch, moe, synth, cfg, dev, reps=5):
@@ -648,10 +685,8 @@ def main():
     if cfg.dtype == "bf16" and args.nf4:
         rec["nf4_dequant"] = nf4_bench(torch, moe, synth, cfg, dev)
     if cfg.backward and args.offload_reps > 0:
-        rec["saved_offload"] = offload_bench(
-            torch, moe, pb, saved, keep,
-            lambda: moe.moe_fwd(pb, x, rt, w, out, saved=saved, keep_expert_out=keep, ws=ws_f,
-                                stream=stream), args.offload_reps)
+        rec["stack_offload"] = stack_offload_bench(torch, moe, cfg, pb, x, logits, w, dout, keep,
+                                                   n=args.offload_layers, reps=args.offload_reps)
     if args.whereloop_steps > 0 and cfg.dtype == "bf16":
         # the library's forward and backward alone (routing excluded), to set
         # against the loop's

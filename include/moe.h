@@ -278,6 +278,60 @@ moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *
 moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to_device, void *saved,
                             void *host, void *wait_event, void *copy_stream, void *done_event);
 
+/* A stack of layers with the double-buffered checkpoint offload and reload
+ * of the Unsloth x NVIDIA blog (section "core idea / structure / how it
+ * works", checkpoint paragraph): each layer's `saved` activations go to
+ * pinned host memory during the forward and come back for the backward,
+ * through two device buffers that take turns, so that the backward of one
+ * layer reads buffer A while a copy stream brings the next layer back into
+ * buffer B. Device memory for activations is two layers' `saved` instead of
+ * n. Layer i uses buffer saved[i % 2].
+ *   moe_stack_fwd: for i = 0 .. n-1 on `stream`: wait for the offload of
+ *     layer i-2 (it reads saved[i % 2]); moe_route (logits -> rt); moe_fwd
+ *     into saved[i % 2]; then, for i <= n-3, copy_stream copies saved[i % 2]
+ *     to host_saved after the forward. Layers n-2 and n-1 stay on the device.
+ *   moe_stack_bwd (after moe_stack_fwd with the same arguments and nothing
+ *     else written to the two buffers in between): for i = n-1 down to 0:
+ *     layers i <= n-3 wait for their reload; moe_bwd from saved[i % 2]; then
+ *     copy_stream reloads layer i-2 into saved[i % 2], under the backward of
+ *     layer i-1.
+ * Every layer has the problem pb. The caller wires the stack: layer i+1's x
+ * is typically layer i's out, and layer i's dout layer i+1's dx. Results are
+ * bit-identical to moe_route + moe_fwd + moe_bwd per layer with a saved
+ * buffer each. */
+typedef struct {
+    const float *logits;           /* [T,E] router logits of the layer        */
+    const moe_routing_t *rt;       /* routing outputs (written by the fwd)    */
+    const moe_weights_t *w;        /* the layer's weights                     */
+    const void *x;                 /* [T,d] layer input                       */
+    void *out;                     /* [T,d] layer output (fwd)                */
+    const void *dout;              /* [T,d] gradient of out (bwd)             */
+    void *dx;                      /* [T,d] gradient of x (bwd)               */
+    const moe_lora_grads_t *grads; /* LoRA gradients (bwd)                    */
+    float *d_topk_w, *d_logits;    /* optional, as in moe_bwd (bwd)           */
+    void *host_saved;              /* (host) pinned, moe_saved_bytes bytes; needed for layers 0 .. n-3 */
+} moe_stack_layer_t;
+
+typedef struct {
+    void *saved[2];      /* two device buffers of moe_saved_bytes(pb, keep) bytes (saved[1] unused if n = 1) */
+    void *copy_stream;   /* hipStream_t of the copies; must differ from `stream` when n >= 3 */
+    void *events[4];     /* four hipEvent_t the caller created (needed when n >= 3) */
+} moe_offload_t;
+
+/* Workspace bytes of moe_stack_fwd / moe_stack_bwd (the largest of the
+ * route, forward and backward workspaces: they run one after another on one
+ * stream); 0 for an invalid problem. */
+size_t moe_stack_workspace(const moe_problem_t *pb, int keep_expert_out);
+
+/* Errors: MOE_E_ARG for n < 1, NULL or misaligned buffers, equal device
+ * buffers, host_saved of a layer <= n-3 that is not pinned, copy_stream equal
+ * to stream or missing events when n >= 3; MOE_E_WORKSPACE below
+ * moe_stack_workspace. All checks run before anything is enqueued. */
+moe_status_t moe_stack_fwd(const moe_problem_t *pb, int n, const moe_stack_layer_t *layers, int keep_expert_out,
+                           const moe_offload_t *off, void *ws, size_t ws_bytes, void *stream);
+moe_status_t moe_stack_bwd(const moe_problem_t *pb, int n, const moe_stack_layer_t *layers, int keep_expert_out,
+                           const moe_offload_t *off, void *ws, size_t ws_bytes, void *stream);
+
 /* 4-bit NormalFloat (NF4) frozen base weights, the 4-bit QLoRA variant the
  * pages name for MoE fine-tuning (Unsloth 2026 wiki chapter, model-support
  * table; QLoRA's NF4 in the GPU MODE lecture 32 notes, closing open

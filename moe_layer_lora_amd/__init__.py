@@ -39,7 +39,8 @@ MOE_K_COUNT = len(KERNELS)
 EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe_saved_bytes",
            "moe_route", "moe_fwd", "moe_bwd", "moe_status_str", "moe_router_workspace",
            "moe_router_fwd", "moe_router_bwd", "moe_saved_copy", "moe_nf4_dequant",
-           "moe_workspace_part", "moe_route_noalloc"]
+           "moe_workspace_part", "moe_route_noalloc", "moe_stack_workspace", "moe_stack_fwd",
+           "moe_stack_bwd"]
 MOE_PART_Y, MOE_PART_DGU, MOE_PART_DXP = range(3)
 
 
@@ -74,6 +75,19 @@ class LoraGrads(ctypes.Structure):
                 ("da_gate", "db_gate", "da_up", "db_up", "da_down", "db_down")]
 
 
+class StackLayer(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("rt", ctypes.POINTER(Routing)),
+                ("w", ctypes.POINTER(Weights)), ("x", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("dout", ctypes.c_void_p), ("dx", ctypes.c_void_p),
+                ("grads", ctypes.POINTER(LoraGrads)), ("d_topk_w", ctypes.c_void_p),
+                ("d_logits", ctypes.c_void_p), ("host_saved", ctypes.c_void_p)]
+
+
+class Offload(ctypes.Structure):
+    _fields_ = [("saved", ctypes.c_void_p * 2), ("copy_stream", ctypes.c_void_p),
+                ("events", ctypes.c_void_p * 4)]
+
+
 class Trace(ctypes.Structure):
     _fields_ = [("start", ctypes.c_void_p * MOE_K_COUNT), ("stop", ctypes.c_void_p * MOE_K_COUNT)]
 
@@ -100,6 +114,12 @@ _lib.moe_bwd.argtypes = [_P(Problem), _vp, _vp, _P(Routing), _P(Weights), _vp, _
                          _P(LoraGrads), _vp, _vp, _vp, _sz, _vp, _P(Trace)]
 _lib.moe_workspace_part.argtypes = [_P(Problem), _i32, _i32, _i32]
 _lib.moe_workspace_part.restype = _sz
+_lib.moe_stack_workspace.argtypes = [_P(Problem), _i32]
+_lib.moe_stack_workspace.restype = _sz
+_lib.moe_stack_fwd.argtypes = [_P(Problem), _i32, _P(StackLayer), _i32, _P(Offload), _vp, _sz, _vp]
+_lib.moe_stack_bwd.argtypes = [_P(Problem), _i32, _P(StackLayer), _i32, _P(Offload), _vp, _sz, _vp]
+_lib.moe_stack_fwd.restype = _i32
+_lib.moe_stack_bwd.restype = _i32
 _lib.moe_router_workspace.argtypes = [_P(Problem)]
 _lib.moe_router_workspace.restype = _sz
 _lib.moe_router_fwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _P(Trace)]
@@ -276,6 +296,59 @@ def moe_saved_copy(pb, keep_expert_out, to_device, saved, host, wait_event=None,
     st = _lib.moe_saved_copy(ctypes.byref(pb), int(keep_expert_out), int(to_device), _ptr(saved), hp,
                              ev(wait_event), _stream(copy_stream), ev(done_event))
     _check(st, "moe_saved_copy")
+
+
+def stack_workspace(pb: Problem, keep_expert_out: bool) -> int:
+    return _lib.moe_stack_workspace(ctypes.byref(pb), int(keep_expert_out))
+
+
+def _stack_args(layers, saved, copy_stream, events):
+    """ctypes arrays for the stack calls; the returned tuple keeps every
+    referenced structure alive for the duration of the call."""
+    keep = []
+    arr = (StackLayer * len(layers))()
+    for i, L in enumerate(layers):
+        rt, w = _struct(Routing, L["rt"]), _struct(Weights, L["w"])
+        g = _struct(LoraGrads, L["grads"]) if L.get("grads") is not None else None
+        keep += [rt, w, g]
+        hs = L.get("host_saved")
+        arr[i] = StackLayer(_ptr(L.get("logits")), ctypes.pointer(rt), ctypes.pointer(w), _ptr(L.get("x")),
+                            _ptr(L.get("out")), _ptr(L.get("dout")), _ptr(L.get("dx")),
+                            ctypes.pointer(g) if g is not None else None, _ptr(L.get("d_topk_w")),
+                            _ptr(L.get("d_logits")),
+                            hs if (hs is None or isinstance(hs, int)) else _host_buffer(hs, "host_saved")[0])
+
+    def ev(e):
+        if e is None or isinstance(e, int):
+            return e
+        h = e.cuda_event
+        if not h:
+            raise MoeError(MOE_E_ARG, "stack events: a torch.cuda.Event has no HIP event until it is "
+                                      "first recorded; record each once before passing it")
+        return h
+    off = Offload((ctypes.c_void_p * 2)(_ptr(saved[0]), _ptr(saved[1]) if len(saved) > 1 else None),
+                  None if copy_stream is None else _stream(copy_stream),
+                  (ctypes.c_void_p * 4)(*[ev(e) for e in events]))
+    return arr, off, keep
+
+
+def moe_stack_fwd(pb, layers: list, keep_expert_out, saved, copy_stream, events, ws, stream=None):
+    """Forward of a stack of layers with saved activations offloaded to each
+    layer's pinned host_saved through the two device buffers `saved`.
+    layers: dicts with logits, rt, w, x, out, host_saved (see moe.h)."""
+    arr, off, _keep = _stack_args(layers, saved, copy_stream, events)
+    st = _lib.moe_stack_fwd(ctypes.byref(pb), len(layers), arr, int(keep_expert_out), ctypes.byref(off),
+                            _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "moe_stack_fwd")
+
+
+def moe_stack_bwd(pb, layers: list, keep_expert_out, saved, copy_stream, events, ws, stream=None):
+    """Backward of the stack moe_stack_fwd ran: layers additionally carry dout,
+    dx, grads and optionally d_topk_w / d_logits."""
+    arr, off, _keep = _stack_args(layers, saved, copy_stream, events)
+    st = _lib.moe_stack_bwd(ctypes.byref(pb), len(layers), arr, int(keep_expert_out), ctypes.byref(off),
+                            _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "moe_stack_bwd")
 
 
 def moe_nf4_dequant(codes, scales, rows, cols, out, stream=None):

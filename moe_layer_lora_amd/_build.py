@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "layer.hip", "router.hip", "nf4.hip", "api.hip", "noalloc.hip"]
+SOURCES = ["route.hip", "layer.hip", "router.hip", "nf4.hip", "api.hip", "noalloc.hip", "offload.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -213,6 +213,8 @@ size_t moe_saved_bytes(const moe_problem_t *pb, int keep_expert_out) {
 namespace moe {
 namespace api {
 
+moe_status_t problem_status(const moe_problem_t *pb) { return check_problem(pb); }
+
 // Argument checks of a routing call, without its workspace: MOE_OK and the
 // workspace bytes it needs in *ws_bytes, or the error.
 moe_status_t route_check(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt, size_t *ws_bytes) {

@@ -9,6 +9,10 @@
 namespace moe {
 namespace api {
 
+// MOE_OK if the library supports the problem, else the status every call
+// returns for it
+moe_status_t problem_status(const moe_problem_t *pb);
+
 // Argument checks of a routing call, without its workspace: MOE_OK and the
 // workspace bytes it needs in *ws_bytes, or the error.
 moe_status_t route_check(const moe_problem_t *pb, const float *logits, const moe_routing_t *rt, size_t *ws_bytes);

@@ -1,0 +1,127 @@
+// offload.hip - a stack of MoE layers with their saved activations offloaded
+// to pinned host memory in the forward and reloaded, double-buffered, in the
+// backward: the checkpoint reload of the Unsloth x NVIDIA blog (section "core
+// idea / structure / how it works", checkpoint paragraph), where two device
+// buffers take turns so that the backward of one layer reads buffer A while
+// a copy stream brings the next layer's activations back into buffer B.
+//
+// Host code only: it orders moe_route / moe_fwd / moe_bwd on the compute
+// stream and the copies on the copy stream with the caller's four events.
+// Buffer of layer i: saved[i % 2].
+//  forward,  layer i: wait until the offload of layer i - 2 has finished
+//            reading saved[i % 2]; route; forward into saved[i % 2]; then
+//            (layers 0 .. n-3 only) the copy stream copies it to host i.
+//  backward, layer i (n-1 down to 0): layers n-1 and n-2 are still on the
+//            device; a lower layer waits for its reload. After the backward
+//            of layer i, saved[i % 2] is free and the copy stream reloads
+//            layer i - 2 into it, under the backward of layer i - 1.
+#include <hip/hip_runtime.h>
+
+#include "moe.h"
+#include "api_internal.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+bool a16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+moe_status_t hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+// checks shared by both directions; *bytes = one layer's saved bytes
+moe_status_t check_stack(const moe_problem_t *pb, int n, const moe_stack_layer_t *layers, int keep,
+                         const moe_offload_t *off, size_t ws_bytes, void *stream, bool bwd, size_t *bytes) {
+    const moe_status_t pst = moe::api::problem_status(pb);
+    if (pst != MOE_OK) return pst;
+    const size_t ws_need = moe_stack_workspace(pb, keep);
+    if (n < 1 || !layers || !off) return MOE_E_ARG;
+    if (ws_bytes < ws_need) return MOE_E_WORKSPACE;
+    *bytes = moe_saved_bytes(pb, keep);
+    if (!a16(off->saved[0]) || (n > 1 && !a16(off->saved[1]))) return MOE_E_ARG;
+    if (n > 1 && off->saved[0] == off->saved[1]) return MOE_E_ARG;
+    if (n >= 3) {
+        if (off->copy_stream == stream) return MOE_E_ARG;  // the copies must run beside the compute
+        for (int i = 0; i < 4; ++i)
+            if (!off->events[i]) return MOE_E_ARG;
+    }
+    for (int i = 0; i < n; ++i) {
+        const moe_stack_layer_t &L = layers[i];
+        if (!L.rt || !L.w) return MOE_E_ARG;
+        if (pb->T > 0 && (!a16(L.x) || (!bwd && (!a16(L.logits) || !a16(L.out)))))
+            return MOE_E_ARG;
+        if (bwd && (!L.grads || (pb->T > 0 && (!a16(L.dout) || !a16(L.dx))))) return MOE_E_ARG;
+        if (bwd && (L.d_topk_w || L.d_logits) && !keep) return MOE_E_ARG;
+        if (i <= n - 3 && (!L.host_saved || !moe::api::pinned_host(L.host_saved))) return MOE_E_ARG;
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_stack_workspace(const moe_problem_t *pb, int keep_expert_out) {
+    const size_t r = moe_route_workspace(pb), f = moe_fwd_workspace(pb, 1, keep_expert_out),
+                 b = moe_bwd_workspace(pb);
+    if (moe::api::problem_status(pb) != MOE_OK) return 0;
+    size_t m = r > f ? r : f;
+    m = m > b ? m : b;
+    return (m + kAlign - 1) / kAlign * kAlign;
+}
+
+moe_status_t moe_stack_fwd(const moe_problem_t *pb, int n, const moe_stack_layer_t *layers, int keep_expert_out,
+                           const moe_offload_t *off, void *ws, size_t ws_bytes, void *stream) {
+    size_t bytes = 0;
+    moe_status_t st = check_stack(pb, n, layers, keep_expert_out, off, ws_bytes, stream, false, &bytes);
+    if (st != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(off->copy_stream);
+    hipEvent_t fwd_done[2] = {static_cast<hipEvent_t>(off->events[0]), static_cast<hipEvent_t>(off->events[1])};
+    hipEvent_t copy_done[2] = {static_cast<hipEvent_t>(off->events[2]), static_cast<hipEvent_t>(off->events[3])};
+    for (int i = 0; i < n; ++i) {
+        const moe_stack_layer_t &L = layers[i];
+        void *buf = off->saved[i % 2];
+        // the offload of layer i - 2 reads this buffer: it must finish first
+        if (i >= 2 && (st = hip_ok(hipStreamWaitEvent(s, copy_done[i % 2], 0))) != MOE_OK) return st;
+        if ((st = moe_route(pb, L.logits, L.rt, nullptr, ws, ws_bytes, stream, nullptr)) != MOE_OK) return st;
+        if ((st = moe_fwd(pb, L.x, L.rt, L.w, L.out, buf, keep_expert_out, ws, ws_bytes, stream, nullptr)) != MOE_OK)
+            return st;
+        if (i <= n - 3) {  // layers n-2 and n-1 stay on the device for the backward
+            if ((st = hip_ok(hipEventRecord(fwd_done[i % 2], s))) != MOE_OK) return st;
+            if ((st = hip_ok(hipStreamWaitEvent(cs, fwd_done[i % 2], 0))) != MOE_OK) return st;
+            if ((st = hip_ok(hipMemcpyAsync(L.host_saved, buf, bytes, hipMemcpyDeviceToHost, cs))) != MOE_OK)
+                return st;
+            if ((st = hip_ok(hipEventRecord(copy_done[i % 2], cs))) != MOE_OK) return st;
+        }
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_stack_bwd(const moe_problem_t *pb, int n, const moe_stack_layer_t *layers, int keep_expert_out,
+                           const moe_offload_t *off, void *ws, size_t ws_bytes, void *stream) {
+    size_t bytes = 0;
+    moe_status_t st = check_stack(pb, n, layers, keep_expert_out, off, ws_bytes, stream, true, &bytes);
+    if (st != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(off->copy_stream);
+    hipEvent_t bwd_done[2] = {static_cast<hipEvent_t>(off->events[0]), static_cast<hipEvent_t>(off->events[1])};
+    hipEvent_t copy_done[2] = {static_cast<hipEvent_t>(off->events[2]), static_cast<hipEvent_t>(off->events[3])};
+    for (int i = n - 1; i >= 0; --i) {
+        const moe_stack_layer_t &L = layers[i];
+        void *buf = off->saved[i % 2];
+        // layers below n-2 were reloaded into their buffer: wait for the copy
+        if (i <= n - 3 && (st = hip_ok(hipStreamWaitEvent(s, copy_done[i % 2], 0))) != MOE_OK) return st;
+        if ((st = moe_bwd(pb, L.x, L.dout, L.rt, L.w, buf, keep_expert_out, L.dx, L.grads, L.d_topk_w, L.d_logits,
+                          ws, ws_bytes, stream, nullptr)) != MOE_OK)
+            return st;
+        if (i - 2 >= 0) {  // the buffer is free: bring layer i - 2 back into it under layer i - 1's backward
+            if ((st = hip_ok(hipEventRecord(bwd_done[i % 2], s))) != MOE_OK) return st;
+            if ((st = hip_ok(hipStreamWaitEvent(cs, bwd_done[i % 2], 0))) != MOE_OK) return st;
+            if ((st = hip_ok(hipMemcpyAsync(buf, layers[i - 2].host_saved, bytes, hipMemcpyHostToDevice, cs))) !=
+                MOE_OK)
+                return st;
+            if ((st = hip_ok(hipEventRecord(copy_done[i % 2], cs))) != MOE_OK) return st;
+        }
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

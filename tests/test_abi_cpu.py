@@ -222,3 +222,31 @@ def test_binding_checks_host_buffers():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_saved_copy(p, False, False, 1 << 20, short, copy_stream=0)
     assert ei.value.status == moe.MOE_E_ARG
+
+
+def test_stack_argument_errors_before_launch():
+    p, L, A = pb(), moe.lib(), 1 << 20
+    assert moe.stack_workspace(pb(k=0), False) == 0
+    need = moe.stack_workspace(p, False)
+    assert need == max(moe.route_workspace(p), moe.fwd_workspace(p, True, False), moe.bwd_workspace(p))
+    rt, w, g = _routing(A), _weights(A), _grads(A)
+
+    def layers(n, host=A):
+        arr = (moe.StackLayer * n)()
+        for i in range(n):
+            arr[i] = moe.StackLayer(A, ctypes.pointer(rt), ctypes.pointer(w), A, A, A, A,
+                                    ctypes.pointer(g), None, None, host)
+        return arr
+
+    def off(s0=A, s1=2 * A, cs=3 * A, ev=4 * A):
+        return moe.Offload((ctypes.c_void_p * 2)(s0, s1), cs, (ctypes.c_void_p * 4)(ev, ev, ev, ev))
+
+    for fn in (L.moe_stack_fwd, L.moe_stack_bwd):
+        assert fn(ctypes.byref(p), 0, layers(1), 0, ctypes.byref(off()), A, need, None) == moe.MOE_E_ARG
+        assert fn(ctypes.byref(p), 2, layers(2), 0, ctypes.byref(off()), A, need - 1, None) == moe.MOE_E_WORKSPACE
+        assert fn(ctypes.byref(p), 2, layers(2), 0, ctypes.byref(off(s1=A)), A, need, None) == moe.MOE_E_ARG
+        assert fn(ctypes.byref(p), 3, layers(3), 0, ctypes.byref(off(cs=None)), A, need, None) == moe.MOE_E_ARG
+        assert fn(ctypes.byref(p), 3, layers(3), 0, ctypes.byref(off(ev=None)), A, need, None) == moe.MOE_E_ARG
+        # host memory of the offloaded layers must be pinned (a fake address is not)
+        assert fn(ctypes.byref(p), 3, layers(3), 0, ctypes.byref(off()), A, need, None) == moe.MOE_E_ARG
+        assert fn(ctypes.byref(pb(k=0)), 1, layers(1), 0, ctypes.byref(off()), A, need, None) == moe.MOE_E_ARG
