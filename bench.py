@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay of the step")
     ap.add_argument("--no-nf4", dest="nf4", action="store_false",
-                    help="skip the 4-bit weight dequantisation measurement")
+                    help="skip the step on 4-bit NormalFloat base weights")
     ap.add_argument("--offload-reps", type=int, default=3,
                     help="repetitions of the stacked-layer offload measurement (0 = skip)")
     ap.add_argument("--offload-layers", type=int, default=4,
@@ -422,37 +422,78 @@ def stack_offload_bench(torch, moe, cfg, pb, x, logits, w, dout, keep, n=4, reps
                     "2(n-2) copies alone); layers n-2 and n-1 stay on the device" % reps}
 
 
-def nf4_bench(torch, moe, synth, cfg, dev, reps=5):
-    """Dequantisation of 4-bit NormalFloat frozen weights (W_g, W_u, W_d of the
-    layer) to bf16: ms for all three and the HBM rate (code + scale bytes read,
-    bf16 bytes written)."""
-    import numpy as np
-    mats = [(cfg.E * cfg.F, cfg.d, 20), (cfg.E * cfg.F, cfg.d, 21), (cfg.E * cfg.d, cfg.F, 22)]
-    if any(c % 64 for _, c, _ in mats):
+def nf4_step_bench(torch, moe, synth, cfg, pb, ctx, hip, bf16_step_ms, steps, warmup):
+    """The same step with the frozen base weights W_g, W_u, W_d in 4-bit
+    NormalFloat (codes + one fp32 scale per 64 weights; random codes, scales
+    for a weight standard deviation of about 0.02): moe_fwd_nf4 / moe_bwd_nf4
+    dequantise every weight tile as the grouped GEMMs stage it into LDS, so no
+    bf16 copy of a weight exists. Step time against the bf16 step, the four
+    grouped GEMMs' times, and the weight bytes each form keeps resident."""
+    dev = ctx["x"].device
+    keys = (("gate", cfg.E * cfg.F, cfg.d, 20), ("up", cfg.E * cfg.F, cfg.d, 21),
+            ("down", cfg.E * cfg.d, cfg.F, 22))
+    if cfg.d % 64 or cfg.F % 64:
         return None
-    bufs = []
-    for rows, cols, tau in mats:
+    q4 = {}
+    for name, rows, cols, tau in keys:
         q = synth.make_nf4(rows, cols, seed=0, tensor=tau)
-        bufs.append((torch.from_numpy(q["codes"]).to(dev), torch.from_numpy(q["scales"]).to(dev),
-                     torch.empty((rows, cols), dtype=torch.bfloat16, device=dev), rows, cols))
-    stream = torch.cuda.current_stream()
+        q4["codes_" + name] = torch.from_numpy(q["codes"]).to(dev)
+        q4["scales_" + name] = torch.from_numpy(q["scales"]).to(dev)
+    lora = {k: v for k, v in ctx["w"].items() if not k.startswith("w_")}
+    keep = ctx["keep"]
+    st = torch.cuda.current_stream()
 
-    def run():
-        for c, s, o, rows, cols in bufs:
-            moe.moe_nf4_dequant(c, s, rows, cols, o, stream=stream)
-    run()
+    def step(trace=None):
+        moe.moe_route(pb, ctx["logits"], ctx["rt"], ws=ctx["ws_r"], stream=st, trace=trace)
+        moe.moe_fwd_nf4(pb, ctx["x"], ctx["rt"], lora, q4, ctx["out"], saved=ctx["saved"], keep_expert_out=keep,
+                        ws=ctx["ws_f"], stream=st, trace=trace)
+        if cfg.backward:
+            moe.moe_bwd_nf4(pb, ctx["x"], ctx["dout"], ctx["rt"], lora, q4, ctx["saved"], keep, ctx["dx"],
+                            ctx["grads"], d_topk_w=ctx["dtw"], d_logits=ctx["dlg"], ws=ctx["ws_b"], stream=st,
+                            trace=trace)
+
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        run()
-    e1.record()
+    ev = [(hip.event(), hip.event()) for _ in range(steps)]
+    for a, b in ev:
+        hip.record(a, st.cuda_stream)
+        step()
+        hip.record(b, st.cuda_stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    nbytes = sum(c.numel() + s.numel() * 4 + o.numel() * 2 for c, s, o, _, _ in bufs)
-    return {"ms": round(ms, 4), "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": int(nbytes),
-            "weights": int(sum(r * c for _, _, _, r, c in bufs)),
-            "note": "W_g, W_u, W_d from 4-bit NormalFloat to bf16; not part of the step"}
+    ms = sorted(hip.elapsed_ms(a, b) for a, b in ev)
+    # per-GEMM times from traced steps after the timed ones
+    names = [n for n in ("gateup", "down", "down_bwd", "gateup_bwd") if cfg.backward or n in ("gateup", "down")]
+    traces = []
+    for _ in range(min(steps, 10)):
+        tr = moe.Trace()
+        for n in names:
+            i = moe.KERNELS.index(n)
+            tr.start[i], tr.stop[i] = hip.event(), hip.event()
+        traces.append(tr)
+        step(tr)
+    torch.cuda.synchronize()
+    kms = {}
+    for n in names:
+        i = moe.KERNELS.index(n)
+        v = [hip.elapsed_ms(tr.start[i], tr.stop[i]) for tr in traces]
+        kms[n] = round(sum(v) / len(v), 4)
+    for tr in traces:
+        for n in names:
+            i = moe.KERNELS.index(n)
+            hip.destroy(tr.start[i])
+            hip.destroy(tr.stop[i])
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    med = ms[len(ms) // 2]
+    nf4_bytes = sum(v.numel() * v.element_size() for v in q4.values())
+    bf16_bytes = sum(rows * cols * 2 for _, rows, cols, _ in keys)
+    return {"ms_per_step_median": round(med, 4), "ms_per_step_min": round(ms[0], 4),
+            "ratio_to_bf16_step": round(med / bf16_step_ms, 3), "gemm_kernels_ms": kms,
+            "base_weight_bytes": {"nf4": int(nf4_bytes), "bf16": int(bf16_bytes)},
+            "note": "route + moe_fwd_nf4 + moe_bwd_nf4: NF4 codes dequantised inside the grouped GEMMs' "
+                    "B-tile staging; no dequantisation pass, no bf16 weight copy"}
 
 
 def graph_replay(torch, step, out, dx, steps):
@@ -683,7 +724,12 @@ def main():
     if cfg.dtype == "bf16":
         rec["router_projection"] = router_bench(torch, moe, synth, cfg, pb, x, hip, dev)
     if cfg.dtype == "bf16" and args.nf4:
-        rec["nf4_dequant"] = nf4_bench(torch, moe, synth, cfg, dev)
+        ctx = {"x": x, "logits": logits, "dout": dout, "w": w, "rt": rt, "ws_r": ws_r, "ws_f": ws_f,
+               "ws_b": ws_b if cfg.backward else None, "saved": saved, "keep": keep, "out": out,
+               "dx": dx if cfg.backward else None, "grads": grads if cfg.backward else None,
+               "dtw": dtw if cfg.backward else None, "dlg": dlg if cfg.backward else None}
+        rec["nf4_step"] = nf4_step_bench(torch, moe, synth, cfg, pb, ctx, hip, step_ms[len(step_ms) // 2],
+                                         args.steps, args.warmup)
     if cfg.backward and args.offload_reps > 0:
         rec["stack_offload"] = stack_offload_bench(torch, moe, cfg, pb, x, logits, w, dout, keep,
                                                    n=args.offload_layers, reps=args.offload_reps)

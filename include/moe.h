@@ -353,6 +353,34 @@ moe_status_t moe_stack_bwd(const moe_problem_t *pb, int n, const moe_stack_layer
 moe_status_t moe_nf4_dequant(const uint8_t *codes, const float *scales, int64_t rows, int32_t cols, void *out,
                              void *stream);
 
+/* The forward and backward with the frozen base weights W_gate, W_up, W_down
+ * held in 4-bit NormalFloat (the 4-bit QLoRA variant the pages name for MoE
+ * fine-tuning: Unsloth 2026 wiki chapter, model-support table; QLoRA's NF4 in
+ * the GPU MODE lecture 32 notes, closing open questions), dequantised inside
+ * the grouped GEMMs as each weight tile is staged into LDS: no bf16 copy of
+ * a weight is ever written to memory. Format as for moe_nf4_dequant; the
+ * tile the GEMM multiplies is exactly the bf16 one moe_nf4_dequant would have
+ * written, so moe_fwd_nf4 / moe_bwd_nf4 give bit-identical results to
+ * moe_nf4_dequant followed by moe_fwd / moe_bwd on the dequantised weights.
+ * Split-LoRA is unchanged (A and B stay in dtype).
+ *   codes_gate, codes_up [E*F, d/2], codes_down [E*d, F/2] uint8 (16-byte aligned)
+ *   scales_gate, scales_up [E*F, d/64], scales_down [E*d, F/64] float32 (4-byte aligned)
+ * Arguments otherwise as moe_fwd / moe_bwd (same workspaces and `saved`);
+ * w->w_gate, w_up, w_down are not read and may be NULL. Requires dtype bf16
+ * and d, F multiples of 64 (else MOE_E_UNSUPPORTED). */
+typedef struct {
+    const uint8_t *codes_gate, *codes_up, *codes_down;
+    const float *scales_gate, *scales_up, *scales_down;
+} moe_nf4_base_t;
+
+moe_status_t moe_fwd_nf4(const moe_problem_t *pb, const void *x, const moe_routing_t *rt, const moe_weights_t *w,
+                         const moe_nf4_base_t *q4, void *out, void *saved, int keep_expert_out, void *ws,
+                         size_t ws_bytes, void *stream, const moe_trace_t *trace);
+moe_status_t moe_bwd_nf4(const moe_problem_t *pb, const void *x, const void *dout, const moe_routing_t *rt,
+                         const moe_weights_t *w, const moe_nf4_base_t *q4, const void *saved, int keep_expert_out,
+                         void *dx, const moe_lora_grads_t *grads, float *d_topk_w, float *d_logits, void *ws,
+                         size_t ws_bytes, void *stream, const moe_trace_t *trace);
+
 /* Static string naming a status code. */
 const char *moe_status_str(moe_status_t st);
 

@@ -40,7 +40,7 @@ EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe
            "moe_route", "moe_fwd", "moe_bwd", "moe_status_str", "moe_router_workspace",
            "moe_router_fwd", "moe_router_bwd", "moe_saved_copy", "moe_nf4_dequant",
            "moe_workspace_part", "moe_route_noalloc", "moe_stack_workspace", "moe_stack_fwd",
-           "moe_stack_bwd"]
+           "moe_stack_bwd", "moe_fwd_nf4", "moe_bwd_nf4"]
 MOE_PART_Y, MOE_PART_DGU, MOE_PART_DXP = range(3)
 
 
@@ -68,6 +68,11 @@ class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down",
                  "b_down")]
+
+
+class Nf4Base(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("codes_gate", "codes_up", "codes_down", "scales_gate", "scales_up", "scales_down")]
 
 
 class LoraGrads(ctypes.Structure):
@@ -120,6 +125,12 @@ _lib.moe_stack_fwd.argtypes = [_P(Problem), _i32, _P(StackLayer), _i32, _P(Offlo
 _lib.moe_stack_bwd.argtypes = [_P(Problem), _i32, _P(StackLayer), _i32, _P(Offload), _vp, _sz, _vp]
 _lib.moe_stack_fwd.restype = _i32
 _lib.moe_stack_bwd.restype = _i32
+_lib.moe_fwd_nf4.argtypes = [_P(Problem), _vp, _P(Routing), _P(Weights), _P(Nf4Base), _vp, _vp, _i32, _vp,
+                             _sz, _vp, _P(Trace)]
+_lib.moe_bwd_nf4.argtypes = [_P(Problem), _vp, _vp, _P(Routing), _P(Weights), _P(Nf4Base), _vp, _i32, _vp,
+                             _P(LoraGrads), _vp, _vp, _vp, _sz, _vp, _P(Trace)]
+_lib.moe_fwd_nf4.restype = _i32
+_lib.moe_bwd_nf4.restype = _i32
 _lib.moe_router_workspace.argtypes = [_P(Problem)]
 _lib.moe_router_workspace.restype = _sz
 _lib.moe_router_fwd.argtypes = [_P(Problem), _vp, _vp, _vp, _vp, _P(Trace)]
@@ -173,7 +184,7 @@ def _stream(stream):
 
 
 def _struct(cls, d):
-    return cls(*[_ptr(d[n]) for n, _ in cls._fields_])
+    return cls(*[_ptr(d.get(n)) for n, _ in cls._fields_])
 
 
 def route_workspace(pb: Problem) -> int:
@@ -254,6 +265,28 @@ def moe_bwd(pb, x, dout, rt: dict, w: dict, saved, keep_expert_out, dx, grads: d
                       _ptr(d_logits), _ptr(ws), _nbytes(ws), _stream(stream),
                       ctypes.byref(trace) if trace is not None else None)
     _check(st, "moe_bwd")
+
+
+def moe_fwd_nf4(pb, x, rt: dict, w: dict, q4: dict, out, saved=None, keep_expert_out=False, ws=None,
+                stream=None, trace=None):
+    """moe_fwd with the base weights in NF4: q4 holds codes_gate/up/down and
+    scales_gate/up/down; w needs only the LoRA factors."""
+    st = _lib.moe_fwd_nf4(ctypes.byref(pb), _ptr(x), ctypes.byref(_struct(Routing, rt)),
+                          ctypes.byref(_struct(Weights, w)), ctypes.byref(_struct(Nf4Base, q4)), _ptr(out),
+                          _ptr(saved), int(keep_expert_out), _ptr(ws), _nbytes(ws), _stream(stream),
+                          ctypes.byref(trace) if trace is not None else None)
+    _check(st, "moe_fwd_nf4")
+
+
+def moe_bwd_nf4(pb, x, dout, rt: dict, w: dict, q4: dict, saved, keep_expert_out, dx, grads: dict,
+                d_topk_w=None, d_logits=None, ws=None, stream=None, trace=None):
+    """moe_bwd with the base weights in NF4 (see moe_fwd_nf4)."""
+    st = _lib.moe_bwd_nf4(ctypes.byref(pb), _ptr(x), _ptr(dout), ctypes.byref(_struct(Routing, rt)),
+                          ctypes.byref(_struct(Weights, w)), ctypes.byref(_struct(Nf4Base, q4)), _ptr(saved),
+                          int(keep_expert_out), _ptr(dx), ctypes.byref(_struct(LoraGrads, grads)),
+                          _ptr(d_topk_w), _ptr(d_logits), _ptr(ws), _nbytes(ws), _stream(stream),
+                          ctypes.byref(trace) if trace is not None else None)
+    _check(st, "moe_bwd_nf4")
 
 
 def router_workspace(pb: Problem) -> int:

@@ -137,6 +137,31 @@ bool weights_ok(const moe_weights_t *w) {
     return true;
 }
 
+// the LoRA factors (the base-weight pointers are not read when the base is NF4)
+bool lora_ok(const moe_weights_t *w) {
+    if (!w) return false;
+    const void *p[6] = {w->a_gate, w->b_gate, w->a_up, w->b_up, w->a_down, w->b_down};
+    for (const void *q : p)
+        if (!q || !aligned16(q)) return false;
+    return true;
+}
+
+// NF4 base weights: supported shapes and pointers (MOE_OK or the error)
+moe_status_t nf4_ok(const moe_problem_t *pb, const moe_nf4_base_t *q) {
+    if (pb->dtype != MOE_BF16 || pb->d % 64 || pb->F % 64) return MOE_E_UNSUPPORTED;
+    if (!q) return MOE_E_ARG;
+    const void *c[3] = {q->codes_gate, q->codes_up, q->codes_down};
+    for (const void *p : c)
+        if (!p || !aligned16(p)) return MOE_E_ARG;
+    const void *sc[3] = {q->scales_gate, q->scales_up, q->scales_down};
+    for (const void *p : sc)
+        if (!p || ((uintptr_t)p & 3u)) return MOE_E_ARG;
+    // per-expert code and scale slices are addressed with 32-bit byte offsets
+    const long long codes = (long long)pb->F * pb->d / 2;
+    if (codes > (1LL << 31)) return MOE_E_UNSUPPORTED;
+    return MOE_OK;
+}
+
 bool grads_ok(const moe_lora_grads_t *g) {
     if (!g) return false;
     const void *p[6] = {g->da_gate, g->db_gate, g->da_up, g->db_up, g->da_down, g->db_down};
@@ -286,12 +311,18 @@ moe_status_t moe_route(const moe_problem_t *pb, const float *logits, const moe_r
     return moe::api::route_impl(pb, logits, rt, host_counts, ws, stream, trace);
 }
 
-moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t *rt, const moe_weights_t *w,
-                     void *out, void *saved, int keep_expert_out, void *ws, size_t ws_bytes, void *stream,
-                     const moe_trace_t *trace) {
+}  // extern "C"
+
+namespace {
+
+// moe_fwd and moe_fwd_nf4 (q4 non-null: NF4 base weights, w's base pointers unused)
+moe_status_t fwd_impl(const moe_problem_t *pb, const void *x, const moe_routing_t *rt, const moe_weights_t *w,
+                      const moe_nf4_base_t *q4, void *out, void *saved, int keep_expert_out, void *ws,
+                      size_t ws_bytes, void *stream, const moe_trace_t *trace) {
     moe_status_t st = check_problem(pb);
     if (st != MOE_OK) return st;
-    if (!routing_ok(rt, pb->T) || !weights_ok(w)) return MOE_E_ARG;
+    if (q4 && (st = nf4_ok(pb, q4)) != MOE_OK) return st;
+    if (!routing_ok(rt, pb->T) || !(q4 ? lora_ok(w) : weights_ok(w))) return MOE_E_ARG;
     if (pb->T > 0 && (!buf_ok(x) || !buf_ok(out))) return MOE_E_ARG;
     if (saved && !aligned16(saved)) return MOE_E_ARG;
     const bool training = saved != nullptr, keep = keep_expert_out != 0;
@@ -318,6 +349,11 @@ moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t
     }
     b.out = out;
     b.tiles = pb->dtype == MOE_BF16 ? reinterpret_cast<int32_t *>(at(ws, fw.tiles)) : nullptr;
+    moe::Nf4Base qb{};
+    if (q4) {
+        qb = {q4->codes_gate, q4->codes_up, q4->codes_down, q4->scales_gate, q4->scales_up, q4->scales_down};
+        b.q4 = &qb;
+    }
     const moe::Trace tr = to_trace(trace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Dims D = dims_of(pb);
@@ -326,13 +362,37 @@ moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t
     return e == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
-moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout, const moe_routing_t *rt,
-                     const moe_weights_t *w, const void *saved, int keep_expert_out, void *dx,
-                     const moe_lora_grads_t *grads, float *d_topk_w, float *d_logits, void *ws, size_t ws_bytes,
-                     void *stream, const moe_trace_t *trace) {
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_fwd(const moe_problem_t *pb, const void *x, const moe_routing_t *rt, const moe_weights_t *w,
+                     void *out, void *saved, int keep_expert_out, void *ws, size_t ws_bytes, void *stream,
+                     const moe_trace_t *trace) {
+    return fwd_impl(pb, x, rt, w, nullptr, out, saved, keep_expert_out, ws, ws_bytes, stream, trace);
+}
+
+moe_status_t moe_fwd_nf4(const moe_problem_t *pb, const void *x, const moe_routing_t *rt, const moe_weights_t *w,
+                         const moe_nf4_base_t *q4, void *out, void *saved, int keep_expert_out, void *ws,
+                         size_t ws_bytes, void *stream, const moe_trace_t *trace) {
+    if (!q4) return MOE_E_ARG;
+    return fwd_impl(pb, x, rt, w, q4, out, saved, keep_expert_out, ws, ws_bytes, stream, trace);
+}
+
+}  // extern "C"
+
+namespace {
+
+// moe_bwd and moe_bwd_nf4 (q4 non-null: NF4 base weights)
+moe_status_t bwd_impl(const moe_problem_t *pb, const void *x, const void *dout, const moe_routing_t *rt,
+                      const moe_weights_t *w, const moe_nf4_base_t *q4, const void *saved, int keep_expert_out,
+                      void *dx, const moe_lora_grads_t *grads, float *d_topk_w, float *d_logits, void *ws,
+                      size_t ws_bytes, void *stream, const moe_trace_t *trace) {
     moe_status_t st = check_problem(pb);
     if (st != MOE_OK) return st;
-    if (!routing_ok(rt, pb->T) || !weights_ok(w) || !grads_ok(grads) || !buf_ok(saved)) return MOE_E_ARG;
+    if (q4 && (st = nf4_ok(pb, q4)) != MOE_OK) return st;
+    if (!routing_ok(rt, pb->T) || !(q4 ? lora_ok(w) : weights_ok(w)) || !grads_ok(grads) || !buf_ok(saved))
+        return MOE_E_ARG;
     if (pb->T > 0 && (!buf_ok(x) || !buf_ok(dout) || !buf_ok(dx))) return MOE_E_ARG;
     const bool keep = keep_expert_out != 0;
     if ((d_topk_w || d_logits) && !keep) return MOE_E_ARG;
@@ -365,12 +425,38 @@ moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout, c
     b.da_d = grads->da_down; b.db_d = grads->db_down;
     b.d_topk_w = d_topk_w; b.d_logits = d_logits;
     b.tiles = pb->dtype == MOE_BF16 ? reinterpret_cast<int32_t *>(at(ws, bw.tiles)) : nullptr;
+    moe::Nf4Base qb{};
+    if (q4) {
+        qb = {q4->codes_gate, q4->codes_up, q4->codes_down, q4->scales_gate, q4->scales_up, q4->scales_down};
+        b.q4 = &qb;
+    }
     const moe::Trace tr = to_trace(trace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Dims D = dims_of(pb);
     const hipError_t e = pb->dtype == MOE_BF16 ? moe::run_bwd<moe::bf16_t>(D, b, s, trace ? &tr : nullptr)
                                                : moe::run_bwd<float>(D, b, s, trace ? &tr : nullptr);
     return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_bwd(const moe_problem_t *pb, const void *x, const void *dout, const moe_routing_t *rt,
+                     const moe_weights_t *w, const void *saved, int keep_expert_out, void *dx,
+                     const moe_lora_grads_t *grads, float *d_topk_w, float *d_logits, void *ws, size_t ws_bytes,
+                     void *stream, const moe_trace_t *trace) {
+    return bwd_impl(pb, x, dout, rt, w, nullptr, saved, keep_expert_out, dx, grads, d_topk_w, d_logits, ws,
+                    ws_bytes, stream, trace);
+}
+
+moe_status_t moe_bwd_nf4(const moe_problem_t *pb, const void *x, const void *dout, const moe_routing_t *rt,
+                         const moe_weights_t *w, const moe_nf4_base_t *q4, const void *saved, int keep_expert_out,
+                         void *dx, const moe_lora_grads_t *grads, float *d_topk_w, float *d_logits, void *ws,
+                         size_t ws_bytes, void *stream, const moe_trace_t *trace) {
+    if (!q4) return MOE_E_ARG;
+    return bwd_impl(pb, x, dout, rt, w, q4, saved, keep_expert_out, dx, grads, d_topk_w, d_logits, ws, ws_bytes,
+                    stream, trace);
 }
 
 size_t moe_router_workspace(const moe_problem_t *pb) {

@@ -510,6 +510,242 @@ __device__ __forceinline__ void run(const Op &op, int nlora, const Lora &lora, c
 }
 
 // ---------------------------------------------------------------------------
+// 4-bit NormalFloat (NF4) B operand, dequantised while it is staged to LDS.
+// A frozen weight is stored as codes (two per byte, element 2i of a row in
+// the low nibble of byte i) and one fp32 scale per 64 consecutive elements of
+// a row; element = bf16(level[code] * scale), the rounding the standalone
+// dequantisation kernel applies, so the GEMM reads exactly the bf16 tile the
+// unfused path would have loaded.
+struct Nf4Lv { float v[16]; };
+
+// The 16 products bf16(level[j] * s) of one scale block as byte planes:
+// byte i of lo[m] / hi[m] is the low / high byte of entry 4m + i.
+struct Nf4Table { uint32_t lo[4], hi[4]; };
+
+__device__ __forceinline__ Nf4Table nf4_table(float s, const Nf4Lv &lv) {
+    uint32_t p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        p[i] = (uint32_t)f32_to_bf16(lv.v[2 * i] * s) | ((uint32_t)f32_to_bf16(lv.v[2 * i + 1] * s) << 16);
+    Nf4Table t;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        // v_perm_b32(a, b, sel): byte i of the result is byte sel[i] of the
+        // 8-byte value a:b (b = bytes 0-3, a = bytes 4-7)
+        t.lo[m] = __builtin_amdgcn_perm(p[2 * m + 1], p[2 * m], 0x06040200u);
+        t.hi[m] = __builtin_amdgcn_perm(p[2 * m + 1], p[2 * m], 0x07050301u);
+    }
+    return t;
+}
+
+// one byte plane looked up for 4 codes (one per byte of c, 0..15): entries
+// 0-7 and 8-15 by the low 3 bits, then bit 3 (m = 0xff in the bytes whose
+// code has it) picks between them
+__device__ __forceinline__ uint32_t nf4_plane(const uint32_t (&pl)[4], uint32_t c7, uint32_t m) {
+    const uint32_t a = __builtin_amdgcn_perm(pl[1], pl[0], c7);
+    const uint32_t b = __builtin_amdgcn_perm(pl[3], pl[2], c7);
+    return (m & b) | (~m & a);
+}
+
+// 8 codes (one dword, element i in nibble i) -> 8 bf16 in element order
+__device__ __forceinline__ chunk_t nf4_lookup8(uint32_t q, const Nf4Table &t) {
+    const uint32_t ce = q & 0x07070707u, co = (q >> 4) & 0x07070707u;  // elements 0,2,4,6 / 1,3,5,7
+    const uint32_t me = ((q >> 3) & 0x01010101u) * 0xffu, mo = ((q >> 7) & 0x01010101u) * 0xffu;
+    const uint32_t lo_e = nf4_plane(t.lo, ce, me), hi_e = nf4_plane(t.hi, ce, me);
+    const uint32_t lo_o = nf4_plane(t.lo, co, mo), hi_o = nf4_plane(t.hi, co, mo);
+    const uint32_t e02 = __builtin_amdgcn_perm(hi_e, lo_e, 0x05010400u), e46 = __builtin_amdgcn_perm(hi_e, lo_e, 0x07030602u);
+    const uint32_t o13 = __builtin_amdgcn_perm(hi_o, lo_o, 0x05010400u), o57 = __builtin_amdgcn_perm(hi_o, lo_o, 0x07030602u);
+    return chunk_t{__builtin_amdgcn_perm(o13, e02, 0x05040100u), __builtin_amdgcn_perm(o13, e02, 0x07060302u),
+                   __builtin_amdgcn_perm(o57, e46, 0x05040100u), __builtin_amdgcn_perm(o57, e46, 0x07060302u)};
+}
+
+// The B tile of one 64-deep step from NF4 weights. Every thread owns one
+// group of 32 elements that share a scale block:
+//  K-contiguous B (rows of the tile = weight rows, k along the row): tile
+//    row tid / 2, k half tid % 2 of the step;
+//  N-contiguous B (k-rows of the tile = weight rows, n along the row): k-row
+//    tid / 8, columns 32 (tid % 8) .. + 31.
+// NSEG K segments (like Operands), each through one codes and one scales
+// descriptor (the weight of the segment; for K-contiguous gate/up, whose tile
+// interleaves gate and up rows in 32-row blocks, the weight of this wave's
+// block). Few descriptors: they must stay in scalar registers.
+template <class C, int NSEG = 1>
+struct Q4B {
+    static_assert(C::BK == 64, "one 64-element scale block per weight row and step");
+    static_assert(C::BN * C::BK == 32 * C::NTHREADS, "one 32-element group per thread");
+    static_assert(NSEG == 1 || NSEG == 2, "one or two K segments");
+    rsrc_t rc[NSEG], rs[NSEG];
+    uint32_t coff = kInvalid;   // K-contig: byte offset of the group's codes at k = 0; N-contig: column bytes
+    uint32_t soff = 0;          // K-contig: byte offset of the row's scales; N-contig: column-block bytes
+    uint32_t ldc[2] = {0, 0}, ldsc[2] = {0, 0};  // N-contig: code / scale bytes per weight row
+    int nt0 = 0, nt = 0;
+    struct Regs { chunk_t c; float s; };
+
+    __device__ __forceinline__ int row() const { return (int)threadIdx.x >> (C::B_NCONTIG ? 3 : 1); }
+
+    // global loads of step t's codes and scale into r (zeros past the end or
+    // outside the weight)
+    __device__ __forceinline__ void load(int t, Regs &r) const {
+        const bool s1 = NSEG == 2 && t >= nt0, ok = t < nt && coff != kInvalid;
+        const int tt = s1 ? t - nt0 : t;
+        rsrc_t cd = rc[0], sd = rs[0];
+        if constexpr (NSEG == 2) {
+            const rsrc_t c1 = rc[1], sc1 = rs[1];
+            cd = s1 ? c1 : cd;
+            sd = s1 ? sc1 : sd;
+        }
+        uint32_t co, so;
+        if constexpr (C::B_NCONTIG) {
+            const uint32_t krow = (uint32_t)(tt * 64 + row());
+            co = krow * (s1 ? ldc[1] : ldc[0]) + coff;
+            so = krow * (s1 ? ldsc[1] : ldsc[0]) + soff;
+        } else {
+            co = coff + (uint32_t)tt * 32;
+            so = soff + (uint32_t)tt * 4;
+        }
+        r.c = buf_load16(cd, ok ? co : kInvalid);
+        r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sd, ok ? so : kInvalid, 0, 0));
+    }
+
+    // elements 8i .. 8i+7 of the group (codes dword i) as bf16 into the B
+    // tile at `sb`, in the layout the direct loads produce
+    __device__ __forceinline__ void store8(const Regs &r, const Nf4Table &tb, int i, char *sb) const {
+        const chunk_t v = nf4_lookup8(r.c[i], tb);
+        if constexpr (C::B_NCONTIG) st_ncontig<C::BN>(sb, row(), ((int)threadIdx.x & 7) * 32 + i * 8, v);
+        else st_kcontig<C::CPR>(sb, row(), ((int)threadIdx.x & 1) * 4 + i, v);
+    }
+    // the whole group
+    __device__ __forceinline__ void store(const Regs &r, char *sb, const Nf4Lv &lv) const {
+        const Nf4Table tb = nf4_table(r.s, lv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store8(r, tb, i, sb);
+    }
+};
+
+// A k group (as kg_group) whose extra work is VALU-heavy: NV vector ALU
+// instructions are placed after each MFMA and the group's NW LDS writes are
+// spread over its MFMAs, so the dequantisation runs under the matrix pipe
+// instead of in one block before it.
+template <class C, int KG, int NL, int NV, int NW, class Issue>
+__device__ __forceinline__ void kg_group_v(const Issue &issue, const char *sa, const char *sb, Frags<C> (&f)[2],
+                                           f32x16_t (&acc)[C::TM][C::TN]) {
+    constexpr int NMMA = C::TM * C::TN, NRD = C::TM + (C::B_NCONTIG ? 2 : 1) * C::TN;
+    constexpr int LSTEP = NL > 0 ? NMMA / NL : NMMA;
+    constexpr int WSTEP = NW > 0 ? NMMA / NW : NMMA;
+    constexpr int HALF = NMMA > 1 ? NMMA / 2 : 1;
+    constexpr int RPM = (NRD + HALF - 1) / HALF;
+    issue(KGroup<KG>{});
+    read_frags<C>(sa, sb, KG, f[KG & 1]);
+    mma_frags<C>(f[(KG + 1) & 1], acc);
+#pragma unroll
+    for (int i = 0; i < NMMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, KG);                           // MFMA
+        if (NL > 0 && i % LSTEP == 0 && i / LSTEP < NL)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, KG);                       // direct / vector load
+        if (i < HALF) __builtin_amdgcn_sched_group_barrier(0x100, RPM, KG);           // LDS reads
+        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, KG);              // VALU
+        if (NW > 0 && i % WSTEP == WSTEP - 1 && i / WSTEP < NW)
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, KG);                       // LDS write
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// One steady iteration of the operand-slot ring with an NF4 B operand, at
+// step t: the A tile of step t + 1 into `da` (direct loads, as split_iter),
+// the codes of step t + 2 into `fill`, and the B tile of step t + 1 from
+// `use` (its codes, loaded one iteration earlier) dequantised into `db`;
+// the MFMA work of step t out of `sa` / `sb`. Five distinct slots (restrict).
+template <class C, class Op, class QB>
+__device__ __forceinline__ void q4_iter(const Op &op, const QB &qb, const Nf4Lv &lv, int t,
+                                        char *__restrict__ da, char *__restrict__ db, const char *__restrict__ sa,
+                                        const char *__restrict__ sb, int wave, const typename QB::Regs &use,
+                                        typename QB::Regs &fill, Frags<C> (&f)[2], f32x16_t (&acc)[C::TM][C::TN]) {
+    static_assert(C::NKG == 4, "64-deep steps");
+    constexpr int AH = C::A_INSTR / 2;
+    constexpr int NMMA = C::TM * C::TN;
+    // the codes of step t + 2 first (a whole iteration to arrive), the table
+    // (~32 VALU) with the first half of A(t + 1), then one code dword (8
+    // weights, ~31 VALU + one LDS write) with the rest of A(t + 1), one more,
+    // and the last two
+    Nf4Table tb;
+    kg_group_v<C, 0, AH + 2, (32 + NMMA - 1) / NMMA, 0>(
+        [&](auto) {
+            qb.load(t + 2, fill);
+            op.template issue_a<0, AH>(t + 1, da, wave);
+            tb = nf4_table(use.s, lv);
+        },
+        sa, sb, f, acc);
+    kg_group_v<C, 1, C::A_INSTR - AH, (32 + NMMA - 1) / NMMA, 1>(
+        [&](auto) {
+            op.template issue_a<AH, C::A_INSTR>(t + 1, da, wave);
+            qb.store8(use, tb, 0, db);
+        },
+        sa, sb, f, acc);
+    kg_group_v<C, 2, 0, (32 + NMMA - 1) / NMMA, 1>([&](auto) { qb.store8(use, tb, 1, db); }, sa, sb, f, acc);
+    kg_group_v<C, 3, 0, (64 + NMMA - 1) / NMMA, 2>(
+        [&](auto) {
+            qb.store8(use, tb, 2, db);
+            qb.store8(use, tb, 3, db);
+        },
+        sa, sb, f, acc);
+}
+
+// Ring driver for an NF4 B operand: like run() with 64-deep steps, except
+// that B tiles are written by the threads (dequantised) one iteration ahead
+// instead of loaded directly two ahead. Half-tile h in slot h % 5 as in run();
+// iteration t writes B of step t + 1 (half 2t + 2, the slot of A(t - 2)).
+template <class C, class Op, class QB, class Lora>
+__device__ __forceinline__ void run_q4(const Op &op, const QB &qb, const Nf4Lv &lv, int nlora, const Lora &lora,
+                                       char *smem, f32x16_t (&acc)[C::TM][C::TN]) {
+    static_assert(C::SPLIT, "64-deep operand-slot ring");
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    auto slot = [&](int h) { return smem + (h % C::NSTAGE) * C::SLOT_BYTES; };
+    Frags<C> f[2];
+    typename QB::Regs q0, q1;
+    {
+        typename Lora::Regs lr;
+        if (nlora > 0) lora.load(0, lr);
+        __builtin_amdgcn_sched_barrier(0);
+        qb.load(0, q0);
+        op.issue_a(0, slot(1), wave);
+        qb.load(1, q1);
+        qb.store(q0, slot(0), lv);  // B of step 0
+        lora_tiles<C>(nlora, lora, lr, slot(4), acc);
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) f[1].a[i] = chunk_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < C::TN; ++i) f[1].b[i] = chunk_t{0u, 0u, 0u, 0u};
+    // every load of the previous iteration (the codes of step t + 1, then A(t))
+    // has landed at the top of iteration t: nothing is issued after A(t)
+    for (int t = 0; t < op.nt; t += 2) {
+        wait_vm<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        q4_iter<C>(op, qb, lv, t, slot(2 * t + 3), slot(2 * t + 2), slot(2 * t + 1), slot(2 * t), wave, q1, q0, f,
+                   acc);
+        if (t + 1 < op.nt) {
+            wait_vm<0>();
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            q4_iter<C>(op, qb, lv, t + 1, slot(2 * t + 5), slot(2 * t + 4), slot(2 * t + 3), slot(2 * t + 2), wave,
+                       q0, q1, f, acc);
+        }
+    }
+    if (op.nt > 0) mma_frags<C>(f[1], acc);
+    wait_vm<0>();
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // LoRA tile pieces (register-staged). A side: rows p of an fp32 [S, nz]
 // matrix times s, k = 32 lt + ..., into the K-contiguous A tile.
 template <class C>

@@ -40,6 +40,14 @@ hipError_t launch_route_scatter(const int32_t *topk_idx, const int32_t *base, in
                                 int32_t *sorted_slot, int32_t *slot_row, hipStream_t st);
 
 // ---- forward / backward (T = float or bf16 bits) -----------------------------
+// 4-bit NormalFloat frozen weights (bf16 layers only): codes [E*rows, cols/2]
+// and fp32 scales [E*rows, cols/64] of W_gate, W_up ([F, d] per expert) and
+// W_down ([d, F]); the grouped GEMMs dequantise them as they stage B tiles.
+struct Nf4Base {
+    const uint8_t *cg, *cu, *cd;
+    const float *sg, *su, *sd;
+};
+
 struct FwdBufs {
     const void *x;
     const int32_t *sorted_slot, *offsets, *slot_row;
@@ -51,6 +59,7 @@ struct FwdBufs {
     void *Y;              // [S,d]
     void *out;            // [T,d]
     int32_t *tiles;       // workspace: row-tile table of the grouped GEMMs
+    const Nf4Base *q4;    // non-null: base weights in NF4 (wg, wu, wd unused)
 };
 
 struct BwdBufs {
@@ -70,6 +79,7 @@ struct BwdBufs {
     float *da_g, *db_g, *da_u, *db_u, *da_d, *db_d;
     float *d_topk_w, *d_logits;  // optional
     int32_t *tiles;              // workspace: row-tile table of the grouped GEMMs
+    const Nf4Base *q4;           // non-null: base weights in NF4 (wg, wu, wd unused)
 };
 
 // per-kernel timing events (hipEvent_t or null), indexed like MOE_K_*
@@ -97,6 +107,8 @@ hipError_t run_router_bwd(const Dims &D, const void *x, const void *wr, const fl
                           void *dx, float *dw, void *dlT, void *partial, hipStream_t st, const Trace *tr);
 
 // ---- 4-bit NormalFloat frozen weights -> bf16 ---------------------------------
+// the 16 NF4 levels, ascending (code q -> level q)
+void nf4_level_values(float out[16]);
 hipError_t run_nf4_dequant(const uint8_t *codes, const float *scales, int64_t rows, int cols, bf16_t *out,
                            hipStream_t st);
 

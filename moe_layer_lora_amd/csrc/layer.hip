@@ -370,12 +370,40 @@ template <class C> __device__ __forceinline__ int lds_row(int wave, int lane, in
     return (wave * instr + j) * C::RPI + lane / C::CPR;
 }
 
-template <class C>
-__device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, char *ring) {
+// NF4 frozen weights (4-bit NormalFloat codes and per-64 fp32 scales) for the
+// four grouped GEMMs: the B operand is dequantised while it is staged to LDS
+// (lds::Q4B); c1 / s1 are the second weight of the gate/up pair.
+struct Q4P {
+    const uint8_t *c0, *c1;
+    const float *s0, *s1;
+    lds::Nf4Lv lv;
+};
+
+// codes and scales descriptors of expert e's [rows, cols] NF4 weight. The
+// sizes go through readfirstlane: the compiler may otherwise reuse a copy of
+// cols / 2 that a lane-dependent branch left in a vector register, and a
+// descriptor in vector registers turns every load into a loop over lanes.
+__device__ __forceinline__ rsrc_t q4_codes(const uint8_t *c, int e, int rows, int cols) {
+    const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)rows * (uint32_t)(cols / 2));
+    return make_rsrc(c + (size_t)e * n, n);
+}
+__device__ __forceinline__ rsrc_t q4_scales(const float *s, int e, int rows, int cols) {
+    const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)rows * (uint32_t)(cols / 64));
+    return make_rsrc(s + (size_t)e * n, n * 4);
+}
+
+// --- gate/up -----------------------------------------------------------------
+// B rows interleave gate / up in 32-row blocks: tile row n -> FFN index f and
+// which weight (up = second) it comes from
+template <class C> __device__ __forceinline__ int gateup_f(int f_base, int n, bool &up) {
+    const int wn = n / C::WTN, ni = (n % C::WTN) / 32;
+    up = ni & 1;
+    return f_base + wn * (C::WTN / 2) + (ni / 2) * 32 + (n % 32);
+}
+
+template <class C> __device__ __forceinline__ void gateup_a(const GateUpP &p, const Tile &tl, lds::Operands<C> &op) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int f_base = tl.nt * (C::BN / 2);
-    lds::Operands<C> op;
-    uint32_t aro[C::A_INSTR], bro[C::B_INSTR];
+    uint32_t aro[C::A_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
         const int m = lds_row<C>(wave, lane, j, C::A_INSTR);
@@ -385,12 +413,88 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
     op.ra[0] = op.ra[1] = make_rsrc(p.x, (uint32_t)p.T * p.d * 2);
     op.K[0] = op.K[1] = p.d;
     op.nt0 = op.nt = cdiv(p.d, C::BK);
-    // B rows interleave gate / up in 32-row blocks; one load covers 16 rows of one block
+}
+
+template <class C> using GateUpLora = lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBK<typename C::LoraCfg>>;
+
+// LoRA tile: [s Zg | s Zu] rows against [B_g | 0] (gate rows) and [0 | B_u] (up rows)
+template <class C> __device__ __forceinline__ GateUpLora<C> gateup_lora(const GateUpP &p, const Tile &tl) {
+    const int f_base = tl.nt * (C::BN / 2);
+    const bf16_t *bg = static_cast<const bf16_t *>(p.bg) + (size_t)tl.e * p.F * p.r;
+    const bf16_t *bu = static_cast<const bf16_t *>(p.bu) + (size_t)tl.e * p.F * p.r;
+    GateUpLora<C> lora;
+    lora.pa = {p.zgu, 2 * p.r, tl.row0, tl.rows, p.s};
+    lora.pb.r = p.r;
+    lora.pb.safe = bg;
+#pragma unroll
+    for (int i = 0; i < lds::LoraBK<typename C::LoraCfg>::PER; ++i) {
+        bool up;
+        const int f = gateup_f<C>(f_base, ((int)threadIdx.x + C::NTHREADS * i) >> 2, up);
+        lora.pb.rowp[i] = f < p.F ? (up ? bu : bg) + (size_t)f * p.r : nullptr;
+        lora.pb.klo[i] = up ? p.r : 0;
+    }
+    return lora;
+}
+
+// SwiGLU epilogue: wave columns are pairs [gate 32 | up 32] for
+// f = f_base + wn * WTN / 2 + (0 .. WTN / 2 - 1); writes G, U (training) and H
+template <class C>
+__device__ __forceinline__ void gateup_epilogue(const GateUpP &p, const Tile &tl, const f32x16_t (&acc)[C::TM][C::TN],
+                                                char *ring) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int f_base = tl.nt * (C::BN / 2);
+    bf16_t *G = static_cast<bf16_t *>(p.G), *U = static_cast<bf16_t *>(p.U), *H = static_cast<bf16_t *>(p.H);
+    const int wn = wave % C::WN, wm = wave / C::WN;
+    float *buf = reinterpret_cast<float *>(ring) + wave * 32 * C::WTN;
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                buf[acc_row(i, lane) * C::WTN + ni * 32 + acc_col(lane)] = acc[mi][ni][i];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // WTN / 2 f per row = LPR lanes x 8 f; RPP rows per pass
+        constexpr int LPR = C::WTN / 16, RPP = 64 / LPR;
+#pragma unroll
+        for (int pass = 0; pass < 32 / RPP; ++pass) {
+            const int r = pass * RPP + lane / LPR, q = lane % LPR;  // q: 8-f group
+            const int gc = (q / 4) * 64 + (q % 4) * 8;             // gate column in the wave tile
+            const float4 g0 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc);
+            const float4 g1 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 4);
+            const float4 u0 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 32);
+            const float4 u1 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 36);
+            const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            const int m = wm * C::WTM + mi * 32 + r;
+            const int f = f_base + wn * (C::WTN / 2) + (q / 4) * 32 + (q % 4) * 8;
+            if (m < tl.rows && f < p.F) {
+                float h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = g[e] * sigmoid_fast(g[e]) * u[e];
+                const size_t o = (size_t)(tl.row0 + m) * p.F + f;
+                if (G) st_stream(G + o, Elem<bf16_t>::pack(g));
+                if (U) st_stream(U + o, Elem<bf16_t>::pack(u));
+                st_stream(H + o, Elem<bf16_t>::pack(h));
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, char *ring) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int f_base = tl.nt * (C::BN / 2);
+    lds::Operands<C> op;
+    gateup_a<C>(p, tl, op);
+    uint32_t bro[C::B_INSTR];
+    // one load covers 16 rows of one 32-row gate or up block
 #pragma unroll
     for (int j = 0; j < C::B_INSTR; ++j) {
-        const int n = lds_row<C>(wave, lane, j, C::B_INSTR);
-        const int wn = n / C::WTN, ni = (n % C::WTN) / 32;
-        const int f = f_base + wn * (C::WTN / 2) + (ni / 2) * 32 + (n % 32);
+        bool up;
+        const int f = gateup_f<C>(f_base, lds_row<C>(wave, lane, j, C::B_INSTR), up);
         bro[j] = f < p.F ? (uint32_t)f * p.d * 2 : kInvalid;
         const int n0 = (wave * C::B_INSTR + j) * C::RPI;  // first row of the load (same block for every lane)
         op.bsel_mask |= (uint32_t)(((n0 % C::WTN) / 32) & 1) << j;
@@ -399,66 +503,29 @@ __device__ __forceinline__ void gateup_tile(const GateUpP &p, const Tile &tl, ch
     const size_t wofs = (size_t)tl.e * p.F * p.d;
     op.rb[0][0] = op.rb[1][0] = make_rsrc(static_cast<const bf16_t *>(p.wg) + wofs, (uint32_t)p.F * p.d * 2);
     op.rb[0][1] = op.rb[1][1] = make_rsrc(static_cast<const bf16_t *>(p.wu) + wofs, (uint32_t)p.F * p.d * 2);
-    const bf16_t *bg = static_cast<const bf16_t *>(p.bg) + (size_t)tl.e * p.F * p.r;
-    const bf16_t *bu = static_cast<const bf16_t *>(p.bu) + (size_t)tl.e * p.F * p.r;
-    // LoRA tile: [s Zg | s Zu] rows against [B_g | 0] (gate rows) and [0 | B_u] (up rows)
-    lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBK<typename C::LoraCfg>> lora;
-    lora.pa = {p.zgu, 2 * p.r, tl.row0, tl.rows, p.s};
-    lora.pb.r = p.r;
-    lora.pb.safe = bg;
-#pragma unroll
-    for (int i = 0; i < lds::LoraBK<typename C::LoraCfg>::PER; ++i) {
-        const int n = ((int)threadIdx.x + C::NTHREADS * i) >> 2;
-        const int wn = n / C::WTN, ni = (n % C::WTN) / 32;
-        const int f = f_base + wn * (C::WTN / 2) + (ni / 2) * 32 + (n % 32);
-        const bool up = ni & 1;
-        lora.pb.rowp[i] = f < p.F ? (up ? bu : bg) + (size_t)f * p.r : nullptr;
-        lora.pb.klo[i] = up ? p.r : 0;
-    }
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(2 * p.r, C::LoraCfg::BK), lora, ring, acc);
+    lds::run<C>(op, cdiv(2 * p.r, C::LoraCfg::BK), gateup_lora<C>(p, tl), ring, acc);
+    gateup_epilogue<C>(p, tl, acc, ring);
+}
 
-    // wave columns: pairs [gate 32 | up 32] for f = f_base + wn * WTN / 2 + (0 .. WTN / 2 - 1)
-    bf16_t *G = static_cast<bf16_t *>(p.G), *U = static_cast<bf16_t *>(p.U), *H = static_cast<bf16_t *>(p.H);
-    {
-        const int wn = wave % C::WN, wm = wave / C::WN;
-        float *buf = reinterpret_cast<float *>(ring) + wave * 32 * C::WTN;
-        __syncthreads();
-#pragma unroll
-        for (int mi = 0; mi < C::TM; ++mi) {
-#pragma unroll
-            for (int ni = 0; ni < C::TN; ++ni)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    buf[acc_row(i, lane) * C::WTN + ni * 32 + acc_col(lane)] = acc[mi][ni][i];
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // WTN / 2 f per row = LPR lanes x 8 f; RPP rows per pass
-            constexpr int LPR = C::WTN / 16, RPP = 64 / LPR;
-#pragma unroll
-            for (int pass = 0; pass < 32 / RPP; ++pass) {
-                const int r = pass * RPP + lane / LPR, q = lane % LPR;  // q: 8-f group
-                const int gc = (q / 4) * 64 + (q % 4) * 8;             // gate column in the wave tile
-                const float4 g0 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc);
-                const float4 g1 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 4);
-                const float4 u0 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 32);
-                const float4 u1 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + gc + 36);
-                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-                const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-                const int m = wm * C::WTM + mi * 32 + r;
-                const int f = f_base + wn * (C::WTN / 2) + (q / 4) * 32 + (q % 4) * 8;
-                if (m < tl.rows && f < p.F) {
-                    float h[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) h[e] = g[e] * sigmoid_fast(g[e]) * u[e];
-                    const size_t o = (size_t)(tl.row0 + m) * p.F + f;
-                    if (G) st_stream(G + o, Elem<bf16_t>::pack(g));
-                    if (U) st_stream(U + o, Elem<bf16_t>::pack(u));
-                    st_stream(H + o, Elem<bf16_t>::pack(h));
-                }
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
-    }
+// NF4 weights: each thread dequantises one 32-element group of a B row
+template <class C>
+__device__ __forceinline__ void gateup_tile_q4(const GateUpP &p, const Q4P &q, const Tile &tl, char *ring) {
+    lds::Operands<C> op;
+    gateup_a<C>(p, tl, op);
+    lds::Q4B<C> qb;
+    bool up;
+    const int f = gateup_f<C>(tl.nt * (C::BN / 2), qb.row(), up);
+    // a wave's 32 rows are one gate or one up block: its weight is uniform
+    const bool wup = __builtin_amdgcn_readfirstlane((int)up) != 0;
+    qb.coff = f < p.F ? (uint32_t)f * (p.d / 2) + ((int)threadIdx.x & 1) * 16 : kInvalid;
+    qb.soff = f < p.F ? (uint32_t)f * (p.d / 64) * 4 : 0;
+    qb.rc[0] = q4_codes(wup ? q.c1 : q.c0, tl.e, p.F, p.d);
+    qb.rs[0] = q4_scales(wup ? q.s1 : q.s0, tl.e, p.F, p.d);
+    qb.nt0 = qb.nt = op.nt;
+    f32x16_t acc[C::TM][C::TN];
+    lds::run_q4<C>(op, qb, q.lv, cdiv(2 * p.r, C::LoraCfg::BK), gateup_lora<C>(p, tl), ring, acc);
+    gateup_epilogue<C>(p, tl, acc, ring);
 }
 
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
@@ -478,12 +545,21 @@ __global__ MOE_LDS_BLOCK(C) void k_gateup_lds(GateUpP p) {
     else gateup_tile<CQ>(p, tl, sm.ring);
 }
 
-template <class C>
-__device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *ring) {
+template <class C, class CH>
+__global__ MOE_LDS_BLOCK(C) void k_gateup_q4(GateUpP p, Q4P q) {
+    static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
+    __shared__ LdsSmem<C> sm;
+    static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
+    Tile tl;
+    if (!table_tile(p.tiles, cdiv(p.F, C::BN / 2), blockIdx.x, tl)) return;
+    if (tl.rows > CH::BM) gateup_tile_q4<C>(p, q, tl, sm.ring);
+    else gateup_tile_q4<CH>(p, q, tl, sm.ring);
+}
+
+// --- down ----------------------------------------------------------------------
+template <class C> __device__ __forceinline__ void down_a(const DownP &p, const Tile &tl, lds::Operands<C> &op) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n_base = tl.nt * C::BN;
-    lds::Operands<C> op;
-    uint32_t aro[C::A_INSTR], bro[C::B_INSTR];
+    uint32_t aro[C::A_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
         const int m = lds_row<C>(wave, lane, j, C::A_INSTR);
@@ -493,16 +569,14 @@ __device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *
     op.ra[0] = op.ra[1] = make_rsrc(p.H, (uint32_t)p.S * p.F * 2);
     op.K[0] = op.K[1] = p.F;
     op.nt0 = op.nt = cdiv(p.F, C::BK);
-#pragma unroll
-    for (int j = 0; j < C::B_INSTR; ++j) {
-        const int n = n_base + lds_row<C>(wave, lane, j, C::B_INSTR);
-        bro[j] = n < p.d ? (uint32_t)n * p.F * 2 : kInvalid;
-    }
-    op.bk.init_rows(wave, lane, bro);
-    op.rb[0][0] = op.rb[0][1] = op.rb[1][0] = op.rb[1][1] =
-        make_rsrc(static_cast<const bf16_t *>(p.wd) + (size_t)tl.e * p.d * p.F, (uint32_t)p.d * p.F * 2);
+}
+
+template <class C> using KLora = lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBK<typename C::LoraCfg>>;
+
+template <class C> __device__ __forceinline__ KLora<C> down_lora(const DownP &p, const Tile &tl) {
+    const int n_base = tl.nt * C::BN;
     const bf16_t *bd = static_cast<const bf16_t *>(p.bd) + (size_t)tl.e * p.d * p.r;
-    lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBK<typename C::LoraCfg>> lora;
+    KLora<C> lora;
     lora.pa = {p.zd, p.r, tl.row0, tl.rows, p.s};
     lora.pb.r = p.r;
     lora.pb.safe = bd;
@@ -512,13 +586,54 @@ __device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *
         lora.pb.rowp[i] = n < p.d ? bd + (size_t)n * p.r : nullptr;
         lora.pb.klo[i] = 0;
     }
-    f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(p.r, C::LoraCfg::BK), lora, ring, acc);
+    return lora;
+}
+
+template <class C>
+__device__ __forceinline__ void down_epilogue(const DownP &p, const Tile &tl, const f32x16_t (&acc)[C::TM][C::TN],
+                                              char *ring) {
+    const int n_base = tl.nt * C::BN;
     bf16_t *Y = static_cast<bf16_t *>(p.Y);
     lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
         if (m < tl.rows && n_base + n < p.d)
             st_stream(Y + (size_t)(tl.row0 + m) * p.d + n_base + n, Elem<bf16_t>::pack(v));
     });
+}
+
+template <class C>
+__device__ __forceinline__ void down_tile(const DownP &p, const Tile &tl, char *ring) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_base = tl.nt * C::BN;
+    lds::Operands<C> op;
+    down_a<C>(p, tl, op);
+    uint32_t bro[C::B_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::B_INSTR; ++j) {
+        const int n = n_base + lds_row<C>(wave, lane, j, C::B_INSTR);
+        bro[j] = n < p.d ? (uint32_t)n * p.F * 2 : kInvalid;
+    }
+    op.bk.init_rows(wave, lane, bro);
+    op.rb[0][0] = op.rb[0][1] = op.rb[1][0] = op.rb[1][1] =
+        make_rsrc(static_cast<const bf16_t *>(p.wd) + (size_t)tl.e * p.d * p.F, (uint32_t)p.d * p.F * 2);
+    f32x16_t acc[C::TM][C::TN];
+    lds::run<C>(op, cdiv(p.r, C::LoraCfg::BK), down_lora<C>(p, tl), ring, acc);
+    down_epilogue<C>(p, tl, acc, ring);
+}
+
+template <class C>
+__device__ __forceinline__ void down_tile_q4(const DownP &p, const Q4P &q, const Tile &tl, char *ring) {
+    lds::Operands<C> op;
+    down_a<C>(p, tl, op);
+    lds::Q4B<C> qb;
+    const int n = tl.nt * C::BN + qb.row();
+    qb.coff = n < p.d ? (uint32_t)n * (p.F / 2) + ((int)threadIdx.x & 1) * 16 : kInvalid;
+    qb.soff = n < p.d ? (uint32_t)n * (p.F / 64) * 4 : 0;
+    qb.rc[0] = q4_codes(q.c0, tl.e, p.d, p.F);
+    qb.rs[0] = q4_scales(q.s0, tl.e, p.d, p.F);
+    qb.nt0 = qb.nt = op.nt;
+    f32x16_t acc[C::TM][C::TN];
+    lds::run_q4<C>(op, qb, q.lv, cdiv(p.r, C::LoraCfg::BK), down_lora<C>(p, tl), ring, acc);
+    down_epilogue<C>(p, tl, acc, ring);
 }
 
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
@@ -533,12 +648,20 @@ __global__ MOE_LDS_BLOCK(C) void k_down_lds(DownP p) {
     else down_tile<CH>(p, tl, sm.ring);
 }
 
-template <class C>
-__device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl, char *ring) {
+template <class C, class CH>
+__global__ MOE_LDS_BLOCK(C) void k_down_q4(DownP p, Q4P q) {
+    static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
+    __shared__ LdsSmem<C> sm;
+    static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
+    Tile tl;
+    if (!table_tile(p.tiles, cdiv(p.d, C::BN), blockIdx.x, tl)) return;
+    if (tl.rows > CH::BM) down_tile_q4<C>(p, q, tl, sm.ring);
+    else down_tile_q4<CH>(p, q, tl, sm.ring);
+}
+
+// --- down backward ---------------------------------------------------------------
+template <class C> __device__ __forceinline__ void down_bwd_a(const DownBwdP &p, const Tile &tl, lds::Operands<C> &op) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n_base = tl.nt * C::BN;
-    const int ncol = min(C::BN, p.F - n_base);
-    lds::Operands<C> op;
     uint32_t aro[C::A_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
@@ -549,20 +672,28 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
     op.ra[0] = op.ra[1] = make_rsrc(p.dout, (uint32_t)p.T * p.d * 2);
     op.K[0] = op.K[1] = p.d;
     op.nt0 = op.nt = cdiv(p.d, C::BK);
-    // W_d[e] is [d, F]: k = model dim, n = f
-    op.bn.init(wave, lane, ncol);
-    op.rb[0][0] = op.rb[1][0] = make_rsrc(static_cast<const bf16_t *>(p.wd) + (size_t)tl.e * p.d * p.F + n_base,
-                                          (uint32_t)((size_t)p.d * p.F - n_base) * 2);
-    op.ldb[0] = op.ldb[1] = (uint32_t)p.F * 2;
+}
+
+template <class C> using NLora = lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBN<typename C::LoraCfg>>;
+
+template <class C> __device__ __forceinline__ NLora<C> down_bwd_lora(const DownBwdP &p, const Tile &tl) {
+    const int n_base = tl.nt * C::BN;
+    const int ncol = min(C::BN, p.F - n_base);
     const bf16_t *ad = static_cast<const bf16_t *>(p.ad) + (size_t)tl.e * p.r * p.F + n_base;
-    lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBN<typename C::LoraCfg>> lora;
+    NLora<C> lora;
     lora.pa = {p.pd, p.r, tl.row0, tl.rows, p.s};
     lora.pb = {ad, ad, p.r, p.r, p.F, ncol};
-    f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(p.r, C::LoraCfg::BK), lora, ring, acc);
-    // SwiGLU backward epilogue. Per 32-row slab of each wave: the fp32 tile
-    // goes through LDS to 16-byte row chunks; G, U and the row weight of the
-    // next slab are loaded while this slab is computed and stored.
+    return lora;
+}
+
+// SwiGLU backward epilogue. Per 32-row slab of each wave: the fp32 tile goes
+// through LDS to 16-byte row chunks; G, U and the row weight of the next
+// slab are loaded while this slab is computed and stored.
+template <class C>
+__device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile &tl,
+                                                  const f32x16_t (&acc)[C::TM][C::TN], char *ring) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_base = tl.nt * C::BN;
     const bf16_t *G = static_cast<const bf16_t *>(p.G), *U = static_cast<const bf16_t *>(p.U);
     bf16_t *dGU = static_cast<bf16_t *>(p.dGU);
     constexpr int LPR = C::WTN / 8, RPP = 64 / LPR, NPASS = 32 / RPP;
@@ -624,6 +755,42 @@ __device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl,
     }
 }
 
+template <class C>
+__device__ __forceinline__ void down_bwd_tile(const DownBwdP &p, const Tile &tl, char *ring) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_base = tl.nt * C::BN;
+    const int ncol = min(C::BN, p.F - n_base);
+    lds::Operands<C> op;
+    down_bwd_a<C>(p, tl, op);
+    // W_d[e] is [d, F]: k = model dim, n = f
+    op.bn.init(wave, lane, ncol);
+    op.rb[0][0] = op.rb[1][0] = make_rsrc(static_cast<const bf16_t *>(p.wd) + (size_t)tl.e * p.d * p.F + n_base,
+                                          (uint32_t)((size_t)p.d * p.F - n_base) * 2);
+    op.ldb[0] = op.ldb[1] = (uint32_t)p.F * 2;
+    f32x16_t acc[C::TM][C::TN];
+    lds::run<C>(op, cdiv(p.r, C::LoraCfg::BK), down_bwd_lora<C>(p, tl), ring, acc);
+    down_bwd_epilogue<C>(p, tl, acc, ring);
+}
+
+template <class C>
+__device__ __forceinline__ void down_bwd_tile_q4(const DownBwdP &p, const Q4P &q, const Tile &tl, char *ring) {
+    lds::Operands<C> op;
+    down_bwd_a<C>(p, tl, op);
+    lds::Q4B<C> qb;
+    // W_d[e] is [d, F]: the tile's k-rows are weight rows, its columns f
+    const int n = tl.nt * C::BN + ((int)threadIdx.x & 7) * 32;
+    qb.coff = n < p.F ? (uint32_t)n / 2 : kInvalid;
+    qb.soff = (uint32_t)(n / 64) * 4;
+    qb.ldc[0] = qb.ldc[1] = (uint32_t)p.F / 2;
+    qb.ldsc[0] = qb.ldsc[1] = (uint32_t)(p.F / 64) * 4;
+    qb.rc[0] = q4_codes(q.c0, tl.e, p.d, p.F);
+    qb.rs[0] = q4_scales(q.s0, tl.e, p.d, p.F);
+    qb.nt0 = qb.nt = op.nt;
+    f32x16_t acc[C::TM][C::TN];
+    lds::run_q4<C>(op, qb, q.lv, cdiv(p.r, C::LoraCfg::BK), down_bwd_lora<C>(p, tl), ring, acc);
+    down_bwd_epilogue<C>(p, tl, acc, ring);
+}
+
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
 template <class C, class CH>
 __global__ MOE_LDS_BLOCK(C) void k_down_bwd_lds(DownBwdP p) {
@@ -636,12 +803,21 @@ __global__ MOE_LDS_BLOCK(C) void k_down_bwd_lds(DownBwdP p) {
     else down_bwd_tile<CH>(p, tl, sm.ring);
 }
 
+template <class C, class CH>
+__global__ MOE_LDS_BLOCK(C) void k_down_bwd_q4(DownBwdP p, Q4P q) {
+    static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
+    __shared__ LdsSmem<C> sm;
+    static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
+    Tile tl;
+    if (!table_tile(p.tiles, cdiv(p.F, C::BN), blockIdx.x, tl)) return;
+    if (tl.rows > CH::BM) down_bwd_tile_q4<C>(p, q, tl, sm.ring);
+    else down_bwd_tile_q4<CH>(p, q, tl, sm.ring);
+}
+
+// --- gate/up backward --------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile &tl, char *ring) {
+__device__ __forceinline__ void gateup_bwd_a(const GateUpBwdP &p, const Tile &tl, lds::Operands<C> &op) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n_base = tl.nt * C::BN;
-    const int ncol = min(C::BN, p.d - n_base);
-    lds::Operands<C> op;
     uint32_t aro[C::A_INSTR];
 #pragma unroll
     for (int j = 0; j < C::A_INSTR; ++j) {
@@ -655,24 +831,69 @@ __device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile 
     op.K[0] = op.K[1] = p.F;
     op.nt0 = cdiv(p.F, C::BK);
     op.nt = 2 * op.nt0;
+}
+
+template <class C> __device__ __forceinline__ NLora<C> gateup_bwd_lora(const GateUpBwdP &p, const Tile &tl) {
+    const int n_base = tl.nt * C::BN;
+    const int ncol = min(C::BN, p.d - n_base);
+    const size_t aofs = (size_t)tl.e * p.r * p.d + n_base;
+    const bf16_t *ag = static_cast<const bf16_t *>(p.ag) + aofs, *au = static_cast<const bf16_t *>(p.au) + aofs;
+    NLora<C> lora;
+    lora.pa = {p.pgu, 2 * p.r, tl.row0, tl.rows, p.s};
+    lora.pb = {ag, au, p.r, 2 * p.r, p.d, ncol};
+    return lora;
+}
+
+template <class C>
+__device__ __forceinline__ void gateup_bwd_epilogue(const GateUpBwdP &p, const Tile &tl,
+                                                    const f32x16_t (&acc)[C::TM][C::TN], char *ring) {
+    const int n_base = tl.nt * C::BN;
+    bf16_t *dXp = static_cast<bf16_t *>(p.dXp);
+    lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
+        if (m < tl.rows && n_base + n < p.d)
+            st_stream(dXp + (size_t)(tl.row0 + m) * p.d + n_base + n, Elem<bf16_t>::pack(v));
+    });
+}
+
+template <class C>
+__device__ __forceinline__ void gateup_bwd_tile(const GateUpBwdP &p, const Tile &tl, char *ring) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_base = tl.nt * C::BN;
+    const int ncol = min(C::BN, p.d - n_base);
+    lds::Operands<C> op;
+    gateup_bwd_a<C>(p, tl, op);
     op.bn.init(wave, lane, ncol);
     const size_t wofs = (size_t)tl.e * p.F * p.d + n_base;
     const uint32_t wbytes = (uint32_t)((size_t)p.F * p.d - n_base) * 2;
     op.rb[0][0] = make_rsrc(static_cast<const bf16_t *>(p.wg) + wofs, wbytes);
     op.rb[1][0] = make_rsrc(static_cast<const bf16_t *>(p.wu) + wofs, wbytes);
     op.ldb[0] = op.ldb[1] = (uint32_t)p.d * 2;
-    const size_t aofs = (size_t)tl.e * p.r * p.d + n_base;
-    const bf16_t *ag = static_cast<const bf16_t *>(p.ag) + aofs, *au = static_cast<const bf16_t *>(p.au) + aofs;
-    lds::LoraTile<lds::LoraA<typename C::LoraCfg>, lds::LoraBN<typename C::LoraCfg>> lora;
-    lora.pa = {p.pgu, 2 * p.r, tl.row0, tl.rows, p.s};
-    lora.pb = {ag, au, p.r, 2 * p.r, p.d, ncol};
     f32x16_t acc[C::TM][C::TN];
-    lds::run<C>(op, cdiv(2 * p.r, C::LoraCfg::BK), lora, ring, acc);
-    bf16_t *dXp = static_cast<bf16_t *>(p.dXp);
-    lds::epilogue_rows<C>(acc, ring, [&](int m, int n, const float *v) {
-        if (m < tl.rows && n_base + n < p.d)
-            st_stream(dXp + (size_t)(tl.row0 + m) * p.d + n_base + n, Elem<bf16_t>::pack(v));
-    });
+    lds::run<C>(op, cdiv(2 * p.r, C::LoraCfg::BK), gateup_bwd_lora<C>(p, tl), ring, acc);
+    gateup_bwd_epilogue<C>(p, tl, acc, ring);
+}
+
+template <class C>
+__device__ __forceinline__ void gateup_bwd_tile_q4(const GateUpBwdP &p, const Q4P &q, const Tile &tl, char *ring) {
+    lds::Operands<C> op;
+    gateup_bwd_a<C>(p, tl, op);
+    lds::Q4B<C, 2> qb;
+    // W_g[e], W_u[e] are [F, d]: the tile's k-rows are weight rows (segment 0
+    // gate, 1 up), its columns the model dim
+    const int n = tl.nt * C::BN + ((int)threadIdx.x & 7) * 32;
+    qb.coff = n < p.d ? (uint32_t)n / 2 : kInvalid;
+    qb.soff = (uint32_t)(n / 64) * 4;
+    qb.ldc[0] = qb.ldc[1] = (uint32_t)p.d / 2;
+    qb.ldsc[0] = qb.ldsc[1] = (uint32_t)(p.d / 64) * 4;
+    qb.rc[0] = q4_codes(q.c0, tl.e, p.F, p.d);
+    qb.rc[1] = q4_codes(q.c1, tl.e, p.F, p.d);
+    qb.rs[0] = q4_scales(q.s0, tl.e, p.F, p.d);
+    qb.rs[1] = q4_scales(q.s1, tl.e, p.F, p.d);
+    qb.nt0 = op.nt0;
+    qb.nt = op.nt;
+    f32x16_t acc[C::TM][C::TN];
+    lds::run_q4<C>(op, qb, q.lv, cdiv(2 * p.r, C::LoraCfg::BK), gateup_bwd_lora<C>(p, tl), ring, acc);
+    gateup_bwd_epilogue<C>(p, tl, acc, ring);
 }
 
 // full 256-row tiles run C, an expert's last tile with at most CH::BM rows runs CH
@@ -685,6 +906,17 @@ __global__ MOE_LDS_BLOCK(C) void k_gateup_bwd_lds(GateUpBwdP p) {
     if (!table_tile(p.tiles, cdiv(p.d, C::BN), blockIdx.x, tl)) return;
     if (tl.rows > CH::BM) gateup_bwd_tile<C>(p, tl, sm.ring);
     else gateup_bwd_tile<CH>(p, tl, sm.ring);
+}
+
+template <class C, class CH>
+__global__ MOE_LDS_BLOCK(C) void k_gateup_bwd_q4(GateUpBwdP p, Q4P q) {
+    static_assert(C::NTHREADS == CH::NTHREADS, "one block size for both tile shapes");
+    __shared__ LdsSmem<C> sm;
+    static_assert(C::BM == kRowTile, "tiles come from the row-tile table");
+    Tile tl;
+    if (!table_tile(p.tiles, cdiv(p.d, C::BN), blockIdx.x, tl)) return;
+    if (tl.rows > CH::BM) gateup_bwd_tile_q4<C>(p, q, tl, sm.ring);
+    else gateup_bwd_tile_q4<CH>(p, q, tl, sm.ring);
 }
 
 // ===========================================================================
@@ -1529,6 +1761,12 @@ static hipError_t launch_proj(const Dims &D, const ProjP &pp, hipStream_t st) {
     return hipSuccess;
 }
 
+static Q4P q4_params(const uint8_t *c0, const uint8_t *c1, const float *s0, const float *s1) {
+    Q4P q{c0, c1, s0, s1, {}};
+    nf4_level_values(q.lv.v);
+    return q;
+}
+
 template <typename T>
 hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace *tr) {
     using Cfg = typename MainCfg<T>::type;
@@ -1545,9 +1783,16 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
         TraceScope ts(tr, K_GATEUP, st);
         GateUpP gp{b.x, b.wg, b.wu, b.bg, b.bu, b.Zgu, b.sorted_slot, b.offsets, b.G, b.U, b.H,
                    D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.tiles};
-        if constexpr (std::is_same<T, bf16_t>::value)
-            MOE_LAUNCH((k_gateup_lds<LdsGU, LdsGUh>), grid_for<Cfg>(D, LdsGU::BM, cdiv(D.F, LdsGU::BN / 2)), LdsGU::NTHREADS, gp);
-        else
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            if (b.q4) {
+                const Q4P q = q4_params(b.q4->cg, b.q4->cu, b.q4->sg, b.q4->su);
+                MOE_LAUNCH((k_gateup_q4<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.F, LdsNT::BN / 2)),
+                           LdsNT::NTHREADS, gp, q);
+            } else {
+                MOE_LAUNCH((k_gateup_lds<LdsGU, LdsGUh>), grid_for<Cfg>(D, LdsGU::BM, cdiv(D.F, LdsGU::BN / 2)),
+                           LdsGU::NTHREADS, gp);
+            }
+        } else
             MOE_LAUNCH(k_gateup<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN / 2)), Cfg::NTHREADS, gp);
     }
     {
@@ -1560,9 +1805,16 @@ hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace 
     {
         TraceScope ts(tr, K_DOWN, st);
         DownP dp{b.H, b.wd, b.bd, b.Zd, b.offsets, b.Y, D.S(), D.E, D.d, D.F, D.r, D.s, b.tiles};
-        if constexpr (std::is_same<T, bf16_t>::value)
-            MOE_LAUNCH((k_down_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)), LdsNT::NTHREADS, dp);
-        else
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            if (b.q4) {
+                const Q4P q = q4_params(b.q4->cd, b.q4->cd, b.q4->sd, b.q4->sd);
+                MOE_LAUNCH((k_down_q4<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)),
+                           LdsNT::NTHREADS, dp, q);
+            } else {
+                MOE_LAUNCH((k_down_lds<LdsNT, LdsNTh>), grid_for<Cfg>(D, LdsNT::BM, cdiv(D.d, LdsNT::BN)),
+                           LdsNT::NTHREADS, dp);
+            }
+        } else
             MOE_LAUNCH(k_down<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, dp);
     }
     {
@@ -1637,9 +1889,16 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
             TraceScope ts(tr, K_DOWN_BWD, st);
             DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
                         D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row, b.tiles};
-            if constexpr (std::is_same<T, bf16_t>::value)
-                MOE_LAUNCH((k_down_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.F, LdsNN64::BN)), LdsNN64::NTHREADS, dp);
-            else
+            if constexpr (std::is_same<T, bf16_t>::value) {
+                if (b.q4) {
+                    const Q4P q = q4_params(b.q4->cd, b.q4->cd, b.q4->sd, b.q4->sd);
+                    MOE_LAUNCH((k_down_bwd_q4<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.F, LdsNN64::BN)),
+                               LdsNN64::NTHREADS, dp, q);
+                } else {
+                    MOE_LAUNCH((k_down_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.F, LdsNN64::BN)),
+                               LdsNN64::NTHREADS, dp);
+                }
+            } else
                 MOE_LAUNCH(k_down_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.F, Cfg::BN)), Cfg::NTHREADS, dp);
         }
         {
@@ -1653,9 +1912,16 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
             TraceScope ts(tr, K_GATEUP_BWD, st);
             GateUpBwdP gp{b.dGU, b.wg, b.wu, b.ag, b.au, b.Pgu, b.offsets, b.dXp, D.S(), D.E, D.d, D.F, D.r, D.s,
                           b.tiles};
-            if constexpr (std::is_same<T, bf16_t>::value)
-                MOE_LAUNCH((k_gateup_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.d, LdsNN64::BN)), LdsNN64::NTHREADS, gp);
-            else
+            if constexpr (std::is_same<T, bf16_t>::value) {
+                if (b.q4) {
+                    const Q4P q = q4_params(b.q4->cg, b.q4->cu, b.q4->sg, b.q4->su);
+                    MOE_LAUNCH((k_gateup_bwd_q4<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.d, LdsNN64::BN)),
+                               LdsNN64::NTHREADS, gp, q);
+                } else {
+                    MOE_LAUNCH((k_gateup_bwd_lds<LdsNN64, LdsNN64h>), grid_for<Cfg>(D, LdsNN64::BM, cdiv(D.d, LdsNN64::BN)),
+                               LdsNN64::NTHREADS, gp);
+                }
+            } else
                 MOE_LAUNCH(k_gateup_bwd<Cfg>, grid_for<Cfg>(D, Cfg::BM, cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, gp);
         }
         {

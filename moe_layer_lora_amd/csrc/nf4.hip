@@ -81,6 +81,11 @@ __global__ __launch_bounds__(256) void k_nf4_dequant(const uint8_t *__restrict__
 
 }  // namespace
 
+void nf4_level_values(float out[16]) {
+    const Nf4Levels lv = nf4_levels();
+    for (int i = 0; i < 16; ++i) out[i] = lv.v[i];
+}
+
 hipError_t run_nf4_dequant(const uint8_t *codes, const float *scales, int64_t rows, int cols, bf16_t *out,
                            hipStream_t st) {
     const int64_t n8 = rows * (cols / 8);

@@ -31,7 +31,7 @@ class Layer:
     """Device copies of one layer's inputs and every buffer the three calls need."""
 
     def __init__(self, cfg, inputs: dict, T=None, device="cuda", keep_expert_out=False,
-                 training=True):
+                 training=True, q4=None):
         self.cfg = cfg
         self.pb = moe.Problem.from_config(cfg, T=T)
         self.device = device
@@ -41,7 +41,11 @@ class Layer:
         self.dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.x = to_dev(inputs["x"], device)
         self.logits = to_dev(inputs["logits"], device)
-        self.w = {n: to_dev(inputs[n], device) for n in WEIGHTS}
+        # q4: NF4 base weights (codes_* / scales_* numpy arrays): the forward and
+        # backward then take them through moe_fwd_nf4 / moe_bwd_nf4
+        self.q4 = None if q4 is None else {n: to_dev(v, device) for n, v in q4.items()}
+        self.w = {n: to_dev(inputs[n], device) for n in WEIGHTS
+                  if q4 is None or n not in ("w_gate", "w_up", "w_down")}
         self.dout = to_dev(inputs["dout"], device) if "dout" in inputs else None
         self.rt = moe.alloc_routing(pb, device)
         self.ws_route = moe.alloc_bytes(moe.route_workspace(pb), device)
@@ -59,10 +63,19 @@ class Layer:
         moe.moe_route(self.pb, self.logits, self.rt, host_counts=host_counts, ws=self.ws_route)
 
     def fwd(self):
+        if self.q4 is not None:
+            moe.moe_fwd_nf4(self.pb, self.x, self.rt, self.w, self.q4, self.out, saved=self.saved,
+                            keep_expert_out=self.keep, ws=self.ws_fwd)
+            return
         moe.moe_fwd(self.pb, self.x, self.rt, self.w, self.out, saved=self.saved,
                     keep_expert_out=self.keep, ws=self.ws_fwd)
 
     def bwd(self, router_grad=False):
+        if self.q4 is not None:
+            moe.moe_bwd_nf4(self.pb, self.x, self.dout, self.rt, self.w, self.q4, self.saved, self.keep,
+                            self.dx, self.grads, d_topk_w=self.d_topk_w if router_grad else None,
+                            d_logits=self.d_logits if router_grad else None, ws=self.ws_bwd)
+            return
         moe.moe_bwd(self.pb, self.x, self.dout, self.rt, self.w, self.saved, self.keep, self.dx,
                     self.grads, d_topk_w=self.d_topk_w if router_grad else None,
                     d_logits=self.d_logits if router_grad else None, ws=self.ws_bwd)

@@ -250,3 +250,30 @@ def test_stack_argument_errors_before_launch():
         # host memory of the offloaded layers must be pinned (a fake address is not)
         assert fn(ctypes.byref(p), 3, layers(3), 0, ctypes.byref(off()), A, need, None) == moe.MOE_E_ARG
         assert fn(ctypes.byref(pb(k=0)), 1, layers(1), 0, ctypes.byref(off()), A, need, None) == moe.MOE_E_ARG
+
+
+def test_nf4_layer_argument_errors_before_launch():
+    L, A = moe.lib(), 1 << 20
+    p = pb(d=256, F=128)
+    rt, w, g = _routing(A), _weights(A), _grads(A)
+    q = moe.Nf4Base(A, A, A, A, A, A)
+    # fp32 layers and d or F not a multiple of 64 are unsupported
+    for bad in (pb(dtype=moe.MOE_F32), pb(d=200), pb(F=136)):
+        assert L.moe_fwd_nf4(ctypes.byref(bad), A, ctypes.byref(rt), ctypes.byref(w), ctypes.byref(q), A, A, 0,
+                             A, 1 << 40, None, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_fwd_nf4(ctypes.byref(p), A, ctypes.byref(rt), ctypes.byref(w), None, A, A, 0, A, 1 << 40,
+                         None, None) == moe.MOE_E_ARG
+    q2 = moe.Nf4Base(A + 8, A, A, A, A, A)   # codes must be 16-byte aligned
+    assert L.moe_fwd_nf4(ctypes.byref(p), A, ctypes.byref(rt), ctypes.byref(w), ctypes.byref(q2), A, A, 0, A,
+                         1 << 40, None, None) == moe.MOE_E_ARG
+    q3 = moe.Nf4Base(A, A, A, A, A + 2, A)   # scales 4-byte aligned
+    assert L.moe_bwd_nf4(ctypes.byref(p), A, A, ctypes.byref(rt), ctypes.byref(w), ctypes.byref(q3), A, 1, A,
+                         ctypes.byref(g), None, None, A, 1 << 40, None, None) == moe.MOE_E_ARG
+    # base-weight pointers are not needed, the LoRA factors are
+    w0 = _weights(A)
+    w0.w_gate = w0.w_up = w0.w_down = None
+    assert L.moe_fwd_nf4(ctypes.byref(p), A, ctypes.byref(rt), ctypes.byref(w0), ctypes.byref(q), A, A, 0, A,
+                         0, None, None) == moe.MOE_E_WORKSPACE
+    w0.a_up = None
+    assert L.moe_fwd_nf4(ctypes.byref(p), A, ctypes.byref(rt), ctypes.byref(w0), ctypes.byref(q), A, A, 0, A,
+                         1 << 40, None, None) == moe.MOE_E_ARG

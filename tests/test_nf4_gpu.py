@@ -96,3 +96,85 @@ def test_nf4_full_size_gate_weights_sampled_rows():
     want = nf4.dequant(q["codes"][sel], q["scales"][sel], cols)
     assert _within_one_bf16_rounding(lr.to_f64(got[torch.from_numpy(sel).cuda()]), want)
     assert not torch.isnan(got.float()).any()
+
+
+# ------------------------------------------------------------------ NF4 inside the GEMMs
+
+def _nf4_base(cfg, seed=0):
+    """NF4 codes and scales of W_g, W_u ([E*F, d]) and W_d ([E*d, F])."""
+    q = {"gate": synth.make_nf4(cfg.E * cfg.F, cfg.d, seed=seed, tensor=20),
+         "up": synth.make_nf4(cfg.E * cfg.F, cfg.d, seed=seed, tensor=21),
+         "down": synth.make_nf4(cfg.E * cfg.d, cfg.F, seed=seed, tensor=22)}
+    out = {}
+    for n, v in q.items():
+        out["codes_" + n] = v["codes"]
+        out["scales_" + n] = v["scales"]
+    return out
+
+
+FUSED = {
+    # d, F multiples of 64 but not of the 256-wide tiles: ragged column tiles
+    # in every GEMM (gate/up 320 = 2.5 x 128 f, down-backward 320 = 1.25 x 256,
+    # gate/up-backward and down 192 < 256), ragged row tiles, 3 of 6 experts
+    # with a 128-row tail
+    "ragged": LayerConfig("nf4_ragged", T=300, d=192, E=6, k=3, F=320, r=16, dtype="bf16", alpha=32.0,
+                          router_grad=True),
+    "qwen3_30b_a3b": synth.get_config("qwen3_30b_a3b"),
+    # GPT-OSS-120B widths (2880 = 11.25 x 256) on 2048 tokens
+    "gptoss120b_2048": synth.get_config("gptoss120b").with_(T=2048),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_fused_nf4_equals_dequantise_then_bf16(name):
+    """moe_fwd_nf4 / moe_bwd_nf4 (codes dequantised while each B tile is
+    staged into LDS) against moe_nf4_dequant + moe_fwd / moe_bwd on the
+    dequantised weights: every output and intermediate bit for bit (the GEMMs
+    multiply the same bf16 tiles in the same order)."""
+    import layer_runner as lr
+    cfg = FUSED[name]
+    print(f"[nf4 fused] {name}", flush=True)
+    inp = synth.make_inputs(cfg, seed=0)
+    q = _nf4_base(cfg)
+    ref = lr.Layer(cfg, inp, keep_expert_out=True)
+    for n, key, rows, cols in (("w_gate", "gate", cfg.E * cfg.F, cfg.d), ("w_up", "up", cfg.E * cfg.F, cfg.d),
+                               ("w_down", "down", cfg.E * cfg.d, cfg.F)):
+        ref.w[n].copy_(_dequant_gpu(q["codes_" + key], q["scales_" + key], rows, cols).view(ref.w[n].shape))
+    ref.step(backward=True, router_grad=True)
+    want = ref.results(backward=True, router_grad=True, intermediates=True)
+    del ref
+    fused = lr.Layer(cfg, inp, keep_expert_out=True, q4=q)
+    assert "w_gate" not in fused.w  # no bf16 base weight exists on the fused path
+    fused.step(backward=True, router_grad=True)
+    got = fused.results(backward=True, router_grad=True, intermediates=True)
+    assert set(got) == set(want)
+    for n in want:
+        assert np.array_equal(got[n], want[n]), f"{name}: {n} differs from the unfused path"
+
+
+def test_fused_nf4_layer_matches_oracle():
+    """The fused path against the oracle layer on the oracle's own
+    dequantisation rounded to bf16 (routing bit-exact, rel-L2 within the
+    bf16 bound)."""
+    import layer_runner as lr
+    cfg = FUSED["ragged"]
+    inp = synth.make_inputs(cfg, seed=3)
+    q = _nf4_base(cfg, seed=3)
+    L = lr.Layer(cfg, inp, keep_expert_out=True, q4=q)
+    L.step(backward=True, router_grad=True)
+    r = L.results(backward=True, router_grad=True)
+    t = {n: synth.to_f64(inp[n], "bf16") for n in ("x", "a_gate", "b_gate", "a_up", "b_up", "a_down",
+                                                   "b_down")}
+    for n, key, shape in (("w_gate", "gate", (cfg.E, cfg.F, cfg.d)), ("w_up", "up", (cfg.E, cfg.F, cfg.d)),
+                          ("w_down", "down", (cfg.E, cfg.d, cfg.F))):
+        t[n] = nf4.round_bf16(nf4.dequant(q["codes_" + key], q["scales_" + key], shape[2])).reshape(shape)
+    OL = oracle.Layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.r, cfg.s, "f64", t)
+    rt = oracle.route(inp["logits"], cfg.k)
+    f = oracle.fwd(OL, rt)
+    b = oracle.bwd(OL, rt, synth.to_f64(inp["dout"], "bf16"))
+    for n in ("topk_idx", "counts", "offsets", "sorted_slot", "slot_row"):
+        assert np.array_equal(r[n], rt[n]), n
+    assert lr.rel_l2(r["out"], f["out"]) <= 2e-2
+    for n in ("dx", "da_gate", "db_gate", "da_up", "db_up", "da_down", "db_down", "d_topk_w",
+              "d_logits"):
+        assert lr.rel_l2(r[n], b[n]) <= 2e-2, n
