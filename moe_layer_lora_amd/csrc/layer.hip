@@ -1730,7 +1730,10 @@ enum {
     K_DX_COMBINE = MOE_K_DX_COMBINE, K_LORA_GRAD = MOE_K_LORA_GRAD
 };
 
-template <class Cfg> static int grid_for(const Dims &D, int BM, int NT) { return max_row_tiles(D.S(), D.E, BM) * NT; }
+// blocks of a grouped-GEMM launch: every work item, plus the phase-split halves
+template <class Cfg> static int grid_for(const Dims &D, int BM, int NT) {
+    return max_row_tiles(D.S(), D.E, BM) * NT + kPhaseSplitBlocks;
+}
 
 #define MOE_LAUNCH(kern, grid, block, ...)                   \
     do {                                                     \
