@@ -115,11 +115,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel), or None if
-    there is none for these sources."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
+def profile_values(name):
+    """The `- key: value` lines of a committed rocprofv3 summary under
+    profiles/, or None if it is absent or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -130,9 +129,29 @@ def measured_traffic(kernel, workload):
                 kv[k.strip()] = v.strip().strip("`")
     if kv.get("source_hash") != kernel_source_hash():
         return None
+    return kv
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel), or None if
+    there is none for these sources."""
+    kv = profile_values(f"hbm_traffic_{kernel}_{workload}.md")
     try:
         return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
-    except (KeyError, ValueError):
+    except (TypeError, KeyError, ValueError):
+        return None
+
+
+def measured_clock(kernel, workload):
+    """Shader clock (GHz) while `kernel` runs, from the committed counter
+    summary: GRBM_GUI_ACTIVE cycles per XCD over the kernel-trace duration.
+    The counter window also spans the dispatch, so this bounds the clock from
+    above; None if there is no summary for these sources."""
+    kv = profile_values(f"counters_{workload}.md")
+    try:
+        return float(kv[f"clock_ghz_{kernel}"])
+    except (TypeError, KeyError, ValueError):
         return None
 
 
@@ -193,60 +212,6 @@ def cpu_baseline(cfg, tokens, tokens_1t):
                       f"the {cfg.T} tokens of the same layer (same weights and generator), route+fwd" +
                       ("+bwd" if cfg.backward else "") + "; fp64 row loops, OpenMP over experts; bwd "
                       "recomputes each row's forward; gflops = algorithmic GEMM flops / seconds"}
-
-
-class ClockSampler:
-    """The GPU's current graphics clock from amdsmi, sampled from a host
-    thread about every millisecond while the GPU runs steps."""
-
-    def __init__(self):
-        self.err = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self.amdsmi = amdsmi
-            self.h = amdsmi.amdsmi_get_processor_handles()[0]
-            self.read()
-        except Exception as e:  # no amdsmi, no permission: reported, not fatal
-            self.amdsmi, self.err = None, f"{type(e).__name__}: {e}"
-
-    def read(self):
-        info = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)
-        return float(info["clk"]), float(info.get("max_clk", 0) or 0)
-
-    def sample_during(self, fn):
-        import threading
-        if self.amdsmi is None:
-            fn()
-            return None
-        samples, done = [], threading.Event()
-
-        def loop():
-            while not done.is_set():
-                try:
-                    samples.append(self.read())
-                except Exception:
-                    pass
-                time.sleep(0.001)
-        th = threading.Thread(target=loop, daemon=True)
-        th.start()
-        try:
-            fn()
-        finally:
-            done.set()
-            th.join()
-        if not samples:
-            return None
-        clk = sorted(c for c, _ in samples)
-        rec = {"gfx_mhz_median": clk[len(clk) // 2], "gfx_mhz_min": clk[0], "gfx_mhz_max": clk[-1],
-               "max_clk_mhz": samples[-1][1], "samples": len(samples),
-               "source": "amdsmi current GFX clock, sampled about every 1 ms from a host thread "
-                         "while steps run"}
-        # a reading far below the engine's range while the GPU is busy is not
-        # the shader clock (some boards report an idle or another domain's
-        # value here): kept for the record, not used for a peak
-        rec["plausible"] = rec["gfx_mhz_median"] >= 0.5 * (rec["max_clk_mhz"] or 2400.0)
-        return rec
 
 
 def whereloop_baseline(torch, cfg, x, logits, w, dout, steps, warmup=1):
@@ -652,16 +617,6 @@ def main():
     for ev in events:
         hip.destroy(ev)
 
-    # the graphics clock while the step runs (untimed steps after the timed region)
-    def clock_steps():
-        for _ in range(max(100, args.steps)):
-            step()
-        torch.cuda.synchronize()
-    clock = ClockSampler()
-    clk = clock.sample_during(clock_steps)
-    if clk is None and clock.err:
-        clk = {"error": clock.err}
-
     graph = graph_replay(torch, step, out, dx if cfg.backward else None, args.steps) \
         if args.graph else None
     ms_per_step = elapsed / args.steps * 1e3
@@ -716,7 +671,6 @@ def main():
                      "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                      "flops_per_launch": fps[dom] * S},
         "hbm_kernels": hbm,
-        "clock": clk,
         "graph_replay": graph,
         "kernel_source_hash": kernel_source_hash(),
         "input_setup_s": round(t_gen, 2),
@@ -759,12 +713,17 @@ def main():
             "fwd_speedup": round(wl_fwd / lib_fwd, 2),
             "bwd_speedup": round(wl_bwd / lib_bwd, 2) if cfg.backward else None,
             "out_rel_l2_vs_library": float(diff)}
-    if clk and clk.get("plausible"):
-        # the dense bf16 rate the chip can reach at the clock it held while the step ran
-        pk = peak * clk["gfx_mhz_median"] / 2400.0
-        rec["roofline"]["peak_at_measured_clock"] = round(pk, 1)
-        rec["roofline"]["frac_at_measured_clock"] = round(ach / pk, 4)
-        rec["grouped_gemm"]["frac_of_peak_at_measured_clock"] = round(gemm_tflops / pk, 4)
+    ghz = measured_clock(dom, cfg.name)
+    if ghz:
+        # the dense bf16 rate at the clock the kernel ran at (the published
+        # peak is at 2.4 GHz); the clock is an upper bound, so this fraction
+        # is a lower bound
+        pk = peak * min(ghz, 2.4) / 2.4
+        rec["roofline"]["clock_ghz"] = ghz
+        rec["roofline"]["peak_at_clock"] = round(pk, 1)
+        rec["roofline"]["frac_at_clock"] = round(ach / pk, 4)
+        rec["roofline"]["clock_source"] = (f"profiles/counters_{cfg.name}.md: GRBM_GUI_ACTIVE / 8 "
+                                           "XCDs / kernel-trace duration (upper bound)")
     if not args.skip_cpu:
         rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T),
                                            min(args.cpu_tokens_1t, cfg.T))
