@@ -96,7 +96,7 @@ FwdWs fwd_ws(const moe_problem_t *pb, int training, int keep) {
     return w;
 }
 
-struct BwdWs { size_t Pd, Pgu, wPdT, PguT, w_row, dGU, dXp, partial, tiles, total; };
+struct BwdWs { size_t Pd, Pgu, wPdT, PguT, w_row, dGU, dXp, partial, tiles, ppart, total; };
 BwdWs bwd_ws(const moe_problem_t *pb) {
     const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
     const bool bf = pb->dtype == MOE_BF16;
@@ -112,6 +112,7 @@ BwdWs bwd_ws(const moe_problem_t *pb) {
     w.dXp = o; o += al(S * pb->d * es);
     w.partial = o; o += al(moe::lora_grad_partial_bytes(dims_of(pb)));
     w.tiles = o; o += tile_table_bytes(pb);
+    w.ppart = o; if (bf && moe::pgu_in_down_bwd(pb->r)) o += al(moe::pgu_part_bytes(dims_of(pb)));
     w.total = o;
     return w;
 }
@@ -425,6 +426,8 @@ moe_status_t bwd_impl(const moe_problem_t *pb, const void *x, const void *dout, 
     b.da_d = grads->da_down; b.db_d = grads->db_down;
     b.d_topk_w = d_topk_w; b.d_logits = d_logits;
     b.tiles = pb->dtype == MOE_BF16 ? reinterpret_cast<int32_t *>(at(ws, bw.tiles)) : nullptr;
+    b.ppart = pb->dtype == MOE_BF16 && moe::pgu_in_down_bwd(pb->r) ? reinterpret_cast<float *>(at(ws, bw.ppart))
+                                                                    : nullptr;
     moe::Nf4Base qb{};
     if (q4) {
         qb = {q4->codes_gate, q4->codes_up, q4->codes_down, q4->scales_gate, q4->scales_up, q4->scales_down};

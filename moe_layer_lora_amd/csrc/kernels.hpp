@@ -80,7 +80,14 @@ struct BwdBufs {
     float *d_topk_w, *d_logits;  // optional
     int32_t *tiles;              // workspace: row-tile table of the grouped GEMMs
     const Nf4Base *q4;           // non-null: base weights in NF4 (wg, wu, wd unused)
+    float *ppart;                // workspace (bf16, pgu_in_down_bwd): column-strip shares of Pgu
 };
+
+// The bf16 down-backward GEMM projects its dG, dU tiles onto B_g, B_u in the
+// epilogue (instead of a separate pass over dGU) for these ranks; the shares
+// of its 256-column strips take pgu_part_bytes of workspace.
+inline bool pgu_in_down_bwd(int r) { return r % 16 == 0 && r <= 32; }
+inline size_t pgu_part_bytes(const Dims &D) { return (size_t)cdiv(D.F, 256) * D.S() * 2 * D.r * sizeof(float); }
 
 // per-kernel timing events (hipEvent_t or null), indexed like MOE_K_*
 struct Trace {

@@ -213,6 +213,11 @@ struct DownBwdP {
     float s;
     const float *w_row;  // bf16 path: combine weight of each row p (topk_w[sorted_slot[p]])
     const int32_t *tiles;  // bf16 path: row-tile table (build_row_tiles)
+    // bf16 path with r in {16, 32}: the epilogue also projects the tile's dG,
+    // dU onto B_g, B_u; ppart [cdiv(F, 256), S, 2r] fp32 gets each column
+    // strip's share of Pgu = [dG B_g | dU B_u] (k_pgu_sum adds them up)
+    const void *bg, *bu;
+    float *ppart;
 };
 
 template <class Cfg>
@@ -699,6 +704,21 @@ __device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile 
     constexpr int LPR = C::WTN / 8, RPP = 64 / LPR, NPASS = 32 / RPP;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int c8 = (lane % LPR) * 8, f = n_base + wn * C::WTN + c8;
+    // Projection of dG | dU onto B_g | B_u (when p.ppart is set). Past the
+    // per-wave fp32 slabs the ring holds, per row group wm, the current 32
+    // rows of bf16 dG (k = f - n_base) and dU (k = 256 + f - n_base) with
+    // 16-byte chunks XOR-swizzled by row, and the tile's slices of B_g and
+    // B_u transposed: sbt[n][f - n_base], rows n < r from B_g, r <= n < 2r
+    // from B_u. Each slab gives r / 4 jobs of 16 rows x 16 columns (a column
+    // block uses the dG half of k if it is below r, else the dU half), spread
+    // over the WN waves of the row group; each job is 8 MFMAs over 256 k.
+    constexpr int SLABS = C::NWAVES * 32 * C::WTN * 4;
+    static_assert(C::BN == 256 && C::WN * C::WTN == 256, "one 256-column strip per tile");
+    static_assert(SLABS + C::WM * 32 * 1024 + 64 * 512 <= C::SMEM_BYTES, "staging fits the ring");
+    const bool fuse = p.ppart != nullptr;
+    char *stage = ring + SLABS + wm * 32 * 1024;
+    char *sbt = ring + SLABS + C::WM * 32 * 1024;
+    const int r2 = 2 * p.r;
     struct Pre {
         chunk_t g[NPASS], u[NPASS];
         float w[NPASS];
@@ -716,6 +736,27 @@ __device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile 
     };
     float *buf = reinterpret_cast<float *>(ring) + wave * 32 * C::WTN;
     __syncthreads();  // every wave is done with the ring
+    if (fuse) {
+        // B_x[e] is [F, r]: thread w takes two rows f, f + 1 of eight columns
+        // and writes them as eight column pairs of sbt
+        const int ng = r2 / 8;
+        for (int w = threadIdx.x; w < ng * 128; w += C::NTHREADS) {
+            const int fp = w % 128, g8 = w / 128, n0 = g8 * 8;
+            const bool up = n0 >= p.r;
+            const bf16_t *src = static_cast<const bf16_t *>(up ? p.bu : p.bg) + (size_t)tl.e * p.F * p.r +
+                                (up ? n0 - p.r : n0);
+            const int f0 = n_base + 2 * fp;
+            const chunk_t zero = {0u, 0u, 0u, 0u};
+            const chunk_t v0 = f0 < p.F ? *reinterpret_cast<const chunk_t *>(src + (size_t)f0 * p.r) : zero;
+            const chunk_t v1 = f0 + 1 < p.F ? *reinterpret_cast<const chunk_t *>(src + (size_t)(f0 + 1) * p.r) : zero;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t lo = (v0[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
+                const uint32_t hi = (v1[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
+                *reinterpret_cast<uint32_t *>(sbt + (n0 + i) * 512 + fp * 4) = lo | (hi << 16);
+            }
+        }
+    }
     Pre q[2];
     prefetch(0, q[0]);
 #pragma unroll
@@ -733,6 +774,7 @@ __device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile 
             const float4 a = *reinterpret_cast<const float4 *>(buf + r * C::WTN + c8);
             const float4 b4 = *reinterpret_cast<const float4 *>(buf + r * C::WTN + c8 + 4);
             const float v[8] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
+            chunk_t pg = {0u, 0u, 0u, 0u}, pu = {0u, 0u, 0u, 0u};
             if (m < tl.rows && f < p.F) {
                 const Pre &cq = q[mi & 1];
                 float g[8], u[8], dg[8], du[8];
@@ -746,12 +788,44 @@ __device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile 
                     dg[h] = dh * u[h] * sg * (1.0f + g[h] * (1.0f - sg));
                     du[h] = dh * g[h] * sg;
                 }
+                pg = Elem<bf16_t>::pack(dg);
+                pu = Elem<bf16_t>::pack(du);
                 const size_t pr = (size_t)(tl.row0 + m);
-                st_stream(dGU + pr * 2 * p.F + f, Elem<bf16_t>::pack(dg));
-                st_stream(dGU + pr * 2 * p.F + p.F + f, Elem<bf16_t>::pack(du));
+                st_stream(dGU + pr * 2 * p.F + f, pg);
+                st_stream(dGU + pr * 2 * p.F + p.F + f, pu);
+            }
+            if (fuse) {
+                const int cg = (wn * C::WTN + c8) / 8, cu = 32 + cg;
+                *reinterpret_cast<chunk_t *>(stage + r * 1024 + ((cg ^ (r & 7)) * 16)) = pg;
+                *reinterpret_cast<chunk_t *>(stage + r * 1024 + ((cu ^ (r & 7)) * 16)) = pu;
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next slab overwrites
+        if (fuse) {
+            __syncthreads();  // both row groups' slabs (and sbt) are staged
+            const int jobs = p.r / 4;
+            for (int job = wn; job < jobs; job += C::WN) {
+                const int rh = job & 1, nb = job >> 1;
+                const int half = nb * 16 >= p.r ? 1 : 0;
+                const int row = rh * 16 + (lane & 15), n = nb * 16 + (lane & 15);
+                f32x4_t pacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kq = 0; kq < 8; ++kq) {
+                    const int ca = half * 32 + kq * 4 + (lane >> 4);
+                    const chunk_t av = *reinterpret_cast<const chunk_t *>(stage + row * 1024 + ((ca ^ (row & 7)) * 16));
+                    const chunk_t bv = *reinterpret_cast<const chunk_t *>(sbt + n * 512 + (kq * 32 + (lane >> 4) * 8) * 2);
+                    pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                   __builtin_bit_cast(bf16x8_t, bv), pacc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = wm * C::WTM + mi * 32 + rh * 16 + (lane >> 4) * 4 + i;
+                    if (m < tl.rows)
+                        p.ppart[((size_t)tl.nt * (p.T * p.k) + tl.row0 + m) * r2 + n] = pacc[i];
+                }
+            }
+            __syncthreads();  // every job has read the staged slab
+        }
     }
 }
 
@@ -1155,6 +1229,34 @@ __global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
                 p.outT[(size_t)(n_base + n) * p.ldT + pr] = Elem<bf16_t>::from_f32(stg[n * P + m] * sc);
         }
     }
+}
+
+// Pgu = sum over the column strips of the down-backward epilogues' shares
+// (strip order, fixed), as fp32 [S, 2r] and as the bf16 transpose [2r, ldT]
+// the LoRA-gradient kernel reads (columns S .. ldT-1 set to zero). A block
+// owns 64 rows; the transpose goes through LDS so each store instruction
+// writes 64 consecutive rows of one column.
+__global__ __launch_bounds__(256) void k_pgu_sum(const float *__restrict__ part, int nstrip, int S, int r2,
+                                                 float *__restrict__ pgu, bf16_t *__restrict__ pguT, int ldT) {
+    __shared__ float t[64][65];
+    const int row0 = blockIdx.x * 64;
+    for (int i = threadIdx.x; i < 64 * r2; i += 256) {
+        const int m = i / r2, j = i % r2, pr = row0 + m;
+        float v = 0.0f;
+        if (pr < S) {
+            for (int sidx = 0; sidx < nstrip; ++sidx) v += part[((size_t)sidx * S + pr) * r2 + j];
+            pgu[(size_t)pr * r2 + j] = v;
+        }
+        if (j < 64) t[j][m] = v;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * r2; i += 256) {
+        const int j = i / 64, m = i % 64, pr = row0 + m;
+        if (pr < S) pguT[(size_t)j * ldT + pr] = Elem<bf16_t>::from_f32(t[j][m]);
+    }
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < r2 * (ldT - S); i += 256)
+            pguT[(size_t)(i / (ldT - S)) * ldT + S + i % (ldT - S)] = Elem<bf16_t>::from_f32(0.0f);
 }
 
 // ===========================================================================
@@ -1890,8 +1992,10 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         }
         {
             TraceScope ts(tr, K_DOWN_BWD, st);
+            // with NF4 weights the down-backward tile already spends its slack
+            // on dequantisation: Pgu then comes from the separate projection
             DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
-                        D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row, b.tiles};
+                        D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row, b.tiles, b.bg, b.bu, b.q4 ? nullptr : b.ppart};
             if constexpr (std::is_same<T, bf16_t>::value) {
                 if (b.q4) {
                     const Q4P q = q4_params(b.q4->cd, b.q4->cd, b.q4->sd, b.q4->sd);
@@ -1906,10 +2010,16 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         }
         {
             TraceScope ts(tr, K_PROJ_DGU, st);
-            ProjP pp{b.dGU, b.bg, b.bu, b.sorted_slot, b.offsets, b.Pgu, D.E, D.k, D.d, D.F, D.r,
-                     static_cast<bf16_t *>(b.PguT), nullptr, lgrad_ldT(D), D.S()};
-            hipError_t e = launch_proj<T, PROJ_DGU>(D, pp, st);
-            if (e != hipSuccess) return e;
+            if (b.ppart && !b.q4) {
+                // the down-backward epilogues left Pgu's column-strip shares
+                MOE_LAUNCH(k_pgu_sum, cdiv(S, 64), 256, b.ppart, cdiv(D.F, 256), S, 2 * D.r, b.Pgu,
+                           static_cast<bf16_t *>(b.PguT), lgrad_ldT(D));
+            } else {
+                ProjP pp{b.dGU, b.bg, b.bu, b.sorted_slot, b.offsets, b.Pgu, D.E, D.k, D.d, D.F, D.r,
+                         static_cast<bf16_t *>(b.PguT), nullptr, lgrad_ldT(D), D.S()};
+                hipError_t e = launch_proj<T, PROJ_DGU>(D, pp, st);
+                if (e != hipSuccess) return e;
+            }
         }
         {
             TraceScope ts(tr, K_GATEUP_BWD, st);
