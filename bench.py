@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-tokens-1t", type=int, default=128,
                     help="tokens of the workload for the single-thread oracle run")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--no-other-workloads", dest="other_workloads", action="store_false",
+                    help="skip the timing of the other configurations")
+    ap.add_argument("--other-steps", type=int, default=10)
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay of the step")
     ap.add_argument("--no-nf4", dest="nf4", action="store_false",
@@ -113,6 +116,11 @@ def kernel_source_hash():
     with open(os.path.join(ROOT, "moe_layer_lora_amd", "_build.py"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
+
+
+# the other configurations the bench line also times (parity cases of the
+# tests; the headline metric is the workload above)
+OTHER_WORKLOADS = ("gptoss20b", "qwen3_30b_a3b_skewed", "gptoss120b")
 
 
 def profile_values(name):
@@ -495,6 +503,112 @@ def graph_replay(torch, step, out, dx, steps):
             "note": "same step captured once and replayed; value above is the eager step"}
 
 
+class Setup:
+    pass
+
+
+def setup(torch, np, moe, synth, cfg, dev, no_readback=False):
+    """Seeded synthetic inputs of the workload in HBM, the library's buffers
+    and workspaces, and the step (route + fwd + bwd) as a closure."""
+    W = Setup()
+    W.cfg = cfg
+    W.pb = pb = moe.Problem.from_config(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t_gen = time.perf_counter()
+    inputs = synth.make_inputs(cfg, seed=0, with_dout=cfg.backward)
+    W.x, W.logits = up(inputs["x"]), up(inputs["logits"])
+    names = ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
+    W.w = {n: up(inputs[n]) for n in names}
+    W.dout = up(inputs["dout"]) if cfg.backward else None
+    del inputs
+    W.t_gen = time.perf_counter() - t_gen
+
+    W.keep = keep = cfg.router_grad
+    W.rt = moe.alloc_routing(pb, dev)
+    W.ws_r = moe.alloc_bytes(moe.route_workspace(pb), dev)
+    W.ws_f = moe.alloc_bytes(moe.fwd_workspace(pb, cfg.backward, keep), dev)
+    W.saved = moe.alloc_bytes(moe.saved_bytes(pb, keep), dev) if cfg.backward else None
+    W.out = torch.empty((cfg.T, cfg.d), dtype=dt, device=dev)
+    W.ws_b = W.dx = W.grads = W.dtw = W.dlg = None
+    if cfg.backward:
+        W.ws_b = moe.alloc_bytes(moe.bwd_workspace(pb), dev)
+        W.dx = torch.empty((cfg.T, cfg.d), dtype=dt, device=dev)
+        W.grads = moe.alloc_grads(pb, dev)
+        W.dtw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev) if keep else None
+        W.dlg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev) if keep else None
+    # pinned: the count readback is a stream-ordered copy that needs no host wait
+    host_counts = torch.zeros(cfg.E, dtype=torch.int32, pin_memory=True)
+    W.stream = stream = torch.cuda.current_stream()
+
+    def step(trace=None, st=None):
+        st = stream if st is None else st
+        moe.moe_route(pb, W.logits, W.rt, host_counts=None if no_readback else host_counts,
+                      ws=W.ws_r, stream=st, trace=trace)
+        moe.moe_fwd(pb, W.x, W.rt, W.w, W.out, saved=W.saved, keep_expert_out=keep, ws=W.ws_f,
+                    stream=st, trace=trace)
+        if cfg.backward:
+            moe.moe_bwd(pb, W.x, W.dout, W.rt, W.w, W.saved, keep, W.dx, W.grads, d_topk_w=W.dtw,
+                        d_logits=W.dlg, ws=W.ws_b, stream=st, trace=trace)
+    W.step = step
+    return W
+
+
+def other_workload(torch, np, moe, synth, hip, name, steps, warmup):
+    """One of the other configurations: route + fwd (+ bwd) timed like the
+    headline step (per-step HIP events, median), with the grouped GEMMs'
+    rate from one traced step after the timed ones."""
+    cfg = synth.get_config(name)
+    dev = torch.device("cuda:0")
+    W = setup(torch, np, moe, synth, cfg, dev)
+    for _ in range(warmup):
+        W.step()
+    torch.cuda.synchronize()
+    sh = W.stream.cuda_stream
+    ev = [(hip.event(), hip.event()) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        hip.record(a, sh)
+        W.step()
+        hip.record(b, sh)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = sorted(hip.elapsed_ms(a, b) for a, b in ev)
+    fps = gemm_flops_per_slot(cfg)
+    names = [n for n in fps if cfg.backward or n in ("proj_gu", "gateup", "proj_d", "down")]
+    tr = moe.Trace()
+    tev = []
+    for n in names:
+        i = moe.KERNELS.index(n)
+        tr.start[i], tr.stop[i] = hip.event(), hip.event()
+        tev += [tr.start[i], tr.stop[i]]
+    W.step(tr)
+    torch.cuda.synchronize()
+    gemm_ms = sum(hip.elapsed_ms(tr.start[moe.KERNELS.index(n)], tr.stop[moe.KERNELS.index(n)]) for n in names)
+    gemm_flops = sum(fps[n] * cfg.S for n in names)
+    for e in tev + [e for pair in ev for e in pair]:
+        hip.destroy(e)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    rec = {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "F": cfg.F, "r": cfg.r,
+           "step": "route(+count readback)+fwd" + ("+bwd" if cfg.backward else "") +
+                   ("+router-weight grad" if cfg.router_grad else ""),
+           "steps": steps, "warmup": warmup,
+           "ms_per_step": round(elapsed / steps * 1e3, 4),
+           "step_ms": {"median": round(ms[len(ms) // 2], 4), "min": round(ms[0], 4)},
+           "tokens_per_s": round(cfg.T * steps / elapsed, 1),
+           "grouped_gemm": {"tflops": round(tflops, 2), "frac_of_peak": round(tflops / peak, 4),
+                            "ms": round(gemm_ms, 4), "kernels": names}}
+    del W
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -512,50 +626,14 @@ def main():
     cfg = synth.get_config(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    pb = moe.Problem.from_config(cfg)
-    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-
-    def up(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
-
-    t_gen = time.perf_counter()
-    inputs = synth.make_inputs(cfg, seed=0, with_dout=cfg.backward)
-    x, logits = up(inputs["x"]), up(inputs["logits"])
-    names = ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
-    w = {n: up(inputs[n]) for n in names}
-    dout = up(inputs["dout"]) if cfg.backward else None
-    del inputs
-    t_gen = time.perf_counter() - t_gen
-
-    keep = cfg.router_grad
-    rt = moe.alloc_routing(pb, dev)
-    ws_r = moe.alloc_bytes(moe.route_workspace(pb), dev)
-    ws_f = moe.alloc_bytes(moe.fwd_workspace(pb, cfg.backward, keep), dev)
-    saved = moe.alloc_bytes(moe.saved_bytes(pb, keep), dev) if cfg.backward else None
-    out = torch.empty((cfg.T, cfg.d), dtype=dt, device=dev)
+    W = setup(torch, np, moe, synth, cfg, dev, args.no_readback)
+    pb, x, logits, w, dout, rt, out = W.pb, W.x, W.logits, W.w, W.dout, W.rt, W.out
+    ws_r, ws_f, saved, keep, step, t_gen = W.ws_r, W.ws_f, W.saved, W.keep, W.step, W.t_gen
     if cfg.backward:
-        ws_b = moe.alloc_bytes(moe.bwd_workspace(pb), dev)
-        dx = torch.empty((cfg.T, cfg.d), dtype=dt, device=dev)
-        grads = moe.alloc_grads(pb, dev)
-        dtw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev) if keep else None
-        dlg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev) if keep else None
-    # pinned: the count readback is a stream-ordered copy that needs no host wait
-    host_counts = torch.zeros(cfg.E, dtype=torch.int32, pin_memory=True)
-    stream = torch.cuda.current_stream()
+        ws_b, dx, grads, dtw, dlg = W.ws_b, W.dx, W.grads, W.dtw, W.dlg
+    stream = W.stream
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration, dev)
-
-    def step(trace=None, st=None):
-        st = stream if st is None else st
-        moe.moe_route(pb, logits, rt, host_counts=None if args.no_readback else host_counts,
-                      ws=ws_r, stream=st, trace=trace)
-        moe.moe_fwd(pb, x, rt, w, out, saved=saved, keep_expert_out=keep, ws=ws_f, stream=st,
-                    trace=trace)
-        if cfg.backward:
-            moe.moe_bwd(pb, x, dout, rt, w, saved, keep, dx, grads, d_topk_w=dtw, d_logits=dlg,
-                        ws=ws_b, stream=st, trace=trace)
 
     hip = Hip()
     gemm_kernels = [n for n in ("gateup", "down", "down_bwd", "gateup_bwd") if cfg.backward or
@@ -724,6 +802,9 @@ def main():
         rec["roofline"]["frac_at_clock"] = round(ach / pk, 4)
         rec["roofline"]["clock_source"] = (f"profiles/counters_{cfg.name}.md: GRBM_GUI_ACTIVE / 8 "
                                            "XCDs / kernel-trace duration (upper bound)")
+    if args.other_workloads:
+        rec["other_workloads"] = [other_workload(torch, np, moe, synth, hip, n, args.other_steps, 3)
+                                  for n in OTHER_WORKLOADS if n != cfg.name]
     if not args.skip_cpu:
         rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T),
                                            min(args.cpu_tokens_1t, cfg.T))
