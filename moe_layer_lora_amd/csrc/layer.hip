@@ -706,10 +706,13 @@ __device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile 
     const int c8 = (lane % LPR) * 8, f = n_base + wn * C::WTN + c8;
     // Projection of dG | dU onto B_g | B_u (when p.ppart is set). Past the
     // per-wave fp32 slabs the ring holds, per row group wm, the current 32
-    // rows of bf16 dG (k = f - n_base) and dU (k = 256 + f - n_base) with
-    // 16-byte chunks XOR-swizzled by row, and the tile's slices of B_g and
-    // B_u transposed: sbt[n][f - n_base], rows n < r from B_g, r <= n < 2r
-    // from B_u. Each slab gives r / 4 jobs of 16 rows x 16 columns (a column
+    // rows of bf16 dG (k = f - n_base) and dU (k = 256 + f - n_base), and the
+    // tile's slices of B_g and B_u transposed: sbt[n][f - n_base], rows n < r
+    // from B_g, r <= n < 2r from B_u. Both swap 16-byte chunks within groups
+    // of 16 (256 bytes, all 64 banks): staged row r by ((r & 1) << 3) |
+    // ((r >> 1) & 7), so the two rows a write instruction's 16-lane groups
+    // cover fall in different bank halves and any 16 rows a fragment read
+    // covers fall on distinct chunks; sbt row n by n & 15. Each slab gives r / 4 jobs of 16 rows x 16 columns (a column
     // block uses the dG half of k if it is below r, else the dU half), spread
     // over the WN waves of the row group; each job is 8 MFMAs over 256 k.
     constexpr int SLABS = C::NWAVES * 32 * C::WTN * 4;
@@ -753,7 +756,9 @@ __device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile 
             for (int i = 0; i < 8; ++i) {
                 const uint32_t lo = (v0[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
                 const uint32_t hi = (v1[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
-                *reinterpret_cast<uint32_t *>(sbt + (n0 + i) * 512 + fp * 4) = lo | (hi << 16);
+                const int n = n0 + i;
+                *reinterpret_cast<uint32_t *>(sbt + n * 512 + (((fp >> 2) ^ (n & 15)) * 16) + (fp & 3) * 4) =
+                    lo | (hi << 16);
             }
         }
     }
@@ -795,9 +800,9 @@ __device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile 
                 st_stream(dGU + pr * 2 * p.F + p.F + f, pu);
             }
             if (fuse) {
-                const int cg = (wn * C::WTN + c8) / 8, cu = 32 + cg;
-                *reinterpret_cast<chunk_t *>(stage + r * 1024 + ((cg ^ (r & 7)) * 16)) = pg;
-                *reinterpret_cast<chunk_t *>(stage + r * 1024 + ((cu ^ (r & 7)) * 16)) = pu;
+                const int cg = (wn * C::WTN + c8) / 8, cu = 32 + cg, sw = ((r & 1) << 3) | ((r >> 1) & 7);
+                *reinterpret_cast<chunk_t *>(stage + r * 1024 + ((cg ^ sw) * 16)) = pg;
+                *reinterpret_cast<chunk_t *>(stage + r * 1024 + ((cu ^ sw) * 16)) = pu;
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next slab overwrites
@@ -811,9 +816,10 @@ __device__ __forceinline__ void down_bwd_epilogue(const DownBwdP &p, const Tile 
                 f32x4_t pacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kq = 0; kq < 8; ++kq) {
-                    const int ca = half * 32 + kq * 4 + (lane >> 4);
-                    const chunk_t av = *reinterpret_cast<const chunk_t *>(stage + row * 1024 + ((ca ^ (row & 7)) * 16));
-                    const chunk_t bv = *reinterpret_cast<const chunk_t *>(sbt + n * 512 + (kq * 32 + (lane >> 4) * 8) * 2);
+                    const int ca = half * 32 + kq * 4 + (lane >> 4), sw = ((row & 1) << 3) | ((row >> 1) & 7);
+                    const int cb = kq * 4 + (lane >> 4);
+                    const chunk_t av = *reinterpret_cast<const chunk_t *>(stage + row * 1024 + ((ca ^ sw) * 16));
+                    const chunk_t bv = *reinterpret_cast<const chunk_t *>(sbt + n * 512 + ((cb ^ (n & 15)) * 16));
                     pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                                    __builtin_bit_cast(bf16x8_t, bv), pacc, 0, 0, 0);
                 }
