@@ -1558,8 +1558,10 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_lora_grad(LGradP p) {
 }
 
 // bf16 LoRA weight gradients, all modes in one launch. A block takes
-// (mode, expert, chunk of up to kLgRC of its rows, 256 columns of the big
-// operand) and forms out^T[j][c] = sum_p SmallT[j][p] Big[p][c]. Both
+// (mode, expert, chunk of up to kLgRC of its rows, kLgNTB tiles of 256
+// columns of the big operand) and forms out^T[j][c] = sum_p SmallT[j][p]
+// Big[p][c] tile after tile (the chunk's row table and the tile scheduler's
+// work are shared by the block's tiles). Both
 // operands stream through a ring of direct loads, one 32-row step per stage:
 //  - the big rows (gathered by token for modes 0 and 3), 32 x 256 bf16,
 //    N-contiguous, read back with transposing LDS reads;
@@ -1570,7 +1572,11 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_lora_grad(LGradP p) {
 // products whatever the SmallT columns hold.
 constexpr int kLgRC = 1024;         // rows per chunk
 constexpr int kLgRows = kLgRC + 8;   // chunk rows plus the alignment lead-in
-constexpr int kLgBN = 256;           // big-operand columns per block
+constexpr int kLgBN = 256;           // big-operand columns per tile
+#ifndef MOE_LG_NTB
+#define MOE_LG_NTB 4
+#endif
+constexpr int kLgNTB = MOE_LG_NTB;   // column tiles per block (one ring, one row table)
 
 template <int NR> struct LgRing {
     static constexpr int NSTAGE = NR <= 32 ? 4 : 3;
@@ -1601,10 +1607,9 @@ struct LGradSet {
 
 template <int NR>
 __device__ __forceinline__ void lg_issue(const LGradP &p, int p0, const uint32_t *__restrict__ rowoff, rsrc_t rs,
-                                         rsrc_t rsm, int c_base, int ncol, int nsteps, int t,
+                                         rsrc_t rsm, int c_base, int ncol, bool live, int t,
                                          char *__restrict__ st, int wave, int lane) {
     using R = LgRing<NR>;
-    const bool live = t < nsteps;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // big: 2 rows of 512 B per 1 KB load
         const int q = wave * 4 + j;
@@ -1628,17 +1633,18 @@ __device__ __forceinline__ void lg_issue(const LGradP &p, int p0, const uint32_t
     }
 }
 
-// One steady step: the loads of step t + NSTAGE - 1 into `dst` (a different
-// ring slot from `st`, as the restrict qualifiers state, so the compiler
-// inserts no vmcnt drain before the LDS reads) and the MFMA work of step t.
+// One steady step: the loads of a later step (t, c_base, ncol, live: the
+// step NSTAGE - 1 ahead) into `dst` (a different ring slot from `st`, as the
+// restrict qualifiers state, so the compiler inserts no vmcnt drain before
+// the LDS reads) and the MFMA work of the step in `st`.
 template <int NR>
 __device__ __forceinline__ void lg_iter(const LGradP &p, int p0, const uint32_t *__restrict__ rowoff, rsrc_t rs,
-                                        rsrc_t rsm, int c_base, int ncol, int nsteps, int t,
+                                        rsrc_t rsm, int c_base, int ncol, bool live, int t,
                                         char *__restrict__ dst, const char *__restrict__ st, int wave, int lane,
                                         f32x16_t (&acc)[NR / 32][2]) {
     using R = LgRing<NR>;
     constexpr int TM = NR / 32;
-    lg_issue<NR>(p, p0, rowoff, rs, rsm, c_base, ncol, nsteps, t + R::NSTAGE - 1, dst, wave, lane);
+    lg_issue<NR>(p, p0, rowoff, rs, rsm, c_base, ncol, live, t, dst, wave, lane);
     const char *sa = st + R::BIG;
     const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
@@ -1684,13 +1690,15 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
     const LGradP &p = set.m[mi];
     const int ntn = cdiv(p.D, kLgBN);
     Tile tl;
-    if (!schedule_tile<kLgRC, 256>(p.offsets, p.E, ntn, b - set.base[mi], sm.start, tl)) return;
+    if (!schedule_tile<kLgRC, 256>(p.offsets, p.E, cdiv(ntn, kLgNTB), b - set.base[mi], sm.start, tl)) return;
     __syncthreads();  // every thread has read the scheduler table before the ring overwrites it
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool gather = p.mode == 0 || p.mode == 3;
-    const int c_base = tl.nt * kLgBN;
-    const int ncol = min(kLgBN, p.D - c_base);
+    // the block's column tiles nt0 .. nt0 + ntiles - 1, one after the other
+    // through one ring (the next tile's loads are in flight while a tile's
+    // results are stored)
+    const int nt0 = tl.nt * kLgNTB, ntiles = min(kLgNTB, ntn - nt0);
     // steps start at p0, the chunk's first row rounded down to a multiple of
     // 8, so SmallT columns load as aligned 16-byte chunks; the lead-in rows
     // (previous expert) load as zeros on the big side
@@ -1706,8 +1714,17 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
     __syncthreads();
     const rsrc_t rs = make_rsrc(p.big, 0x7fffffff);  // rows are range-checked through rowoff
     const rsrc_t rsm = make_rsrc(p.smallT, (uint32_t)p.nr * (uint32_t)p.ldT * 2u);
-    const int nsteps = cdiv(lead + tl.rows, 32);
+    const int nsteps = cdiv(lead + tl.rows, 32), total = ntiles * nsteps;
     auto stage = [&](int t) { return sm.ring + (t % R::NSTAGE) * R::STAGE; };
+    // global step u -> (column tile, step within it); past the last tile the
+    // loads are issued as zeros so every step waits on the same count
+    auto issue_at = [&](int u, int &cb, int &nc, bool &live, int &t) {
+        live = u < total;
+        const int jt = live ? u / nsteps : 0;
+        t = live ? u - jt * nsteps : 0;
+        cb = (nt0 + jt) * kLgBN;
+        nc = min(kLgBN, p.D - cb);
+    };
     constexpr int TM = NR / 32;
     f32x16_t acc[TM][2];
 #pragma unroll
@@ -1717,39 +1734,55 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi2][ni][i] = 0.0f;
 #pragma unroll
-    for (int t = 0; t < R::NSTAGE - 1; ++t)
-        lg_issue<NR>(p, p0, sm.rowoff, rs, rsm, c_base, ncol, nsteps, t, stage(t), wave, lane);
-    for (int t = 0; t < nsteps; ++t) {
+    for (int u = 0; u < R::NSTAGE - 1; ++u) {
+        int cb, nc, t;
+        bool live;
+        issue_at(u, cb, nc, live, t);
+        lg_issue<NR>(p, p0, sm.rowoff, rs, rsm, cb, nc, live, t, stage(u), wave, lane);
+    }
+    const bool single = (p.offsets[tl.e + 1] - p.offsets[tl.e]) <= kLgRC;
+    const LgOut dst(p, tl.e);
+    int tt = 0, jt = 0;  // step within the current tile, current tile
+    for (int u = 0; u < total; ++u) {
         // every step issues the same loads (zeros past the end): a fixed wait count
         lds::wait_vm<(R::NSTAGE - 2) * R::LOADS>();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        lg_iter<NR>(p, p0, sm.rowoff, rs, rsm, c_base, ncol, nsteps, t, stage(t + R::NSTAGE - 1), stage(t), wave,
-                    lane, acc);
+        int cb, nc, t;
+        bool live;
+        issue_at(u + R::NSTAGE - 1, cb, nc, live, t);
+        lg_iter<NR>(p, p0, sm.rowoff, rs, rsm, cb, nc, live, t, stage(u + R::NSTAGE - 1), stage(u), wave, lane,
+                    acc);
+        if (++tt < nsteps) continue;
+        tt = 0;
+        // tile jt done: acc[mi2][ni] holds out^T rows j = mi2*32 + ..,
+        // columns c = wave*64 + ni*32 + ..; a lane's accumulator rows 4q ..
+        // 4q+3 are four consecutive j of one column m; nr, NR and j0 are
+        // multiples of 8, so the four share a fate
+        const int c_base = (nt0 + jt) * kLgBN, ncol = min(kLgBN, p.D - c_base);
+        ++jt;
+#pragma unroll
+        for (int mi2 = 0; mi2 < TM; ++mi2)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int j = p.j0 + mi2 * 32 + acc_row(4 * q, lane);
+                    const int cl = wave * 64 + ni * 32 + acc_col(lane);
+                    if (j < p.nr && j < p.j0 + NR && cl < ncol) {
+                        const int m = c_base + cl;
+                        const f32x4_t v{acc[mi2][ni][4 * q], acc[mi2][ni][4 * q + 1], acc[mi2][ni][4 * q + 2],
+                                        acc[mi2][ni][4 * q + 3]};
+                        if (single) dst.store4(m, j, p.s * v);
+                        else *reinterpret_cast<f32x4_t *>(p.partial + ((size_t)tl.gmt * p.D + m) * p.nr + j) = v;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mi2][ni][i] = 0.0f;
+            }
     }
     lds::wait_vm<0>();  // the zero loads of the last steps
-    // acc[mi2][ni] holds out^T rows j = mi2*32 + .., columns c = wave*64 + ni*32 + ..
-    const bool single = (p.offsets[tl.e + 1] - p.offsets[tl.e]) <= kLgRC;
-    const LgOut dst(p, tl.e);
-    // a lane's accumulator rows 4q .. 4q+3 are four consecutive j of one
-    // column m; nr, NR and j0 are multiples of 8, so the four share a fate
-#pragma unroll
-    for (int mi2 = 0; mi2 < TM; ++mi2)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = p.j0 + mi2 * 32 + acc_row(4 * q, lane);
-                const int cl = wave * 64 + ni * 32 + acc_col(lane);
-                if (j < p.nr && j < p.j0 + NR && cl < ncol) {
-                    const int m = c_base + cl;
-                    const f32x4_t v{acc[mi2][ni][4 * q], acc[mi2][ni][4 * q + 1], acc[mi2][ni][4 * q + 2],
-                                    acc[mi2][ni][4 * q + 3]};
-                    if (single) dst.store4(m, j, p.s * v);
-                    else *reinterpret_cast<f32x4_t *>(p.partial + ((size_t)tl.gmt * p.D + m) * p.nr + j) = v;
-                }
-            }
 }
 
 // Finalize of the bf16 path: kLgFinSplit blocks per (expert, mode). Experts
@@ -1969,7 +2002,7 @@ static hipError_t launch_lgrad_set(const Dims &D, const LGradP (&lp)[4], hipStre
             set.m[set.n].j0 = j0;
             set.base[set.n] = grid;
             ++set.n;
-            grid += (max_row_tiles(D.S(), D.E, kLgRC) * cdiv(lp[m].D, kLgBN) + 7) & ~7;
+            grid += (max_row_tiles(D.S(), D.E, kLgRC) * cdiv(cdiv(lp[m].D, kLgBN), kLgNTB) + 7) & ~7;
         }
     }
     if (set.n == 0) return hipSuccess;
