@@ -2031,10 +2031,8 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         }
         {
             TraceScope ts(tr, K_DOWN_BWD, st);
-            // with NF4 weights the down-backward tile already spends its slack
-            // on dequantisation: Pgu then comes from the separate projection
             DownBwdP dp{b.dout, b.wd, b.ad, b.G, b.U, b.Pd, b.topk_w, b.sorted_slot, b.offsets, b.dGU,
-                        D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row, b.tiles, b.bg, b.bu, b.q4 ? nullptr : b.ppart};
+                        D.T, D.E, D.k, D.d, D.F, D.r, D.s, b.w_row, b.tiles, b.bg, b.bu, b.ppart};
             if constexpr (std::is_same<T, bf16_t>::value) {
                 if (b.q4) {
                     const Q4P q = q4_params(b.q4->cd, b.q4->cd, b.q4->sd, b.q4->sd);
@@ -2049,7 +2047,7 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
         }
         {
             TraceScope ts(tr, K_PROJ_DGU, st);
-            if (b.ppart && !b.q4) {
+            if (b.ppart) {
                 // the down-backward epilogues left Pgu's column-strip shares
                 MOE_LAUNCH(k_pgu_sum, cdiv(S, 64), 256, b.ppart, cdiv(D.F, 256), S, 2 * D.r, b.Pgu,
                            static_cast<bf16_t *>(b.PguT), lgrad_ldT(D));
