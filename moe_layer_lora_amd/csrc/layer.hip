@@ -1245,15 +1245,29 @@ __global__ __launch_bounds__(256) void k_proj_lds(ProjP p) {
 __global__ __launch_bounds__(256) void k_pgu_sum(const float *__restrict__ part, int nstrip, int S, int r2,
                                                  float *__restrict__ pgu, bf16_t *__restrict__ pguT, int ldT) {
     __shared__ float t[64][65];
-    const int row0 = blockIdx.x * 64;
-    for (int i = threadIdx.x; i < 64 * r2; i += 256) {
-        const int m = i / r2, j = i % r2, pr = row0 + m;
-        float v = 0.0f;
+    const int row0 = blockIdx.x * 64, nq = r2 / 4;
+    const size_t ss = (size_t)S * nq;  // strip stride in float4
+    // a thread sums four consecutive j of one row, strip by strip in order;
+    // the loads of four strips are issued before their adds
+    for (int i = threadIdx.x; i < 64 * nq; i += 256) {
+        const int m = i / nq, j = (i % nq) * 4, pr = row0 + m;
+        f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
         if (pr < S) {
-            for (int sidx = 0; sidx < nstrip; ++sidx) v += part[((size_t)sidx * S + pr) * r2 + j];
-            pgu[(size_t)pr * r2 + j] = v;
+            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(part + (size_t)pr * r2 + j);
+            int sidx = 0;
+            for (; sidx + 4 <= nstrip; sidx += 4) {
+                const f32x4_t a = src[sidx * ss], b = src[(sidx + 1) * ss], c = src[(sidx + 2) * ss],
+                              d = src[(sidx + 3) * ss];
+                v += a;
+                v += b;
+                v += c;
+                v += d;
+            }
+            for (; sidx < nstrip; ++sidx) v += src[sidx * ss];
+            *reinterpret_cast<f32x4_t *>(pgu + (size_t)pr * r2 + j) = v;
         }
-        if (j < 64) t[j][m] = v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) t[j + c][m] = v[c];
     }
     __syncthreads();
     for (int i = threadIdx.x; i < 64 * r2; i += 256) {
