@@ -30,6 +30,13 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// two values, same rounding, lo in bits 0-15: one v_cvt_pk_bf16_f32 (two
+// scalar conversions cost two of them plus a shift and an or)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 
 // ---------------------------------------------------------------------------
 // Element traits. A "chunk" is 16 bytes: VEC elements. Both MFMA operands
@@ -70,8 +77,7 @@ template <> struct Elem<bf16_t> {
     __device__ static chunk_t pack(const float *v) {
         chunk_t c;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            c[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; ++i) c[i] = f32x2_to_bf16x2(v[2 * i], v[2 * i + 1]);
         return c;
     }
 };

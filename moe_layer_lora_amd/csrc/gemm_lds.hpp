@@ -526,7 +526,7 @@ __device__ __forceinline__ Nf4Table nf4_table(float s, const Nf4Lv &lv) {
     uint32_t p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        p[i] = (uint32_t)f32_to_bf16(lv.v[2 * i] * s) | ((uint32_t)f32_to_bf16(lv.v[2 * i + 1] * s) << 16);
+        p[i] = f32x2_to_bf16x2(lv.v[2 * i] * s, lv.v[2 * i + 1] * s);
     Nf4Table t;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -547,10 +547,16 @@ __device__ __forceinline__ uint32_t nf4_plane(const uint32_t (&pl)[4], uint32_t 
     return (m & b) | (~m & a);
 }
 
-// 8 codes (one dword, element i in nibble i) -> 8 bf16 in element order
+// 8 codes (one dword, element i in nibble i) -> 8 bf16 in element order.
+// The bit-3 masks come from v_perm's sign selectors (8, 9, 10, 11 give
+// 0xff or 0x00 from bit 7 of bytes 1, 3, 5, 7 of the 8-byte source): for
+// the odd elements that bit is bit 7 of each code byte already, for the even
+// ones it is moved there by a 4-bit shift (a multiply by 0xff would be a
+// quarter-rate instruction).
 __device__ __forceinline__ chunk_t nf4_lookup8(uint32_t q, const Nf4Table &t) {
     const uint32_t ce = q & 0x07070707u, co = (q >> 4) & 0x07070707u;  // elements 0,2,4,6 / 1,3,5,7
-    const uint32_t me = ((q >> 3) & 0x01010101u) * 0xffu, mo = ((q >> 7) & 0x01010101u) * 0xffu;
+    const uint32_t me = __builtin_amdgcn_perm(q << 4, q << 12, 0x0B090A08u);
+    const uint32_t mo = __builtin_amdgcn_perm(q, q << 8, 0x0B090A08u);
     const uint32_t lo_e = nf4_plane(t.lo, ce, me), hi_e = nf4_plane(t.hi, ce, me);
     const uint32_t lo_o = nf4_plane(t.lo, co, mo), hi_o = nf4_plane(t.hi, co, mo);
     const uint32_t e02 = __builtin_amdgcn_perm(hi_e, lo_e, 0x05010400u), e46 = __builtin_amdgcn_perm(hi_e, lo_e, 0x07030602u);
