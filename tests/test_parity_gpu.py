@@ -57,6 +57,11 @@ SMALL = {
     # E = 300: 5 logits per lane in the top-k kernel
     "many_experts_bf16": LayerConfig("many_experts_bf16", T=256, d=64, E=300, k=6, F=64, r=16,
                                      dtype="bf16", alpha=32.0, router_grad=True),
+    # F = 1288: six 256-column strips of Pgu shares (four summed as a group,
+    # two after), an 11th gate/up column tile with 8 valid f and a ragged
+    # 64-deep K tail in the down GEMM
+    "wide_ffn_bf16": LayerConfig("wide_ffn_bf16", T=256, d=128, E=4, k=2, F=1288, r=16, dtype="bf16",
+                                 alpha=32.0, router_grad=True),
 }
 
 
