@@ -174,6 +174,57 @@ def test_edge_cases(name):
     check("d_logits", r["d_logits"], b["d_logits"], tol, name)
 
 
+# ------------------------------------------------------------------ shape sweep
+
+def sweep_configs(n=24, seed=20261203):
+    """Seeded random legal shapes beside the hand-picked ones: d, F and r any
+    multiple of 8 up to 512 / 640 / 72 (ranks that are not a multiple of 16
+    take the register-staged projection and odd LoRA K windows), 1 to 130
+    experts with k up to 8, and a Zipf-like skew on some, so that empty
+    experts, one-row experts and ragged tiles all occur. Every fourth case
+    runs without the kept expert outputs (no router gradient)."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        dt = "f32" if i % 6 == 5 else "bf16"
+        E = int(rs.choice([1, 2, 3, 7, 16, 33, 64, 130]))
+        k = int(rs.randint(1, min(E, 8) + 1))
+        r = 8 * int(rs.randint(1, 10))
+        out.append(LayerConfig(f"sweep{i:02d}_{dt}", T=int(rs.randint(1, 601)), d=8 * int(rs.randint(1, 65)),
+                               E=E, k=k, F=8 * int(rs.randint(1, 81)), r=r, dtype=dt, alpha=2.0 * r,
+                               router_grad=i % 4 != 3, skew_bias=float(rs.choice([0.0, 0.0, 2.0, 4.0]))))
+    return out
+
+
+SWEEP = {c.name: c for c in sweep_configs()}
+
+
+@pytest.mark.parametrize("name", list(SWEEP))
+def test_shape_sweep(name):
+    cfg = SWEEP[name]
+    print(f"[sweep] {cfg}", flush=True)
+    inputs = synth.make_inputs(cfg, seed=4)
+    _, r = run_small(cfg, inputs, keep=cfg.router_grad, router_grad=cfg.router_grad)
+    rt, f, b = oracle_full(cfg, inputs)
+    check_routing(r, rt, name)
+    tol = TOL[cfg.dtype]
+    for n in ("G", "U", "H", "Zd", "out", "dx", "dXp"):
+        check(n, r[n], (b if n in ("dx", "dXp") else f)[n], tol, name)
+    check("Zgu", r["Zgu"], np.concatenate([f["Zg"], f["Zu"]], 1), tol, name)
+    check("dGU", r["dGU"], np.concatenate([b["dG"], b["dU"]], 1), tol, name)
+    if cfg.router_grad:
+        check("Y", r["Y"], f["Y"], tol, name)
+        check("d_topk_w", r["d_topk_w"], b["d_topk_w"], tol, name)
+        check("d_logits", r["d_logits"], b["d_logits"], tol, name)
+    empty = rt["counts"] == 0
+    ne = np.nonzero(~empty)[0]
+    for g in GRADS:
+        check(g, r[g], b[g], tol, name)
+        assert np.all(r[g][empty] == 0.0), f"{name} {g}: empty experts must get exact zeros"
+        for e in ne:
+            check(f"{g}[{e}]", r[g][e], b[g][e], tol, name)
+
+
 def test_empty_batch():
     lr = _runner()
     cfg = LayerConfig("empty", T=0, d=64, E=4, k=2, F=64, r=8, dtype="bf16", alpha=16.0)
