@@ -125,31 +125,61 @@ FUSED = {
 }
 
 
+def _fused_equals_unfused(cfg, name, keep=True, seed=0):
+    import layer_runner as lr
+    inp = synth.make_inputs(cfg, seed=seed)
+    q = _nf4_base(cfg, seed=seed)
+    ref = lr.Layer(cfg, inp, keep_expert_out=keep)
+    for n, key, rows, cols in (("w_gate", "gate", cfg.E * cfg.F, cfg.d), ("w_up", "up", cfg.E * cfg.F, cfg.d),
+                               ("w_down", "down", cfg.E * cfg.d, cfg.F)):
+        ref.w[n].copy_(_dequant_gpu(q["codes_" + key], q["scales_" + key], rows, cols).view(ref.w[n].shape))
+    ref.step(backward=True, router_grad=keep)
+    want = ref.results(backward=True, router_grad=keep, intermediates=True)
+    del ref
+    fused = lr.Layer(cfg, inp, keep_expert_out=keep, q4=q)
+    assert "w_gate" not in fused.w  # no bf16 base weight exists on the fused path
+    fused.step(backward=True, router_grad=keep)
+    got = fused.results(backward=True, router_grad=keep, intermediates=True)
+    assert set(got) == set(want)
+    for n in want:
+        assert np.array_equal(got[n], want[n]), f"{name}: {n} differs from the unfused path"
+
+
 @pytest.mark.parametrize("name", list(FUSED))
 def test_fused_nf4_equals_dequantise_then_bf16(name):
     """moe_fwd_nf4 / moe_bwd_nf4 (codes dequantised while each B tile is
     staged into LDS) against moe_nf4_dequant + moe_fwd / moe_bwd on the
     dequantised weights: every output and intermediate bit for bit (the GEMMs
     multiply the same bf16 tiles in the same order)."""
-    import layer_runner as lr
-    cfg = FUSED[name]
     print(f"[nf4 fused] {name}", flush=True)
-    inp = synth.make_inputs(cfg, seed=0)
-    q = _nf4_base(cfg)
-    ref = lr.Layer(cfg, inp, keep_expert_out=True)
-    for n, key, rows, cols in (("w_gate", "gate", cfg.E * cfg.F, cfg.d), ("w_up", "up", cfg.E * cfg.F, cfg.d),
-                               ("w_down", "down", cfg.E * cfg.d, cfg.F)):
-        ref.w[n].copy_(_dequant_gpu(q["codes_" + key], q["scales_" + key], rows, cols).view(ref.w[n].shape))
-    ref.step(backward=True, router_grad=True)
-    want = ref.results(backward=True, router_grad=True, intermediates=True)
-    del ref
-    fused = lr.Layer(cfg, inp, keep_expert_out=True, q4=q)
-    assert "w_gate" not in fused.w  # no bf16 base weight exists on the fused path
-    fused.step(backward=True, router_grad=True)
-    got = fused.results(backward=True, router_grad=True, intermediates=True)
-    assert set(got) == set(want)
-    for n in want:
-        assert np.array_equal(got[n], want[n]), f"{name}: {n} differs from the unfused path"
+    _fused_equals_unfused(FUSED[name], name)
+
+
+def nf4_sweep_configs(n=10, seed=20261204):
+    """Seeded random shapes the 4-bit path accepts: d and F any multiple of
+    64 up to 576 / 704 (the per-64 scale groups), r any multiple of 8 up to
+    72, 1 to 130 experts, k up to 8, skew on some, every third case without
+    the kept expert outputs."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        E = int(rs.choice([1, 3, 8, 33, 130]))
+        k = int(rs.randint(1, min(E, 8) + 1))
+        r = 8 * int(rs.randint(1, 10))
+        out.append(LayerConfig(f"nf4_sweep{i:02d}", T=int(rs.randint(1, 601)), d=64 * int(rs.randint(1, 10)),
+                               E=E, k=k, F=64 * int(rs.randint(1, 12)), r=r, dtype="bf16", alpha=2.0 * r,
+                               router_grad=i % 3 != 2, skew_bias=float(rs.choice([0.0, 0.0, 3.0]))))
+    return out
+
+
+NF4_SWEEP = {c.name: c for c in nf4_sweep_configs()}
+
+
+@pytest.mark.parametrize("name", list(NF4_SWEEP))
+def test_fused_nf4_shape_sweep(name):
+    cfg = NF4_SWEEP[name]
+    print(f"[nf4 sweep] {cfg}", flush=True)
+    _fused_equals_unfused(cfg, name, keep=cfg.router_grad, seed=5)
 
 
 def test_fused_nf4_layer_matches_oracle():
