@@ -328,16 +328,17 @@ def stack_offload_bench(torch, moe, cfg, pb, x, logits, w, dout, keep, n=4, reps
     a device `saved` buffer per layer and (b) with moe_stack_fwd / bwd, which
     offload layers 0 .. n-3 to pinned host memory and reload them
     double-buffered. Also the time of one layer's copy each way alone, so the
-    share of the copies the schedule hides is measured, not assumed."""
+    share of the copies the schedule hides is measured, not assumed. A copy
+    moves `saved` without H (rebuilt from G and U on the reload)."""
     dev = x.device
     dt = x.dtype
-    nbytes = moe.saved_bytes(pb, keep)
+    nbytes, nhost = moe.saved_bytes(pb, keep), moe.saved_host_bytes(pb, keep)
     layers = []
     for i in range(n):
         L = {"logits": torch.roll(logits, shifts=i, dims=1).contiguous(), "w": w,
              "rt": moe.alloc_routing(pb, dev), "grads": moe.alloc_grads(pb, dev),
              "out": torch.empty_like(x), "dx": torch.empty_like(x),
-             "host_saved": torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) if i <= n - 3 else None}
+             "host_saved": torch.empty(nhost, dtype=torch.uint8, pin_memory=True) if i <= n - 3 else None}
         layers.append(L)
     for i, L in enumerate(layers):
         L["x"] = x if i == 0 else layers[i - 1]["out"]
@@ -383,16 +384,17 @@ def stack_offload_bench(torch, moe, cfg, pb, x, logits, w, dout, keep, n=4, reps
     h2d = timed(lambda: moe.moe_saved_copy(pb, keep, True, dsaved[0], host, copy_stream=cs))
     copies = (n - 2) * (d2h + h2d)
     hidden = 1.0 - (t_off - t_res) / copies if copies > 0 else None
-    return {"layers": n, "saved_bytes_per_layer": nbytes,
+    return {"layers": n, "saved_bytes_per_layer": nbytes, "copied_bytes_per_layer": nhost,
             "device_activation_bytes": {"per_layer_buffers": n * nbytes, "double_buffered": 2 * nbytes},
             "fwd_bwd_ms_per_layer_buffers": round(t_res, 3), "fwd_bwd_ms_offloaded": round(t_off, 3),
             "copy_ms_per_layer": {"d2h": round(d2h, 3), "h2d": round(h2d, 3)},
-            "copy_GBs": {"d2h": round(nbytes / d2h / 1e6, 1), "h2d": round(nbytes / h2d / 1e6, 1)},
+            "copy_GBs": {"d2h": round(nhost / d2h / 1e6, 1), "h2d": round(nhost / h2d / 1e6, 1)},
             "copies_ms_total": round(copies, 3),
             "hidden_fraction": None if hidden is None else round(max(0.0, min(1.0, hidden)), 3),
             "dx_equal_to_per_layer_buffers": same,
             "note": "median of %d runs each; hidden_fraction = 1 - (offloaded - resident) / (time of the "
-                    "2(n-2) copies alone); layers n-2 and n-1 stay on the device" % reps}
+                    "2(n-2) copies alone); layers n-2 and n-1 stay on the device; h2d includes the "
+                    "rebuild of H from G and U" % reps}
 
 
 def nf4_step_bench(torch, moe, synth, cfg, pb, ctx, hip, bf16_step_ms, steps, warmup):

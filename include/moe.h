@@ -159,13 +159,20 @@ enum { MOE_PART_Y = 0, MOE_PART_DGU = 1, MOE_PART_DXP = 2 };
 size_t moe_workspace_part(const moe_problem_t *pb, int part, int training, int keep_expert_out);
 
 /* Bytes of the `saved` buffer that moe_fwd fills for moe_bwd. Layout, each
- * part starting on a 256-byte boundary: G, U, H [S,F] dtype; Zgu [S,2r]
+ * part starting on a 256-byte boundary: G, U [S,F] dtype; Zgu [S,2r]
  * float32 (x A_gate^T | x A_up^T); Zd [S,r] float32 (h A_down^T); for bf16
  * only, ZguT [2r,ldT] bf16 (Zgu transposed) and wZdT [r,ldT] bf16 (Zd
  * transposed, row p scaled by its combine weight), ldT = S rounded up to a
- * multiple of 8, the operands of the LoRA-gradient kernels; and, if keep_expert_out, Y [S,d] dtype (expert outputs, needed
- * for d_topk_w). Rows are indexed by row p. */
+ * multiple of 8, the operands of the LoRA-gradient kernels; if
+ * keep_expert_out, Y [S,d] dtype (expert outputs, needed for d_topk_w);
+ * last, H [S,F] dtype, computed from G and U as stored (bf16-rounded for
+ * bf16 layers), so that it can be rebuilt from them. Rows are indexed by
+ * row p. */
 size_t moe_saved_bytes(const moe_problem_t *pb, int keep_expert_out);
+
+/* Bytes of `saved` that an offload moves to host memory: everything before
+ * H (moe_saved_copy and the stack calls rebuild H on the reload). */
+size_t moe_saved_host_bytes(const moe_problem_t *pb, int keep_expert_out);
 
 /* Routing. logits [T,E] float32 -> rt (all six arrays written).
  * host_counts: (host) int32[E] that receives counts, or NULL: the one
@@ -266,14 +273,17 @@ moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *
  * activations in pinned host memory and brings them back for the backward on
  * a copy stream, two device buffers taking turns so that the backward of one
  * layer reads buffer A while the next layer's activations arrive in B.
- * moe_saved_copy copies the moe_saved_bytes(pb, keep_expert_out) bytes of one
- * `saved` buffer to (to_device = 0) or from (to_device = 1) `host`, on
- * `copy_stream`, after `wait_event` (a hipEvent_t the caller recorded on its
- * compute stream, e.g. after moe_fwd, or before the backward that last read
- * the device buffer; NULL: no wait), and records `done_event` on copy_stream
- * after the copy (NULL: none); the compute stream waits on that event before
- * moe_bwd reads the buffer. `host` must be pinned (page-locked, e.g.
- * hipHostMalloc): pageable memory would make the copy synchronous, so it is
+ * moe_saved_copy copies the first moe_saved_host_bytes(pb, keep_expert_out)
+ * bytes of one `saved` buffer (all of it but H) to (to_device = 0) or from
+ * (to_device = 1) `host`, on `copy_stream`, after `wait_event` (a hipEvent_t
+ * the caller recorded on its compute stream, e.g. after moe_fwd, or before
+ * the backward that last read the device buffer; NULL: no wait). After a
+ * copy to the device it rebuilds H from G and U with a kernel on
+ * copy_stream, bit-identical to the H moe_fwd stored. It records
+ * `done_event` on copy_stream after that (NULL: none); the compute stream
+ * waits on that event before moe_bwd reads the buffer. `host` must be
+ * pinned (page-locked, e.g. hipHostMalloc), of moe_saved_host_bytes bytes
+ * at least: pageable memory would make the copy synchronous, so it is
  * rejected (MOE_E_ARG). The bytes are copied unchanged. */
 moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to_device, void *saved,
                             void *host, void *wait_event, void *copy_stream, void *done_event);
@@ -289,12 +299,13 @@ moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to
  *   moe_stack_fwd: for i = 0 .. n-1 on `stream`: wait for the offload of
  *     layer i-2 (it reads saved[i % 2]); moe_route (logits -> rt); moe_fwd
  *     into saved[i % 2]; then, for i <= n-3, copy_stream copies saved[i % 2]
- *     to host_saved after the forward. Layers n-2 and n-1 stay on the device.
+ *     (all but H, as moe_saved_copy) to host_saved after the forward. Layers
+ *     n-2 and n-1 stay on the device.
  *   moe_stack_bwd (after moe_stack_fwd with the same arguments and nothing
  *     else written to the two buffers in between): for i = n-1 down to 0:
  *     layers i <= n-3 wait for their reload; moe_bwd from saved[i % 2]; then
- *     copy_stream reloads layer i-2 into saved[i % 2], under the backward of
- *     layer i-1.
+ *     copy_stream reloads layer i-2 into saved[i % 2] and rebuilds its H,
+ *     under the backward of layer i-1.
  * Every layer has the problem pb. The caller wires the stack: layer i+1's x
  * is typically layer i's out, and layer i's dout layer i+1's dx. Results are
  * bit-identical to moe_route + moe_fwd + moe_bwd per layer with a saved
@@ -309,7 +320,7 @@ typedef struct {
     void *dx;                      /* [T,d] gradient of x (bwd)               */
     const moe_lora_grads_t *grads; /* LoRA gradients (bwd)                    */
     float *d_topk_w, *d_logits;    /* optional, as in moe_bwd (bwd)           */
-    void *host_saved;              /* (host) pinned, moe_saved_bytes bytes; needed for layers 0 .. n-3 */
+    void *host_saved;              /* (host) pinned, moe_saved_host_bytes bytes; layers 0 .. n-3 */
 } moe_stack_layer_t;
 
 typedef struct {

@@ -40,7 +40,7 @@ EXPORTS = ["moe_route_workspace", "moe_fwd_workspace", "moe_bwd_workspace", "moe
            "moe_route", "moe_fwd", "moe_bwd", "moe_status_str", "moe_router_workspace",
            "moe_router_fwd", "moe_router_bwd", "moe_saved_copy", "moe_nf4_dequant",
            "moe_workspace_part", "moe_route_noalloc", "moe_stack_workspace", "moe_stack_fwd",
-           "moe_stack_bwd", "moe_fwd_nf4", "moe_bwd_nf4"]
+           "moe_stack_bwd", "moe_fwd_nf4", "moe_bwd_nf4", "moe_saved_host_bytes"]
 MOE_PART_Y, MOE_PART_DGU, MOE_PART_DXP = range(3)
 
 
@@ -108,8 +108,9 @@ _lib.moe_route_workspace.argtypes = [_P(Problem)]
 _lib.moe_fwd_workspace.argtypes = [_P(Problem), _i32, _i32]
 _lib.moe_bwd_workspace.argtypes = [_P(Problem)]
 _lib.moe_saved_bytes.argtypes = [_P(Problem), _i32]
+_lib.moe_saved_host_bytes.argtypes = [_P(Problem), _i32]
 for _f in (_lib.moe_route_workspace, _lib.moe_fwd_workspace, _lib.moe_bwd_workspace,
-           _lib.moe_saved_bytes):
+           _lib.moe_saved_bytes, _lib.moe_saved_host_bytes):
     _f.restype = _sz
 _lib.moe_route.argtypes = [_P(Problem), _vp, _P(Routing), _vp, _vp, _sz, _vp, _P(Trace)]
 _lib.moe_route_noalloc.argtypes = [_P(Problem), _vp, _P(Routing), _vp, _vp, _P(Trace)]
@@ -201,6 +202,11 @@ def bwd_workspace(pb: Problem) -> int:
 
 def saved_bytes(pb: Problem, keep_expert_out: bool) -> int:
     return _lib.moe_saved_bytes(ctypes.byref(pb), int(keep_expert_out))
+
+
+def saved_host_bytes(pb: Problem, keep_expert_out: bool) -> int:
+    """Bytes of `saved` an offload moves to host memory (all of it but H)."""
+    return _lib.moe_saved_host_bytes(ctypes.byref(pb), int(keep_expert_out))
 
 
 def _check(st, what):
@@ -311,9 +317,10 @@ def moe_router_bwd(pb, x, w_router, d_logits, dx_in=None, dx=None, dw_router=Non
 
 def moe_saved_copy(pb, keep_expert_out, to_device, saved, host, wait_event=None, copy_stream=None,
                    done_event=None):
-    """Copy a `saved` buffer to (to_device=False) or from a pinned host tensor
-    on copy_stream, after wait_event (a torch.cuda.Event or raw hipEvent_t);
-    records done_event on copy_stream."""
+    """Copy a `saved` buffer (all but H) to (to_device=False) or from a
+    pinned host tensor of saved_host_bytes on copy_stream, after wait_event (a
+    torch.cuda.Event or raw hipEvent_t); a reload then rebuilds H from G and U
+    on copy_stream; records done_event on copy_stream."""
     def ev(e):
         if e is None or isinstance(e, int):
             return e
@@ -322,10 +329,10 @@ def moe_saved_copy(pb, keep_expert_out, to_device, saved, host, wait_event=None,
         hp = host
     else:
         hp, nbytes, _ = _host_buffer(host, "moe_saved_copy host")
-        need = saved_bytes(pb, keep_expert_out)
+        need = saved_host_bytes(pb, keep_expert_out)
         if nbytes < need:
-            raise MoeError(MOE_E_ARG, f"moe_saved_copy host: {nbytes} bytes for a {need}-byte "
-                                      "saved buffer")
+            raise MoeError(MOE_E_ARG, f"moe_saved_copy host: {nbytes} bytes, the offloaded part of "
+                                      f"saved is {need}")
     st = _lib.moe_saved_copy(ctypes.byref(pb), int(keep_expert_out), int(to_device), _ptr(saved), hp,
                              ev(wait_event), _stream(copy_stream), ev(done_event))
     _check(st, "moe_saved_copy")
@@ -335,16 +342,23 @@ def stack_workspace(pb: Problem, keep_expert_out: bool) -> int:
     return _lib.moe_stack_workspace(ctypes.byref(pb), int(keep_expert_out))
 
 
-def _stack_args(layers, saved, copy_stream, events):
+def _stack_args(pb, keep_expert_out, layers, saved, copy_stream, events):
     """ctypes arrays for the stack calls; the returned tuple keeps every
-    referenced structure alive for the duration of the call."""
+    referenced structure alive for the duration of the call. A host_saved
+    buffer shorter than saved_host_bytes is refused here (the C ABI cannot
+    see its size)."""
     keep = []
+    need = saved_host_bytes(pb, keep_expert_out)
     arr = (StackLayer * len(layers))()
     for i, L in enumerate(layers):
         rt, w = _struct(Routing, L["rt"]), _struct(Weights, L["w"])
         g = _struct(LoraGrads, L["grads"]) if L.get("grads") is not None else None
         keep += [rt, w, g]
         hs = L.get("host_saved")
+        if hs is not None and not isinstance(hs, int):
+            nbytes = _host_buffer(hs, "host_saved")[1]
+            if nbytes < need:
+                raise MoeError(MOE_E_ARG, f"host_saved of layer {i}: {nbytes} bytes, need {need}")
         arr[i] = StackLayer(_ptr(L.get("logits")), ctypes.pointer(rt), ctypes.pointer(w), _ptr(L.get("x")),
                             _ptr(L.get("out")), _ptr(L.get("dout")), _ptr(L.get("dx")),
                             ctypes.pointer(g) if g is not None else None, _ptr(L.get("d_topk_w")),
@@ -369,7 +383,7 @@ def moe_stack_fwd(pb, layers: list, keep_expert_out, saved, copy_stream, events,
     """Forward of a stack of layers with saved activations offloaded to each
     layer's pinned host_saved through the two device buffers `saved`.
     layers: dicts with logits, rt, w, x, out, host_saved (see moe.h)."""
-    arr, off, _keep = _stack_args(layers, saved, copy_stream, events)
+    arr, off, _keep = _stack_args(pb, keep_expert_out, layers, saved, copy_stream, events)
     st = _lib.moe_stack_fwd(ctypes.byref(pb), len(layers), arr, int(keep_expert_out), ctypes.byref(off),
                             _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "moe_stack_fwd")
@@ -378,7 +392,7 @@ def moe_stack_fwd(pb, layers: list, keep_expert_out, saved, copy_stream, events,
 def moe_stack_bwd(pb, layers: list, keep_expert_out, saved, copy_stream, events, ws, stream=None):
     """Backward of the stack moe_stack_fwd ran: layers additionally carry dout,
     dx, grads and optionally d_topk_w / d_logits."""
-    arr, off, _keep = _stack_args(layers, saved, copy_stream, events)
+    arr, off, _keep = _stack_args(pb, keep_expert_out, layers, saved, copy_stream, events)
     st = _lib.moe_stack_bwd(ctypes.byref(pb), len(layers), arr, int(keep_expert_out), ctypes.byref(off),
                             _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "moe_stack_bwd")
@@ -453,13 +467,14 @@ def saved_views(pb: Problem, saved, keep_expert_out: bool) -> dict:
     def al(x):
         return (x + 255) // 256 * 256
 
-    parts = [("G", (S, F), dt, es), ("U", (S, F), dt, es), ("H", (S, F), dt, es),
+    parts = [("G", (S, F), dt, es), ("U", (S, F), dt, es),
              ("Zgu", (S, 2 * r), torch.float32, 4), ("Zd", (S, r), torch.float32, 4)]
     ldT = (S + 7) // 8 * 8
     if bf:
         parts += [("ZguT", (2 * r, ldT), torch.bfloat16, 2), ("wZdT", (r, ldT), torch.bfloat16, 2)]
     if keep_expert_out:
         parts += [("Y", (S, d), dt, es)]
+    parts += [("H", (S, F), dt, es)]
     out, o = {}, 0
     for name, shape, t, e in parts:
         n = shape[0] * shape[1]

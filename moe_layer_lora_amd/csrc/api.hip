@@ -53,7 +53,9 @@ RouteWs route_ws(const moe_problem_t *pb) {
     return w;
 }
 
-struct SavedLayout { size_t G, U, H, Zgu, Zd, ZguT, wZdT, Y, total; };
+// H last: everything before it is what an offload moves (H is rebuilt from
+// G and U on the reload)
+struct SavedLayout { size_t G, U, Zgu, Zd, ZguT, wZdT, Y, H, total; };
 SavedLayout saved_layout(const moe_problem_t *pb, int keep) {
     const size_t S = (size_t)pb->T * pb->k, es = esize(pb->dtype);
     const bool bf = pb->dtype == MOE_BF16;
@@ -61,13 +63,13 @@ SavedLayout saved_layout(const moe_problem_t *pb, int keep) {
     size_t o = 0;
     l.G = o; o += al(S * pb->F * es);
     l.U = o; o += al(S * pb->F * es);
-    l.H = o; o += al(S * pb->F * es);
     l.Zgu = o; o += al(S * 2 * pb->r * sizeof(float));
     l.Zd = o; o += al(S * pb->r * sizeof(float));
     const size_t ldT = (S + 7) & ~(size_t)7;
     l.ZguT = o; if (bf) o += al(ldT * 2 * pb->r * 2);
     l.wZdT = o; if (bf) o += al(ldT * pb->r * 2);
     l.Y = o; if (keep) o += al(S * pb->d * es);
+    l.H = o; o += al(S * pb->F * es);
     l.total = o;
     return l;
 }
@@ -297,6 +299,25 @@ bool pinned_host(const void *p) {
     return pa.type == hipMemoryTypeHost;
 }
 
+// Offload: the part of `saved` before H (moe_saved_host_bytes) to host, on
+// stream s. Reload: that part back, then H rebuilt from G and U on s.
+moe_status_t saved_offload(const moe_problem_t *pb, int keep, const void *saved, void *host, hipStream_t s) {
+    const SavedLayout l = saved_layout(pb, keep != 0);
+    if (l.H > 0 && hipMemcpyAsync(host, saved, l.H, hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_E_HIP;
+    return MOE_OK;
+}
+
+moe_status_t saved_reload(const moe_problem_t *pb, int keep, void *saved, const void *host, hipStream_t s) {
+    const SavedLayout l = saved_layout(pb, keep != 0);
+    if (l.H > 0 && hipMemcpyAsync(saved, host, l.H, hipMemcpyHostToDevice, s) != hipSuccess) return MOE_E_HIP;
+    const size_t n = (size_t)pb->T * pb->k * pb->F;
+    const hipError_t e =
+        pb->dtype == MOE_BF16
+            ? moe::run_rebuild_h<moe::bf16_t>(n, at(saved, l.G), at(saved, l.U), at(saved, l.H), s)
+            : moe::run_rebuild_h<float>(n, at(saved, l.G), at(saved, l.U), at(saved, l.H), s);
+    return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
 }  // namespace api
 }  // namespace moe
 
@@ -518,18 +539,22 @@ moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *
     return e == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
+size_t moe_saved_host_bytes(const moe_problem_t *pb, int keep_expert_out) {
+    if (check_problem(pb) != MOE_OK) return 0;
+    return saved_layout(pb, keep_expert_out != 0).H;
+}
+
 moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to_device, void *saved, void *host,
                             void *wait_event, void *copy_stream, void *done_event) {
     moe_status_t st = check_problem(pb);
     if (st != MOE_OK) return st;
     if (!buf_ok(saved) || !host || !moe::api::pinned_host(host)) return MOE_E_ARG;
-    const size_t n = saved_layout(pb, keep_expert_out != 0).total;
     hipStream_t cs = static_cast<hipStream_t>(copy_stream);
     if (wait_event && hipStreamWaitEvent(cs, static_cast<hipEvent_t>(wait_event), 0) != hipSuccess)
         return MOE_E_HIP;
-    const hipError_t e = to_device ? hipMemcpyAsync(saved, host, n, hipMemcpyHostToDevice, cs)
-                                   : hipMemcpyAsync(host, saved, n, hipMemcpyDeviceToHost, cs);
-    if (e != hipSuccess) return MOE_E_HIP;
+    st = to_device ? moe::api::saved_reload(pb, keep_expert_out, saved, host, cs)
+                   : moe::api::saved_offload(pb, keep_expert_out, saved, host, cs);
+    if (st != MOE_OK) return st;
     if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), cs) != hipSuccess) return MOE_E_HIP;
     return MOE_OK;
 }

@@ -4,6 +4,8 @@
 
 #include <stddef.h>
 
+#include <hip/hip_runtime.h>
+
 #include "moe.h"
 
 namespace moe {
@@ -25,6 +27,12 @@ moe_status_t route_impl(const moe_problem_t *pb, const float *logits, const moe_
 // true if p is page-locked host memory; pageable memory returns false and
 // leaves no HIP error behind
 bool pinned_host(const void *p);
+
+// Offload of a `saved` buffer of a checked problem to pinned host memory (the
+// moe_saved_host_bytes bytes before H), and its reload: those bytes back,
+// then H rebuilt from G and U; both enqueued on `stream`.
+moe_status_t saved_offload(const moe_problem_t *pb, int keep, const void *saved, void *host, hipStream_t stream);
+moe_status_t saved_reload(const moe_problem_t *pb, int keep, void *saved, const void *host, hipStream_t stream);
 
 }  // namespace api
 }  // namespace moe

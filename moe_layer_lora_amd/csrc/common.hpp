@@ -106,6 +106,31 @@ __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 // instructions per element would dominate the tile's epilogue.
 __device__ __forceinline__ float sigmoid_fast(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// SwiGLU h = silu(g) u of one element: the fast logistic for bf16 layers,
+// IEEE exp and division for fp32 layers.
+__device__ __forceinline__ float swiglu_fast(float g, float u) { return g * sigmoid_fast(g) * u; }
+__device__ __forceinline__ float swiglu_ieee(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// One 16-byte chunk of H from the chunks of G and U as stored. H is a
+// function of the stored (rounded) G and U, not of the accumulators, so the
+// forward's epilogue and a later rebuild from the stored G and U (the reload
+// of offloaded activations) give bit-identical H.
+template <typename T> __device__ __forceinline__ chunk_t swiglu_chunk(const chunk_t &cg, const chunk_t &cu);
+template <> __device__ __forceinline__ chunk_t swiglu_chunk<bf16_t>(const chunk_t &cg, const chunk_t &cu) {
+    float g[8], u[8], h[8];
+    unpack<bf16_t>(cg, g);
+    unpack<bf16_t>(cu, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = swiglu_fast(g[e], u[e]);
+    return Elem<bf16_t>::pack(h);
+}
+template <> __device__ __forceinline__ chunk_t swiglu_chunk<float>(const chunk_t &cg, const chunk_t &cu) {
+    chunk_t h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = __float_as_uint(swiglu_ieee(__uint_as_float(cg[e]), __uint_as_float(cu[e])));
+    return h;
+}
+
 // ---------------------------------------------------------------------------
 // Grouped-tile scheduler. Expert e owns rows offsets[e] .. offsets[e+1]-1,
 // cut into mt_e = ceil(n_e / BM) row tiles; each row tile is crossed with NT

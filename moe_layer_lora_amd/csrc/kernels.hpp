@@ -96,6 +96,9 @@ struct Trace {
 
 template <typename T> hipError_t run_fwd(const Dims &D, const FwdBufs &b, hipStream_t st, const Trace *tr);
 template <typename T> hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace *tr);
+// H = silu(G) U over `elems` elements (a multiple of the 16-byte chunk) from
+// G and U as the forward stored them, bit-identical to the forward's H
+template <typename T> hipError_t run_rebuild_h(size_t elems, const void *G, const void *U, void *H, hipStream_t st);
 
 // ---- router projection (logits = x W_r^T) and its backward ---------------------
 // Workspace of the backward: d_logits transposed [E, Tp] (Tp = T rounded up

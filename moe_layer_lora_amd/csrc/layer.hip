@@ -64,6 +64,7 @@ struct GateUpP {
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup(GateUpP p) {
     using T = typename Cfg::T;
+    static_assert(std::is_same<T, float>::value, "fp32 layers (bf16 gate/up runs on the LDS ring)");
     __shared__ Smem<Cfg> sm;
     constexpr int HALF = Cfg::BN / 2;
     static_assert(Cfg::TN % 2 == 0, "gate/up pairs");
@@ -131,9 +132,9 @@ __global__ __launch_bounds__(Cfg::NTHREADS) MOE_ONE_WAVE_PER_SIMD void k_gateup(
                 if (m < tl.rows && f < p.F) {
                     const float g = acc[mi][2 * c][i], u = acc[mi][2 * c + 1][i];
                     const size_t o = (size_t)(tl.row0 + m) * p.F + f;
-                    if (G) G[o] = Elem<T>::from_f32(g);
-                    if (U) U[o] = Elem<T>::from_f32(u);
-                    H[o] = Elem<T>::from_f32(g / (1.0f + expf(-g)) * u);
+                    if (G) G[o] = g;
+                    if (U) U[o] = u;
+                    H[o] = swiglu_ieee(g, u);
                 }
             }
 }
@@ -475,13 +476,11 @@ __device__ __forceinline__ void gateup_epilogue(const GateUpP &p, const Tile &tl
             const int m = wm * C::WTM + mi * 32 + r;
             const int f = f_base + wn * (C::WTN / 2) + (q / 4) * 32 + (q % 4) * 8;
             if (m < tl.rows && f < p.F) {
-                float h[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) h[e] = g[e] * sigmoid_fast(g[e]) * u[e];
+                const chunk_t cg = Elem<bf16_t>::pack(g), cu = Elem<bf16_t>::pack(u);
                 const size_t o = (size_t)(tl.row0 + m) * p.F + f;
-                if (G) st_stream(G + o, Elem<bf16_t>::pack(g));
-                if (U) st_stream(U + o, Elem<bf16_t>::pack(u));
-                st_stream(H + o, Elem<bf16_t>::pack(h));
+                if (G) st_stream(G + o, cg);
+                if (U) st_stream(U + o, cu);
+                st_stream(H + o, swiglu_chunk<bf16_t>(cg, cu));  // from G and U as stored
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -2124,6 +2123,29 @@ hipError_t run_bwd(const Dims &D, const BwdBufs &b, hipStream_t st, const Trace 
     return hipSuccess;
 }
 
+// H = silu(G) U rebuilt from G and U as stored, one 16-byte chunk per
+// thread and step (S F is a multiple of 8, so whole chunks): the reload of
+// offloaded activations moves G and U only, and the same chunk function as
+// the gate/up epilogue makes the rebuilt H bit-identical to the forward's.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rebuild_h(const chunk_t *__restrict__ G, const chunk_t *__restrict__ U,
+                                                   chunk_t *__restrict__ H, size_t nchunk) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nchunk; i += (size_t)gridDim.x * 256)
+        st_stream(H + i, swiglu_chunk<T>(ld_stream(G + i), ld_stream(U + i)));
+}
+
+template <typename T>
+hipError_t run_rebuild_h(size_t elems, const void *G, const void *U, void *H, hipStream_t st) {
+    const size_t nchunk = elems * sizeof(T) / sizeof(chunk_t);
+    if (nchunk == 0) return hipSuccess;
+    const int grid = (int)std::min<size_t>((nchunk + 255) / 256, 8192);
+    k_rebuild_h<T><<<dim3(grid), dim3(256), 0, st>>>(static_cast<const chunk_t *>(G), static_cast<const chunk_t *>(U),
+                                                     static_cast<chunk_t *>(H), nchunk);
+    return hipGetLastError();
+}
+
+template hipError_t run_rebuild_h<float>(size_t, const void *, const void *, void *, hipStream_t);
+template hipError_t run_rebuild_h<bf16_t>(size_t, const void *, const void *, void *, hipStream_t);
 template hipError_t run_fwd<float>(const Dims &, const FwdBufs &, hipStream_t, const Trace *);
 template hipError_t run_fwd<bf16_t>(const Dims &, const FwdBufs &, hipStream_t, const Trace *);
 template hipError_t run_bwd<float>(const Dims &, const BwdBufs &, hipStream_t, const Trace *);

@@ -7,7 +7,8 @@
 //
 // Host code only: it orders moe_route / moe_fwd / moe_bwd on the compute
 // stream and the copies on the copy stream with the caller's four events.
-// Buffer of layer i: saved[i % 2].
+// A copy moves `saved` without H, which the reload rebuilds from G and U on
+// the copy stream. Buffer of layer i: saved[i % 2].
 //  forward,  layer i: wait until the offload of layer i - 2 has finished
 //            reading saved[i % 2]; route; forward into saved[i % 2]; then
 //            (layers 0 .. n-3 only) the copy stream copies it to host i.
@@ -28,15 +29,14 @@ bool a16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 moe_status_t hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
 
-// checks shared by both directions; *bytes = one layer's saved bytes
+// checks shared by both directions
 moe_status_t check_stack(const moe_problem_t *pb, int n, const moe_stack_layer_t *layers, int keep,
-                         const moe_offload_t *off, size_t ws_bytes, void *stream, bool bwd, size_t *bytes) {
+                         const moe_offload_t *off, size_t ws_bytes, void *stream, bool bwd) {
     const moe_status_t pst = moe::api::problem_status(pb);
     if (pst != MOE_OK) return pst;
     const size_t ws_need = moe_stack_workspace(pb, keep);
     if (n < 1 || !layers || !off) return MOE_E_ARG;
     if (ws_bytes < ws_need) return MOE_E_WORKSPACE;
-    *bytes = moe_saved_bytes(pb, keep);
     if (!a16(off->saved[0]) || (n > 1 && !a16(off->saved[1]))) return MOE_E_ARG;
     if (n > 1 && off->saved[0] == off->saved[1]) return MOE_E_ARG;
     if (n >= 3) {
@@ -71,8 +71,7 @@ size_t moe_stack_workspace(const moe_problem_t *pb, int keep_expert_out) {
 
 moe_status_t moe_stack_fwd(const moe_problem_t *pb, int n, const moe_stack_layer_t *layers, int keep_expert_out,
                            const moe_offload_t *off, void *ws, size_t ws_bytes, void *stream) {
-    size_t bytes = 0;
-    moe_status_t st = check_stack(pb, n, layers, keep_expert_out, off, ws_bytes, stream, false, &bytes);
+    moe_status_t st = check_stack(pb, n, layers, keep_expert_out, off, ws_bytes, stream, false);
     if (st != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(off->copy_stream);
     hipEvent_t fwd_done[2] = {static_cast<hipEvent_t>(off->events[0]), static_cast<hipEvent_t>(off->events[1])};
@@ -88,8 +87,7 @@ moe_status_t moe_stack_fwd(const moe_problem_t *pb, int n, const moe_stack_layer
         if (i <= n - 3) {  // layers n-2 and n-1 stay on the device for the backward
             if ((st = hip_ok(hipEventRecord(fwd_done[i % 2], s))) != MOE_OK) return st;
             if ((st = hip_ok(hipStreamWaitEvent(cs, fwd_done[i % 2], 0))) != MOE_OK) return st;
-            if ((st = hip_ok(hipMemcpyAsync(L.host_saved, buf, bytes, hipMemcpyDeviceToHost, cs))) != MOE_OK)
-                return st;
+            if ((st = moe::api::saved_offload(pb, keep_expert_out, buf, L.host_saved, cs)) != MOE_OK) return st;
             if ((st = hip_ok(hipEventRecord(copy_done[i % 2], cs))) != MOE_OK) return st;
         }
     }
@@ -98,8 +96,7 @@ moe_status_t moe_stack_fwd(const moe_problem_t *pb, int n, const moe_stack_layer
 
 moe_status_t moe_stack_bwd(const moe_problem_t *pb, int n, const moe_stack_layer_t *layers, int keep_expert_out,
                            const moe_offload_t *off, void *ws, size_t ws_bytes, void *stream) {
-    size_t bytes = 0;
-    moe_status_t st = check_stack(pb, n, layers, keep_expert_out, off, ws_bytes, stream, true, &bytes);
+    moe_status_t st = check_stack(pb, n, layers, keep_expert_out, off, ws_bytes, stream, true);
     if (st != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(off->copy_stream);
     hipEvent_t bwd_done[2] = {static_cast<hipEvent_t>(off->events[0]), static_cast<hipEvent_t>(off->events[1])};
@@ -115,8 +112,7 @@ moe_status_t moe_stack_bwd(const moe_problem_t *pb, int n, const moe_stack_layer
         if (i - 2 >= 0) {  // the buffer is free: bring layer i - 2 back into it under layer i - 1's backward
             if ((st = hip_ok(hipEventRecord(bwd_done[i % 2], s))) != MOE_OK) return st;
             if ((st = hip_ok(hipStreamWaitEvent(cs, bwd_done[i % 2], 0))) != MOE_OK) return st;
-            if ((st = hip_ok(hipMemcpyAsync(buf, layers[i - 2].host_saved, bytes, hipMemcpyHostToDevice, cs))) !=
-                MOE_OK)
+            if ((st = moe::api::saved_reload(pb, keep_expert_out, buf, layers[i - 2].host_saved, cs)) != MOE_OK)
                 return st;
             if ((st = hip_ok(hipEventRecord(copy_done[i % 2], cs))) != MOE_OK) return st;
         }

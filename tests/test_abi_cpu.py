@@ -65,6 +65,10 @@ def test_saved_and_workspace_sizes():
             + al(2 * p.r * ldT * 2) + al(p.r * ldT * 2))  # bf16: transposed copies for the LoRA gradients
     assert moe.saved_bytes(p, False) == want
     assert moe.saved_bytes(p, True) == want + al(S * p.d * es)
+    # an offload moves everything but H, which is last
+    assert moe.saved_host_bytes(p, False) == want - al(S * p.F * es)
+    assert moe.saved_host_bytes(p, True) == want + al(S * p.d * es) - al(S * p.F * es)
+    assert moe.saved_host_bytes(pb(k=0), True) == 0
     tiles = al((1 + (S + 255) // 256 + p.E) * 16)  # bf16: row-tile table of the grouped GEMMs
     assert moe.fwd_workspace(p, True, True) == tiles
     assert moe.fwd_workspace(p, True, False) == al(S * p.d * es) + tiles
@@ -74,6 +78,7 @@ def test_saved_and_workspace_sizes():
     p32 = pb(dtype=moe.MOE_F32)
     assert moe.fwd_workspace(p32, True, True) == 0
     assert moe.saved_bytes(p32, False) == 3 * al(S * p.F * 4) + al(S * 2 * p.r * 4) + al(S * p.r * 4)
+    assert moe.saved_host_bytes(p32, False) == 2 * al(S * p.F * 4) + al(S * 2 * p.r * 4) + al(S * p.r * 4)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -218,10 +223,19 @@ def test_binding_checks_host_buffers():
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_route(p, 1 << 20, rt, host_counts=bad, stream=0)
         assert ei.value.status == moe.MOE_E_ARG
-    short = np.zeros(moe.saved_bytes(p, False) - 1, np.uint8)
+    short = np.zeros(moe.saved_host_bytes(p, False) - 1, np.uint8)
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_saved_copy(p, False, False, 1 << 20, short, copy_stream=0)
     assert ei.value.status == moe.MOE_E_ARG
+    # the stack calls' host_saved buffers likewise
+    A = 1 << 20
+    rt = {n: A for n in ("topk_idx", "topk_w", "counts", "offsets", "sorted_slot", "slot_row")}
+    w = {n: A for n in ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")}
+    layer = {"logits": A, "rt": rt, "w": w, "x": A, "out": A}
+    layers = [dict(layer, host_saved=short), dict(layer), dict(layer)]
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_stack_fwd(p, layers, False, [A, 2 * A], 3 * A, [4 * A] * 4, A, stream=0)
+    assert ei.value.status == moe.MOE_E_ARG and "host_saved of layer 0" in str(ei.value)
 
 
 def test_stack_argument_errors_before_launch():

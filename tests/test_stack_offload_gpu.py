@@ -76,9 +76,9 @@ def _run_per_layer(cfg, pb, layers, keep, dev):
 
 
 def _run_stack(cfg, pb, layers, keep, dev):
-    nbytes = moe.saved_bytes(pb, keep)
+    nbytes, nhost = moe.saved_bytes(pb, keep), moe.saved_host_bytes(pb, keep)
     for i, L in enumerate(layers):
-        L["host_saved"] = (torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        L["host_saved"] = (torch.empty(nhost, dtype=torch.uint8, pin_memory=True)
                            if i <= len(layers) - 3 else None)
     dsaved = [moe.alloc_bytes(nbytes, dev) for _ in range(2)]
     # stale bytes in the buffers: whatever the forward does not write must not matter
