@@ -496,7 +496,8 @@ moe_status_t moe_router_fwd(const moe_problem_t *pb, const void *x, const void *
     if (pb->E % 8) return MOE_E_UNSUPPORTED;
     if (!buf_ok(w_router)) return MOE_E_ARG;
     if (pb->T > 0 && (!buf_ok(x) || !buf_ok(logits))) return MOE_E_ARG;
-    if ((long long)pb->T * pb->d >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+    if ((long long)pb->T * pb->d >= (1LL << 31) || (long long)pb->E * pb->d * esize(pb->dtype) > (1LL << 31))
+        return MOE_E_UNSUPPORTED;
     const moe::Trace tr = to_trace(trace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Dims D = dims_of(pb);
@@ -513,7 +514,8 @@ moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *
     if (st != MOE_OK) return st;
     if (pb->E % 8) return MOE_E_UNSUPPORTED;
     if (!buf_ok(w_router)) return MOE_E_ARG;
-    if ((long long)pb->T * pb->d >= (1LL << 31) || (long long)pb->E * ((pb->T + 7) & ~7) >= (1LL << 31))
+    if ((long long)pb->T * pb->d >= (1LL << 31) || (long long)pb->E * ((pb->T + 7) & ~7) >= (1LL << 31) ||
+        (long long)pb->E * pb->d * esize(pb->dtype) > (1LL << 31))
         return MOE_E_UNSUPPORTED;
     if (pb->T > 0 && (dx || dw_router) && (!buf_ok(x) || !buf_ok(d_logits))) return MOE_E_ARG;
     if (dx && pb->T > 0 && (!buf_ok(dx) || !buf_ok(dx_in))) return MOE_E_ARG;

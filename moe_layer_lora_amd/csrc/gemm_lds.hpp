@@ -909,4 +909,10 @@ __device__ __forceinline__ void epilogue_rows(const f32x16_t (&acc)[C::TM][C::TN
 }
 
 }  // namespace lds
+
+// K-contiguous tile row that load j (of instr per wave) of this lane covers
+template <class C> __device__ __forceinline__ int lds_row(int wave, int lane, int j, int instr) {
+    return (wave * instr + j) * C::RPI + lane / C::CPR;
+}
+
 }  // namespace moe

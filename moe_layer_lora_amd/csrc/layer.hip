@@ -371,10 +371,6 @@ template <class C> union LdsSmem {  // the tile scheduler's table is dead once t
     int start[kMaxE + 1];
 };
 
-// K-contiguous tile row that load j (of instr per wave) of this lane covers
-template <class C> __device__ __forceinline__ int lds_row(int wave, int lane, int j, int instr) {
-    return (wave * instr + j) * C::RPI + lane / C::CPR;
-}
 
 // NF4 frozen weights (4-bit NormalFloat codes and per-64 fp32 scales) for the
 // four grouped GEMMs: the B operand is dequantised while it is staged to LDS

@@ -5,9 +5,10 @@
 // Unsloth 2026 wiki chapter, "Optimisation 3: grouped_mm and Split-LoRA in
 // MoE training", opening paragraph); this is the plain linear gate.
 //
-// All three products run on the register-staged MFMA tile engine
-// (gemm.hpp), tiles of 4 waves (64 x 64 for the logits, else 128 x 128),
-// fp32 accumulation:
+// bf16 logits run on the direct-load ring (gemm_lds.hpp); the other products
+// and every fp32 product on the register-staged MFMA tile engine (gemm.hpp),
+// tiles of 4 waves (64 x 64 for the logits, else 128 x 128), fp32
+// accumulation:
 //   logits [T,E]   = x [T,d] . W_r[E,d]^T          (both K-contiguous)
 //   dx     [T,d]   = dx_in + d_logits [T,E] . W_r  (d_logits fp32, rounded
 //                    to the storage type as it is staged; W_r N-contiguous)
@@ -16,6 +17,7 @@
 //                    split into chunks whose fp32 partial products are summed
 //                    in chunk order, so the result is deterministic)
 #include "gemm.hpp"
+#include "gemm_lds.hpp"
 #include "kernels.hpp"
 #include "moe.h"
 
@@ -72,6 +74,60 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_router_logits(RouterP p) {
     for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
         if (m0 + m < p.T && n0 + n < p.E) p.logits[(size_t)(m0 + m) * p.E + n0 + n] = v;
     });
+}
+
+// bf16 logits on the direct-load ring: 64 x 64 tiles (x rows by experts),
+// 32-deep steps through an 8-stage ring, so seven steps of loads (56 KB per
+// block) are in flight while one is multiplied. The product is a stream over
+// x (W_r stays in L2), and the register-staged engine, which waits on each
+// step's loads, reaches a fraction of the HBM rate on it.
+using LogitsLds = lds::Cfg<64, 64, 8, false>;
+
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS) void k_router_logits_lds(RouterP p) {
+    __shared__ __align__(16) char ring[C::SMEM_BYTES];
+    // the hardware deals blocks to the 8 XCDs round-robin: each XCD takes a
+    // contiguous range of tiles, so the column tiles of one row tile (same x
+    // rows) share that XCD's L2; the grid is 8 * per
+    const int ntn = cdiv(p.E, C::BN), ntiles = cdiv(p.T, C::BM) * ntn, per = cdiv(ntiles, 8);
+    const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (tile >= ntiles) return;
+    const int m0 = (tile / ntn) * C::BM, n0 = (tile % ntn) * C::BN;
+    const int lane = (int)threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    lds::Operands<C> op;
+    uint32_t aro[C::A_INSTR], bro[C::B_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::A_INSTR; ++j) {
+        const int m = m0 + lds_row<C>(wave, lane, j, C::A_INSTR);
+        aro[j] = m < p.T ? (uint32_t)m * (uint32_t)p.d * 2u : kInvalid;
+    }
+#pragma unroll
+    for (int j = 0; j < C::B_INSTR; ++j) {
+        const int n = n0 + lds_row<C>(wave, lane, j, C::B_INSTR);
+        bro[j] = n < p.E ? (uint32_t)n * (uint32_t)p.d * 2u : kInvalid;
+    }
+    op.a.init_rows(wave, lane, aro);
+    op.bk.init_rows(wave, lane, bro);
+    op.ra[0] = op.ra[1] = make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.d * 2u);
+    op.rb[0][0] = op.rb[0][1] = op.rb[1][0] = op.rb[1][1] = make_rsrc(p.wr, (uint32_t)p.E * (uint32_t)p.d * 2u);
+    op.K[0] = op.K[1] = p.d;
+    op.nt0 = op.nt = cdiv(p.d, C::BK);
+    f32x16_t acc[C::TM][C::TN];
+    lds::NoLora nolora;
+    lds::run<C>(op, 0, nolora, ring, acc);
+    // lane: column acc_col of rows acc_row(i) of each 32 x 32 piece, so each
+    // store instruction writes 128-byte runs of two rows
+    const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + wm * C::WTM + mi * 32 + acc_row(i, lane);
+                const int n = n0 + wn * C::WTN + ni * 32 + acc_col(lane);
+                if (m < p.T && n < p.E) p.logits[(size_t)m * p.E + n] = acc[mi][ni][i];
+            }
 }
 
 // dx = dx_in + d_logits W_r: tile (m0, n0) of [T, d], K = E
@@ -233,7 +289,12 @@ hipError_t run_router_fwd(const Dims &D, const void *x, const void *wr, float *l
     RouterP p{};
     p.x = x; p.wr = wr; p.logits = logits; p.T = D.T; p.d = D.d; p.E = D.E;
     Scope sc(tr, MOE_K_ROUTER_LOGITS, st);
-    MOE_RLAUNCH(k_router_logits<Cfg>, dim3(cdiv(D.T, Cfg::BM) * cdiv(D.E, Cfg::BN)), Cfg::NTHREADS, p);
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        using C = LogitsLds;
+        MOE_RLAUNCH(k_router_logits_lds<C>, dim3(8 * cdiv(cdiv(D.T, C::BM) * cdiv(D.E, C::BN), 8)), C::NTHREADS, p);
+    } else {
+        MOE_RLAUNCH(k_router_logits<Cfg>, dim3(cdiv(D.T, Cfg::BM) * cdiv(D.E, Cfg::BN)), Cfg::NTHREADS, p);
+    }
     return hipSuccess;
 }
 
