@@ -514,7 +514,8 @@ moe_status_t moe_router_bwd(const moe_problem_t *pb, const void *x, const void *
     if (st != MOE_OK) return st;
     if (pb->E % 8) return MOE_E_UNSUPPORTED;
     if (!buf_ok(w_router)) return MOE_E_ARG;
-    if ((long long)pb->T * pb->d >= (1LL << 31) || (long long)pb->E * ((pb->T + 7) & ~7) >= (1LL << 31) ||
+    if ((long long)pb->T * pb->d >= (1LL << 31) ||
+        (long long)pb->E * ((pb->T + 7) & ~7) * esize(pb->dtype) > (1LL << 31) ||
         (long long)pb->E * pb->d * esize(pb->dtype) > (1LL << 31))
         return MOE_E_UNSUPPORTED;
     if (pb->T > 0 && (dx || dw_router) && (!buf_ok(x) || !buf_ok(d_logits))) return MOE_E_ARG;

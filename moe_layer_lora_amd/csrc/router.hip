@@ -36,7 +36,8 @@ template <class Cfg> struct RSmem {
 struct RouterP {
     const void *x, *wr;
     const float *dl;      // d_logits [T,E]
-    float *dlT;           // workspace [E,Tp]: d_logits transposed, zero for T <= t < Tp
+    void *dlT;            // workspace [E,Tp]: d_logits transposed (fp32 for fp32 layers, bf16 for
+                          // bf16 layers), zero for T <= t < Tp
     const void *dx_in;
     void *dx;
     float *logits, *dw, *partial;
@@ -189,9 +190,12 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_router_dx(RouterP p) {
     }
 }
 
-// dlT[e][t] = d_logits[t][e] for t < T, 0 for T <= t < Tp; 32 x 32 tiles
+// dlT[e][t] = d_logits[t][e] for t < T, 0 for T <= t < Tp; 32 x 32 tiles;
+// TO = bf16 rounds to nearest even, as the fp32 product's staging does
+template <typename TO>
 __global__ __launch_bounds__(256) void k_router_dlT(RouterP p) {
     __shared__ float tile[32][33];
+    TO *dlT = static_cast<TO *>(p.dlT);
     const int t0 = (int)blockIdx.x * 32, e0 = (int)blockIdx.y * 32;
     const int tx = (int)threadIdx.x & 31, ty = (int)threadIdx.x >> 5;
 #pragma unroll
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(256) void k_router_dlT(RouterP p) {
 #pragma unroll
     for (int i = ty; i < 32; i += 8) {
         const int e = e0 + i, t = t0 + tx;
-        if (e < p.E && t < p.Tp) p.dlT[(size_t)e * p.Tp + t] = tile[tx][i];
+        if (e < p.E && t < p.Tp) dlT[(size_t)e * p.Tp + t] = Elem<TO>::from_f32(tile[tx][i]);
     }
 }
 
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_router_dw(RouterP p) {
     KLoader<Cfg, Cfg::BM, true> la;
     la.K0 = 0; la.nk0 = 0; la.K1 = kc; la.scale1 = 1.0f;
     la.b0[0] = la.b0[1] = static_cast<const T *>(p.x);  // never read (no segment 0)
-    la.b1[0] = la.b1[1] = p.dlT + t0;
+    la.b1[0] = la.b1[1] = static_cast<const float *>(p.dlT) + t0;
 #pragma unroll
     for (int i = 0; i < la.PER; ++i) {
         const int m = la.row_of(i);
@@ -241,6 +245,58 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_router_dw(RouterP p) {
     for_each_acc<Cfg>(acc, [&](int m, int n, int, int, int, float v) {
         if (m0 + m < p.E && n0 + n < p.d) dst[(size_t)(m0 + m) * p.d + n0 + n] = v;
     });
+}
+
+// bf16 dW_r (one chunk of tokens) on the direct-load ring: tile of 128
+// experts x 128 model columns; A = the experts' rows of the bf16 transposed
+// d_logits over the chunk's tokens (K-contiguous), B = the chunk's x rows as
+// k-rows (N-contiguous, read with transposing LDS reads), so x streams
+// through once. A 16-byte A chunk may run past the chunk's last token into
+// the next chunk's; the B k-rows past the chunk read as zero, so those
+// products vanish. Written to dw directly when there is one chunk, else to
+// partial[c].
+using DwLds = lds::Cfg<128, 128, 5, true>;
+
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS) void k_router_dw_lds(RouterP p) {
+    __shared__ __align__(16) char ring[C::SMEM_BYTES];
+    const int ntn = cdiv(p.d, C::BN), ntm = cdiv(p.E, C::BM);
+    const int c = (int)blockIdx.x / (ntm * ntn), rem = (int)blockIdx.x % (ntm * ntn);
+    const int m0 = (rem / ntn) * C::BM, n0 = (rem % ntn) * C::BN;
+    const int t0 = c * p.chunk, kc = min(p.chunk, p.T - t0);
+    const int lane = (int)threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    lds::Operands<C> op;
+    uint32_t aro[C::A_INSTR];
+#pragma unroll
+    for (int j = 0; j < C::A_INSTR; ++j) {
+        const int e = m0 + lds_row<C>(wave, lane, j, C::A_INSTR);
+        aro[j] = e < p.E ? (uint32_t)e * (uint32_t)p.Tp * 2u : kInvalid;
+    }
+    op.a.init_rows(wave, lane, aro);
+    op.ra[0] = op.ra[1] = make_rsrc(p.dlT, (uint32_t)p.E * (uint32_t)p.Tp * 2u);
+    op.acol[0] = op.acol[1] = (uint32_t)t0 * 2u;
+    op.K[0] = op.K[1] = kc;
+    op.nt0 = op.nt = cdiv(kc, C::BK);
+    op.bn.init(wave, lane, min(C::BN, p.d - n0));
+    op.ldb[0] = op.ldb[1] = (uint32_t)p.d * 2u;
+    const bf16_t *xb = static_cast<const bf16_t *>(p.x) + (size_t)t0 * p.d + n0;
+    op.rb[0][0] = op.rb[0][1] = op.rb[1][0] = op.rb[1][1] =
+        make_rsrc(xb, (uint32_t)((size_t)(p.T - t0) * p.d - n0) * 2u);
+    f32x16_t acc[C::TM][C::TN];
+    lds::NoLora nolora;
+    lds::run<C>(op, 0, nolora, ring, acc);
+    float *dst = p.nch == 1 ? p.dw : p.partial + (size_t)c * p.E * p.d;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + wm * C::WTM + mi * 32 + acc_row(i, lane);
+                const int n = n0 + wn * C::WTN + ni * 32 + acc_col(lane);
+                if (m < p.E && n < p.d) dst[(size_t)m * p.d + n] = acc[mi][ni][i];
+            }
 }
 
 // dw = sum of the chunk partials in chunk order (zeros when there are no tokens)
@@ -273,7 +329,10 @@ struct Scope {  // event pair around one launch, if asked for
 RouterWs router_ws(const Dims &D) {
     RouterWs w{};
     w.Tp = (D.T + 7) & ~7;
-    const int nch0 = D.T > 0 ? min(32, max(1, (D.T + 255) / 256)) : 1;
+    // token chunks: enough for about 256 blocks of 128 x 128 dW_r tiles, at
+    // most 32, at least about 256 tokens each
+    const int tiles = cdiv(D.E, 128) * cdiv(D.d, 128);
+    const int nch0 = D.T > 0 ? min(min(32, cdiv(256, tiles)), max(1, cdiv(D.T, 256))) : 1;
     w.chunk = D.T > 0 ? ((D.T + nch0 - 1) / nch0 + 31) & ~31 : 32;
     w.nch = D.T > 0 ? (D.T + w.chunk - 1) / w.chunk : 1;
     w.dlT_bytes = (size_t)D.E * w.Tp * sizeof(float);
@@ -304,7 +363,7 @@ hipError_t run_router_bwd(const Dims &D, const void *x, const void *wr, const fl
     using Cfg = typename RouterCfg<T>::type;
     const RouterWs w = router_ws(D);
     RouterP p{};
-    p.x = x; p.wr = wr; p.dl = d_logits; p.dlT = static_cast<float *>(dlT); p.dx_in = dx_in; p.dx = dx;
+    p.x = x; p.wr = wr; p.dl = d_logits; p.dlT = dlT; p.dx_in = dx_in; p.dx = dx;
     p.dw = dw; p.partial = static_cast<float *>(partial);
     p.T = D.T; p.d = D.d; p.E = D.E; p.Tp = w.Tp; p.chunk = w.chunk; p.nch = w.nch;
     if (dx && D.T > 0) {
@@ -318,8 +377,13 @@ hipError_t run_router_bwd(const Dims &D, const void *x, const void *wr, const fl
             MOE_RLAUNCH(k_router_dw_sum, dim3(min(1024, cdiv(D.E * D.d, 256))), 256, p);
             return hipSuccess;
         }
-        MOE_RLAUNCH(k_router_dlT, dim3(cdiv(w.Tp, 32), cdiv(D.E, 32)), 256, p);
-        MOE_RLAUNCH(k_router_dw<Cfg>, dim3(w.nch * cdiv(D.E, Cfg::BM) * cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, p);
+        MOE_RLAUNCH(k_router_dlT<T>, dim3(cdiv(w.Tp, 32), cdiv(D.E, 32)), 256, p);
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            using C = DwLds;
+            MOE_RLAUNCH(k_router_dw_lds<C>, dim3(w.nch * cdiv(D.E, C::BM) * cdiv(D.d, C::BN)), C::NTHREADS, p);
+        } else {
+            MOE_RLAUNCH(k_router_dw<Cfg>, dim3(w.nch * cdiv(D.E, Cfg::BM) * cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, p);
+        }
         if (w.nch > 1) MOE_RLAUNCH(k_router_dw_sum, dim3(min(1024, cdiv(D.E * D.d, 256))), 256, p);
     }
     return hipSuccess;
