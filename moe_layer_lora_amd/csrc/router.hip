@@ -5,8 +5,8 @@
 // Unsloth 2026 wiki chapter, "Optimisation 3: grouped_mm and Split-LoRA in
 // MoE training", opening paragraph); this is the plain linear gate.
 //
-// bf16 logits run on the direct-load ring (gemm_lds.hpp); the other products
-// and every fp32 product on the register-staged MFMA tile engine (gemm.hpp),
+// bf16 logits and dW_r run on the direct-load ring (gemm_lds.hpp); dx and
+// every fp32 product on the register-staged MFMA tile engine (gemm.hpp),
 // tiles of 4 waves (64 x 64 for the logits, else 128 x 128), fp32
 // accumulation:
 //   logits [T,E]   = x [T,d] . W_r[E,d]^T          (both K-contiguous)
@@ -25,6 +25,8 @@ namespace moe {
 namespace {
 
 template <typename T> struct RouterCfg { using type = GemmCfg<T, 128, 128, 32, 2, 2>; };
+// dx has K = E only: 64-deep steps halve its chain of dependent steps
+template <typename T> struct DxCfg { using type = GemmCfg<T, 128, 128, 64, 2, 2>; };
 // the logits have only E columns: 64 x 64 tiles give 4x the blocks of 128 x 128
 template <typename T> struct LogitsCfg { using type = GemmCfg<T, 64, 64, 32, 2, 2>; };
 
@@ -368,7 +370,8 @@ hipError_t run_router_bwd(const Dims &D, const void *x, const void *wr, const fl
     p.T = D.T; p.d = D.d; p.E = D.E; p.Tp = w.Tp; p.chunk = w.chunk; p.nch = w.nch;
     if (dx && D.T > 0) {
         Scope sc(tr, MOE_K_ROUTER_DX, st);
-        MOE_RLAUNCH(k_router_dx<Cfg>, dim3(cdiv(D.T, Cfg::BM) * cdiv(D.d, Cfg::BN)), Cfg::NTHREADS, p);
+        using CfgX = typename DxCfg<T>::type;
+        MOE_RLAUNCH(k_router_dx<CfgX>, dim3(cdiv(D.T, CfgX::BM) * cdiv(D.d, CfgX::BN)), CfgX::NTHREADS, p);
     }
     if (dw) {
         Scope sc(tr, MOE_K_ROUTER_DW, st);
