@@ -165,7 +165,10 @@ def test_binding_raises_on_error():
 def test_router_workspace_and_argument_errors():
     p = pb()  # T=512, d=256, E=16
     Tp = (p.T + 7) // 8 * 8
-    nch0 = min(32, max(1, (p.T + 255) // 256))
+    # token chunks for dW_r: about 256 blocks of 128 x 128 tiles, at most 32,
+    # at least ~256 tokens each
+    tiles = -(-p.E // 128) * -(-p.d // 128)
+    nch0 = min(32, -(-256 // tiles), max(1, -(-p.T // 256)))
     chunk = ((p.T + nch0 - 1) // nch0 + 31) // 32 * 32
     nch = (p.T + chunk - 1) // chunk
     want = al(p.E * Tp * 4) + (al(nch * p.E * p.d * 4) if nch > 1 else 0)
@@ -183,6 +186,12 @@ def test_router_workspace_and_argument_errors():
                             None) == moe.MOE_E_ARG
     assert L.moe_router_bwd(ctypes.byref(p), A, A, A, None, None, A, A, want - 1, None,
                             None) == moe.MOE_E_WORKSPACE
+    # a router weight above 2 GiB (E d bf16 elements) is refused by both calls
+    big = pb(T=8, d=(1 << 20) + 8, E=1024, k=1, F=8)
+    assert moe.route_workspace(big) > 0  # the layer itself is accepted
+    assert L.moe_router_fwd(ctypes.byref(big), A, A, A, None, None) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_router_bwd(ctypes.byref(big), A, A, A, None, None, A, A, 1 << 40, None,
+                            None) == moe.MOE_E_UNSUPPORTED
 
 
 def test_saved_copy_argument_errors_before_any_call():
