@@ -30,6 +30,11 @@ SMALL = {
                                dtype="bf16", alpha=16.0),
     "one_token_bf16": LayerConfig("router_one_token_bf16", T=1, d=64, E=8, k=2, F=64, r=8,
                                   dtype="bf16", alpha=16.0),
+    # E = 200: a second 128-expert row tile of dW_r (72 experts) and a ragged
+    # fourth 64-expert tile of the logits; d = 392: a ragged last 128-column
+    # tile (8 columns); T = 777 in four token chunks, the last one ragged
+    "many_experts_bf16": LayerConfig("router_many_experts_bf16", T=777, d=392, E=200, k=4, F=64, r=8,
+                                     dtype="bf16", alpha=16.0),
 }
 
 
