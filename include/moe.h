@@ -298,14 +298,18 @@ moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to
  * n. Layer i uses buffer saved[i % 2].
  *   moe_stack_fwd: for i = 0 .. n-1 on `stream`: wait for the offload of
  *     layer i-2 (it reads saved[i % 2]); moe_route (logits -> rt); moe_fwd
- *     into saved[i % 2]; then, for i <= n-3, copy_stream copies saved[i % 2]
- *     (all but H, as moe_saved_copy) to host_saved after the forward. Layers
- *     n-2 and n-1 stay on the device.
+ *     into saved[i % 2]; for i <= n-3, copy_stream copies saved[i % 2] (all
+ *     but H, as moe_saved_copy) to host_saved: G and U once the gate/up GEMM
+ *     has run, the rest after the forward. Layers n-2 and n-1 stay on the
+ *     device.
  *   moe_stack_bwd (after moe_stack_fwd with the same arguments and nothing
  *     else written to the two buffers in between): for i = n-1 down to 0:
  *     layers i <= n-3 wait for their reload; moe_bwd from saved[i % 2]; then
- *     copy_stream reloads layer i-2 into saved[i % 2] and rebuilds its H,
- *     under the backward of layer i-1.
+ *     copy_stream reloads layer i-2 into saved[i % 2] (G and U as soon as
+ *     layer i's down-backward GEMM, their last reader, has run; the rest
+ *     after layer i's backward) and rebuilds its H, under the backward of
+ *     layer i-1. The mid-call points are taken with the caller's events in
+ *     the moe_trace_t hook, which the stack calls therefore do not offer.
  * Every layer has the problem pb. The caller wires the stack: layer i+1's x
  * is typically layer i's out, and layer i's dout layer i+1's dx. Results are
  * bit-identical to moe_route + moe_fwd + moe_bwd per layer with a saved

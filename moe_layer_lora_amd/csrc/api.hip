@@ -299,17 +299,21 @@ bool pinned_host(const void *p) {
     return pa.type == hipMemoryTypeHost;
 }
 
-// Offload: the part of `saved` before H (moe_saved_host_bytes) to host, on
-// stream s. Reload: that part back, then H rebuilt from G and U on s.
-moe_status_t saved_offload(const moe_problem_t *pb, int keep, const void *saved, void *host, hipStream_t s) {
+SavedParts saved_parts(const moe_problem_t *pb, int keep) {
     const SavedLayout l = saved_layout(pb, keep != 0);
-    if (l.H > 0 && hipMemcpyAsync(host, saved, l.H, hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_E_HIP;
-    return MOE_OK;
+    return SavedParts{l.Zgu, l.H};
 }
 
-moe_status_t saved_reload(const moe_problem_t *pb, int keep, void *saved, const void *host, hipStream_t s) {
+// bytes [lo, hi) of `saved` to or from the same offsets of `host`, on s
+moe_status_t saved_copy_range(void *saved, void *host, bool to_device, size_t lo, size_t hi, hipStream_t s) {
+    if (hi <= lo) return MOE_OK;
+    const hipError_t e = to_device ? hipMemcpyAsync(at(saved, lo), at(host, lo), hi - lo, hipMemcpyHostToDevice, s)
+                                   : hipMemcpyAsync(at(host, lo), at(saved, lo), hi - lo, hipMemcpyDeviceToHost, s);
+    return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+moe_status_t saved_rebuild_h(const moe_problem_t *pb, int keep, void *saved, hipStream_t s) {
     const SavedLayout l = saved_layout(pb, keep != 0);
-    if (l.H > 0 && hipMemcpyAsync(saved, host, l.H, hipMemcpyHostToDevice, s) != hipSuccess) return MOE_E_HIP;
     const size_t n = (size_t)pb->T * pb->k * pb->F;
     const hipError_t e =
         pb->dtype == MOE_BF16
@@ -555,8 +559,9 @@ moe_status_t moe_saved_copy(const moe_problem_t *pb, int keep_expert_out, int to
     hipStream_t cs = static_cast<hipStream_t>(copy_stream);
     if (wait_event && hipStreamWaitEvent(cs, static_cast<hipEvent_t>(wait_event), 0) != hipSuccess)
         return MOE_E_HIP;
-    st = to_device ? moe::api::saved_reload(pb, keep_expert_out, saved, host, cs)
-                   : moe::api::saved_offload(pb, keep_expert_out, saved, host, cs);
+    const moe::api::SavedParts parts = moe::api::saved_parts(pb, keep_expert_out);
+    st = moe::api::saved_copy_range(saved, host, to_device != 0, 0, parts.host_end, cs);
+    if (st == MOE_OK && to_device) st = moe::api::saved_rebuild_h(pb, keep_expert_out, saved, cs);
     if (st != MOE_OK) return st;
     if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), cs) != hipSuccess) return MOE_E_HIP;
     return MOE_OK;

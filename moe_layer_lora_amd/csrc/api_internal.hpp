@@ -28,11 +28,17 @@ moe_status_t route_impl(const moe_problem_t *pb, const float *logits, const moe_
 // leaves no HIP error behind
 bool pinned_host(const void *p);
 
-// Offload of a `saved` buffer of a checked problem to pinned host memory (the
-// moe_saved_host_bytes bytes before H), and its reload: those bytes back,
-// then H rebuilt from G and U; both enqueued on `stream`.
-moe_status_t saved_offload(const moe_problem_t *pb, int keep, const void *saved, void *host, hipStream_t stream);
-moe_status_t saved_reload(const moe_problem_t *pb, int keep, void *saved, const void *host, hipStream_t stream);
+// What an offload of a `saved` buffer (checked problem) moves to pinned host
+// memory, as byte ranges at the same offsets on both sides: [0, gu_end) is
+// G and U (final once the gate/up GEMM has run, last read by the
+// down-backward GEMM), [gu_end, host_end) the rest before H (H is rebuilt
+// from G and U after a reload).
+struct SavedParts { size_t gu_end, host_end; };
+SavedParts saved_parts(const moe_problem_t *pb, int keep);
+// bytes [lo, hi) of `saved` to (to_device) or from `host`, enqueued on stream
+moe_status_t saved_copy_range(void *saved, void *host, bool to_device, size_t lo, size_t hi, hipStream_t stream);
+// H = silu(G) U from G and U as stored, enqueued on stream
+moe_status_t saved_rebuild_h(const moe_problem_t *pb, int keep, void *saved, hipStream_t stream);
 
 }  // namespace api
 }  // namespace moe

@@ -8,14 +8,22 @@
 // Host code only: it orders moe_route / moe_fwd / moe_bwd on the compute
 // stream and the copies on the copy stream with the caller's four events.
 // A copy moves `saved` without H, which the reload rebuilds from G and U on
-// the copy stream. Buffer of layer i: saved[i % 2].
+// the copy stream. G and U (95% of the bytes at typical shapes) have their
+// own timing: they are final as soon as the gate/up GEMM has run, and the
+// down-backward GEMM is their last reader, so their copies start at those
+// points instead of at the end of the call. Buffer of layer i: saved[i % 2].
 //  forward,  layer i: wait until the offload of layer i - 2 has finished
-//            reading saved[i % 2]; route; forward into saved[i % 2]; then
-//            (layers 0 .. n-3 only) the copy stream copies it to host i.
+//            reading saved[i % 2]; route; forward into saved[i % 2]; for
+//            layers 0 .. n-3 the copy stream copies G, U to host i after
+//            the gate/up GEMM and the rest after the forward.
 //  backward, layer i (n-1 down to 0): layers n-1 and n-2 are still on the
-//            device; a lower layer waits for its reload. After the backward
-//            of layer i, saved[i % 2] is free and the copy stream reloads
-//            layer i - 2 into it, under the backward of layer i - 1.
+//            device; a lower layer waits for its reload. The copy stream
+//            reloads G, U of layer i - 2 into saved[i % 2] once layer i's
+//            down-backward GEMM has run, and the rest (then rebuilds H) once
+//            its whole backward has, under the backward of layer i - 1.
+// The mid-call points come from the library's per-kernel event hook
+// (moe_trace_t): one of the caller's events in both the start and the stop
+// slot of a kernel ends up recorded right after that kernel.
 #include <hip/hip_runtime.h>
 
 #include "moe.h"
@@ -76,18 +84,27 @@ moe_status_t moe_stack_fwd(const moe_problem_t *pb, int n, const moe_stack_layer
     hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(off->copy_stream);
     hipEvent_t fwd_done[2] = {static_cast<hipEvent_t>(off->events[0]), static_cast<hipEvent_t>(off->events[1])};
     hipEvent_t copy_done[2] = {static_cast<hipEvent_t>(off->events[2]), static_cast<hipEvent_t>(off->events[3])};
+    const moe::api::SavedParts parts = moe::api::saved_parts(pb, keep_expert_out);
     for (int i = 0; i < n; ++i) {
         const moe_stack_layer_t &L = layers[i];
         void *buf = off->saved[i % 2];
+        const bool offload = i <= n - 3;  // layers n-2 and n-1 stay on the device for the backward
         // the offload of layer i - 2 reads this buffer: it must finish first
         if (i >= 2 && (st = hip_ok(hipStreamWaitEvent(s, copy_done[i % 2], 0))) != MOE_OK) return st;
         if ((st = moe_route(pb, L.logits, L.rt, nullptr, ws, ws_bytes, stream, nullptr)) != MOE_OK) return st;
-        if ((st = moe_fwd(pb, L.x, L.rt, L.w, L.out, buf, keep_expert_out, ws, ws_bytes, stream, nullptr)) != MOE_OK)
+        moe_trace_t gu_done{};  // fwd_done[i % 2] recorded right after the gate/up GEMM
+        gu_done.start[MOE_K_GATEUP] = gu_done.stop[MOE_K_GATEUP] = fwd_done[i % 2];
+        if ((st = moe_fwd(pb, L.x, L.rt, L.w, L.out, buf, keep_expert_out, ws, ws_bytes, stream,
+                          offload ? &gu_done : nullptr)) != MOE_OK)
             return st;
-        if (i <= n - 3) {  // layers n-2 and n-1 stay on the device for the backward
-            if ((st = hip_ok(hipEventRecord(fwd_done[i % 2], s))) != MOE_OK) return st;
+        if (offload) {
             if ((st = hip_ok(hipStreamWaitEvent(cs, fwd_done[i % 2], 0))) != MOE_OK) return st;
-            if ((st = moe::api::saved_offload(pb, keep_expert_out, buf, L.host_saved, cs)) != MOE_OK) return st;
+            if ((st = moe::api::saved_copy_range(buf, L.host_saved, false, 0, parts.gu_end, cs)) != MOE_OK) return st;
+            if ((st = hip_ok(hipEventRecord(fwd_done[i % 2], s))) != MOE_OK) return st;  // the whole forward
+            if ((st = hip_ok(hipStreamWaitEvent(cs, fwd_done[i % 2], 0))) != MOE_OK) return st;
+            if ((st = moe::api::saved_copy_range(buf, L.host_saved, false, parts.gu_end, parts.host_end, cs)) !=
+                MOE_OK)
+                return st;
             if ((st = hip_ok(hipEventRecord(copy_done[i % 2], cs))) != MOE_OK) return st;
         }
     }
@@ -101,19 +118,27 @@ moe_status_t moe_stack_bwd(const moe_problem_t *pb, int n, const moe_stack_layer
     hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(off->copy_stream);
     hipEvent_t bwd_done[2] = {static_cast<hipEvent_t>(off->events[0]), static_cast<hipEvent_t>(off->events[1])};
     hipEvent_t copy_done[2] = {static_cast<hipEvent_t>(off->events[2]), static_cast<hipEvent_t>(off->events[3])};
+    const moe::api::SavedParts parts = moe::api::saved_parts(pb, keep_expert_out);
     for (int i = n - 1; i >= 0; --i) {
         const moe_stack_layer_t &L = layers[i];
         void *buf = off->saved[i % 2];
+        const bool reload = i - 2 >= 0;  // layer i - 2 comes back into this buffer
         // layers below n-2 were reloaded into their buffer: wait for the copy
         if (i <= n - 3 && (st = hip_ok(hipStreamWaitEvent(s, copy_done[i % 2], 0))) != MOE_OK) return st;
+        moe_trace_t gu_free{};  // bwd_done[i % 2] recorded right after the down-backward GEMM
+        gu_free.start[MOE_K_DOWN_BWD] = gu_free.stop[MOE_K_DOWN_BWD] = bwd_done[i % 2];
         if ((st = moe_bwd(pb, L.x, L.dout, L.rt, L.w, buf, keep_expert_out, L.dx, L.grads, L.d_topk_w, L.d_logits,
-                          ws, ws_bytes, stream, nullptr)) != MOE_OK)
+                          ws, ws_bytes, stream, reload ? &gu_free : nullptr)) != MOE_OK)
             return st;
-        if (i - 2 >= 0) {  // the buffer is free: bring layer i - 2 back into it under layer i - 1's backward
-            if ((st = hip_ok(hipEventRecord(bwd_done[i % 2], s))) != MOE_OK) return st;
+        if (reload) {  // under the rest of layer i's backward and under layer i - 1's
+            void *host = layers[i - 2].host_saved;
             if ((st = hip_ok(hipStreamWaitEvent(cs, bwd_done[i % 2], 0))) != MOE_OK) return st;
-            if ((st = moe::api::saved_reload(pb, keep_expert_out, buf, layers[i - 2].host_saved, cs)) != MOE_OK)
+            if ((st = moe::api::saved_copy_range(buf, host, true, 0, parts.gu_end, cs)) != MOE_OK) return st;
+            if ((st = hip_ok(hipEventRecord(bwd_done[i % 2], s))) != MOE_OK) return st;  // the whole backward
+            if ((st = hip_ok(hipStreamWaitEvent(cs, bwd_done[i % 2], 0))) != MOE_OK) return st;
+            if ((st = moe::api::saved_copy_range(buf, host, true, parts.gu_end, parts.host_end, cs)) != MOE_OK)
                 return st;
+            if ((st = moe::api::saved_rebuild_h(pb, keep_expert_out, buf, cs)) != MOE_OK) return st;
             if ((st = hip_ok(hipEventRecord(copy_done[i % 2], cs))) != MOE_OK) return st;
         }
     }
