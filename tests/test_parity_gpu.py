@@ -295,6 +295,28 @@ def test_graph_capture_has_no_hidden_sync():
 
 # ------------------------------------------------------------------ full-size workloads
 
+@pytest.mark.slow
+def test_full_size_step_is_bitwise_deterministic():
+    """The Qwen3-30B-A3B-shaped step (65536 routed rows, 2560 tiles per
+    grouped GEMM spread over all CUs and XCDs) run twice: every output,
+    gradient and stored intermediate bit-identical (no float atomics; every
+    cross-block sum has a fixed order)."""
+    lr = _runner()
+    cfg = synth.get_config("qwen3_30b_a3b")
+    print("[determinism] qwen3_30b_a3b", flush=True)
+    inputs = synth.make_inputs(cfg, seed=7)
+    L = lr.Layer(cfg, inputs, keep_expert_out=True)
+    L.step(backward=True, router_grad=True)
+    first = L.results(backward=True, router_grad=True, intermediates=True)
+    for t in [L.out, L.dx, L.d_topk_w, L.d_logits, *L.grads.values()]:
+        t.fill_(7.0)
+    L.step(backward=True, router_grad=True)
+    second = L.results(backward=True, router_grad=True, intermediates=True)
+    assert set(first) == set(second)
+    for n in first:
+        assert np.array_equal(first[n], second[n]), f"{n} differs between two runs"
+
+
 FULL = ["gptoss20b", "qwen3_30b_a3b", "qwen3_30b_a3b_skewed", "gptoss120b"]
 
 
