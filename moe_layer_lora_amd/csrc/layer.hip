@@ -1721,7 +1721,10 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
         sm.rowoff[i] = o;
     }
     __syncthreads();
-    const rsrc_t rs = make_rsrc(p.big, 0x7fffffff);  // rows are range-checked through rowoff
+    // rows are range-checked through rowoff; the range is the 2 GiB every
+    // tensor fits, so the last 16-byte chunk of a tensor of exactly 2^31
+    // bytes is in range and the kInvalid offset (2^31) is not
+    const rsrc_t rs = make_rsrc(p.big, 0x80000000u);
     const rsrc_t rsm = make_rsrc(p.smallT, (uint32_t)p.nr * (uint32_t)p.ldT * 2u);
     const int nsteps = cdiv(lead + tl.rows, 32), total = ntiles * nsteps;
     auto stage = [&](int t) { return sm.ring + (t % R::NSTAGE) * R::STAGE; };

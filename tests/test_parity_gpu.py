@@ -293,6 +293,59 @@ def test_graph_capture_has_no_hidden_sync():
             assert np.array_equal(got[n], ref[n]), f"replay {it}: {n} differs from eager"
 
 
+# ------------------------------------------------------------------ largest accepted batches
+
+MAX_SIZE = {
+    # the largest GPT-OSS-120B-shaped batch the byte bound admits: dG|dU
+    # [S, 2F] bf16 is 2,147,466,240 bytes, 17 KB under 2 GiB
+    "gptoss120b_max": synth.get_config("gptoss120b").with_(T=46603),
+    # dG|dU exactly 2^31 bytes (S = 262144 rows of 2F = 4096)
+    "exact_2gib": LayerConfig("exact_2gib", T=65536, d=1024, E=128, k=4, F=2048, r=16, dtype="bf16",
+                              alpha=32.0, router_grad=True),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", list(MAX_SIZE))
+def test_largest_accepted_batch(name):
+    """The largest batches the library accepts (every tensor at most 2 GiB,
+    addressed through 32-bit byte offsets): routing bit-exact over the whole
+    batch; out, dx, d_topk_w and d_logits of the tokens whose rows come last
+    in the expert order (the largest offsets) and of tokens spread over the
+    batch, and the six LoRA gradients of the expert owning the last rows,
+    against the oracle's per-token and per-expert entry points."""
+    import moe_layer_lora_amd as moe
+    lr = _runner()
+    cfg = MAX_SIZE[name]
+    assert moe.route_workspace(moe.Problem.from_config(cfg)) > 0  # accepted
+    print(f"[max] {name}: generating inputs", flush=True)
+    inputs = synth.make_inputs(cfg, seed=0)
+    L = lr.Layer(cfg, inputs, keep_expert_out=True)
+    print(f"[max] {name}: GPU step", flush=True)
+    L.step(backward=True, router_grad=True)
+    r = L.results(backward=True, router_grad=True)
+    del L
+    torch.cuda.empty_cache()
+    rt = oracle.route(inputs["logits"], cfg.k)
+    check_routing(r, rt, name)
+    last = rt["sorted_slot"][cfg.S - 16:] // cfg.k
+    toks = np.unique(np.concatenate([last, np.linspace(0, cfg.T - 1, 16).astype(np.int64)])).astype(np.int32)
+    print(f"[max] {name}: oracle, {len(toks)} tokens", flush=True)
+    OL = oracle.Layer.from_config(cfg, inputs)
+    f = oracle.fwd_tokens(OL, rt, toks)
+    b = oracle.bwd_tokens(OL, rt, inputs["dout"], toks)
+    tol = TOL[cfg.dtype]
+    check("out", r["out"][toks], f["out"], tol, name)
+    check("dx", r["dx"][toks], b["dx"], tol, name)
+    check("d_topk_w", r["d_topk_w"][toks], b["d_topk_w"], tol, name)
+    check("d_logits", r["d_logits"][toks], b["d_logits"], tol, name)
+    e_last = int(np.searchsorted(rt["offsets"], cfg.S - 1, side="right") - 1)
+    print(f"[max] {name}: oracle LoRA gradients of expert {e_last}", flush=True)
+    g = oracle.lora_grads(OL, rt, inputs["dout"], [e_last])
+    for n in GRADS:
+        check(f"{n}[{e_last}]", r[n][e_last], g[n][0], tol, name)
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.mark.slow
