@@ -149,6 +149,26 @@ struct Tile {
     int gmt;    // row tile index over all experts (expert-major)
 };
 
+// Inclusive scan of s[1..E] in place (__shared__, E <= 1024) by one wave,
+// lane l taking the l-th sequential segment of up to 16 entries.
+__device__ __forceinline__ void wave_scan_shared(int *s, int E, int lane) {
+    const int per = (E + kWave - 1) / kWave;
+    const int lo = 1 + lane * per, hi = min(E + 1, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += s[i];
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += v;
+    }
+    int run = incl - sum;
+    for (int i = lo; i < hi; ++i) {
+        run += s[i];
+        s[i] = run;
+    }
+}
+
 // Per-expert row-tile counts ceil(n_e / BM) and their inclusive scan into
 // s_start[0..E] (__shared__ int[E+1], E <= 1024); ends with a barrier.
 template <int BM, int NTHREADS>
@@ -160,24 +180,7 @@ __device__ void scan_row_tiles(const int *__restrict__ offsets, int E, int *s_st
     }
     if (tid == 0) s_start[0] = 0;
     __syncthreads();
-    if (tid < kWave) {
-        // one wave scans sequential segments of up to 16 entries per lane
-        const int per = (E + kWave - 1) / kWave;
-        const int lo = 1 + tid * per, hi = min(E + 1, lo + per);
-        int sum = 0;
-        for (int i = lo; i < hi; ++i) sum += s_start[i];
-        int incl = sum;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int v = __shfl_up(incl, off, kWave);
-            if (tid >= off) incl += v;
-        }
-        int run = incl - sum;
-        for (int i = lo; i < hi; ++i) {
-            run += s_start[i];
-            s_start[i] = run;
-        }
-    }
+    if (tid < kWave) wave_scan_shared(s_start, E, tid);
     __syncthreads();
 }
 

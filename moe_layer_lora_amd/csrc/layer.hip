@@ -1453,6 +1453,13 @@ struct LgOut {
         if (diag && h != (m >= mo)) return;
         (h ? o1 : o0)[(size_t)(h ? n - split : n) * sn + (size_t)(h ? m - mo : m) * sm] = v;
     }
+    // rows m .. m+3 of column n of an output laid out [n][m] (sm == 1, m a
+    // multiple of 4): one 16-byte store
+    __device__ __forceinline__ void store4m(int m, int n, f32x4_t v) const {
+        const bool h = n >= split;
+        if (diag && h != (m >= mo)) return;
+        *reinterpret_cast<f32x4_t *>((h ? o1 : o0) + (size_t)(h ? n - split : n) * sn + (h ? m - mo : m)) = v;
+    }
     // columns n .. n+3 (n a multiple of 4, as split is): one 16-byte store
     // where they are adjacent in memory ([m][n] outputs), four otherwise
     __device__ __forceinline__ void store4(int m, int n, f32x4_t v) const {
@@ -1567,8 +1574,8 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_lora_grad(LGradP p) {
 }
 
 // bf16 LoRA weight gradients, all modes in one launch. A block takes
-// (mode, expert, chunk of up to kLgRC of its rows, kLgNTB tiles of 256
-// columns of the big operand) and forms out^T[j][c] = sum_p SmallT[j][p]
+// (mode, expert, chunk of up to kLgRC of its rows, a group of lg_ntb tiles
+// of 256 columns of the big operand) and forms out^T[j][c] = sum_p SmallT[j][p]
 // Big[p][c] tile after tile (the chunk's row table and the tile scheduler's
 // work are shared by the block's tiles). Both
 // operands stream through a ring of direct loads, one 32-row step per stage:
@@ -1582,10 +1589,20 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void k_lora_grad(LGradP p) {
 constexpr int kLgRC = 1024;         // rows per chunk
 constexpr int kLgRows = kLgRC + 8;   // chunk rows plus the alignment lead-in
 constexpr int kLgBN = 256;           // big-operand columns per tile
-#ifndef MOE_LG_NTB
-#define MOE_LG_NTB 4
+#ifndef MOE_LG_ITEM
+#define MOE_LG_ITEM 2048
 #endif
-constexpr int kLgNTB = MOE_LG_NTB;   // column tiles per block (one ring, one row table)
+// Column tiles per block (one ring, one row table): about kLgItem / (rows of
+// the expert's chunks), at most kLgNTB, so that the blocks' costs stay close
+// whatever the routing: an expert of ~500 rows takes 4 tiles a block, the
+// full 1024-row chunks of a large expert 2.
+constexpr int kLgNTB = 4;
+constexpr int kLgItem = MOE_LG_ITEM;
+__host__ __device__ constexpr int lg_ntb(int chunk_rows) {
+    const int t = (kLgItem + chunk_rows / 2) / chunk_rows;
+    return t < 1 ? 1 : (t > kLgNTB ? kLgNTB : t);
+}
+constexpr int kLgNTBMin = lg_ntb(kLgRC);  // chunks hold at most kLgRC rows
 
 template <int NR> struct LgRing {
     static constexpr int NSTAGE = NR <= 32 ? 4 : 3;
@@ -1596,21 +1613,29 @@ template <int NR> struct LgRing {
     static constexpr int LOADS = 4 + SMALL_INSTR;        // direct loads per wave per step
 };
 
-template <int NR> struct LgSmem {
-    union {  // the tile scheduler's table is dead once the ring starts
-        __align__(16) char ring[LgRing<NR>::NSTAGE * LgRing<NR>::STAGE];
-        int start[kMaxE + 1];
-    };
-    uint32_t rowoff[kLgRows];  // byte offset of each step row in Big (kInvalid outside the chunk)
-};
-
 // Slices of the four modes in one launch: a slice covers NR columns j of a
 // mode's small operand (nr up to 2r = 512 takes several slices).
 constexpr int kLgMaxSlices = 24;
 constexpr int kLgSliceMax = 64;  // columns per slice of the NR = 64 kernel (NR = 32 slices take nr <= 32)
+
+// the work-item scheduler's tables (LDS)
+struct LgSched {
+    int item[kMaxE + 1];   // first work item of each expert in the block's slice
+    int chunk[kMaxE + 1];  // first chunk of each expert (over all experts)
+    int ntb[kMaxE];        // column tiles per item of each expert
+    int tot[kLgMaxSlices]; // items of each slice
+};
+
+template <int NR> struct LgSmem {
+    union {  // the scheduler's tables are dead once the ring starts
+        __align__(16) char ring[LgRing<NR>::NSTAGE * LgRing<NR>::STAGE];
+        LgSched sch;
+    };
+    uint32_t rowoff[kLgRows];  // byte offset of each step row in Big (kInvalid outside the chunk)
+};
+
 struct LGradSet {
     LGradP m[kLgMaxSlices];
-    int base[kLgMaxSlices];  // first block of each slice (multiples of 8: the tile scheduler's XCD map)
     int n;
 };
 
@@ -1689,25 +1714,81 @@ __device__ __forceinline__ void lg_iter(const LGradP &p, int p0, const uint32_t 
     }
 }
 
+// Work item of block b. A slice's items are (expert e, group of column
+// tiles, chunk of up to kLgRC rows of e), ordered expert-major, then group,
+// then chunk; the slices' items follow one another in slice order and the
+// blocks past them have no work, so they come last in dispatch order. Items
+// run on XCD b mod 8, so each XCD takes every eighth item: items differ in
+// cost (tail chunks, groups of fewer tiles), and the items of one chunk read
+// disjoint columns of the big operand, so an even spread matters and L2
+// locality does not. Sets mi (the slice), tl.e, tl.nt (the group), tl.mt
+// (the chunk within e), tl.row0, tl.rows, tl.gmt (the chunk over all
+// experts) and ntb (tiles per item of e). Returns false if the block has no
+// work; ends with every thread past the tables' last read.
+__device__ bool lg_schedule(const LGradSet &set, int b, LgSched &sc, int &mi, Tile &tl, int &ntb) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int *__restrict__ offsets = set.m[0].offsets;  // the slices share the routing
+    const int E = set.m[0].E;
+    for (int e = tid; e < E; e += 256) {
+        const int n = offsets[e + 1] - offsets[e];
+        sc.chunk[e + 1] = (n + kLgRC - 1) / kLgRC;
+        sc.ntb[e] = n > 0 ? lg_ntb(min(n, kLgRC)) : 1;
+    }
+    if (tid == 0) sc.chunk[0] = 0;
+    __syncthreads();
+    for (int m = wave; m < set.n; m += 4) {  // items of each slice, one wave a slice
+        const int ntn = cdiv(set.m[m].D, kLgBN);
+        int t = 0;
+        for (int e = lane; e < E; e += kWave) t += sc.chunk[e + 1] * cdiv(ntn, sc.ntb[e]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, kWave);
+        if (lane == 0) sc.tot[m] = t;
+    }
+    __syncthreads();
+    int s = 0, base = 0;
+    while (s < set.n && b >= base + sc.tot[s]) base += sc.tot[s++];
+    if (s == set.n) return false;  // the same in every thread
+    mi = __builtin_amdgcn_readfirstlane(s);
+    const int item = b - base, ntn = cdiv(set.m[mi].D, kLgBN);
+    for (int e = tid; e < E; e += 256) sc.item[e + 1] = sc.chunk[e + 1] * cdiv(ntn, sc.ntb[e]);
+    if (tid == 0) sc.item[0] = 0;
+    __syncthreads();
+    if (tid < kWave) wave_scan_shared(sc.item, E, tid);
+    else if (tid < 2 * kWave) wave_scan_shared(sc.chunk, E, tid - kWave);
+    __syncthreads();
+    int lo = 0, hi = E;  // invariant: item[lo] <= item < item[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sc.item[mid] <= item) lo = mid; else hi = mid;
+    }
+    const int e = lo, nch = sc.chunk[e + 1] - sc.chunk[e], rem = item - sc.item[e];
+    tl.e = __builtin_amdgcn_readfirstlane(e);
+    tl.nt = __builtin_amdgcn_readfirstlane(rem / nch);
+    tl.mt = __builtin_amdgcn_readfirstlane(rem % nch);
+    tl.row0 = __builtin_amdgcn_readfirstlane(offsets[e] + tl.mt * kLgRC);
+    tl.rows = __builtin_amdgcn_readfirstlane(min(kLgRC, offsets[e + 1] - tl.row0));
+    tl.gmt = __builtin_amdgcn_readfirstlane(sc.chunk[e] + tl.mt);
+    ntb = __builtin_amdgcn_readfirstlane(sc.ntb[e]);
+    __syncthreads();  // every thread has read the tables before the ring overwrites them
+    return true;
+}
+
 template <int NR>
 __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
     using R = LgRing<NR>;
     __shared__ LgSmem<NR> sm;
-    const int b = blockIdx.x;
-    int mi = 0;
-    while (mi + 1 < set.n && b >= set.base[mi + 1]) ++mi;  // uniform
+    Tile tl;
+    int mi, ntb;
+    if (!lg_schedule(set, blockIdx.x, sm.sch, mi, tl, ntb)) return;
     const LGradP &p = set.m[mi];
     const int ntn = cdiv(p.D, kLgBN);
-    Tile tl;
-    if (!schedule_tile<kLgRC, 256>(p.offsets, p.E, cdiv(ntn, kLgNTB), b - set.base[mi], sm.start, tl)) return;
-    __syncthreads();  // every thread has read the scheduler table before the ring overwrites it
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool gather = p.mode == 0 || p.mode == 3;
     // the block's column tiles nt0 .. nt0 + ntiles - 1, one after the other
     // through one ring (the next tile's loads are in flight while a tile's
     // results are stored)
-    const int nt0 = tl.nt * kLgNTB, ntiles = min(kLgNTB, ntn - nt0);
+    const int nt0 = tl.nt * ntb, ntiles = min(ntb, ntn - nt0);
     // steps start at p0, the chunk's first row rounded down to a multiple of
     // 8, so SmallT columns load as aligned 16-byte chunks; the lead-in rows
     // (previous expert) load as zeros on the big side
@@ -1786,8 +1867,14 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
                         const int m = c_base + cl;
                         const f32x4_t v{acc[mi2][ni][4 * q], acc[mi2][ni][4 * q + 1], acc[mi2][ni][4 * q + 2],
                                         acc[mi2][ni][4 * q + 3]};
-                        if (single) dst.store4(m, j, p.s * v);
-                        else *reinterpret_cast<f32x4_t *>(p.partial + ((size_t)tl.gmt * p.D + m) * p.nr + j) = v;
+                        if (single) {
+                            dst.store4(m, j, p.s * v);
+                        } else if (!dst.diag || (j >= dst.split) == (m >= dst.mo)) {
+                            // [chunk][j][m]: lanes of consecutive m store 128-byte
+                            // runs (the off-diagonal blocks of mode 1 are dropped)
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) p.partial[((size_t)tl.gmt * p.nr + j + u) * p.D + m] = v[u];
+                        }
                     }
                 }
 #pragma unroll
@@ -1797,30 +1884,102 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
     lds::wait_vm<0>();  // the zero loads of the last steps
 }
 
-// Finalize of the bf16 path: kLgFinSplit blocks per (expert, mode). Experts
-// with one chunk were written by the gradient kernel and exit at once; empty
-// experts get exact zeros, multi-chunk experts the chunk-ordered sums.
-constexpr int kLgFinSplit = 16;  // finalize blocks per (expert, mode)
+// Finalize of the bf16 path. A unit is (expert, kLgFinM columns m of the
+// big operand); block g of a slice takes units g, g + gridDim.x, ... Units
+// of experts with one chunk were written by the gradient kernel and are
+// skipped, empty experts get exact zeros, multi-chunk experts the
+// chunk-ordered sums of their [chunk][j][m] fp32 partials: a thread sums
+// four consecutive m of one j with 16-byte loads, eight chunks' loads in
+// flight at a time. Outputs laid out [j][m] take 16-byte stores from
+// there; outputs laid out [m][j] go through an LDS transpose so that their
+// stores are whole lines too.
+#ifndef MOE_LG_FIN_BLOCKS
+#define MOE_LG_FIN_BLOCKS 512
+#endif
+constexpr int kLgFinM = 64;                        // m per unit
+constexpr int kLgFinBlocks = MOE_LG_FIN_BLOCKS;  // blocks per slice
 
 __global__ __launch_bounds__(256) void k_lgrad_finalize(LGradSet set) {
-    __shared__ int s_start[kMaxE + 1];
-    const int mi = blockIdx.y;
-    const LGradP &p = set.m[mi];
-    const int e = blockIdx.x / kLgFinSplit, part = blockIdx.x % kLgFinSplit;
-    const int ne = p.offsets[e + 1] - p.offsets[e];
-    if (ne > 0 && ne <= kLgRC) return;
-    for (int x = threadIdx.x; x < p.E; x += 256) s_start[x] = (p.offsets[x + 1] - p.offsets[x] + kLgRC - 1) / kLgRC;
+    __shared__ int s_chunk[kMaxE + 1];  // first chunk of each expert
+    __shared__ float s_t[kLgSliceMax][kLgFinM + 1];
+    const LGradP &p = set.m[blockIdx.y];
+    const int tid = threadIdx.x;
+    constexpr int M4 = kLgFinM / 4;
+    const int ntm = cdiv(p.D, kLgFinM), ns = min(p.nr - p.j0, kLgSliceMax);
+    {  // leave at once if every unit of the block belongs to an expert of one chunk
+        bool need = false;
+        for (int u = blockIdx.x + tid * gridDim.x; u < p.E * ntm; u += 256 * gridDim.x) {
+            const int n = p.offsets[u / ntm + 1] - p.offsets[u / ntm];
+            need = need || n == 0 || n > kLgRC;
+        }
+        if (!__syncthreads_or(need)) return;
+    }
+    for (int e = tid; e < p.E; e += 256) s_chunk[e + 1] = cdiv(p.offsets[e + 1] - p.offsets[e], kLgRC);
+    if (tid == 0) s_chunk[0] = 0;
     __syncthreads();
-    int c0 = 0;
-    for (int x = 0; x < e; ++x) c0 += s_start[x];
-    const int nch = s_start[e];
-    const int ns = min(p.nr - p.j0, kLgSliceMax);
-    const LgOut dst(p, e);
-    for (int idx = part * 256 + threadIdx.x; idx < p.D * ns; idx += 256 * kLgFinSplit) {
-        const int m = idx / ns, n = p.j0 + idx % ns;
-        float v = 0.0f;
-        for (int c = 0; c < nch; ++c) v += p.partial[((size_t)(c0 + c) * p.D + m) * p.nr + n];
-        dst.store(m, n, p.s * v);
+    if (tid < kWave) wave_scan_shared(s_chunk, p.E, tid);
+    __syncthreads();
+    const size_t cs4 = (size_t)p.nr * p.D / 4;  // chunk stride of the partials in 16-byte units
+    for (int u = blockIdx.x; u < p.E * ntm; u += gridDim.x) {
+        const int e = u / ntm, m0 = (u - e * ntm) * kLgFinM;
+        const int c0 = s_chunk[e], nch = s_chunk[e + 1] - c0;
+        if (nch == 1) continue;  // uniform per block
+        const LgOut dst(p, e);
+        const bool mrow = dst.sn == 1;  // output [m][j]
+        if (nch == 0) {  // no rows: exact zeros, stored in the output's own order
+            for (int i = tid; i < ns * kLgFinM; i += 256) {
+                const int a = mrow ? i / ns : i % kLgFinM, n = mrow ? i - a * ns : i / kLgFinM, m = m0 + a;
+                if (m < p.D) dst.store(m, p.j0 + n, 0.0f);
+            }
+            continue;
+        }
+        for (int i = tid; i < ns * M4; i += 256) {
+            const int n = i / M4, ml = (i - n * M4) * 4, m = m0 + ml, j = p.j0 + n;
+            // D is a multiple of 8 and so are split and mo: the four m share a fate
+            const bool live = m < p.D && (!dst.diag || (j >= dst.split) == (m >= dst.mo));
+            f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (live) {
+                const f32x4_t *src = reinterpret_cast<const f32x4_t *>(p.partial + ((size_t)c0 * p.nr + j) * p.D + m);
+                int c = 0;
+                for (; c + 8 <= nch; c += 8) {
+                    f32x4_t a[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) a[q] = src[(size_t)(c + q) * cs4];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) v += a[q];  // chunk order
+                }
+                if (c + 4 <= nch) {
+                    f32x4_t a[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) a[q] = src[(size_t)(c + q) * cs4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v += a[q];
+                    c += 4;
+                }
+                for (; c < nch; ++c) v += src[(size_t)c * cs4];
+            }
+            v = p.s * v;
+            if (mrow) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) s_t[n][ml + q] = v[q];
+            } else if (live) {
+                dst.store4m(m, j, v);
+            }
+        }
+        if (mrow) {
+            // LDS-only barriers: the global stores need not land before the
+            // next unit, so the waves do not wait for them
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            for (int i = tid; i < ns * kLgFinM; i += 256) {
+                const int ml = i / ns, n = i - ml * ns, m = m0 + ml;
+                if (m < p.D) dst.store(m, p.j0 + n, s_t[n][ml]);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();  // the tile is read before the next unit overwrites it
+            asm volatile("" ::: "memory");
+        }
     }
 }
 
@@ -2004,7 +2163,7 @@ static hipError_t launch_lgrad_f32(const Dims &D, const LGradP &lp, hipStream_t 
 template <int NR>
 static hipError_t launch_lgrad_set(const Dims &D, const LGradP (&lp)[4], hipStream_t st) {
     LGradSet set{};
-    int grid = 0;
+    int grid = 0;  // the most items the slices can have together
     for (int m = 0; m < 4; ++m) {
         const bool mine = NR == 32 ? lp[m].nr <= 32 : lp[m].nr > 32;
         if (!mine) continue;
@@ -2012,14 +2171,13 @@ static hipError_t launch_lgrad_set(const Dims &D, const LGradP (&lp)[4], hipStre
             if (set.n == kLgMaxSlices) return hipErrorInvalidValue;
             set.m[set.n] = lp[m];
             set.m[set.n].j0 = j0;
-            set.base[set.n] = grid;
             ++set.n;
-            grid += (max_row_tiles(D.S(), D.E, kLgRC) * cdiv(cdiv(lp[m].D, kLgBN), kLgNTB) + 7) & ~7;
+            grid += max_row_tiles(D.S(), D.E, kLgRC) * cdiv(cdiv(lp[m].D, kLgBN), kLgNTBMin);
         }
     }
     if (set.n == 0) return hipSuccess;
     MOE_LAUNCH(k_lgrad<NR>, grid, 256, set);
-    k_lgrad_finalize<<<dim3(D.E * kLgFinSplit, set.n), dim3(256), 0, st>>>(set);
+    k_lgrad_finalize<<<dim3(kLgFinBlocks, set.n), dim3(256), 0, st>>>(set);
     return hipGetLastError();
 }
 
