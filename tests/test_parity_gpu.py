@@ -225,6 +225,43 @@ def test_shape_sweep(name):
             check(f"{g}[{e}]", r[g][e], b[g][e], tol, name)
 
 
+# Row counts on both sides of every boundary of the LoRA-gradient kernel's
+# work items: one chunk holds up to 1024 rows, and an expert takes 4, 3 or 2
+# column tiles per item as its chunks hold up to 585, 586-819 or 820-1024
+# rows (about 2048 / rows). d = 1800 and 2F = 1680 leave ragged last column
+# tiles and groups of unequal size; r = 40 runs the gate/up modes as two
+# slices (64 + 16 columns) of the wide-rank kernel.
+ITEM_COUNTS = [0, 1, 585, 586, 587, 819, 820, 1024, 1025, 2049, 3000]
+
+
+@pytest.mark.parametrize("r", [16, 40])
+def test_lora_grad_item_boundaries(r):
+    from oracle import grouped
+    counts = np.array(ITEM_COUNTS)
+    T, E = int(counts.sum()), len(counts)
+    cfg = LayerConfig(f"items_r{r}", T=T, d=1800, E=E, k=1, F=840, r=r, dtype="bf16", alpha=2.0 * r,
+                      router_grad=True)
+    print(f"[items] {cfg}", flush=True)
+    inputs = synth.make_inputs(cfg, seed=6)
+    rs = np.random.RandomState(6)
+    assign = rs.permutation(np.repeat(np.arange(E), counts))
+    logits = 0.1 * rs.standard_normal((T, E)).astype(np.float32)
+    logits[np.arange(T), assign] += 10.0  # top-1 is the assigned expert
+    inputs["logits"] = np.ascontiguousarray(logits)
+    _, res = run_small(cfg, inputs)
+    rt = oracle.route(inputs["logits"], cfg.k)
+    assert np.array_equal(rt["counts"], counts)
+    check_routing(res, rt, cfg.name)
+    o = grouped.layer(oracle.Layer.from_config(cfg, inputs), rt, inputs["dout"], intermediates=True)
+    tol = TOL[cfg.dtype]
+    for n in ("out", "dx", "d_topk_w", "d_logits"):
+        check(n, res[n], o[n], tol, cfg.name)
+    for g in GRADS:
+        assert np.all(res[g][0] == 0.0), f"{g}: the empty expert must get exact zeros"
+        for e in range(1, E):
+            check(f"{g}[{e}] ({counts[e]} rows)", res[g][e], o[g][e], tol, cfg.name)
+
+
 def test_empty_batch():
     lr = _runner()
     cfg = LayerConfig("empty", T=0, d=64, E=4, k=2, F=64, r=8, dtype="bf16", alpha=16.0)
