@@ -1892,12 +1892,9 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
 // four consecutive m of one j with 16-byte loads, eight chunks' loads in
 // flight at a time. Outputs laid out [j][m] take 16-byte stores from
 // there; outputs laid out [m][j] go through an LDS transpose so that their
-// stores are whole lines too.
-#ifndef MOE_LG_FIN_BLOCKS
-#define MOE_LG_FIN_BLOCKS 512
-#endif
-constexpr int kLgFinM = 64;                        // m per unit
-constexpr int kLgFinBlocks = MOE_LG_FIN_BLOCKS;  // blocks per slice
+// stores are whole lines too. Empty experts' zeros are 16-byte stores.
+constexpr int kLgFinM = 64;        // m per unit
+constexpr int kLgFinBlocks = 512;  // blocks per slice
 
 __global__ __launch_bounds__(256) void k_lgrad_finalize(LGradSet set) {
     __shared__ int s_chunk[kMaxE + 1];  // first chunk of each expert
@@ -1926,10 +1923,16 @@ __global__ __launch_bounds__(256) void k_lgrad_finalize(LGradSet set) {
         if (nch == 1) continue;  // uniform per block
         const LgOut dst(p, e);
         const bool mrow = dst.sn == 1;  // output [m][j]
-        if (nch == 0) {  // no rows: exact zeros, stored in the output's own order
-            for (int i = tid; i < ns * kLgFinM; i += 256) {
-                const int a = mrow ? i / ns : i % kLgFinM, n = mrow ? i - a * ns : i / kLgFinM, m = m0 + a;
-                if (m < p.D) dst.store(m, p.j0 + n, 0.0f);
+        if (nch == 0) {  // no rows: exact zeros, 16-byte stores in the output's own order
+            const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int i = tid; i < ns * M4; i += 256) {
+                if (mrow) {  // four adjacent j of one m (ns, j0 and split are multiples of 4)
+                    const int ml = i / (ns / 4), m = m0 + ml;
+                    if (m < p.D) dst.store4(m, p.j0 + (i - ml * (ns / 4)) * 4, z);
+                } else {  // four adjacent m of one j (D is a multiple of 8)
+                    const int n = i / M4, m = m0 + (i - n * M4) * 4;
+                    if (m < p.D) dst.store4m(m, p.j0 + n, z);
+                }
             }
             continue;
         }
