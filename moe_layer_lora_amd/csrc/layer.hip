@@ -1891,8 +1891,9 @@ __global__ __launch_bounds__(256) void k_lgrad(LGradSet set) {
 // chunk-ordered sums of their [chunk][j][m] fp32 partials: a thread sums
 // four consecutive m of one j with 16-byte loads, eight chunks' loads in
 // flight at a time. Outputs laid out [j][m] take 16-byte stores from
-// there; outputs laid out [m][j] go through an LDS transpose so that their
-// stores are whole lines too. Empty experts' zeros are 16-byte stores.
+// there; outputs laid out [m][j] go through an LDS transpose and take
+// 16-byte stores of four adjacent j. Empty experts' zeros are 16-byte
+// stores too.
 constexpr int kLgFinM = 64;        // m per unit
 constexpr int kLgFinBlocks = 512;  // blocks per slice
 
@@ -1975,9 +1976,9 @@ __global__ __launch_bounds__(256) void k_lgrad_finalize(LGradSet set) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            for (int i = tid; i < ns * kLgFinM; i += 256) {
-                const int ml = i / ns, n = i - ml * ns, m = m0 + ml;
-                if (m < p.D) dst.store(m, p.j0 + n, s_t[n][ml]);
+            for (int i = tid; i < ns / 4 * kLgFinM; i += 256) {  // four adjacent j of one m
+                const int ml = i / (ns / 4), n = (i - ml * (ns / 4)) * 4, m = m0 + ml;
+                if (m < p.D) dst.store4(m, p.j0 + n, f32x4_t{s_t[n][ml], s_t[n + 1][ml], s_t[n + 2][ml], s_t[n + 3][ml]});
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();  // the tile is read before the next unit overwrites it
