@@ -262,6 +262,35 @@ def test_lora_grad_item_boundaries(r):
             check(f"{g}[{e}] ({counts[e]} rows)", res[g][e], o[g][e], tol, cfg.name)
 
 
+def test_max_experts_skewed():
+    """The largest expert count (E = 1024) under a strong skew. 1004 experts
+    are empty, eight hold more than one 1024-row chunk (up to every token),
+    and the rest hold 136 to 1123 rows, so the LoRA-gradient kernel's
+    scheduler tables and the finalize's scans run at their full length with
+    every tiles-per-item class. Whole tensors; every non-empty expert's
+    gradients are checked on their own, and the empty ones must be exact
+    zeros."""
+    from oracle import grouped
+    cfg = LayerConfig("max_experts", T=2048, d=128, E=1024, k=8, F=64, r=16, dtype="bf16", alpha=32.0,
+                      router_grad=True, skew_bias=4.0)
+    print(f"[max experts] {cfg}", flush=True)
+    inputs = synth.make_inputs(cfg, seed=3)
+    _, r = run_small(cfg, inputs)
+    rt = oracle.route(inputs["logits"], cfg.k)
+    check_routing(r, rt, cfg.name)
+    counts = rt["counts"]
+    assert (counts == 0).sum() > 900 and (counts > 1024).sum() >= 4
+    o = grouped.layer(oracle.Layer.from_config(cfg, inputs), rt, inputs["dout"], intermediates=True)
+    tol = TOL[cfg.dtype]
+    for n in ("out", "dx", "G", "U", "H", "Y", "dXp", "d_topk_w", "d_logits"):
+        check(n, r[n], o[n], tol, cfg.name)
+    empty = counts == 0
+    for g in GRADS:
+        assert np.all(r[g][empty] == 0.0), f"{g}: empty experts must get exact zeros"
+        for e in np.nonzero(~empty)[0]:
+            check(f"{g}[{e}] ({counts[e]} rows)", r[g][e], o[g][e], tol, cfg.name)
+
+
 def test_empty_batch():
     lr = _runner()
     cfg = LayerConfig("empty", T=0, d=64, E=4, k=2, F=64, r=8, dtype="bf16", alpha=16.0)
