@@ -176,8 +176,11 @@ size_t moe_saved_host_bytes(const moe_problem_t *pb, int keep_expert_out);
 
 /* Routing. logits [T,E] float32 -> rt (all six arrays written).
  * host_counts: (host) int32[E] that receives counts, or NULL: the one
- * device->host crossing of the layer, a copy enqueued on `stream` after the
- * routing kernels. With pinned (page-locked) host memory the call returns
+ * device->host crossing of the layer, in stream order after the routing.
+ * Pinned (page-locked) memory that the device reaches at its host address
+ * (as hipHostMalloc memory is) is written by the routing's scan kernel
+ * itself; other host memory by a copy enqueued on `stream` after the
+ * routing kernels. With pinned host memory the call returns
  * at once and host_counts is valid once the stream has passed this point
  * (synchronise the stream or an event recorded after the call); with
  * pageable memory the runtime finishes the copy, and so waits for the

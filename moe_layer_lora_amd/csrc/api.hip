@@ -263,6 +263,21 @@ moe_status_t route_impl(const moe_problem_t *pb, const float *logits, const moe_
     const moe::Trace tr = to_trace(trace);
     int32_t *hist = reinterpret_cast<int32_t *>(at(ws, w.hist));
     int32_t *base = reinterpret_cast<int32_t *>(at(ws, w.base));
+    // The one device->host crossing. Page-locked memory that the device
+    // reaches at its host address (the usual case for hipHostMalloc) takes
+    // the counts from the scan kernel's own stores, so no copy is enqueued;
+    // other host memory gets a copy after the routing kernels (asynchronous
+    // for page-locked memory; the runtime completes a copy to pageable
+    // memory before returning).
+    int32_t *mapped_counts = nullptr;
+    if (host_counts) {
+        hipPointerAttribute_t pa{};
+        if (hipPointerGetAttributes(&pa, host_counts) == hipSuccess) {
+            if (pa.type == hipMemoryTypeHost && pa.devicePointer == host_counts) mapped_counts = host_counts;
+        } else {
+            (void)hipGetLastError();  // pageable memory: not an error
+        }
+    }
     hipError_t e;
     {
         Rec r(&tr, MOE_K_ROUTE_TOPK, s);
@@ -271,7 +286,7 @@ moe_status_t route_impl(const moe_problem_t *pb, const float *logits, const moe_
     if (e != hipSuccess) return MOE_E_HIP;
     {
         Rec r(&tr, MOE_K_ROUTE_SCAN, s);
-        e = moe::launch_route_scan(hist, pb->T, pb->E, pb->k, base, rt->counts, rt->offsets, s);
+        e = moe::launch_route_scan(hist, pb->T, pb->E, pb->k, base, rt->counts, rt->offsets, mapped_counts, s);
     }
     if (e != hipSuccess) return MOE_E_HIP;
     {
@@ -279,11 +294,9 @@ moe_status_t route_impl(const moe_problem_t *pb, const float *logits, const moe_
         e = moe::launch_route_scatter(rt->topk_idx, base, pb->T, pb->E, pb->k, rt->sorted_slot, rt->slot_row, s);
     }
     if (e != hipSuccess) return MOE_E_HIP;
-    // the one device->host copy, in stream order (asynchronous for pinned
-    // host memory; the runtime completes a copy to pageable memory before
-    // returning)
-    if (host_counts && hipMemcpyAsync(host_counts, rt->counts, (size_t)pb->E * sizeof(int32_t),
-                                      hipMemcpyDeviceToHost, s) != hipSuccess)
+    if (host_counts && !mapped_counts &&
+        hipMemcpyAsync(host_counts, rt->counts, (size_t)pb->E * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+            hipSuccess)
         return MOE_E_HIP;
     return MOE_OK;
 }

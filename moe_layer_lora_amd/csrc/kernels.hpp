@@ -34,8 +34,10 @@ inline int route_nblk(int T, int E) {
 }
 hipError_t launch_route_topk(const float *logits, int T, int E, int k, int32_t *topk_idx, float *topk_w,
                              int32_t *hist, hipStream_t st);
+// host_counts: null, or page-locked host memory the device reaches at the
+// same address (the scan stores the counts there)
 hipError_t launch_route_scan(const int32_t *hist, int T, int E, int k, int32_t *base, int32_t *counts,
-                             int32_t *offsets, hipStream_t st);
+                             int32_t *offsets, int32_t *host_counts, hipStream_t st);
 hipError_t launch_route_scatter(const int32_t *topk_idx, const int32_t *base, int T, int E, int k,
                                 int32_t *sorted_slot, int32_t *slot_row, hipStream_t st);
 

@@ -159,10 +159,12 @@ __device__ int block_excl_scan_1024(int v, int *s_wsum) {
 
 // Scan of the block-major [nblk x E] histogram. Thread (g, e) owns expert e
 // over the g-th range of token blocks; per-column passes are coalesced across
-// the lanes (consecutive experts).
+// the lanes (consecutive experts). host_counts, if not null, is page-locked
+// host memory mapped for the device at its host address: the counts are
+// stored there too (vector stores over the bus), in place of a copy.
 __global__ __launch_bounds__(1024) void k_route_scan(const int32_t *__restrict__ hist, int E, int nblk, int S,
                                                      int32_t *__restrict__ base, int32_t *__restrict__ counts,
-                                                     int32_t *__restrict__ offsets) {
+                                                     int32_t *__restrict__ offsets, int32_t *__restrict__ host_counts) {
     __shared__ int s_wsum[16];
     __shared__ int s_part[1024];
     const int tid = threadIdx.x;
@@ -185,6 +187,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(const int32_t *__restrict__
     if (tid < E) {
         counts[tid] = c;
         offsets[tid] = off;
+        if (host_counts) host_counts[tid] = c;
     }
     if (tid == 0) offsets[E] = S;
     // bases: offset of e plus the counts of e in earlier blocks
@@ -273,9 +276,10 @@ hipError_t launch_route_topk(const float *logits, int T, int E, int k, int32_t *
 }
 
 hipError_t launch_route_scan(const int32_t *hist, int T, int E, int k, int32_t *base, int32_t *counts,
-                             int32_t *offsets, hipStream_t st) {
+                             int32_t *offsets, int32_t *host_counts, hipStream_t st) {
     const int nblk = route_nblk(T, E);
-    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, hist, E, nblk, T * k, base, counts, offsets);
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, hist, E, nblk, T * k, base, counts, offsets,
+                       host_counts);
     return hipGetLastError();
 }
 

@@ -302,10 +302,12 @@ def test_empty_batch():
         g.fill_(7.0)
     hc = np.full(cfg.E, -1, np.int32)
     L.route(host_counts=hc)
+    hp = torch.full((cfg.E,), -1, dtype=torch.int32, pin_memory=True)
+    L.route(host_counts=hp)
     L.fwd()
     L.bwd(router_grad=True)
     torch.cuda.synchronize()
-    assert np.all(hc == 0)
+    assert np.all(hc == 0) and torch.all(hp == 0)
     assert L.rt["offsets"].cpu().numpy().tolist() == [0] * (cfg.E + 1)
     for g in L.grads.values():
         assert torch.all(g == 0.0)
@@ -322,11 +324,18 @@ def test_host_counts_readback_and_determinism():
     L.bwd(router_grad=True)
     r1 = L.results(router_grad=True, intermediates=True)
     assert np.array_equal(hc, oracle.route(inputs["logits"], cfg.k)["counts"])
-    # pinned host memory: the copy is asynchronous, valid after a stream sync
+    # pinned host memory: written in stream order (by the scan kernel itself
+    # when the device reaches it at its host address), valid after a sync
     hp = torch.zeros(cfg.E, dtype=torch.int32, pin_memory=True)
     L.route(host_counts=hp)
     torch.cuda.synchronize()
     assert np.array_equal(hp.numpy(), hc)
+    # an interior pointer of a larger pinned buffer: only its E entries change
+    big = torch.full((cfg.E + 8,), -1, dtype=torch.int32, pin_memory=True)
+    L.route(host_counts=big[4:4 + cfg.E])
+    torch.cuda.synchronize()
+    assert np.array_equal(big[4:4 + cfg.E].numpy(), hc)
+    assert torch.all(big[:4] == -1) and torch.all(big[4 + cfg.E:] == -1)
     L.step(backward=True, router_grad=True)
     r2 = L.results(router_grad=True, intermediates=True)
     for n in r1:
